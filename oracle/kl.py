@@ -1,0 +1,51 @@
+"""Predicted-KL reduction q(D) and the step controller (TEST INFRASTRUCTURE ONLY).
+
+[LoGRA] PKL: before an update is applied, the method estimates how much it
+would change next-token probabilities.  It takes a small sample of responses
+from the current batch and compares, at one common temperature, the model's
+current vocabulary distribution with the distribution after the proposed
+update.  The predicted change is quadratic in the step: the mean predicted KL
+scales as alpha^2 q(D), so halving alpha divides it by four.  For a KL budget
+delta the controller sets alpha = min(alpha_max, sqrt(delta / q(D))); with
+q(D) = 4 delta the proposal is at most halved, and alpha_max stops tiny
+predicted KLs from blowing the step up.  The budget may be constant or
+annealed downward.
+
+Readings where the pages leave a step open:
+  * q(D) is the mean over the sampled token positions (rows) of the forward
+    KL(p_cur || p_prop), p = softmax(z / tau), with p_prop the alpha = 1
+    proposal; every row has equal weight.
+  * controller edges: q = 0 or q < 0 (rounding) gives alpha_max; a NaN q
+    gives a NaN alpha.
+All arithmetic is fp64.
+"""
+import numpy as np
+
+
+def log_softmax(a):
+    """Row-wise log softmax of a 2-D fp64 array."""
+    a = np.asarray(a, np.float64)
+    m = a.max(axis=1, keepdims=True)
+    return a - m - np.log(np.exp(a - m).sum(axis=1, keepdims=True))
+
+
+def kl_rows(z_cur, z_prop, tau):
+    """Per-row forward KL(softmax(z_cur/tau) || softmax(z_prop/tau))."""
+    lp = log_softmax(np.asarray(z_cur, np.float64) / tau)
+    lq = log_softmax(np.asarray(z_prop, np.float64) / tau)
+    return (np.exp(lp) * (lp - lq)).sum(axis=1)
+
+
+def predicted_kl(z_cur, z_prop, tau):
+    """q(D): the mean per-row KL."""
+    return float(kl_rows(z_cur, z_prop, tau).mean())
+
+
+def step_size(q, kl_budget, alpha_max):
+    """alpha = min(alpha_max, sqrt(delta / q)) with the edge readings above."""
+    q = float(q)
+    if np.isnan(q):
+        return float("nan")
+    if q <= 0.0:
+        return float(alpha_max)
+    return float(min(float(alpha_max), np.sqrt(float(kl_budget) / q)))
