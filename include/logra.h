@@ -1,0 +1,180 @@
+/*
+ * logra.h - C ABI of the LoGRA low-rank gradient-sketching hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources cited below:
+ *   [LoGRA] wispaper.ai research summary of "LoGRA: Scaling LLM
+ *           Reinforcement Learning with Low-Rank Gradient Sketches";
+ *           sections Sketch (how the sketch replaces the full gradient
+ *           buffer), Sync (the same sketch also compresses policy sync),
+ *           PKL (predicted-KL control), Rank (projection rank vs. refresh).
+ *   [SALMON11] Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3",
+ *           SC'11 (Philox4x64-10).
+ *
+ * Notation: a linear layer computes Y = X W^T with W of shape d x k
+ * (d = out features, k = in features).  X (T x k) is the saved layer input
+ * and dY (T x d) the gradient of the layer output for one microbatch of T
+ * tokens.  G = dY^T X is the d x k weight gradient, A the r x k projection,
+ * S = G A^T the d x r sketch.
+ *
+ * Conventions (every entry point):
+ *   - All matrices are row-major.  bf16 values are passed as uint16_t bit
+ *     patterns (IEEE-style bfloat16).  "ld" arguments are row strides in
+ *     elements; they must be >= the row length and a multiple of 8, and the
+ *     base pointer of a bf16 matrix must be 16-byte aligned.
+ *   - Buffers are device pointers owned by the caller.  The library never
+ *     allocates or frees device memory and keeps no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream);
+ *     scalar results are written to device memory, so no call synchronises.
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     call returns a negative status and enqueues nothing.
+ *   - NaN / Inf inside the data propagate; they are not errors.
+ *   - Calls that share an output buffer (S, W) must be ordered by the caller
+ *     (same stream or events).  Two concurrent calls must not share a
+ *     workspace.
+ */
+#ifndef LOGRA_H
+#define LOGRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOGRA_ABI_VERSION 1
+
+/* Status codes. */
+#define LOGRA_OK 0
+#define LOGRA_EINVAL (-1)     /* invalid argument: null pointer, bad size,
+                                 bad stride/alignment, bad kind, bad scalar */
+#define LOGRA_EWORKSPACE (-2) /* workspace missing or smaller than required */
+#define LOGRA_EHIP (-3)       /* a HIP launch failed (see logra_status_str) */
+
+/* Projection kinds ([LoGRA] Sketch, Rank). */
+#define LOGRA_RADEMACHER 0 /* iid signs scaled by 1/sqrt(r) (default basis) */
+#define LOGRA_GAUSSIAN 1   /* iid N(0, 1/r), stored as bf16 values */
+
+#define LOGRA_MAX_RANK 256
+
+/* Version of this ABI (LOGRA_ABI_VERSION). */
+int logra_abi_version(void);
+
+/* Static text for a status code.  For LOGRA_EHIP it also names the last HIP
+ * error seen by this thread.  Never returns NULL. */
+const char* logra_status_str(int status);
+
+/*
+ * logra_regen_A - materialise the projection A (r x k, fp32, row-major,
+ * contiguous) exactly as the sketch and merge kernels regenerate it.
+ * [LoGRA] Sketch: A is r x k, independent of the batch, fixed while S
+ * accumulates and never learned; its default entries are random signs scaled
+ * by 1/sqrt(r).  [LoGRA] Sync: the rollout side rebuilds A from the seed.
+ * [LoGRA] Rank: per-step refreshed and Gaussian bases are also studied.
+ *
+ * Generator: Philox4x64-10 [SALMON11] with key (seed, stream); `stream` is
+ * the refresh index (0 for a fixed basis).
+ *   Rademacher: counter (j >> 8, i, 0, 0); entry (i, j) takes bit (j & 63) of
+ *     output word ((j >> 6) & 3); a set bit gives -c, a clear bit +c, with
+ *     c = 1/sqrt(r) computed in double and rounded once to float.
+ *   Gaussian: counter (j >> 2, i, 1, 0); each output word w gives the uniform
+ *     u = (2 (w >> 41) + 1) 2^-24; Box-Muller on (u0, u1) gives columns 4q and
+ *     4q+1 (R cos, R sin with R = sqrt(-2 ln u0), angle 2 pi u1), (u2, u3)
+ *     gives 4q+2 and 4q+3; the entry is z / sqrt(r) rounded to bf16 (RNE),
+ *     written widened to float.
+ *
+ * A: device float[r * k].  1 <= r <= 256, k >= 1.  A must be 4-byte aligned.
+ * Returns LOGRA_OK, LOGRA_EINVAL or LOGRA_EHIP.
+ */
+int logra_regen_A(uint64_t seed, uint64_t stream, int kind, int32_t r,
+                  int64_t k, float* A, hipStream_t s);
+
+/* Bytes of workspace logra_sketch_accumulate needs for these sizes (either
+ * projection kind).  Returns 0 for invalid sizes. */
+size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r);
+
+/*
+ * logra_sketch_accumulate - S += dY^T (X A^T), one microbatch.
+ * [LoGRA] Sketch: each microbatch's contribution to S = G A^T is accumulated
+ * in fp32 by projecting the inputs of the weight-gradient product first and
+ * then multiplying with the backward derivatives, so the d x k gradient is
+ * never formed.  The contribution is added as is (no 1/n scaling; any loss
+ * scale is already inside dY).
+ *
+ * X:  device bf16[T x ldx], row-major, ldx >= k, ldx % 8 == 0, 16-B aligned.
+ * dY: device bf16[T x ldd], row-major, ldd >= d, ldd % 8 == 0, 16-B aligned.
+ * S:  device float[d x r], contiguous, in/out, 4-B aligned.
+ * seed, stream, kind: select A as in logra_regen_A.
+ * ws: device scratch of at least logra_sketch_ws_bytes(T, d, k, r) bytes,
+ *     256-B aligned, owned by the caller; its contents on entry do not
+ *     matter.  The result is deterministic (fixed summation order).
+ * T == 0 is a no-op (returns LOGRA_OK; pointers are not inspected).
+ * Constraints: d, k >= 1, T >= 0, 1 <= r <= 256, d, k, T < 2^31.
+ * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
+ */
+int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
+                            int64_t ldd, int64_t T, int64_t d, int64_t k,
+                            int32_t r, uint64_t seed, uint64_t stream, int kind,
+                            float* S, void* ws, size_t ws_bytes, hipStream_t s);
+
+/*
+ * logra_merge - W <- RNE_bf16(W - alpha * eta * S A), in place.
+ * [LoGRA] Sketch: the update is W <- W - alpha eta U A with U = S in the basic
+ * SGD variant, merged directly into the weights (no adapter branch).
+ * [LoGRA] Sync: the rollout engine applies the same merge to the received
+ * alpha*eta*U after rebuilding A from the seed (pass alpha*eta*U as S with
+ * alpha = eta = 1).
+ *
+ * The product S A is accumulated in fp32, scaled by (float)alpha *
+ * (float)eta (and by c for the sign basis) and subtracted from the fp32 value
+ * of W; the result is rounded once to bf16, ties to even.
+ *
+ * W: device bf16[d x ldw], in/out, ldw >= k, ldw % 8 == 0, 16-B aligned.
+ * S: device float[d x r], contiguous, 4-B aligned (read only).
+ * alpha, eta: finite.  Constraints as for logra_sketch_accumulate.
+ * Returns LOGRA_OK, LOGRA_EINVAL or LOGRA_EHIP.
+ */
+int logra_merge(uint16_t* W, int64_t ldw, const float* S, int64_t d, int64_t k,
+                int32_t r, uint64_t seed, uint64_t stream, int kind,
+                float alpha, float eta, hipStream_t s);
+
+/* Bytes of workspace logra_predicted_kl needs when kl_tok is NULL (0 when
+ * kl_tok is given).  Returns 0 for invalid sizes. */
+size_t logra_kl_ws_bytes(int64_t n_tok, int64_t vocab);
+
+/*
+ * logra_predicted_kl - q(D) and the step size alpha.
+ * [LoGRA] PKL: on a small sample of responses, the current and the proposed
+ * model's vocabulary distributions are compared at one common temperature;
+ * the mean predicted KL scales as alpha^2 q(D); for a KL budget delta the
+ * controller sets alpha = min(alpha_max, sqrt(delta / q(D))).
+ *
+ * Computed: for every row t (a sampled token position),
+ *   KL_t = KL(softmax(z_cur[t] / tau) || softmax(z_prop[t] / tau))
+ * (forward KL, z_prop = logits after the alpha = 1 proposal), in one pass
+ * over both rows; q = mean_t KL_t (equal weight per row);
+ * alpha = min(alpha_max, sqrt(kl_budget / q)); q <= 0 gives alpha_max; a NaN
+ * q gives a NaN alpha.
+ *
+ * z_cur, z_prop: device bf16[n_tok x ld], ld >= vocab, ld % 8 == 0, 16-B
+ *     aligned.
+ * q_alpha_out: device float[2] <- {q, alpha}.
+ * kl_tok: device float[n_tok] <- KL_t, or NULL.
+ * ws: device scratch of logra_kl_ws_bytes(n_tok, vocab) bytes (256-B
+ *     aligned) when kl_tok is NULL; ignored otherwise.
+ * tau > 0, kl_budget > 0, alpha_max >= 0, all finite; n_tok, vocab >= 1.
+ * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
+ */
+int logra_predicted_kl(const uint16_t* z_cur, const uint16_t* z_prop,
+                       int64_t n_tok, int64_t vocab, int64_t ld, float tau,
+                       float kl_budget, float alpha_max, float* q_alpha_out,
+                       float* kl_tok, void* ws, size_t ws_bytes, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGRA_H */

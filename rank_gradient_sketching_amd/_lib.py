@@ -1,0 +1,81 @@
+"""ctypes loader for liblogra.so (the HIP library built by build.py).
+
+The library must exist: there is no fallback of any kind.  Loading it does not
+touch the GPU, so CPU-only processes may load it to inspect symbols or drive
+argument validation.
+"""
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblogra.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "logra.h")
+
+_lib = None
+
+c_u16p = ctypes.c_void_p
+c_vp = ctypes.c_void_p
+
+SIGNATURES = {
+    "logra_abi_version": (ctypes.c_int, []),
+    "logra_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "logra_regen_A": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+                                     ctypes.c_int32, ctypes.c_int64, c_vp, c_vp]),
+    "logra_sketch_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_int32]),
+    "logra_sketch_accumulate": (ctypes.c_int, [c_vp, ctypes.c_int64, c_vp, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64,
+                                               ctypes.c_int, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "logra_merge": (ctypes.c_int, [c_vp, ctypes.c_int64, c_vp, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_float, c_vp]),
+    "logra_kl_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+    "logra_predicted_kl": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_float, c_vp, c_vp, c_vp, ctypes.c_size_t,
+                                          c_vp]),
+}
+
+OK, EINVAL, EWORKSPACE, EHIP = 0, -1, -2, -3
+
+
+class LograError(RuntimeError):
+    def __init__(self, status, name):
+        self.status = status
+        super().__init__(f"{name} failed with status {status}: {status_str(status)}")
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m rank_gradient_sketching_amd.build` (needs hipcc)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status):
+    return lib().logra_status_str(int(status)).decode()
+
+
+def check(status, name):
+    if status != OK:
+        raise LograError(status, name)
+
+
+def header_symbols(path=HEADER_PATH):
+    """Names of the functions include/logra.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(logra_[a-z_A-Z0-9]+)\s*\(", text)))

@@ -1,0 +1,135 @@
+"""Python binding of the LoGRA hot path: torch tensors -> liblogra C ABI.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels on the tensors' device, asynchronously on torch's current stream.
+Tensors must live on the GPU; nothing here falls back to the CPU.
+
+Names follow the pages' notation: X (T x k inputs), dY (T x d output
+gradients), S (d x r fp32 sketch), W (d x k bf16 weights), A (r x k
+projection), q and alpha of the predicted-KL controller.
+"""
+import torch
+
+from . import _lib
+
+RADEMACHER = 0
+GAUSSIAN = 1
+
+
+def _stream(t):
+    return ctypes_stream(torch.cuda.current_stream(t.device))
+
+
+def ctypes_stream(s):
+    return s.cuda_stream
+
+
+def _require(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
+
+
+def _rows(t, name):
+    """(rows, cols, row stride) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    rows, cols = t.shape
+    # a single row has no meaningful stride; any legal value reads the same bytes
+    ld = t.stride(0) if rows > 1 else -(-cols // 8) * 8
+    return rows, cols, ld
+
+
+def regen_A(seed, stream, kind, r, k, device="cuda", out=None):
+    """A (r x k fp32) exactly as the sketch and merge kernels regenerate it."""
+    if out is None:
+        out = torch.empty((r, k), dtype=torch.float32, device=device)
+    _require(out, "out", torch.float32, 2)
+    if not out.is_contiguous() or tuple(out.shape) != (r, k):
+        raise ValueError("out must be a contiguous (r, k) float32 tensor")
+    st = _lib.lib().logra_regen_A(seed, stream, kind, r, k, out.data_ptr(), _stream(out))
+    _lib.check(st, "logra_regen_A")
+    return out
+
+
+def sketch_ws_bytes(T, d, k, r):
+    return int(_lib.lib().logra_sketch_ws_bytes(T, d, k, r))
+
+
+def sketch_workspace(T, d, k, r, device="cuda"):
+    """A workspace tensor large enough for sketch_accumulate at these sizes."""
+    n = sketch_ws_bytes(T, d, k, r)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None):
+    """S += dY^T (X A^T) in place for one microbatch; returns S."""
+    _require(X, "X", torch.bfloat16, 2)
+    _require(dY, "dY", torch.bfloat16, 2)
+    _require(S, "S", torch.float32, 2)
+    T, k, ldx = _rows(X, "X")
+    T2, d, ldd = _rows(dY, "dY")
+    if T2 != T:
+        raise ValueError(f"X has {T} rows but dY has {T2}")
+    if S.shape[0] != d or not S.is_contiguous():
+        raise ValueError("S must be a contiguous (d, r) float32 tensor")
+    r = S.shape[1]
+    if ws is None:
+        ws = sketch_workspace(T, d, k, r, X.device)
+    st = _lib.lib().logra_sketch_accumulate(
+        X.data_ptr(), ldx, dY.data_ptr(), ldd, T, d, k, r, seed, stream, kind,
+        S.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(X))
+    _lib.check(st, "logra_sketch_accumulate")
+    return S
+
+
+def merge(W, S, seed, stream=0, kind=RADEMACHER, alpha=1.0, eta=1.0):
+    """W <- RNE_bf16(W - alpha * eta * S A) in place; returns W."""
+    _require(W, "W", torch.bfloat16, 2)
+    _require(S, "S", torch.float32, 2)
+    d, k, ldw = _rows(W, "W")
+    if S.shape[0] != d or not S.is_contiguous():
+        raise ValueError("S must be a contiguous (d, r) float32 tensor")
+    r = S.shape[1]
+    st = _lib.lib().logra_merge(W.data_ptr(), ldw, S.data_ptr(), d, k, r, seed, stream,
+                                kind, float(alpha), float(eta), _stream(W))
+    _lib.check(st, "logra_merge")
+    return W
+
+
+def kl_ws_bytes(n_tok, vocab):
+    return int(_lib.lib().logra_kl_ws_bytes(n_tok, vocab))
+
+
+def predicted_kl(z_cur, z_prop, tau, kl_budget, alpha_max, out=None, kl_tok=None, ws=None):
+    """Device tensor [q, alpha]; per-row KL goes to kl_tok when given."""
+    _require(z_cur, "z_cur", torch.bfloat16, 2)
+    _require(z_prop, "z_prop", torch.bfloat16, 2)
+    n, V, ld = _rows(z_cur, "z_cur")
+    n2, V2, ld2 = _rows(z_prop, "z_prop")
+    if (n2, V2, ld2) != (n, V, ld):
+        raise ValueError("z_cur and z_prop must have the same shape and row stride")
+    if out is None:
+        out = torch.empty(2, dtype=torch.float32, device=z_cur.device)
+    _require(out, "out", torch.float32, 1)
+    kl_ptr = None
+    if kl_tok is not None:
+        _require(kl_tok, "kl_tok", torch.float32, 1)
+        if kl_tok.numel() != n or not kl_tok.is_contiguous():
+            raise ValueError("kl_tok must be a contiguous float32 vector of n_tok entries")
+        kl_ptr = kl_tok.data_ptr()
+    ws_ptr, ws_n = None, 0
+    if kl_tok is None:
+        if ws is None:
+            ws = torch.empty(max(kl_ws_bytes(n, V), 256), dtype=torch.uint8, device=z_cur.device)
+        ws_ptr, ws_n = ws.data_ptr(), ws.numel() * ws.element_size()
+    st = _lib.lib().logra_predicted_kl(z_cur.data_ptr(), z_prop.data_ptr(), n, V, ld,
+                                       float(tau), float(kl_budget), float(alpha_max),
+                                       out.data_ptr(), kl_ptr, ws_ptr, ws_n, _stream(z_cur))
+    _lib.check(st, "logra_predicted_kl")
+    return out

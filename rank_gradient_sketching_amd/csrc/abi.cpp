@@ -1,0 +1,127 @@
+// C ABI of the LoGRA hot path (declared in include/logra.h).
+//
+// Every entry point validates all of its arguments on the host before the
+// first HIP call and returns a status code; nothing throws across the ABI.
+#include "logra.h"
+
+#include <math.h>
+#include <stdio.h>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return LOGRA_OK;
+  snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP error %d: %s", (int)e,
+           hipGetErrorString(e));
+  return LOGRA_EHIP;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+constexpr int64_t kDimLimit = int64_t(1) << 31;
+
+bool dim_ok(int64_t x) { return x >= 1 && x < kDimLimit; }
+bool rank_ok(int32_t r) { return r >= 1 && r <= LOGRA_MAX_RANK; }
+bool kind_ok(int kind) { return kind == LOGRA_RADEMACHER || kind == LOGRA_GAUSSIAN; }
+// Row stride of a bf16 matrix: >= row length, multiple of 8 (16-byte rows).
+bool ld_ok(int64_t ld, int64_t row) { return ld >= row && ld % 8 == 0 && ld < (int64_t(1) << 40); }
+
+}  // namespace
+
+extern "C" {
+
+int logra_abi_version(void) { return LOGRA_ABI_VERSION; }
+
+const char* logra_status_str(int status) {
+  switch (status) {
+    case LOGRA_OK:
+      return "ok";
+    case LOGRA_EINVAL:
+      return "invalid argument";
+    case LOGRA_EWORKSPACE:
+      return "workspace missing or too small";
+    case LOGRA_EHIP:
+      return g_hip_msg[0] ? g_hip_msg : "HIP error";
+    default:
+      return "unknown status";
+  }
+}
+
+int logra_regen_A(uint64_t seed, uint64_t stream, int kind, int32_t r,
+                  int64_t k, float* A, hipStream_t s) {
+  if (A == nullptr || !aligned(A, 4) || !rank_ok(r) || !dim_ok(k) || !kind_ok(kind))
+    return LOGRA_EINVAL;
+  return hip_status(logra::launch_regen(seed, stream, kind, r, k, A, s));
+}
+
+size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r) {
+  logra::SketchPlan p;
+  if (!logra::make_sketch_plan(T, d, k, r, &p)) return 0;
+  return p.total;
+}
+
+int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
+                            int64_t ldd, int64_t T, int64_t d, int64_t k,
+                            int32_t r, uint64_t seed, uint64_t stream, int kind,
+                            float* S, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dim_ok(d) || !dim_ok(k) || !rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
+  if (T < 0 || T >= kDimLimit) return LOGRA_EINVAL;
+  if (T == 0) return LOGRA_OK;
+  if (X == nullptr || dY == nullptr || S == nullptr) return LOGRA_EINVAL;
+  if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(S, 4)) return LOGRA_EINVAL;
+  if (!ld_ok(ldx, k) || !ld_ok(ldd, d)) return LOGRA_EINVAL;
+  logra::SketchPlan p;
+  if (!logra::make_sketch_plan(T, d, k, r, &p)) return LOGRA_EINVAL;
+  if (ws == nullptr || ws_bytes < p.total || !aligned(ws, 256)) return LOGRA_EWORKSPACE;
+  return hip_status(logra::launch_sketch(p, X, ldx, dY, ldd, (int)T, (int)d, (int)k,
+                                         r, seed, stream, kind, S,
+                                         static_cast<char*>(ws), s));
+}
+
+int logra_merge(uint16_t* W, int64_t ldw, const float* S, int64_t d, int64_t k,
+                int32_t r, uint64_t seed, uint64_t stream, int kind, float alpha,
+                float eta, hipStream_t s) {
+  if (W == nullptr || S == nullptr) return LOGRA_EINVAL;
+  if (!dim_ok(d) || !dim_ok(k) || !rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
+  if (!aligned(W, 16) || !aligned(S, 4) || !ld_ok(ldw, k)) return LOGRA_EINVAL;
+  if (!isfinite(alpha) || !isfinite(eta)) return LOGRA_EINVAL;
+  // one work-group per 256 x 256 tile, flat grid
+  if (((d + 255) / 256) * ((k + 255) / 256) >= (int64_t(1) << 31)) return LOGRA_EINVAL;
+  return hip_status(logra::launch_merge(W, ldw, S, (int)d, (int)k, r, seed, stream,
+                                        kind, alpha, eta, s));
+}
+
+size_t logra_kl_ws_bytes(int64_t n_tok, int64_t vocab) {
+  if (!dim_ok(n_tok) || !dim_ok(vocab)) return 0;
+  return (size_t)logra::round_up(n_tok * 4, 256);
+}
+
+int logra_predicted_kl(const uint16_t* z_cur, const uint16_t* z_prop,
+                       int64_t n_tok, int64_t vocab, int64_t ld, float tau,
+                       float kl_budget, float alpha_max, float* q_alpha_out,
+                       float* kl_tok, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (z_cur == nullptr || z_prop == nullptr || q_alpha_out == nullptr) return LOGRA_EINVAL;
+  if (!dim_ok(n_tok) || !dim_ok(vocab) || !ld_ok(ld, vocab)) return LOGRA_EINVAL;
+  if (!aligned(z_cur, 16) || !aligned(z_prop, 16) || !aligned(q_alpha_out, 4))
+    return LOGRA_EINVAL;
+  if (kl_tok != nullptr && !aligned(kl_tok, 4)) return LOGRA_EINVAL;
+  if (!isfinite(tau) || !(tau > 0.0f)) return LOGRA_EINVAL;
+  if (!isfinite(kl_budget) || !(kl_budget > 0.0f)) return LOGRA_EINVAL;
+  if (!isfinite(alpha_max) || !(alpha_max >= 0.0f)) return LOGRA_EINVAL;
+  float* rows = kl_tok;
+  if (rows == nullptr) {
+    if (ws == nullptr || ws_bytes < logra_kl_ws_bytes(n_tok, vocab) || !aligned(ws, 256))
+      return LOGRA_EWORKSPACE;
+    rows = static_cast<float*>(ws);
+  }
+  return hip_status(logra::launch_kl(z_cur, z_prop, (int)n_tok, (int)vocab, ld, tau,
+                                     kl_budget, alpha_max, q_alpha_out, rows, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+// Device helpers shared by the gfx950 kernels of the LoGRA hot path.
+//
+// Sources:
+//   [SALMON11] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+//              as 1, 2, 3", SC'11 - the Philox4x64 counter-based generator.
+//   [LoGRA]    wispaper.ai summary of "LoGRA: Scaling LLM Reinforcement
+//              Learning with Low-Rank Gradient Sketches", section Sketch: the
+//              default projection entries are random signs scaled by
+//              1/sqrt(r); section Sync: A is rebuilt from the seed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace logra {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- Philox
+// Philox4x64 with 10 rounds [SALMON11].  Each round multiplies words 0 and 2
+// by fixed odd constants to 128-bit products and mixes the halves with words
+// 1 and 3 and the key; the key advances by the Weyl increments between rounds.
+constexpr uint64_t kPhiloxMul0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxMul1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxWeyl0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxWeyl1 = 0xBB67AE8584CAA73Bull;
+
+struct Words4 {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ Words4 philox4x64_10(uint64_t c0, uint64_t c1,
+                                                uint64_t c2, uint64_t c3,
+                                                uint64_t k0, uint64_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round) {
+      k0 += kPhiloxWeyl0;
+      k1 += kPhiloxWeyl1;
+    }
+    const uint64_t hi0 = __umul64hi(kPhiloxMul0, c0);
+    const uint64_t lo0 = kPhiloxMul0 * c0;
+    const uint64_t hi1 = __umul64hi(kPhiloxMul1, c2);
+    const uint64_t lo1 = kPhiloxMul1 * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  Words4 out;
+  out.w[0] = c0;
+  out.w[1] = c1;
+  out.w[2] = c2;
+  out.w[3] = c3;
+  return out;
+}
+
+// Sign block of row i, 256-column group g of the sign basis: bit b of word q
+// is the sign of column 256 g + 64 q + b (set = negative).
+__device__ __forceinline__ Words4 sign_block(uint64_t seed, uint64_t stream,
+                                             uint64_t group, uint64_t row) {
+  return philox4x64_10(group, row, 0, 0, seed, stream);
+}
+
+// Gaussian block of row i, 4-column group q: four standard normals by
+// Box-Muller from the four output words (each gives a 24-bit uniform in (0,1)).
+__device__ __forceinline__ void gaussian_block(uint64_t seed, uint64_t stream,
+                                               uint64_t group, uint64_t row,
+                                               float z[4]) {
+  const Words4 b = philox4x64_10(group, row, 1, 0, seed, stream);
+  float u[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    // (2 (w >> 41) + 1) < 2^24, so both the integer and the scaling are exact.
+    u[a] = (float)(uint32_t)(((b.w[a] >> 41) << 1) | 1u) * 0x1.0p-24f;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const float rad = sqrtf(-2.0f * logf(u[2 * p]));
+    float sn, cs;
+    sincospif(2.0f * u[2 * p + 1], &sn, &cs);
+    z[2 * p] = rad * cs;
+    z[2 * p + 1] = rad * sn;
+  }
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __uint_as_float(w & 0xFFFF0000u);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), each rounded to nearest
+// even (gfx950 lowers this to v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Split x into hi + lo with hi = bf16(x) and lo = bf16(x - hi); the residual
+// x - hi is exact in fp32, so hi + lo carries about 16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  const __bf16 h = (__bf16)x;
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = f32_to_bf16(x - (float)h);
+}
+
+// Eight sign bits (bit e set = negative) -> eight bf16 +-1.0 values packed as
+// an MFMA operand (element 2p in the low half of dword p).  With
+// x = b | (b << 15), bit 2p of b sits at 2p and bit 2p+1 at 2p+16; shifting
+// left by 15 - 2p moves them to bits 15 and 31, the two bf16 sign positions.
+__device__ __forceinline__ u32x4 signs_to_bf16x8(uint32_t byte) {
+  const uint32_t x = byte | (byte << 15);
+  u32x4 v;
+  v[0] = ((x << 15) & 0x80008000u) | 0x3F803F80u;
+  v[1] = ((x << 13) & 0x80008000u) | 0x3F803F80u;
+  v[2] = ((x << 11) & 0x80008000u) | 0x3F803F80u;
+  v[3] = ((x << 9) & 0x80008000u) | 0x3F803F80u;
+  return v;
+}
+
+// Gaussian-basis entries of row i, columns 4q .. 4q+3: z * cr rounded to bf16
+// (cr = 1/sqrt(r) as float).  Every kernel that needs Gaussian entries calls
+// this one function, so they all see bit-identical values.
+__device__ __forceinline__ void gaussian_entries_bf16(uint64_t seed,
+                                                      uint64_t stream,
+                                                      uint64_t q, uint64_t row,
+                                                      float cr,
+                                                      uint16_t out[4]) {
+  float z[4];
+  gaussian_block(seed, stream, q, row, z);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) out[a] = f32_to_bf16(z[a] * cr);
+}
+
+// ---------------------------------------------------------------- MFMA
+// gfx950 bf16 matrix cores, fp32 accumulation.
+//   32x32x16: A row i = lane % 32, B column j = lane % 32; each lane supplies
+//             8 K-values; D lane holds column lane % 32, rows
+//             8 (v / 4) + 4 (lane / 32) + (v % 4) for v = 0..15.
+//   16x16x32: A row i = lane % 16, B column j = lane % 16; each lane supplies
+//             8 K-values; D lane holds column lane % 16, rows
+//             4 (lane / 16) + v for v = 0..3.
+// Which K index a (lane group, element) pair carries is irrelevant here:
+// every caller feeds A and B with the same K assignment.
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- loads
+// 8 bf16 starting at element `col` of a row of `ncols` valid elements; lanes
+// past the end read zeros.  Rows are 16-byte aligned (ld % 8 == 0), so a full
+// group is one 16-byte load.
+__device__ __forceinline__ u32x4 load_bf16x8(const uint16_t* row, int col,
+                                             int ncols) {
+  if (col + 8 <= ncols) {
+    return *reinterpret_cast<const u32x4*>(row + col);
+  }
+  u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (col + e < ncols) {
+      const uint32_t h = row[col + e];
+      v[e >> 1] |= (e & 1) ? (h << 16) : h;
+    }
+  }
+  return v;
+}
+
+}  // namespace logra

@@ -1,0 +1,196 @@
+// logra_predicted_kl: q(D) = mean_t KL(softmax(z_cur[t]/tau) || softmax(z_prop[t]/tau))
+// and the controller's alpha = min(alpha_max, sqrt(delta / q)), on gfx950.
+//
+// [LoGRA] (wispaper.ai summary of "LoGRA: Scaling LLM Reinforcement Learning
+// with Low-Rank Gradient Sketches"), section PKL: before applying an update
+// the method compares, on a small sample of responses and at one common
+// temperature, the current vocabulary distribution with the one after the
+// proposed update; the mean predicted KL scales as alpha^2 q(D) and the
+// controller sets alpha = min(alpha_max, sqrt(delta / q(D))).
+//
+// One pass over both logit rows, no second read.  With a = z/tau, d = (z' - z)/tau
+// and p = softmax(a):
+//   KL = log E_p[e^d] - E_p[d] = E_p[g] + (log1p(x) - x),
+//   g(d) = e^d - 1 - d >= 0,   x = E_p[e^d - 1] = E_p[d] + E_p[g].
+// Each thread keeps (m, s, u1, u3) = (running max of a in log2 units,
+// sum w, sum w d, sum w g) with w = 2^(a log2e - m); g comes from its Taylor
+// polynomial for |d| <= 1/2 (no cancellation) and from exp otherwise.  The
+// states merge by rescaling to the larger max (DPP/shuffle inside a wave,
+// LDS across waves).  Per-row KL goes to kl_tok (or the workspace); a second
+// one-work-group kernel averages the rows in a fixed order in fp64 and
+// applies the controller.
+#include <math.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace logra {
+
+namespace {
+
+constexpr int kKlThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct KlState {
+  float m, s, u1, u3;
+};
+
+__device__ __forceinline__ KlState kl_merge(KlState a, KlState b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return a;
+  const float fa = a.m == -INFINITY ? 0.0f : exp2f(a.m - M);
+  const float fb = b.m == -INFINITY ? 0.0f : exp2f(b.m - M);
+  KlState o;
+  o.m = M;
+  o.s = a.s * fa + b.s * fb;
+  o.u1 = a.u1 * fa + b.u1 * fb;
+  o.u3 = a.u3 * fa + b.u3 * fb;
+  return o;
+}
+
+// e^d - 1 - d.  For |d| <= 1/2 the Taylor series d^2 (1/2 + d/6 + d^2/24 +
+// d^3/120 + d^4/720 + d^5/5040) has relative truncation error below 4e-6.
+__device__ __forceinline__ float excess_exp(float d) {
+  float p = 1.0f / 5040.0f;
+  p = fmaf(p, d, 1.0f / 720.0f);
+  p = fmaf(p, d, 1.0f / 120.0f);
+  p = fmaf(p, d, 1.0f / 24.0f);
+  p = fmaf(p, d, 1.0f / 6.0f);
+  p = fmaf(p, d, 0.5f);
+  float g = d * d * p;
+  if (__builtin_expect(fabsf(d) > 0.5f, 0)) g = expf(d) - 1.0f - d;
+  return g;
+}
+
+// Adds n (<= 8) elements to the state; z and zq are bf16 pairs.
+__device__ __forceinline__ void kl_group(KlState& st, const float* z,
+                                         const float* zq, int n, float l2t,
+                                         float inv_tau) {
+  float a2[8], dd[8];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a2[e] = e < n ? z[e] * l2t : -INFINITY;
+    dd[e] = e < n ? (zq[e] - z[e]) * inv_tau : 0.0f;
+    cmax = fmaxf(cmax, a2[e]);
+  }
+  if (cmax > st.m) {
+    const float f = st.m == -INFINITY ? 0.0f : exp2f(st.m - cmax);
+    st.s *= f;
+    st.u1 *= f;
+    st.u3 *= f;
+    st.m = cmax;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < n) {
+      const float w = exp2f(a2[e] - st.m);
+      st.s += w;
+      st.u1 = fmaf(w, dd[e], st.u1);
+      st.u3 = fmaf(w, excess_exp(dd[e]), st.u3);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
+    const uint16_t* __restrict__ zc, const uint16_t* __restrict__ zp, int V,
+    int64_t ld, float inv_tau, float* __restrict__ kl_out) {
+  __shared__ KlState wst[kKlThreads / 64];
+  const int64_t row = blockIdx.x;
+  const uint16_t* a = zc + row * ld;
+  const uint16_t* b = zp + row * ld;
+  const float l2t = kLog2e * inv_tau;
+  KlState st{-INFINITY, 0.0f, 0.0f, 0.0f};
+  const int nfull = V >> 3;
+  for (int c = threadIdx.x; c < nfull; c += kKlThreads) {
+    const u32x4 va = *reinterpret_cast<const u32x4*>(a + 8 * c);
+    const u32x4 vb = *reinterpret_cast<const u32x4*>(b + 8 * c);
+    float z[8], zq[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      z[2 * p] = bf16_lo(va[p]);
+      z[2 * p + 1] = bf16_hi(va[p]);
+      zq[2 * p] = bf16_lo(vb[p]);
+      zq[2 * p + 1] = bf16_hi(vb[p]);
+    }
+    kl_group(st, z, zq, 8, l2t, inv_tau);
+  }
+  const int tail = V - 8 * nfull;
+  if (tail > 0 && threadIdx.x == (nfull % kKlThreads)) {
+    float z[8], zq[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      z[e] = e < tail ? bf16_to_f32(a[8 * nfull + e]) : 0.0f;
+      zq[e] = e < tail ? bf16_to_f32(b[8 * nfull + e]) : 0.0f;
+    }
+    kl_group(st, z, zq, tail, l2t, inv_tau);
+  }
+  // wave reduction (fixed butterfly), then the four waves in order
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    KlState o;
+    o.m = __shfl_xor(st.m, off);
+    o.s = __shfl_xor(st.s, off);
+    o.u1 = __shfl_xor(st.u1, off);
+    o.u3 = __shfl_xor(st.u3, off);
+    st = kl_merge(st, o);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) wst[wave] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    KlState t = wst[0];
+#pragma unroll
+    for (int w = 1; w < kKlThreads / 64; ++w) t = kl_merge(t, wst[w]);
+    const double s = t.s;
+    const double x = ((double)t.u1 + (double)t.u3) / s;
+    const double kl = (double)t.u3 / s + (log1p(x) - x);
+    kl_out[row] = (float)kl;
+  }
+}
+
+// Mean of n per-row KL values in a fixed order (fp64), then the controller.
+__global__ __launch_bounds__(1024) void kl_mean_kernel(const float* __restrict__ kl,
+                                                       int n, float kl_budget,
+                                                       float alpha_max,
+                                                       float* __restrict__ q_alpha) {
+  __shared__ double part[1024 / 64];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < n; i += 1024) acc += (double)kl[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int w = 0; w < 1024 / 64; ++w) tot += part[w];
+    const double q = tot / (double)n;
+    double alpha;
+    if (isnan(q)) {
+      alpha = NAN;
+    } else if (q <= 0.0) {
+      alpha = alpha_max;
+    } else {
+      alpha = fmin((double)alpha_max, sqrt((double)kl_budget / q));
+    }
+    q_alpha[0] = (float)q;
+    q_alpha[1] = (float)alpha;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kl(const uint16_t* zc, const uint16_t* zp, int n_tok,
+                     int vocab, int64_t ld, float tau, float kl_budget,
+                     float alpha_max, float* q_alpha, float* kl_tok,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(kl_rows_kernel, dim3((unsigned)n_tok), dim3(kKlThreads), 0, s,
+                     zc, zp, vocab, ld, 1.0f / tau, kl_tok);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, s, kl_tok, n_tok,
+                     kl_budget, alpha_max, q_alpha);
+  return hipGetLastError();
+}
+
+}  // namespace logra

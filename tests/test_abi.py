@@ -1,0 +1,134 @@
+"""The C ABI boundary on the CPU: the library loads without a GPU, exports every
+function include/logra.h declares, and rejects invalid arguments with status
+codes before any HIP call (so these paths need no device).
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+from rank_gradient_sketching_amd import _lib
+
+EINVAL, EWS = _lib.EINVAL, _lib.EWORKSPACE
+P = 0x100000          # a 256-byte-aligned stand-in address; never dereferenced
+MIS = P + 2           # misaligned by 2 bytes
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _lib.header_symbols()
+    assert len(declared) == 8
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert L.logra_abi_version() == 1
+    for st in (0, -1, -2, -3, 7):
+        assert isinstance(_lib.status_str(st), str) and _lib.status_str(st)
+
+
+def test_workspace_queries(L):
+    assert L.logra_sketch_ws_bytes(8192, 4096, 4096, 64) > 2 * 8192 * 64 * 2
+    assert L.logra_sketch_ws_bytes(8192, 4096, 4096, 0) == 0
+    assert L.logra_sketch_ws_bytes(8192, 4096, 4096, 257) == 0
+    assert L.logra_sketch_ws_bytes(8192, 0, 4096, 64) == 0
+    assert L.logra_sketch_ws_bytes(-1, 16, 16, 4) == 0
+    assert L.logra_kl_ws_bytes(65536, 152064) >= 65536 * 4
+    assert L.logra_kl_ws_bytes(0, 10) == 0
+    # the workspace grows with T and shrinks to a floor at T = 0
+    assert L.logra_sketch_ws_bytes(16384, 256, 256, 4) > L.logra_sketch_ws_bytes(128, 256, 256, 4)
+
+
+def _sketch(L, **kw):
+    a = dict(X=P, ldx=256, dY=P, ldd=256, T=128, d=256, k=256, r=4, seed=1234, stream=0,
+             kind=0, S=P, ws=P, ws_bytes=1 << 30, s=None)
+    a.update(kw)
+    return L.logra_sketch_accumulate(a["X"], a["ldx"], a["dY"], a["ldd"], a["T"], a["d"],
+                                     a["k"], a["r"], a["seed"], a["stream"], a["kind"],
+                                     a["S"], a["ws"], a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), EINVAL), (dict(dY=None), EINVAL), (dict(S=None), EINVAL),
+    (dict(r=0), EINVAL), (dict(r=257), EINVAL), (dict(r=-3), EINVAL),
+    (dict(d=0), EINVAL), (dict(k=0), EINVAL), (dict(T=-1), EINVAL),
+    (dict(ldx=255), EINVAL), (dict(ldx=260), EINVAL), (dict(ldd=100), EINVAL),
+    (dict(kind=2), EINVAL), (dict(kind=-1), EINVAL),
+    (dict(X=MIS), EINVAL), (dict(dY=MIS), EINVAL), (dict(S=P + 1), EINVAL),
+    (dict(d=1 << 31), EINVAL), (dict(T=1 << 31), EINVAL),
+    (dict(ws=None), EWS), (dict(ws_bytes=16), EWS), (dict(ws=P + 16), EWS),
+])
+def test_sketch_rejects(L, kw, status):
+    assert _sketch(L, **kw) == status
+
+
+def test_sketch_T0_is_noop_without_touching_pointers(L):
+    assert _sketch(L, T=0, X=None, dY=None, S=None, ws=None, ws_bytes=0) == 0
+    assert _sketch(L, T=0, r=0) == EINVAL      # sizes are still checked
+
+
+def _merge(L, **kw):
+    a = dict(W=P, ldw=256, S=P, d=256, k=256, r=4, seed=1, stream=0, kind=0,
+             alpha=1.0, eta=1e-3, s=None)
+    a.update(kw)
+    return L.logra_merge(a["W"], a["ldw"], a["S"], a["d"], a["k"], a["r"], a["seed"],
+                         a["stream"], a["kind"], a["alpha"], a["eta"], a["s"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(W=None), dict(S=None), dict(r=0), dict(r=300), dict(d=0), dict(k=-5),
+    dict(ldw=200), dict(ldw=257), dict(kind=3), dict(W=MIS), dict(S=P + 2),
+    dict(alpha=float("nan")), dict(eta=float("inf")), dict(alpha=-float("inf")),
+])
+def test_merge_rejects(L, kw):
+    assert _merge(L, **kw) == EINVAL
+
+
+def _kl(L, **kw):
+    a = dict(zc=P, zp=P, n=64, V=1000, ld=1000, tau=1.0, delta=2e-4, amax=4.0,
+             out=P, kl=None, ws=P, ws_bytes=1 << 20, s=None)
+    a.update(kw)
+    return L.logra_predicted_kl(a["zc"], a["zp"], a["n"], a["V"], a["ld"], a["tau"],
+                                a["delta"], a["amax"], a["out"], a["kl"], a["ws"],
+                                a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(zc=None), EINVAL), (dict(zp=None), EINVAL), (dict(out=None), EINVAL),
+    (dict(n=0), EINVAL), (dict(V=0), EINVAL), (dict(ld=999), EINVAL), (dict(ld=1004), EINVAL),
+    (dict(tau=0.0), EINVAL), (dict(tau=-1.0), EINVAL), (dict(tau=float("nan")), EINVAL),
+    (dict(delta=0.0), EINVAL), (dict(delta=float("inf")), EINVAL),
+    (dict(amax=-1.0), EINVAL), (dict(amax=float("nan")), EINVAL),
+    (dict(zc=MIS), EINVAL), (dict(out=P + 1), EINVAL), (dict(kl=P + 2), EINVAL),
+    (dict(ws=None), EWS), (dict(ws_bytes=8), EWS), (dict(ws=P + 64), EWS),
+])
+def test_kl_rejects(L, kw, status):
+    assert _kl(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(A=None), dict(r=0), dict(r=512), dict(k=0), dict(kind=5),
+                                dict(A=P + 2)])
+def test_regen_rejects(L, kw):
+    a = dict(seed=1, stream=0, kind=0, r=4, k=256, A=P, s=None)
+    a.update(kw)
+    assert L.logra_regen_A(a["seed"], a["stream"], a["kind"], a["r"], a["k"], a["A"], a["s"]) == EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import rank_gradient_sketching_amd as lg
+    X = torch.zeros(8, 8, dtype=torch.bfloat16)
+    S = torch.zeros(8, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        lg.sketch_accumulate(X, X, S, seed=1)
+    with pytest.raises(ValueError, match="GPU"):
+        lg.merge(X, S, seed=1)

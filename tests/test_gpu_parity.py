@@ -1,0 +1,295 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Bars: A bit-exact for the sign basis (the Gaussian basis: >= 99.9 % of entries
+equal, the rest within one bf16 ulp, since fp64 and fp32 transcendentals may
+round differently); S and the merged-W delta within 2e-3 relative Frobenius
+error; q(D) within 1e-3 relative error.  Shapes span several tiles and ragged
+tails; every input is seeded.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import bf16 as obf16
+from oracle import kl as okl
+from oracle import merge as omerge
+from oracle import projection as oproj
+from oracle import sketch as osketch
+from rank_gradient_sketching_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+S_TOL = 2e-3
+W_TOL = 2e-3
+Q_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def lg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_gradient_sketching_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def padded_bf16(t, ld):
+    """Copy of a 2-D bf16 tensor on the GPU with row stride ld (>= cols)."""
+    rows, cols = t.shape
+    buf = torch.full((rows, ld), float("nan"), dtype=torch.bfloat16, device="cuda")
+    buf[:, :cols] = t.cuda()
+    return buf[:, :cols]
+
+
+# ------------------------------------------------------------------ regen_A
+
+@pytest.mark.parametrize("seed,stream,r,k", [
+    (1234, 0, 4, 256), (1234, 0, 64, 4096), (7, 3, 1, 1), (99, 1, 3, 257),
+    (2 ** 64 - 1, 2 ** 63, 100, 1000), (1261, 0, 256, 1536), (5, 2, 17, 4099),
+])
+def test_regen_sign_bit_exact(lg, seed, stream, r, k):
+    say("regen sign", seed, stream, r, k)
+    A = lg.regen_A(seed, stream, 0, r, k).cpu().numpy()
+    ref = oproj.projection(seed, stream, 0, r, k).astype(np.float32)
+    np.testing.assert_array_equal(A.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("seed,stream,r,k", [(1234, 0, 64, 4096), (3, 1, 7, 1001), (1261, 2, 256, 1536)])
+def test_regen_gaussian_within_one_ulp(lg, seed, stream, r, k):
+    say("regen gauss", seed, stream, r, k)
+    A = lg.regen_A(seed, stream, 1, r, k).cpu().numpy().astype(np.float64)
+    ref = oproj.projection(seed, stream, 1, r, k)
+    np.testing.assert_array_equal(obf16.round_f64(A), A)      # GPU values are bf16
+    bits_g = obf16.f64_to_bits(A).astype(np.int32)
+    bits_o = obf16.f64_to_bits(ref).astype(np.int32)
+    same = bits_g == bits_o
+    assert same.mean() >= 0.999, same.mean()
+    assert np.abs(bits_g - bits_o).max() <= 1
+
+
+# ------------------------------------------------------------------ sketch
+
+SKETCH_CASES = [
+    # T, d, k, r, kind, n_mb
+    (128, 256, 256, 4, 0, 2),       # the d = k = 256, r = 4 layer
+    (1000, 300, 520, 16, 0, 2),     # ragged T, d, k
+    (77, 1030, 264, 64, 0, 1),
+    (300, 200, 700, 100, 0, 2),     # r not a power of two, rank padding
+    (64, 128, 512, 256, 0, 1),      # maximum rank
+    (33, 17, 9, 3, 0, 3),           # tiny ragged everything
+    (1, 8, 8, 1, 0, 1),             # single token, rank one
+    (2048, 512, 1024, 32, 0, 2),    # several work-groups along T (split path)
+    (4096, 1536, 256, 64, 0, 1),    # narrow k, many splits
+    (200, 300, 520, 16, 1, 2),      # Gaussian basis
+    (129, 256, 1000, 256, 1, 1),
+]
+
+
+def _sketch_case(lg, T, d, k, r, kind, n_mb, seed=1234, stream=0, ld_pad=0):
+    mbs = [(synth.host_normal_bf16((T, k), synth.X_ID, mb=mb, salt=d),
+            synth.host_normal_bf16((T, d), synth.DY_ID, mb=mb, salt=d)) for mb in range(n_mb)]
+    S0 = synth.host_normal_f32((d, r), synth.S_ID, salt=T)
+    S = S0.clone().cuda()
+    ws = lg.sketch_workspace(T, d, k, r)
+    for X, dY in mbs:
+        ldx = -(-k // 8) * 8 + ld_pad
+        ldd = -(-d // 8) * 8 + ld_pad
+        lg.sketch_accumulate(padded_bf16(X, ldx), padded_bf16(dY, ldd), S, seed, stream, kind, ws=ws)
+    torch.cuda.synchronize()
+    A = oproj.projection(seed, stream, kind, r, k)
+    ref = osketch.accumulate(S0.numpy().astype(np.float64),
+                             [(synth.bf16_to_f64(X), synth.bf16_to_f64(dY)) for X, dY in mbs], A)
+    delta_ref = ref - S0.numpy().astype(np.float64)
+    delta_gpu = S.cpu().numpy().astype(np.float64) - S0.numpy().astype(np.float64)
+    return S, rel_fro(delta_gpu, delta_ref), rel_fro(S.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("T,d,k,r,kind,n_mb", SKETCH_CASES)
+def test_sketch_matches_oracle(lg, T, d, k, r, kind, n_mb):
+    say("sketch", T, d, k, r, kind, n_mb)
+    _, err_delta, err_total = _sketch_case(lg, T, d, k, r, kind, n_mb)
+    assert err_delta < S_TOL, err_delta
+    assert err_total < S_TOL, err_total
+
+
+def test_sketch_padded_strides(lg):
+    say("sketch padded strides")
+    _, e1, _ = _sketch_case(lg, 300, 100, 120, 16, 0, 2, ld_pad=24)
+    assert e1 < S_TOL
+
+
+def test_sketch_deterministic(lg):
+    say("sketch determinism")
+    T, d, k, r = 4096, 1024, 1024, 64
+    X = synth.host_normal_bf16((T, k), synth.X_ID, salt=77).cuda()
+    dY = synth.host_normal_bf16((T, d), synth.DY_ID, salt=77).cuda()
+    outs = []
+    for _ in range(3):
+        S = torch.zeros(d, r, device="cuda")
+        lg.sketch_accumulate(X, dY, S, 1234)
+        outs.append(S.cpu().numpy().view(np.uint32).copy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])
+
+
+def test_sketch_zero_tokens_is_noop(lg):
+    S = torch.ones(16, 4, device="cuda")
+    X = torch.empty(0, 32, dtype=torch.bfloat16, device="cuda")
+    dY = torch.empty(0, 16, dtype=torch.bfloat16, device="cuda")
+    lg.sketch_accumulate(X, dY, S, 1)
+    assert torch.equal(S, torch.ones(16, 4, device="cuda"))
+
+
+def test_sketch_linear_across_calls_and_resume(lg):
+    say("sketch linearity")
+    T, d, k, r = 512, 384, 640, 32
+    X = synth.host_normal_bf16((2 * T, k), synth.X_ID, salt=5).cuda()
+    dY = synth.host_normal_bf16((2 * T, d), synth.DY_ID, salt=5).cuda()
+    S_two = torch.zeros(d, r, device="cuda")
+    lg.sketch_accumulate(X[:T], dY[:T], S_two, 42)
+    # checkpoint S to the host and back between the microbatches
+    S_two = S_two.cpu().clone().cuda()
+    lg.sketch_accumulate(X[T:], dY[T:], S_two, 42)
+    S_one = torch.zeros(d, r, device="cuda")
+    lg.sketch_accumulate(X, dY, S_one, 42)
+    assert rel_fro(S_two.cpu().numpy(), S_one.cpu().numpy()) < 1e-5
+
+
+# ------------------------------------------------------------------ merge
+
+MERGE_CASES = [
+    # d, k, r, kind, alpha, eta
+    (256, 256, 4, 0, 1.0, 1e-3),
+    (4096, 4096, 64, 0, 1.0, 2e-4),
+    (300, 520, 16, 0, 0.4, 1e-3),
+    (1030, 264, 100, 0, 2.0, 5e-4),
+    (17, 9, 3, 0, 1.0, 1e-2),
+    (1, 8, 1, 0, 1.0, 1e-2),
+    (512, 1000, 256, 0, 0.5, 1e-3),
+    (300, 520, 16, 1, 1.0, 1e-3),
+    (256, 1000, 256, 1, 1.0, 1e-3),
+]
+
+
+def _merge_case(lg, d, k, r, kind, alpha, eta, seed=1234, stream=0, ld_pad=0):
+    W0 = synth.host_normal_bf16((d, k), synth.W_ID, salt=k)
+    # S of realistic scale for the step: the sketch of a few hundred tokens
+    S = synth.host_normal_f32((d, r), synth.S_ID, salt=d, sigma=15.0)
+    ldw = -(-k // 8) * 8 + ld_pad
+    W = padded_bf16(W0, ldw)
+    lg.merge(W, S.cuda(), seed, stream, kind, alpha, eta)
+    torch.cuda.synchronize()
+    A = oproj.projection(seed, stream, kind, r, k)
+    Wb = synth.bf16_bits(W0)
+    ref_delta = omerge.merged_delta(Wb, S.numpy().astype(np.float64), A, alpha, eta)
+    got = synth.bf16_to_f64(W) - synth.bf16_to_f64(W0)
+    return W, rel_fro(got, ref_delta)
+
+
+@pytest.mark.parametrize("d,k,r,kind,alpha,eta", MERGE_CASES)
+def test_merge_matches_oracle(lg, d, k, r, kind, alpha, eta):
+    say("merge", d, k, r, kind, alpha, eta)
+    _, err = _merge_case(lg, d, k, r, kind, alpha, eta)
+    assert err < W_TOL, err
+
+
+def test_merge_padded_stride_keeps_padding(lg):
+    say("merge padded stride")
+    d, k, r = 70, 100, 8
+    W0 = synth.host_normal_bf16((d, k), synth.W_ID, salt=3)
+    buf = torch.full((d, 112), 7.0, dtype=torch.bfloat16, device="cuda")
+    buf[:, :k] = W0.cuda()
+    S = synth.host_normal_f32((d, r), synth.S_ID, salt=3).cuda()
+    lg.merge(buf[:, :k], S, 9, 0, 0, 1.0, 1e-3)
+    assert torch.all(buf[:, k:] == 7.0)
+    A = oproj.projection(9, 0, 0, r, k)
+    ref = omerge.merged_delta(synth.bf16_bits(W0), S.cpu().numpy().astype(np.float64), A, 1.0, 1e-3)
+    assert rel_fro(synth.bf16_to_f64(buf[:, :k]) - synth.bf16_to_f64(W0), ref) < W_TOL
+
+
+def test_merge_zero_step_is_bitwise_noop(lg):
+    W0 = synth.host_normal_bf16((300, 520), synth.W_ID, salt=8).cuda()
+    W = W0.clone()
+    S = synth.host_normal_f32((300, 16), synth.S_ID, salt=8).cuda()
+    lg.merge(W, S, 5, 0, 0, 0.0, 1e-3)
+    assert torch.equal(W.view(torch.int16), W0.view(torch.int16))
+
+
+def test_rollout_apply_matches_trainer_merge(lg):
+    """The rollout side receives alpha*eta*U and the seed and applies the same
+    merge; passing the scaled factor with alpha = eta = 1 gives the same W."""
+    say("rollout apply")
+    d, k, r = 512, 768, 64
+    W0 = synth.host_normal_bf16((d, k), synth.W_ID, salt=11).cuda()
+    S = synth.host_normal_f32((d, r), synth.S_ID, salt=11, sigma=15.0).cuda()
+    alpha, eta = 0.5, 2e-4
+    W_train = lg.merge(W0.clone(), S, 77, 0, 0, alpha, eta)
+    U_sent = S * np.float32(np.float32(alpha) * np.float32(eta))
+    W_roll = lg.merge(W0.clone(), U_sent, 77, 0, 0, 1.0, 1.0)
+    diff = (W_train.float() - W_roll.float()).abs().max().item()
+    ulp = (W0.float().abs().max() * 2 ** -7).item()
+    assert diff <= ulp
+
+
+# ------------------------------------------------------------------ predicted KL
+
+KL_CASES = [
+    # n, V, tau, sigma_dir
+    (64, 1000, 1.0, 0.05),
+    (7, 152064, 1.0, 0.05),
+    (3, 1001, 0.7, 0.05),
+    (5, 2, 1.0, 0.5),
+    (9, 4099, 1.3, 0.3),      # large steps: exercises the exp fallback for |d| > 1/2
+    (300, 32000, 1.0, 0.01),
+]
+
+
+@pytest.mark.parametrize("n,V,tau,sig", KL_CASES)
+def test_predicted_kl_matches_oracle(lg, n, V, tau, sig):
+    say("kl", n, V, tau, sig)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V)
+    dirn = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V, sigma=sig)
+    zp = synth.proposal_logits(z, dirn, 1.0)
+    ld = -(-V // 8) * 8
+    zc_g, zp_g = padded_bf16(z, ld), padded_bf16(zp, ld)
+    kl_tok = torch.empty(n, device="cuda")
+    out = lg.predicted_kl(zc_g, zp_g, tau, 2e-4, 4.0, kl_tok=kl_tok)
+    out_ws = lg.predicted_kl(zc_g, zp_g, tau, 2e-4, 4.0)
+    torch.cuda.synchronize()
+    ref_rows = okl.kl_rows(synth.bf16_to_f64(z), synth.bf16_to_f64(zp), tau)
+    q_ref = float(ref_rows.mean())
+    q, alpha = out.cpu().numpy().astype(np.float64)
+    assert abs(q / q_ref - 1) < Q_TOL, (q, q_ref)
+    np.testing.assert_allclose(kl_tok.cpu().numpy(), ref_rows, rtol=1e-3, atol=1e-9)
+    assert abs(alpha - okl.step_size(q_ref, 2e-4, 4.0)) <= 1e-3 * okl.step_size(q_ref, 2e-4, 4.0)
+    assert torch.equal(out, out_ws)
+
+
+def test_kl_controller_edges(lg):
+    say("kl controller edges")
+    z = synth.host_normal_bf16((4, 512), synth.Z_ID, salt=1).cuda()
+    out = lg.predicted_kl(z, z, 1.0, 2e-4, 3.0)           # q = 0 -> alpha_max
+    q, a = out.cpu().tolist()
+    assert q == 0.0 and a == 3.0
+    # q = 4 delta -> alpha = 1/2: choose the budget from the measured q
+    dirn = synth.host_normal_bf16((4, 512), synth.DIR_ID, salt=1, sigma=0.1).cuda()
+    zp = synth.proposal_logits(z, dirn, 1.0)
+    q = lg.predicted_kl(z, zp, 1.0, 1.0, 10.0)[0].item()
+    a = lg.predicted_kl(z, zp, 1.0, q / 4, 10.0)[1].item()
+    assert abs(a - 0.5) < 1e-6
+    # NaN logits give a NaN alpha
+    zn = z.clone()
+    zn[0, 0] = float("nan")
+    q, a = lg.predicted_kl(zn, zp, 1.0, 2e-4, 4.0).cpu().tolist()
+    assert np.isnan(q) and np.isnan(a)
