@@ -171,23 +171,36 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------- loads
-// 8 bf16 starting at element `col` of a row of `ncols` valid elements; lanes
-// past the end read zeros.  Rows are 16-byte aligned (ld % 8 == 0), so a full
-// group is one 16-byte load.
-__device__ __forceinline__ u32x4 load_bf16x8(const uint16_t* row, int col,
-                                             int ncols) {
-  if (col + 8 <= ncols) {
-    return *reinterpret_cast<const u32x4*>(row + col);
-  }
-  u32x4 v = {0u, 0u, 0u, 0u};
+// Branch-free row loads.  Callers pass a column that lies inside the row's
+// declared stride (ld >= round_up(ncols, 8) because ld % 8 == 0), so a whole
+// aligned group can always be read; elements at or past `ncols` are then
+// cleared with a bit mask (the padding may hold anything, including NaN).
+
+// Mask keeping the first `valid` (0..8) bf16 of a 16-byte group, per dword.
+__device__ __forceinline__ u32x4 keep_mask8(int valid) {
+  u32x4 k;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (col + e < ncols) {
-      const uint32_t h = row[col + e];
-      v[e >> 1] |= (e & 1) ? (h << 16) : h;
-    }
+  for (int p = 0; p < 4; ++p) {
+    const int v = valid - 2 * p;
+    k[p] = v >= 2 ? 0xFFFFFFFFu : v == 1 ? 0x0000FFFFu : 0u;
   }
-  return v;
+  return k;
+}
+
+// 8 bf16 of `row` from element `col` (a multiple of 8); elements >= ncols
+// read as zero.  Groups entirely past the end read the row's first group and
+// are cleared.  Branch-free, so a run of these loads is issued back to back.
+__device__ __forceinline__ u32x4 load_bf16x8_masked(const uint16_t* row, int col,
+                                                    int ncols) {
+  const int valid = ncols - col;
+  const u32x4 v =
+      *reinterpret_cast<const u32x4*>(row + (valid > 0 ? col : 0));
+  return v & keep_mask8(valid);
+}
+
+// Interior fast path: the whole group is inside the row.
+__device__ __forceinline__ u32x4 load_bf16x8(const uint16_t* row, int col) {
+  return *reinterpret_cast<const u32x4*>(row + col);
 }
 
 }  // namespace logra

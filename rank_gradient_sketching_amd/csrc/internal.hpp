@@ -24,7 +24,7 @@ struct SketchPlan {
   int n_split;      // accumulate work-groups along T
   int steps_per_split;
   int64_t d_pad;    // n_dgroups * 16 * q_cols
-  size_t off_phi, off_plo, off_part, off_cnt, off_gauss, total;
+  size_t off_pt, off_part, off_gauss, total;
 };
 
 bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p);

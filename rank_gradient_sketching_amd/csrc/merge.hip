@@ -30,13 +30,14 @@ constexpr int kMergeRows = 256;
 constexpr int kMergeCols = 256;
 constexpr int kPassCols = 64;
 
-template <int NKS, bool GAUSS>
+template <int NKS, bool GAUSS, bool MASKED>
 __global__ __launch_bounds__(256) void merge_kernel(
     uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ S, int d,
     int k, int r, uint64_t seed, uint64_t stream, float scale, float cr) {
   constexpr int RP = 32 * NKS;    // r padded to whole K steps
   constexpr int LDA = RP + 8;     // bf16 per LDS column (+16 B against conflicts)
-  __shared__ uint16_t At[kPassCols * LDA];
+  constexpr bool kDouble = NKS <= 4;  // two A slices fit in 64 KB of LDS
+  __shared__ uint16_t At[(kDouble ? 2 : 1) * kPassCols * LDA];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -49,18 +50,33 @@ __global__ __launch_bounds__(256) void merge_kernel(
   const int rblk = (int)(blockIdx.x / (unsigned)n_cb);
   const int col0 = cb * kMergeCols;
   const int row0 = rblk * kMergeRows + wave * 64;
+  const int n_pass = min(kMergeCols / kPassCols, (k - col0 + kPassCols - 1) / kPassCols);
 
   // S operands: rows row0 + 16 nt + m, K = r columns 32 ks + 8 g + (0..7),
   // as hi/lo bf16.  They do not depend on the column pass, so for small r
   // they stay in registers; for large r they are rebuilt per pass (L2 hits).
   constexpr bool kHoistS = NKS <= 2;
+  // rows of this wave all inside d and r a multiple of 32: plain float4 loads
+  const bool s_fast = !MASKED;
   auto s_operands = [&](int nt, int ks, u32x4& hi, u32x4& lo) {
     const int row = row0 + 16 * nt + m;
     float v[8];
+    if (s_fast) {
+      const f32x4* sp = reinterpret_cast<const f32x4*>(S + (int64_t)row * r + 32 * ks + 8 * g);
+      const f32x4 a = sp[0], b = sp[1];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int rc = 32 * ks + 8 * g + e;
-      v[e] = (row < d && rc < r) ? S[(int64_t)row * r + rc] : 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        v[e] = a[e];
+        v[4 + e] = b[e];
+      }
+    } else {
+      const int rr = row < d ? row : d - 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int rc = 32 * ks + 8 * g + e;
+        const float x = S[(int64_t)rr * r + (rc < r ? rc : r - 1)];
+        v[e] = (row < d && rc < r) ? x : 0.0f;
+      }
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -96,57 +112,80 @@ __global__ __launch_bounds__(256) void merge_kernel(
     }
   }
 
-#pragma unroll 1
-  for (int pass = 0; pass < kMergeCols / kPassCols; ++pass) {
+  // A slice of pass p into LDS: buf[col * LDA + i] = A[i][col0 + 64 p + col].
+  auto build_A = [&](int pass, uint16_t* buf) {
     const int c0 = col0 + pass * kPassCols;
-    if (c0 >= k) break;
-
-    // 1. A slice into LDS, At[col * LDA + i] = A[i][c0 + col].
     if (GAUSS) {
       for (int job = tid; job < RP * (kPassCols / 4); job += 256) {
         const int i = job / (kPassCols / 4);
-        const int qg = job % (kPassCols / 4);
-        const int cc = 4 * qg;
+        const int cc = 4 * (job % (kPassCols / 4));
         uint16_t v[4] = {0, 0, 0, 0};
         if (i < r && c0 + cc < k) {
           gaussian_entries_bf16(seed, stream, (uint64_t)((c0 + cc) >> 2),
                                 (uint64_t)i, cr, v);
         }
 #pragma unroll
-        for (int a = 0; a < 4; ++a) At[(cc + a) * LDA + i] = v[a];
+        for (int a = 0; a < 4; ++a) buf[(cc + a) * LDA + i] = v[a];
       }
     } else if (tid < RP / 2) {
-      // pass selects word `pass` of each block (columns 64 pass .. +63)
+      // word `pass` of each block holds columns 64 pass .. 64 pass + 63
       const uint64_t wa = pass == 0 ? sw0[0] : pass == 1 ? sw0[1] : pass == 2 ? sw0[2] : sw0[3];
       const uint64_t wb = pass == 0 ? sw1[0] : pass == 1 ? sw1[1] : pass == 2 ? sw1[2] : sw1[3];
       const uint32_t one = 0x3F80u, neg = 0xBF80u;
-      uint32_t* at32 = reinterpret_cast<uint32_t*>(At);
+      uint32_t* b32 = reinterpret_cast<uint32_t*>(buf);
 #pragma unroll 8
       for (int cc = 0; cc < kPassCols; ++cc) {
         const uint32_t lo = ra < r ? (((wa >> cc) & 1u) ? neg : one) : 0u;
         const uint32_t hi = rb < r ? (((wb >> cc) & 1u) ? neg : one) : 0u;
-        at32[(cc * LDA) / 2 + tid] = lo | (hi << 16);
+        b32[(cc * LDA) / 2 + tid] = lo | (hi << 16);
       }
     }
-    __syncthreads();
+  };
 
-    // 3a. Issue this lane's W loads: rows row0 + 16 nt + m, columns
-    // c0 + 16 g + (0..15).
-    u32x4 wv[4][2];
+  // This lane's W elements of pass p: rows row0 + 16 nt + m, columns
+  // col0 + 64 p + 16 g + (0..15).  Rows past d are read from row d - 1 and
+  // never stored; columns past k read as zero.
+  auto load_W = [&](int pass, u32x4 wv[4][2]) {
+    const int c0 = col0 + pass * kPassCols;
     const int wc = c0 + 16 * g;
+    if (!MASKED) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int row = row0 + 16 * nt + m;
-      if (row < d) {
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint16_t* wr = W + (int64_t)(row0 + 16 * nt + m) * ldw;
+        wv[nt][0] = load_bf16x8(wr, wc);
+        wv[nt][1] = load_bf16x8(wr, wc + 8);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = min(row0 + 16 * nt + m, d - 1);
         const uint16_t* wr = W + (int64_t)row * ldw;
-        wv[nt][0] = load_bf16x8(wr, wc, k);
-        wv[nt][1] = load_bf16x8(wr, wc + 8, k);
-      } else {
-        wv[nt][0] = wv[nt][1] = u32x4{0u, 0u, 0u, 0u};
+        wv[nt][0] = load_bf16x8_masked(wr, wc, k);
+        wv[nt][1] = load_bf16x8_masked(wr, wc + 8, k);
       }
     }
+  };
 
-    // 2. MFMA: acc[t][nt] rows m' = 4 g' + v map to columns c0 + 16 g' + 4 t + v.
+  uint16_t* buf0 = At;
+  uint16_t* buf1 = At + (kDouble ? kPassCols * LDA : 0);
+
+  // One column pass: multiply the A slice, update the W elements loaded one
+  // pass earlier (wcur) and, before that, start the loads of the next pass
+  // (wnxt) so they overlap this pass's work.
+  auto do_pass = [&](int pass, u32x4 (&wcur)[4][2], u32x4 (&wnxt)[4][2]) {
+    if (!kDouble && pass > 0) {
+      __syncthreads();          // every wave is done reading the previous slice
+      build_A(pass, buf0);
+    }
+    __syncthreads();            // slice `pass` is complete
+    if (pass + 1 < n_pass) {
+      load_W(pass + 1, wnxt);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kDouble) build_A(pass + 1, (pass & 1) ? buf0 : buf1);
+    }
+    const uint16_t* cur_buf = (kDouble && (pass & 1)) ? buf1 : buf0;
+
+    // MFMA: acc[t][nt] rows m' = 4 g' + v map to columns c0 + 16 g' + 4 t + v.
     f32x4 acc[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -168,7 +207,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
       for (int t = 0; t < 4; ++t) {
         const int cc = (m >> 2) * 16 + 4 * t + (m & 3);
         const u32x4 a =
-            *reinterpret_cast<const u32x4*>(&At[cc * LDA + 32 * ks + 8 * g]);
+            *reinterpret_cast<const u32x4*>(&cur_buf[cc * LDA + 32 * ks + 8 * g]);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           acc[t][nt] = mfma16(a, bh[nt], acc[t][nt]);
@@ -176,13 +215,12 @@ __global__ __launch_bounds__(256) void merge_kernel(
         }
       }
     }
-    __syncthreads();  // At is rewritten by the next pass
 
-    // 3b. Update and store.
+    // Update and store.
+    const int wc = col0 + pass * kPassCols + 16 * g;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int row = row0 + 16 * nt + m;
-      if (row >= d) continue;
       u32x4 out[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -191,30 +229,53 @@ __global__ __launch_bounds__(256) void merge_kernel(
           // element e = 8 hh + 2 p (+1) of the lane's 16 columns = 4 t + v
           const int e0 = 8 * hh + 2 * p;
           const int e1 = e0 + 1;
-          const float w0 = bf16_lo(wv[nt][hh][p]);
-          const float w1 = bf16_hi(wv[nt][hh][p]);
+          const float w0 = bf16_lo(wcur[nt][hh][p]);
+          const float w1 = bf16_hi(wcur[nt][hh][p]);
           const float n0 = w0 - scale * acc[e0 >> 2][nt][e0 & 3];
           const float n1 = w1 - scale * acc[e1 >> 2][nt][e1 & 3];
           out[hh][p] = pack_bf16x2(n0, n1);
         }
       }
-      uint16_t* wr = W + (int64_t)row * ldw;
+      if (!MASKED || row < d) {
+        uint16_t* wr = W + (int64_t)row * ldw;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int cbeg = wc + 8 * hh;
-        if (cbeg + 8 <= k) {
-          *reinterpret_cast<u32x4*>(wr + cbeg) = out[hh];
-        } else {
+        for (int hh = 0; hh < 2; ++hh) {
+          const int cbeg = wc + 8 * hh;
+          if (!MASKED || cbeg + 8 <= k) {
+            *reinterpret_cast<u32x4*>(wr + cbeg) = out[hh];
+          } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (cbeg + e < k) {
-              const uint32_t dw = out[hh][e >> 1];
-              wr[cbeg + e] = (uint16_t)((e & 1) ? (dw >> 16) : (dw & 0xFFFFu));
+            for (int e = 0; e < 8; ++e) {
+              if (cbeg + e < k) {
+                const uint32_t dw = out[hh][e >> 1];
+                wr[cbeg + e] = (uint16_t)((e & 1) ? (dw >> 16) : (dw & 0xFFFFu));
+              }
             }
           }
         }
       }
     }
+  };
+
+  u32x4 wa[4][2], wb[4][2];
+  build_A(0, buf0);
+  load_W(0, wa);
+  do_pass(0, wa, wb);
+  if (n_pass > 1) do_pass(1, wb, wa);
+  if (n_pass > 2) do_pass(2, wa, wb);
+  if (n_pass > 3) do_pass(3, wb, wa);
+}
+
+template <int NKS, bool MASKED>
+void launch_merge_m(uint16_t* W, int64_t ldw, const float* S, int d, int k, int r,
+                    uint64_t seed, uint64_t stream, bool gauss, float scale,
+                    float cr, hipStream_t s, dim3 grid) {
+  if (gauss) {
+    hipLaunchKernelGGL((merge_kernel<NKS, true, MASKED>), grid, dim3(256), 0, s, W,
+                       ldw, S, d, k, r, seed, stream, scale, cr);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<NKS, false, MASKED>), grid, dim3(256), 0, s, W,
+                       ldw, S, d, k, r, seed, stream, scale, cr);
   }
 }
 
@@ -225,13 +286,10 @@ hipError_t launch_merge_t(uint16_t* W, int64_t ldw, const float* S, int d, int k
   const int64_t blocks = (int64_t)((k + kMergeCols - 1) / kMergeCols) *
                          ((d + kMergeRows - 1) / kMergeRows);
   const dim3 grid((unsigned)blocks);
-  if (gauss) {
-    hipLaunchKernelGGL((merge_kernel<NKS, true>), grid, dim3(256), 0, s, W, ldw,
-                       S, d, k, r, seed, stream, scale, cr);
-  } else {
-    hipLaunchKernelGGL((merge_kernel<NKS, false>), grid, dim3(256), 0, s, W, ldw,
-                       S, d, k, r, seed, stream, scale, cr);
-  }
+  // unmasked when every tile is interior and S rows are whole K steps
+  const bool masked = (d % kMergeRows) != 0 || (k % kMergeCols) != 0 || (r % 32) != 0;
+  if (masked) launch_merge_m<NKS, true>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
+  else launch_merge_m<NKS, false>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
   return hipGetLastError();
 }
 

@@ -6,23 +6,27 @@
 // projecting the layer inputs first and only then multiplying with the
 // backward derivatives, so the d x k gradient is never formed.
 //
-// Two kernels on the caller's stream:
-//   project    P = c * X A^T (T x r).  One work-group per 32 tokens; its four
+// Kernels on the caller's stream (no cross-work-group synchronisation inside
+// any of them: on this part an agent-scope fence per work-group costs far more
+// than an extra launch):
+//   project    P = c * X A^T (T x r).  One work-group per 32 tokens; its eight
 //              waves split k in 256-column chunks.  For the sign basis each
 //              lane regenerates the sign bits of its A row in registers from
 //              Philox (one block per row and chunk) and expands them to bf16
 //              +-1 MFMA operands, so A never touches memory.  Products with
 //              +-1 are exact; 32x32x16 bf16 MFMA accumulates in fp32; the
-//              waves' partial sums meet in LDS in a fixed order.  P is written
-//              transposed (r x T, tokens contiguous) as a hi/lo bf16 pair.
+//              waves' partial sums meet in LDS in a fixed order.  P is stored
+//              as a hi/lo bf16 pair in the accumulate kernel's operand order
+//              (one contiguous 1 KB block per 32 tokens x 16 r columns).
 //   accumulate S += dY^T P.  A work-group owns 16*Q columns of d and a range
 //              of 32-token steps.  Each lane loads an 8-token x Q-column block
 //              of dY with row-contiguous loads and transposes it in registers
 //              (v_perm_b32), giving K = token operands for 16x16x32 MFMA
 //              against P_hi and P_lo.  Waves split the steps and are summed in
-//              LDS in a fixed order; work-groups along T write partial tiles
-//              and the last one to finish (device-scope counter) adds them to
-//              S in split order, so S is bit-reproducible.
+//              LDS in a fixed order; with several work-groups along T each
+//              writes its partial tile, and
+//   finalize   adds the partial tiles to S in split order.  S is therefore
+//              bit-reproducible.
 // The Gaussian basis is first written once per call as a bf16 r x k matrix in
 // the workspace (Box-Muller per entry is too costly to repeat per token
 // block) and the project kernel reads its operand tiles from there.
@@ -33,29 +37,52 @@ namespace logra {
 
 namespace {
 
-constexpr int kProjWaves = 4;
-constexpr int kAccWaves = 4;
+// Waves per project work-group: eight (two per SIMD) unless the accumulators
+// of a large rank need the bigger per-wave register budget.
+constexpr int proj_waves(int nb) { return nb <= 4 ? 8 : 4; }
+
+// Waves per accumulate work-group: eight (two per SIMD) while the
+// accumulators are small, four when they need the larger register budget.
+constexpr int acc_waves(int q, int nb16) { return q * nb16 * 4 <= 64 ? 8 : 4; }
 
 // ------------------------------------------------------------------ project
-template <int NB, bool GAUSS>
-__global__ __launch_bounds__(256) void project_kernel(
-    const uint16_t* __restrict__ X, int64_t ldx, int T, int k, int r,
+// X tile of one 256-column chunk for lane (m, h): row t0 + m, columns
+// 256 ch + 128 h + 8 s, s = 0..15 (rows >= T and columns >= k read as zero).
+// `full` (uniform across the wave) selects plain loads for interior tiles.
+__device__ __forceinline__ void load_x_chunk(const uint16_t* xrow, bool trow,
+                                             bool full, int ch, int h, int k,
+                                             u32x4 xv[16]) {
+  const int cbase = ch * 256 + h * 128;
+  if (full) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) xv[s] = load_bf16x8(xrow, cbase + 8 * s);
+  } else {
+    const uint32_t keep = trow ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) xv[s] = load_bf16x8_masked(xrow, cbase + 8 * s, k) & keep;
+  }
+}
+
+// Element offset of the P operand block (step, 16-column block nb, half hl)
+// in the tiled P buffer.  Inside a block, lane slot l = 16 g4 + n holds the
+// eight tokens 32 step + 8 g4 + (0..7) of r column 16 nb + n.
+__device__ __forceinline__ int64_t p_block(int step, int nb, int hl, int nb16) {
+  return ((int64_t)(step * nb16 + nb) * 2 + hl) * 512;
+}
+
+template <int NB, bool GAUSS, bool MASKED, int kProjWaves>
+__global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, int T, int k, int rp,
     uint64_t seed, uint64_t stream, float c, const uint16_t* __restrict__ Ab,
-    int64_t lda, uint16_t* __restrict__ Phi, uint16_t* __restrict__ Plo,
-    int64_t ldp, uint32_t* __restrict__ counters, int n_counters) {
+    int64_t lda, uint16_t* __restrict__ Pt) {
   __shared__ float red[kProjWaves][32 * 33];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int m = lane & 31;  // A-operand row (token) and B-operand column (A row)
   const int h = lane >> 5;  // which half of each 256-column chunk this lane feeds
-  const int t0 = blockIdx.x * 32;
-
-  // The accumulate kernel that follows on the stream counts finished
-  // work-groups per column group; reset its counters here.
-  if (blockIdx.x == 0) {
-    for (int i = tid; i < n_counters; i += 256) counters[i] = 0u;
-  }
+  const int step = blockIdx.x;
+  const int t0 = step * 32;
 
   f32x16 acc[NB];
 #pragma unroll
@@ -66,51 +93,69 @@ __global__ __launch_bounds__(256) void project_kernel(
 
   const int t = t0 + m;
   const bool trow = t < T;
-  const uint16_t* xrow = X + (int64_t)(trow ? t : 0) * ldx;
+  const uint16_t* xrow = X + (int64_t)(trow ? t : T - 1) * ldx;
   const int n_chunks = (k + 255) >> 8;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  for (int ch = wave; ch < n_chunks; ch += kProjWaves) {
+  // Ping-pong pipeline over this wave's chunks (ch, ch + W, ...): one buffer's
+  // loads are in flight while the other buffer's signs are generated and
+  // multiplied.  Rows of A at or past r are generated like any other row; they
+  // only reach sketch columns >= r, which are never written back.
+  // MASKED is false when T % 32 == 0 and k % 256 == 0: every tile is interior.
+  auto load = [&](int cnk, u32x4 xv[16]) {
+    const int cc = cnk < n_chunks ? cnk : n_chunks - 1;   // past the end: re-read
+    load_x_chunk(xrow, trow, !MASKED, cc, h, k, xv);
+  };
+  auto compute = [&](int ch, const u32x4 xv[16]) {
     // K assignment: in step s, lane half h carries columns
     // 256 ch + 128 h + 8 s + (0..7).
-    const int cbase = ch * 256 + h * 128;
-    u32x4 xv[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      xv[s] = trow ? load_bf16x8(xrow, cbase + 8 * s, k) : zero4;
-    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int i = nb * 32 + m;  // row of A feeding B-operand column m
       if (GAUSS) {
-        const uint16_t* arow = Ab + (int64_t)i * lda + cbase;
+        const uint16_t* arow = Ab + (int64_t)i * lda + ch * 256 + h * 128;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
           const u32x4 b = *reinterpret_cast<const u32x4*>(arow + 8 * s);
           acc[nb] = mfma32(xv[s], b, acc[nb]);
         }
       } else {
-        uint64_t w0 = 0, w1 = 0;
-        if (i < r) {
-          const Words4 blk = sign_block(seed, stream, (uint64_t)ch, (uint64_t)i);
-          w0 = h ? blk.w[2] : blk.w[0];
-          w1 = h ? blk.w[3] : blk.w[1];
-        }
-        const bool live = i < r;
+        const Words4 blk = sign_block(seed, stream, (uint64_t)ch, (uint64_t)i);
+        const uint64_t w0 = h ? blk.w[2] : blk.w[0];
+        const uint64_t w1 = h ? blk.w[3] : blk.w[1];
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
           const uint64_t w = s < 8 ? w0 : w1;
           const uint32_t byte = (uint32_t)(w >> (8 * (s & 7))) & 0xFFu;
-          const u32x4 b = live ? signs_to_bf16x8(byte) : zero4;
-          acc[nb] = mfma32(xv[s], b, acc[nb]);
+          acc[nb] = mfma32(xv[s], signs_to_bf16x8(byte), acc[nb]);
         }
       }
     }
+  };
+  u32x4 xa[16], xb[16];
+  int ch = wave;
+  if (ch < n_chunks) {
+    load(ch, xa);
+    load(ch + kProjWaves, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    for (; ch < n_chunks; ch += 2 * kProjWaves) {
+      compute(ch, xa);
+      __builtin_amdgcn_sched_barrier(0);
+      load(ch + 2 * kProjWaves, xa);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ch + kProjWaves < n_chunks) compute(ch + kProjWaves, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      load(ch + 3 * kProjWaves, xb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // Sum the four waves' partial P in a fixed order and write P^T as hi/lo.
-  const int n_out = tid & 31;   // A row within the block
-  const int tg = tid >> 5;      // tokens 4 tg .. 4 tg + 3
+  // Sum the waves' partial P in a fixed order (w0 + w1 + ...) and store the
+  // hi/lo pair in the tiled layout.  Thread (n_out, tg) owns the TPT tokens
+  // TPT tg .. TPT tg + TPT - 1 of A row 32 nb + n_out.
+  constexpr int TPT = 16 / kProjWaves;     // tokens per thread: 2 or 4
+  const int n_out = tid & 31;
+  const int tg = tid >> 5;
+  const int nb16 = rp >> 4;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -119,21 +164,27 @@ __global__ __launch_bounds__(256) void project_kernel(
       red[wave][row * 33 + m] = acc[nb][v];
     }
     __syncthreads();
-    uint16_t hi[4], lo[4];
+    const int i = nb * 32 + n_out;
+    if (i < rp) {
+      uint16_t hi[TPT], lo[TPT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = (4 * tg + u) * 33 + n_out;
-      float p = ((red[0][idx] + red[1][idx]) + red[2][idx]) + red[3][idx];
-      split_bf16(p * c, hi[u], lo[u]);
+      for (int u = 0; u < TPT; ++u) {
+        const int idx = (TPT * tg + u) * 33 + n_out;
+        float p = red[0][idx];
+#pragma unroll
+        for (int w = 1; w < kProjWaves; ++w) p += red[w][idx];
+        split_bf16(p * c, hi[u], lo[u]);
+      }
+      const int u0 = TPT * tg;                 // first token within the step
+      const int64_t slot = (int64_t)(((u0 >> 3) * 16 + (i & 15)) * 8 + (u0 & 7));
+      uint16_t* ph = Pt + p_block(step, i >> 4, 0, nb16) + slot;
+      uint16_t* pl = Pt + p_block(step, i >> 4, 1, nb16) + slot;
+#pragma unroll
+      for (int u = 0; u < TPT; u += 2) {
+        *reinterpret_cast<uint32_t*>(ph + u) = (uint32_t)hi[u] | ((uint32_t)hi[u + 1] << 16);
+        *reinterpret_cast<uint32_t*>(pl + u) = (uint32_t)lo[u] | ((uint32_t)lo[u + 1] << 16);
+      }
     }
-    const int64_t off = (int64_t)(nb * 32 + n_out) * ldp + t0 + 4 * tg;
-    u32x2 vh, vl;
-    vh[0] = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
-    vh[1] = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
-    vl[0] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
-    vl[1] = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
-    *reinterpret_cast<u32x2*>(Phi + off) = vh;
-    *reinterpret_cast<u32x2*>(Plo + off) = vl;
     __syncthreads();
   }
 }
@@ -163,67 +214,89 @@ __global__ __launch_bounds__(256) void gauss_basis_kernel(
 }
 
 // --------------------------------------------------------------- accumulate
-template <int Q>
-struct DyBlock;
-template <>
-struct DyBlock<8> {
-  u32x4 v;
-};
-template <>
-struct DyBlock<4> {
-  u32x2 v;
-};
-template <>
-struct DyBlock<2> {
-  uint32_t v;
+// One pipeline stage of the accumulate kernel for lane (m, g4): eight dY rows
+// (tokens tb .. tb + 7) x Q columns from `col`, and the P_hi / P_lo operands
+// (16 r-columns per block, the same eight tokens).
+template <int Q, int NB16>
+struct AccStage {
+  uint32_t R[8][Q / 2];
+  u32x4 bh[NB16], bl[NB16];
 };
 
-// Q bf16 of one dY row starting at column `col` (zeros past `ncols`).
-template <int Q>
-__device__ __forceinline__ void load_dy(const uint16_t* row, int col, int ncols,
-                                        uint32_t out[Q / 2]) {
-  if (col + Q <= ncols) {
-    if constexpr (Q == 8) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(row + col);
+template <int Q, bool MASKED>
+__device__ __forceinline__ void load_dy_row(const uint16_t* row, int col, int d,
+                                            bool tok_ok, uint32_t out[Q / 2]) {
+  const int valid = d - col;
+  const uint16_t* p = row + (!MASKED || valid > 0 ? col : 0);
+  uint32_t v[Q / 2];
+  if constexpr (Q == 8) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) out[p] = v[p];
-    } else if constexpr (Q == 4) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(row + col);
-      out[0] = v[0];
-      out[1] = v[1];
-    } else {
-      out[0] = *reinterpret_cast<const uint32_t*>(row + col);
-    }
+    for (int i = 0; i < 4; ++i) v[i] = x[i];
+  } else if constexpr (Q == 4) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    v[0] = x[0];
+    v[1] = x[1];
+  } else {
+    v[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+  if constexpr (!MASKED) {
+#pragma unroll
+    for (int i = 0; i < Q / 2; ++i) out[i] = v[i];
     return;
   }
 #pragma unroll
-  for (int p = 0; p < Q / 2; ++p) out[p] = 0u;
-#pragma unroll
-  for (int e = 0; e < Q; ++e) {
-    if (col + e < ncols) {
-      const uint32_t hv = row[col + e];
-      out[e >> 1] |= (e & 1) ? (hv << 16) : hv;
-    }
+  for (int i = 0; i < Q / 2; ++i) {
+    const int left = valid - 2 * i;
+    const uint32_t keep = left >= 2 ? 0xFFFFFFFFu : left == 1 ? 0x0000FFFFu : 0u;
+    out[i] = tok_ok ? (v[i] & keep) : 0u;
   }
 }
 
+template <int Q, int NB16, bool MASKED>
+__device__ __forceinline__ void load_acc_stage(
+    const uint16_t* __restrict__ dY, int64_t ldd, int T, int d, int col, int step,
+    int g4, int lane, const uint16_t* __restrict__ Pt, AccStage<Q, NB16>& st) {
+  const int tb = step * 32 + 8 * g4;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = tb + e;
+    const bool ok = !MASKED || t < T;
+    load_dy_row<Q, MASKED>(dY + (int64_t)(ok ? t : T - 1) * ldd, col, d, ok, st.R[e]);
+  }
+  // one contiguous 1 KB block per (16 r columns, half): lane l reads slot l
+#pragma unroll
+  for (int nb = 0; nb < NB16; ++nb) {
+    st.bh[nb] = *reinterpret_cast<const u32x4*>(Pt + p_block(step, nb, 0, NB16) + 8 * lane);
+    st.bl[nb] = *reinterpret_cast<const u32x4*>(Pt + p_block(step, nb, 1, NB16) + 8 * lane);
+  }
+}
+
+// Register i = (q * NB16 + nb) * 4 + v of lane (n = lane % 16, g = lane / 16)
+// of the accumulators holds d row dc0 + Q (4 g + v) + q, r column 16 nb + n.
 template <int Q, int NB16>
-__global__ __launch_bounds__(256) void accumulate_kernel(
+__device__ __forceinline__ int acc_drow(int dc0, int i, int ln) {
+  return dc0 + Q * (4 * (ln >> 4) + (i & 3)) + i / (NB16 * 4);
+}
+template <int NB16>
+__device__ __forceinline__ int acc_rcol(int i, int ln) {
+  return 16 * ((i >> 2) % NB16) + (ln & 15);
+}
+
+template <int Q, int NB16, int kAccWaves, bool MASKED>
+__global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
     const uint16_t* __restrict__ dY, int64_t ldd, int T, int d, int r,
-    const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ Plo,
-    int64_t ldp, int steps_total, int steps_per_split, int n_split,
-    float* __restrict__ S, float* __restrict__ part, int64_t d_pad,
-    uint32_t* __restrict__ counters) {
-  constexpr int RP = 16 * NB16;   // padded r handled here
-  constexpr int DC = 16 * Q;      // d columns per work-group
-  constexpr int NREG = Q * NB16 * 4;
-  __shared__ float red[NREG * 64];
-  __shared__ int is_last;
+    const uint16_t* __restrict__ Pt, int steps_total, int steps_per_split,
+    float* __restrict__ S, float* __restrict__ part) {
+  constexpr int DC = 16 * Q;            // d columns per work-group
+  constexpr int NREG = Q * NB16 * 4;    // accumulator floats per lane
+  constexpr int CH = NREG < 32 ? NREG : 32;  // registers per LDS round
+  __shared__ float red[(kAccWaves - 1) * CH * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int m = lane & 15;   // A-operand row group (d) and B-operand column (r)
+  const int m = lane & 15;   // A-operand row group (d columns)
   const int g4 = lane >> 4;  // which 8 tokens of the 32-token step
   const int dg = blockIdx.x;
   const int sp = blockIdx.y;
@@ -232,154 +305,175 @@ __global__ __launch_bounds__(256) void accumulate_kernel(
   const int s_begin = sp * steps_per_split;
   const int s_end = min(steps_total, s_begin + steps_per_split);
 
-  f32x4 acc[Q][NB16];
+  float acc[NREG];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-#pragma unroll
-    for (int nb = 0; nb < NB16; ++nb) acc[q][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < NREG; ++i) acc[i] = 0.0f;
 
-  for (int st = s_begin + wave; st < s_end; st += kAccWaves) {
-    const int tb = st * 32 + 8 * g4;
-    uint32_t R[8][Q / 2];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = tb + e;
-      if (t < T) {
-        load_dy<Q>(dY + (int64_t)t * ldd, col, d, R[e]);
-      } else {
-#pragma unroll
-        for (int p = 0; p < Q / 2; ++p) R[e][p] = 0u;
-      }
-    }
-    u32x4 bh[NB16], bl[NB16];
-#pragma unroll
-    for (int nb = 0; nb < NB16; ++nb) {
-      const int64_t off = (int64_t)(16 * nb + m) * ldp + tb;
-      bh[nb] = *reinterpret_cast<const u32x4*>(Phi + off);
-      bl[nb] = *reinterpret_cast<const u32x4*>(Plo + off);
-    }
+  // Ping-pong pipeline over this wave's steps (st, st + W, st + 2W, ...):
+  // the loads of one buffer are in flight while the other buffer is
+  // multiplied.  sched_barrier keeps the scheduler from sinking the loads
+  // back next to their consumers.
+  auto compute = [&](const AccStage<Q, NB16>& cs) {
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       // K assignment: lane group g4, element e <-> token tb + e.
       u32x4 a;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        a[u] = __builtin_amdgcn_perm(R[2 * u + 1][q >> 1], R[2 * u][q >> 1],
+        a[u] = __builtin_amdgcn_perm(cs.R[2 * u + 1][q >> 1], cs.R[2 * u][q >> 1],
                                      (q & 1) ? 0x07060302u : 0x05040100u);
       }
 #pragma unroll
       for (int nb = 0; nb < NB16; ++nb) {
-        acc[q][nb] = mfma16(a, bh[nb], acc[q][nb]);
-        acc[q][nb] = mfma16(a, bl[nb], acc[q][nb]);
+        f32x4 c4 = {acc[(q * NB16 + nb) * 4 + 0], acc[(q * NB16 + nb) * 4 + 1],
+                    acc[(q * NB16 + nb) * 4 + 2], acc[(q * NB16 + nb) * 4 + 3]};
+        c4 = mfma16(a, cs.bh[nb], c4);
+        c4 = mfma16(a, cs.bl[nb], c4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[(q * NB16 + nb) * 4 + v] = c4[v];
       }
+    }
+  };
+  auto load = [&](int step, AccStage<Q, NB16>& ls) {
+    // steps past the end re-read the last step of the range (never used)
+    const int sc = step < s_end ? step : s_end - 1;
+    load_acc_stage<Q, NB16, MASKED>(dY, ldd, T, d, col, sc, g4, lane, Pt, ls);
+  };
+  AccStage<Q, NB16> b0, b1;
+  int st = s_begin + wave;
+  if (st < s_end) {
+    load(st, b0);
+    load(st + kAccWaves, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (; st < s_end; st += 2 * kAccWaves) {
+      compute(b0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(st + 2 * kAccWaves, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + kAccWaves < s_end) compute(b1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(st + 3 * kAccWaves, b1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Fixed-order sum of the four waves: ((w0 + w1) + (w2 + w3)).
-  auto store_lds = [&]() {
+  // Fixed-order sum of the waves into wave 0: (((w0 + w1) + w2) + ...),
+  // CH registers per round through LDS.
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
+  for (int c0 = 0; c0 < NREG; c0 += CH) {
+    if (wave > 0) {
 #pragma unroll
-      for (int nb = 0; nb < NB16; ++nb)
+      for (int i = 0; i < CH; ++i) red[((wave - 1) * CH + i) * 64 + lane] = acc[c0 + i];
+    }
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          red[((q * NB16 + nb) * 4 + v) * 64 + lane] = acc[q][nb][v];
-  };
-  auto add_lds = [&]() {
+      for (int w = 0; w < kAccWaves - 1; ++w)
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
-#pragma unroll
-      for (int nb = 0; nb < NB16; ++nb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          acc[q][nb][v] += red[((q * NB16 + nb) * 4 + v) * 64 + lane];
-  };
-  if (wave == 1) store_lds();
-  __syncthreads();
-  if (wave == 0) add_lds();
-  __syncthreads();
-  if (wave == 3) store_lds();
-  __syncthreads();
-  if (wave == 2) add_lds();
-  __syncthreads();
-  if (wave == 2) store_lds();
-  __syncthreads();
-  if (wave == 0) add_lds();
+        for (int i = 0; i < CH; ++i) acc[c0 + i] += red[(w * CH + i) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
 
-  // Wave 0 lane (n = lane % 16, g = lane / 16) holds, for every (q, nb, v),
-  // the value of d row dc0 + Q (4 g + v) + q, r column 16 nb + n.
-  if (wave == 0) {
-    const int n = lane & 15;
-    const int g = lane >> 4;
+  if (part == nullptr) {          // a single split: add straight into S
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
-#pragma unroll
-      for (int nb = 0; nb < NB16; ++nb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int drow = dc0 + Q * (4 * g + v) + q;
-          const int rc = 16 * nb + n;
-          if (n_split == 1) {
-            if (drow < d && rc < r) S[(int64_t)drow * r + rc] += acc[q][nb][v];
-          } else {
-            part[((int64_t)sp * d_pad + drow) * RP + rc] = acc[q][nb][v];
-          }
-        }
+    for (int i = 0; i < NREG; ++i) {
+      const int drow = acc_drow<Q, NB16>(dc0, i, lane);
+      const int rc = acc_rcol<NB16>(i, lane);
+      if (drow < d && rc < r) S[(int64_t)drow * r + rc] += acc[i];
+    }
+    return;
   }
-  if (n_split == 1) return;
+  // Partial tile of this split, stored register-major ([i][lane], coalesced).
+  float* my = part + ((int64_t)sp * gridDim.x + dg) * (NREG * 64);
+#pragma unroll
+  for (int i = 0; i < NREG; ++i) my[i * 64 + lane] = acc[i];
+}
 
-  // Last work-group of this column group adds the partial tiles to S.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&counters[dg], 1u);
-    is_last = (prev == (uint32_t)(n_split - 1));
+// S += sum over splits of the partial tiles, in split order.  One thread per
+// four consecutive floats of a tile (four lanes with the same d row and four
+// consecutive r columns).
+template <int Q, int NB16>
+__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part,
+                                                       int n_split, int n_dgroups,
+                                                       int d, int r, bool s_vec4,
+                                                       float* __restrict__ S) {
+  constexpr int NREG = Q * NB16 * 4;
+  constexpr int TILE = NREG * 64;
+  const int64_t idx4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_split = (int64_t)n_dgroups * TILE;
+  if (idx4 * 4 >= per_split) return;
+  const int64_t flat = idx4 * 4;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(part + flat);
+  for (int s = 1; s < n_split; ++s)
+    sum += *reinterpret_cast<const f32x4*>(part + (int64_t)s * per_split + flat);
+  const int dg = (int)(flat / TILE);
+  const int within = (int)(flat % TILE);
+  const int i = within >> 6;
+  const int ln = within & 63;       // multiple of 4
+  const int drow = acc_drow<Q, NB16>(dg * 16 * Q, i, ln);
+  const int rc = acc_rcol<NB16>(i, ln);
+  if (drow >= d) return;
+  float* srow = S + (int64_t)drow * r;
+  if (s_vec4 && rc + 4 <= r) {     // r % 4 == 0 and S 16-byte aligned
+    f32x4* p = reinterpret_cast<f32x4*>(srow + rc);
+    *p += sum;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (rc + e < r) srow[rc + e] += sum[e];
   }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int idx = tid; idx < DC * RP; idx += 256) {
-    const int drow = dc0 + idx / RP;
-    const int rc = idx % RP;
-    if (drow >= d || rc >= r) continue;
-    const float* pp = part + (int64_t)drow * RP + rc;
-    float sum = pp[0];
-    for (int s = 1; s < n_split; ++s) sum += pp[(int64_t)s * d_pad * RP];
-    S[(int64_t)drow * r + rc] += sum;
-  }
-  if (tid == 0) counters[dg] = 0u;
+}
+
+template <int NB, bool GAUSS, bool MASKED>
+void launch_project_t(const SketchPlan& p, const uint16_t* X, int64_t ldx, int T,
+                      int k, uint64_t seed, uint64_t stream, float c,
+                      const uint16_t* Ab, uint16_t* Pt, hipStream_t s) {
+  constexpr int W = proj_waves(NB);
+  const dim3 grid((unsigned)(p.t_pad / 32));
+  hipLaunchKernelGGL((project_kernel<NB, GAUSS, MASKED, W>), grid, dim3(64 * W), 0,
+                     s, X, ldx, T, k, p.rp, seed, stream, c, Ab, p.k_pad, Pt);
 }
 
 template <int NB>
 hipError_t launch_project(const SketchPlan& p, const uint16_t* X, int64_t ldx,
-                          int T, int k, int r, uint64_t seed, uint64_t stream,
-                          bool gauss, float c, const uint16_t* Ab,
-                          uint16_t* Phi, uint16_t* Plo, uint32_t* cnt,
-                          hipStream_t s) {
-  const dim3 grid((unsigned)(p.t_pad / 32));
-  const int n_cnt = p.n_split > 1 ? p.n_dgroups : 0;
+                          int T, int k, uint64_t seed, uint64_t stream, bool gauss,
+                          float c, const uint16_t* Ab, uint16_t* Pt, hipStream_t s) {
+  const bool masked = (T % 32) != 0 || (k % 256) != 0;
   if (gauss) {
-    hipLaunchKernelGGL((project_kernel<NB, true>), grid, dim3(256), 0, s, X, ldx,
-                       T, k, r, seed, stream, 1.0f, Ab, p.k_pad, Phi, Plo,
-                       p.t_pad, cnt, n_cnt);
+    if (masked) launch_project_t<NB, true, true>(p, X, ldx, T, k, seed, stream, 1.0f, Ab, Pt, s);
+    else launch_project_t<NB, true, false>(p, X, ldx, T, k, seed, stream, 1.0f, Ab, Pt, s);
   } else {
-    hipLaunchKernelGGL((project_kernel<NB, false>), grid, dim3(256), 0, s, X,
-                       ldx, T, k, r, seed, stream, c, Ab, p.k_pad, Phi, Plo,
-                       p.t_pad, cnt, n_cnt);
+    if (masked) launch_project_t<NB, false, true>(p, X, ldx, T, k, seed, stream, c, Ab, Pt, s);
+    else launch_project_t<NB, false, false>(p, X, ldx, T, k, seed, stream, c, Ab, Pt, s);
   }
   return hipGetLastError();
 }
 
 template <int Q, int NB16>
-hipError_t launch_accumulate(const SketchPlan& p, const uint16_t* dY,
-                             int64_t ldd, int T, int d, int r,
-                             const uint16_t* Phi, const uint16_t* Plo, float* S,
-                             float* part, uint32_t* cnt, hipStream_t s) {
+hipError_t launch_accumulate(const SketchPlan& p, const uint16_t* dY, int64_t ldd,
+                             int T, int d, int r, const uint16_t* Pt, float* S,
+                             float* part, hipStream_t s) {
+  constexpr int kAccWaves = acc_waves(Q, NB16);
   const dim3 grid((unsigned)p.n_dgroups, (unsigned)p.n_split);
-  hipLaunchKernelGGL((accumulate_kernel<Q, NB16>), grid, dim3(256), 0, s, dY,
-                     ldd, T, d, r, Phi, Plo, p.t_pad, p.steps,
-                     p.steps_per_split, p.n_split, S, part, p.d_pad, cnt);
+  float* pp = p.n_split > 1 ? part : nullptr;
+  const bool masked = (T % 32) != 0 || (d % (16 * Q)) != 0;
+  if (masked) {
+    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, true>), grid,
+                       dim3(64 * kAccWaves), 0, s, dY, ldd, T, d, r, Pt, p.steps,
+                       p.steps_per_split, S, pp);
+  } else {
+    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, false>), grid,
+                       dim3(64 * kAccWaves), 0, s, dY, ldd, T, d, r, Pt, p.steps,
+                       p.steps_per_split, S, pp);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_split == 1) return e;
+  const int64_t quads = (int64_t)p.n_dgroups * Q * NB16 * 4 * 64 / 4;
+  const bool s_vec4 = (r % 4) == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+  hipLaunchKernelGGL((finalize_kernel<Q, NB16>), dim3((unsigned)((quads + 255) / 256)),
+                     dim3(256), 0, s, part, p.n_split, p.n_dgroups, d, r, s_vec4, S);
   return hipGetLastError();
 }
 
@@ -394,7 +488,7 @@ bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p) {
   q.rp = r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : r <= 128 ? 128 : 256;
   q.p_rows = q.rp < 32 ? 32 : q.rp;
   q.nb32 = q.p_rows / 32;
-  q.q_cols = q.rp <= 64 ? 8 : q.rp == 128 ? 4 : 2;
+  q.q_cols = q.rp <= 32 ? 8 : q.rp <= 128 ? 4 : 2;
   q.t_pad = round_up(T > 0 ? T : 1, 32);
   q.k_pad = round_up(k, 256);
   q.steps = (int)(q.t_pad / 32);
@@ -402,8 +496,9 @@ bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p) {
   q.n_dgroups = (int)((d + dc - 1) / dc);
   // Enough work-groups to cover the chip (256 CUs) while each wave keeps at
   // least two 32-token steps.
+  const int waves = acc_waves(q.q_cols, q.rp / 16);
   const int want = (256 + q.n_dgroups - 1) / q.n_dgroups;
-  const int max_split = q.steps / (2 * kAccWaves) > 0 ? q.steps / (2 * kAccWaves) : 1;
+  const int max_split = q.steps / (2 * waves) > 0 ? q.steps / (2 * waves) : 1;
   int n_split = want < max_split ? want : max_split;
   if (n_split < 1) n_split = 1;
   q.steps_per_split = (q.steps + n_split - 1) / n_split;
@@ -415,11 +510,8 @@ bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p) {
     off += (size_t)round_up((int64_t)bytes, 256);
     return o;
   };
-  const size_t p_bytes = (size_t)q.p_rows * (size_t)q.t_pad * 2;
-  q.off_phi = take(p_bytes);
-  q.off_plo = take(p_bytes);
+  q.off_pt = take((size_t)2 * q.rp * (size_t)q.t_pad * 2);
   q.off_part = take(q.n_split > 1 ? (size_t)q.n_split * q.d_pad * q.rp * 4 : 0);
-  q.off_cnt = take((size_t)q.n_dgroups * 4);
   q.off_gauss = take((size_t)q.p_rows * (size_t)q.k_pad * 2);
   q.total = off;
   *p = q;
@@ -430,10 +522,8 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
                          const uint16_t* dY, int64_t ldd, int T, int d, int k,
                          int r, uint64_t seed, uint64_t stream, int kind,
                          float* S, char* ws, hipStream_t s) {
-  uint16_t* Phi = reinterpret_cast<uint16_t*>(ws + p.off_phi);
-  uint16_t* Plo = reinterpret_cast<uint16_t*>(ws + p.off_plo);
+  uint16_t* Pt = reinterpret_cast<uint16_t*>(ws + p.off_pt);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
   uint16_t* Ab = reinterpret_cast<uint16_t*>(ws + p.off_gauss);
   const bool gauss = kind == 1;
   const float c = sign_scale(r);
@@ -441,24 +531,23 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
   if (gauss) {
     const int64_t threads = (int64_t)p.p_rows * (p.k_pad >> 2);
     hipLaunchKernelGGL(gauss_basis_kernel, dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, s, seed, stream, r, k, p.p_rows, p.k_pad, c,
-                       Ab);
+                       dim3(256), 0, s, seed, stream, r, k, p.p_rows, p.k_pad, c, Ab);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   switch (p.nb32) {
-    case 1: e = launch_project<1>(p, X, ldx, T, k, r, seed, stream, gauss, c, Ab, Phi, Plo, cnt, s); break;
-    case 2: e = launch_project<2>(p, X, ldx, T, k, r, seed, stream, gauss, c, Ab, Phi, Plo, cnt, s); break;
-    case 4: e = launch_project<4>(p, X, ldx, T, k, r, seed, stream, gauss, c, Ab, Phi, Plo, cnt, s); break;
-    default: e = launch_project<8>(p, X, ldx, T, k, r, seed, stream, gauss, c, Ab, Phi, Plo, cnt, s); break;
+    case 1: e = launch_project<1>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
+    case 2: e = launch_project<2>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
+    case 4: e = launch_project<4>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
+    default: e = launch_project<8>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
   }
   if (e != hipSuccess) return e;
   switch (p.rp) {
-    case 16: return launch_accumulate<8, 1>(p, dY, ldd, T, d, r, Phi, Plo, S, part, cnt, s);
-    case 32: return launch_accumulate<8, 2>(p, dY, ldd, T, d, r, Phi, Plo, S, part, cnt, s);
-    case 64: return launch_accumulate<8, 4>(p, dY, ldd, T, d, r, Phi, Plo, S, part, cnt, s);
-    case 128: return launch_accumulate<4, 8>(p, dY, ldd, T, d, r, Phi, Plo, S, part, cnt, s);
-    default: return launch_accumulate<2, 16>(p, dY, ldd, T, d, r, Phi, Plo, S, part, cnt, s);
+    case 16: return launch_accumulate<8, 1>(p, dY, ldd, T, d, r, Pt, S, part, s);
+    case 32: return launch_accumulate<8, 2>(p, dY, ldd, T, d, r, Pt, S, part, s);
+    case 64: return launch_accumulate<4, 4>(p, dY, ldd, T, d, r, Pt, S, part, s);
+    case 128: return launch_accumulate<4, 8>(p, dY, ldd, T, d, r, Pt, S, part, s);
+    default: return launch_accumulate<2, 16>(p, dY, ldd, T, d, r, Pt, S, part, s);
   }
 }
 
