@@ -201,6 +201,32 @@ def run_kl(lg, synth, reps=5):
     return res
 
 
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "sketch_merge_d4096_r64_traffic.md")
+
+
+def measured_traffic(kernels):
+    """HBM bytes per call of the given kernels from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
+    None when there is no summary or the kernel sources changed since."""
+    from rank_gradient_sketching_amd import profiling
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    text = open(PROFILE_TRAFFIC).read()
+    tag = "<!-- traffic-json: "
+    if tag not in text:
+        return None
+    tr = json.loads(text.split(tag, 1)[1].split(" -->", 1)[0])
+    if tr.get("source_hash") != profiling.kernel_source_hash():
+        return None
+    total = 0.0
+    for want in kernels:
+        hits = [v for k, v in tr["kernels"].items() if k.startswith(want)]
+        if not hits or hits[0]["read_bytes"] is None or hits[0]["write_bytes"] is None:
+            return None
+        total += hits[0]["read_bytes"] + hits[0]["write_bytes"]
+    return total
+
+
 def run_copy_calibration(reps=5, nbytes=1 << 30):
     """A plain device-to-device copy of known size: its achieved GB/s is the
     practical HBM ceiling, and its hardware byte counters calibrate the
@@ -283,9 +309,12 @@ def main():
     tokens_per_s = layer["tokens_per_step"] / (layer["step_ms"] * 1e-3)
     # dominant entry point: the sketch call (4 per step) - its two kernels
     # (project, accumulate) run back to back on the stream
-    roof = dict(kernel="logra_sketch_accumulate (project + accumulate kernels)",
+    # dominant entry point: the sketch call (4 per step); its kernels
+    # (project, accumulate, finalize) run back to back on the library's stream
+    sketch_kernels = ["project_kernel", "accumulate_kernel", "finalize_kernel"]
+    roof = dict(kernel="logra_sketch_accumulate (project + accumulate + finalize kernels)",
                 bound="hbm", achieved=sk["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
-                frac=sk["GBps"] / HBM_PEAK_GBPS, traffic=None,
+                frac=sk["GBps"] / HBM_PEAK_GBPS, traffic=measured_traffic(sketch_kernels),
                 bytes_per_launch=sk["bytes_per_call"], us_per_launch=sk["us_per_call"])
     out = {
         "metric": METRIC,

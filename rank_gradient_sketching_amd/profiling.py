@@ -1,0 +1,149 @@
+"""Summaries of rocprofv3 output for the LoGRA kernels.
+
+Two commands, both reading the CSV files rocprofv3 writes with
+`--output-format csv`:
+
+  stats    kernel-trace statistics (`*_kernel_stats.csv`) -> markdown table
+           of the library's kernels (calls, average / min / max duration).
+  traffic  two counter runs (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`,
+           `*_counter_collection.csv`) -> HBM bytes per dispatch of each
+           kernel, scaled by what the same counters read for a plain device
+           copy of known size (the largest `copyBuffer` dispatch of the run).
+
+`traffic` also records a hash of the kernel sources, so a consumer can tell
+whether the counters still describe the code being run.
+
+Usage:
+  python -m rank_gradient_sketching_amd.profiling stats STATS_CSV --out F.md --cmd "..."
+  python -m rank_gradient_sketching_amd.profiling traffic FETCH_DIR WRITE_DIR \
+      --copy-bytes N --out F.md --cmd "..."
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+
+def kernel_source_hash():
+    """sha256 over the HIP / C++ sources of the library, in name order."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if path.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name):
+    """'void logra::(anon)::accumulate_kernel<4, 4, 8, false>(...)' -> 'accumulate_kernel<4, 4, 8, false>'."""
+    base = name.split("(")[0] if "(anonymous" not in name else name
+    if "logra::" in name:
+        base = name.split("logra::")[-1]
+        base = base.replace("(anonymous namespace)::", "")
+        depth, out = 0, []
+        for ch in base:
+            if ch == "(" and depth == 0:
+                break
+            depth += ch == "<"
+            depth -= ch == ">"
+            out.append(ch)
+        return "".join(out).strip()
+    return base.replace("void ", "").strip()[:80]
+
+
+def stats_table(stats_csv):
+    rows = []
+    for r in csv.DictReader(open(stats_csv)):
+        name = r["Name"]
+        if "logra" not in name and "copyBuffer" not in name:
+            continue
+        rows.append(dict(kernel=short_name(name), calls=int(r["Calls"]),
+                         avg_us=float(r["AverageNs"]) / 1e3, min_us=float(r["MinNs"]) / 1e3,
+                         max_us=float(r["MaxNs"]) / 1e3, pct=float(r["Percentage"])))
+    return rows
+
+
+def counter_per_kernel(run_dir, counter):
+    """{kernel: [value per dispatch]} of one counter (KiB for the size counters)."""
+    out = collections.defaultdict(list)
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic(fetch_dir, write_dir, copy_bytes):
+    fetch = counter_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = counter_per_kernel(write_dir, "WRITE_SIZE")
+    cp_f = max((v for k, vs in fetch.items() if "copyBuffer" in k for v in vs), default=None)
+    cp_w = max((v for k, vs in write.items() if "copyBuffer" in k for v in vs), default=None)
+    if not cp_f or not cp_w:
+        raise SystemExit("no copyBuffer dispatch found for calibration")
+    f_scale = copy_bytes / (cp_f * 1024.0)
+    w_scale = copy_bytes / (cp_w * 1024.0)
+    kernels = {}
+    for k in sorted(set(fetch) | set(write)):
+        if "logra" in k or k.split("<")[0].endswith("_kernel"):
+            fr = statistics.median(fetch[k]) * 1024.0 * f_scale if k in fetch else None
+            wr = statistics.median(write[k]) * 1024.0 * w_scale if k in write else None
+            kernels[k] = dict(read_bytes=fr, write_bytes=wr,
+                              dispatches=max(len(fetch.get(k, [])), len(write.get(k, []))))
+    return dict(copy_bytes=copy_bytes, fetch_scale=f_scale, write_scale=w_scale,
+                copy_fetch_kib=cp_f, copy_write_kib=cp_w, kernels=kernels,
+                source_hash=kernel_source_hash())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("--out", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="Kernel durations")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--cmd", required=True)
+    a = ap.parse_args()
+    if a.cmd_name == "stats":
+        rows = stats_table(a.stats_csv)
+        lines = [f"# {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
+                 f"Kernel sources: `{kernel_source_hash()}`", "",
+                 "| kernel | calls | avg us | min us | max us | % of GPU time |",
+                 "|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| `{r['kernel']}` | {r['calls']} | {r['avg_us']:.2f} | "
+                         f"{r['min_us']:.2f} | {r['max_us']:.2f} | {r['pct']:.2f} |")
+        open(a.out, "w").write("\n".join(lines) + "\n")
+    else:
+        tr = traffic(a.fetch_dir, a.write_dir, a.copy_bytes)
+        lines = ["# HBM traffic per dispatch (rocprofv3 counters, calibrated)", "",
+                 "Commands:", "", "```", a.cmd, "```", "",
+                 f"Calibration: a {a.copy_bytes} B device copy read FETCH_SIZE "
+                 f"{tr['copy_fetch_kib']:.0f} KiB and WRITE_SIZE {tr['copy_write_kib']:.0f} KiB, "
+                 f"so bytes = FETCH_SIZE x 1024 x {tr['fetch_scale']:.3f} and "
+                 f"WRITE_SIZE x 1024 x {tr['write_scale']:.3f}.", "",
+                 f"Kernel sources: `{tr['source_hash']}`", "",
+                 "| kernel | dispatches | read MiB | write MiB |", "|---|---|---|---|"]
+        for k, v in tr["kernels"].items():
+            rd = "-" if v["read_bytes"] is None else f"{v['read_bytes'] / 2**20:.2f}"
+            wr = "-" if v["write_bytes"] is None else f"{v['write_bytes'] / 2**20:.2f}"
+            lines.append(f"| `{k}` | {v['dispatches']} | {rd} | {wr} |")
+        lines += ["", "<!-- traffic-json: " + json.dumps(tr) + " -->"]
+        open(a.out, "w").write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()
