@@ -35,6 +35,19 @@ struct Words4 {
   uint64_t w[4];
 };
 
+// Full 128-bit product of a constant a and b from four 32x32 -> 64 multiply-
+// adds (v_mad_u64_u32); no partial sum can overflow 64 bits.
+__device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t b, uint64_t& hi,
+                                          uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+  const uint64_t p00 = (uint64_t)a0 * b0;
+  const uint64_t p01 = (uint64_t)a0 * b1 + (p00 >> 32);
+  const uint64_t p10 = (uint64_t)a1 * b0 + (uint32_t)p01;
+  hi = (uint64_t)a1 * b1 + (p01 >> 32) + (p10 >> 32);
+  lo = (p10 << 32) | (uint32_t)p00;
+}
+
 __device__ __forceinline__ Words4 philox4x64_10(uint64_t c0, uint64_t c1,
                                                 uint64_t c2, uint64_t c3,
                                                 uint64_t k0, uint64_t k1) {
@@ -44,10 +57,9 @@ __device__ __forceinline__ Words4 philox4x64_10(uint64_t c0, uint64_t c1,
       k0 += kPhiloxWeyl0;
       k1 += kPhiloxWeyl1;
     }
-    const uint64_t hi0 = __umul64hi(kPhiloxMul0, c0);
-    const uint64_t lo0 = kPhiloxMul0 * c0;
-    const uint64_t hi1 = __umul64hi(kPhiloxMul1, c2);
-    const uint64_t lo1 = kPhiloxMul1 * c2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(kPhiloxMul0, c0, hi0, lo0);
+    mulhilo64(kPhiloxMul1, c2, hi1, lo1);
     c0 = hi1 ^ c1 ^ k0;
     c1 = lo1;
     c2 = hi0 ^ c3 ^ k1;
@@ -88,6 +100,17 @@ __device__ __forceinline__ void gaussian_block(uint64_t seed, uint64_t stream,
     z[2 * p] = rad * cs;
     z[2 * p + 1] = rad * sn;
   }
+}
+
+// Value of x held by the lane 32 positions away (lane l <-> l ^ 32), from
+// one v_permlane32_swap.
+__device__ __forceinline__ uint32_t swap_halves(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint64_t swap_halves64(uint64_t x) {
+  return (uint64_t)swap_halves((uint32_t)x) |
+         ((uint64_t)swap_halves((uint32_t)(x >> 32)) << 32);
 }
 
 // ---------------------------------------------------------------- bf16

@@ -105,29 +105,44 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
     const int cc = cnk < n_chunks ? cnk : n_chunks - 1;   // past the end: re-read
     load_x_chunk(xrow, trow, !MASKED, cc, h, k, xv);
   };
+  // Sign words of A row 32 nb + m for this lane's half of chunk ch: words
+  // 2h and 2h+1 of the row's Philox block.  With two or more 32-row blocks the
+  // two lane halves generate different rows (half h makes block nb = 2j + h)
+  // and swap the words the other half needs, so no block is generated twice.
+  auto mfma_signs = [&](int nb, uint64_t w0, uint64_t w1, const u32x4 xv[16]) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const uint64_t w = s < 8 ? w0 : w1;
+      const uint32_t byte = (uint32_t)(w >> (8 * (s & 7))) & 0xFFu;
+      acc[nb] = mfma32(xv[s], signs_to_bf16x8(byte), acc[nb]);
+    }
+  };
   auto compute = [&](int ch, const u32x4 xv[16]) {
     // K assignment: in step s, lane half h carries columns
     // 256 ch + 128 h + 8 s + (0..7).
+    if (GAUSS) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int i = nb * 32 + m;  // row of A feeding B-operand column m
-      if (GAUSS) {
-        const uint16_t* arow = Ab + (int64_t)i * lda + ch * 256 + h * 128;
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint16_t* arow = Ab + (int64_t)(nb * 32 + m) * lda + ch * 256 + h * 128;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
           const u32x4 b = *reinterpret_cast<const u32x4*>(arow + 8 * s);
           acc[nb] = mfma32(xv[s], b, acc[nb]);
         }
-      } else {
-        const Words4 blk = sign_block(seed, stream, (uint64_t)ch, (uint64_t)i);
-        const uint64_t w0 = h ? blk.w[2] : blk.w[0];
-        const uint64_t w1 = h ? blk.w[3] : blk.w[1];
+      }
+    } else if (NB == 1) {
+      const Words4 blk = sign_block(seed, stream, (uint64_t)ch, (uint64_t)m);
+      mfma_signs(0, h ? blk.w[2] : blk.w[0], h ? blk.w[3] : blk.w[1], xv);
+    } else {
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          const uint64_t w = s < 8 ? w0 : w1;
-          const uint32_t byte = (uint32_t)(w >> (8 * (s & 7))) & 0xFFu;
-          acc[nb] = mfma32(xv[s], signs_to_bf16x8(byte), acc[nb]);
-        }
+      for (int j = 0; j < NB / 2; ++j) {
+        const Words4 blk =
+            sign_block(seed, stream, (uint64_t)ch, (uint64_t)((2 * j + h) * 32 + m));
+        // half 0 needs words 0,1 of both blocks; half 1 needs words 2,3
+        const uint64_t r0 = swap_halves64(h ? blk.w[0] : blk.w[2]);
+        const uint64_t r1 = swap_halves64(h ? blk.w[1] : blk.w[3]);
+        mfma_signs(2 * j, h ? r0 : blk.w[0], h ? r1 : blk.w[1], xv);
+        mfma_signs(2 * j + 1, h ? blk.w[2] : r0, h ? blk.w[3] : r1, xv);
       }
     }
   };
