@@ -91,8 +91,8 @@ int logra_merge(uint16_t* W, int64_t ldw, const float* S, int64_t d, int64_t k,
   if (!dim_ok(d) || !dim_ok(k) || !rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
   if (!aligned(W, 16) || !aligned(S, 4) || !ld_ok(ldw, k)) return LOGRA_EINVAL;
   if (!isfinite(alpha) || !isfinite(eta)) return LOGRA_EINVAL;
-  // one work-group per 256 x 256 tile, flat grid
-  if (((d + 255) / 256) * ((k + 255) / 256) >= (int64_t(1) << 31)) return LOGRA_EINVAL;
+  // one work-group per tile of at least 128 rows x 256 columns, flat grid
+  if (((d + 127) / 128) * ((k + 255) / 256) >= (int64_t(1) << 31)) return LOGRA_EINVAL;
   return hip_status(logra::launch_merge(W, ldw, S, (int)d, (int)k, r, seed, stream,
                                         kind, alpha, eta, s));
 }

@@ -9,8 +9,9 @@
 // One work-group owns 256 rows x 256 columns of W (one sign block wide); its
 // four waves own 64 rows each.  Columns are processed in four passes of 64:
 //   1. the pass's slice of A (r x 64) is regenerated into LDS as bf16,
-//      transposed (column-major, r contiguous) - signs from registers holding
-//      the Philox block of two A rows per thread, or Gaussian entries;
+//      transposed (column-major, r contiguous) by all threads - signs from
+//      the Philox words of the block's A rows (drawn once per work-group and
+//      parked in LDS), or Gaussian entries;
 //   2. 16x16x32 bf16 MFMA with M = W columns, N = W rows, K = r computes the
 //      slice of S A; S enters as a hi/lo bf16 pair, so the product keeps about
 //      16 bits of S;
@@ -26,18 +27,18 @@ namespace logra {
 
 namespace {
 
-constexpr int kMergeRows = 256;
 constexpr int kMergeCols = 256;
 constexpr int kPassCols = 64;
 
-template <int NKS, bool GAUSS, bool MASKED>
-__global__ __launch_bounds__(256) void merge_kernel(
+template <int NKS, bool GAUSS, bool MASKED, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void merge_kernel(
     uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ S, int d,
     int k, int r, uint64_t seed, uint64_t stream, float scale, float cr) {
   constexpr int RP = 32 * NKS;    // r padded to whole K steps
   constexpr int LDA = RP + 8;     // bf16 per LDS column (+16 B against conflicts)
   constexpr bool kDouble = NKS <= 4;  // two A slices fit in 64 KB of LDS
-  __shared__ uint16_t At[(kDouble ? 2 : 1) * kPassCols * LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t At[(kDouble ? 2 : 1) * kPassCols * LDA];
+  __shared__ __attribute__((aligned(16))) uint64_t sgn[GAUSS ? 1 : 4 * RP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
   const int cb = (int)(blockIdx.x % (unsigned)n_cb);
   const int rblk = (int)(blockIdx.x / (unsigned)n_cb);
   const int col0 = cb * kMergeCols;
-  const int row0 = rblk * kMergeRows + wave * 64;
+  const int row0 = rblk * (64 * kWaves) + wave * 64;
   const int n_pass = min(kMergeCols / kPassCols, (k - col0 + kPassCols - 1) / kPassCols);
 
   // S operands: rows row0 + 16 nt + m, K = r columns 32 ks + 8 g + (0..7),
@@ -58,9 +59,8 @@ __global__ __launch_bounds__(256) void merge_kernel(
   constexpr bool kHoistS = NKS <= 2;
   // rows of this wave all inside d and r a multiple of 32: plain float4 loads
   const bool s_fast = !MASKED;
-  auto s_operands = [&](int nt, int ks, u32x4& hi, u32x4& lo) {
+  auto s_raw = [&](int nt, int ks, float v[8]) {
     const int row = row0 + 16 * nt + m;
-    float v[8];
     if (s_fast) {
       const f32x4* sp = reinterpret_cast<const f32x4*>(S + (int64_t)row * r + 32 * ks + 8 * g);
       const f32x4 a = sp[0], b = sp[1];
@@ -78,6 +78,8 @@ __global__ __launch_bounds__(256) void merge_kernel(
         v[e] = (row < d && rc < r) ? x : 0.0f;
       }
     }
+  };
+  auto s_split = [&](const float v[8], u32x4& hi, u32x4& lo) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       uint16_t h0, l0, h1, l1;
@@ -87,36 +89,37 @@ __global__ __launch_bounds__(256) void merge_kernel(
       lo[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
   };
+  auto s_operands = [&](int nt, int ks, u32x4& hi, u32x4& lo) {
+    float v[8];
+    s_raw(nt, ks, v);
+    s_split(v, hi, lo);
+  };
   u32x4 sh[4][kHoistS ? NKS : 1], sl[4][kHoistS ? NKS : 1];
-  if constexpr (kHoistS) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) s_operands(nt, ks, sh[nt][ks], sl[nt][ks]);
-  }
 
-  // Sign basis: thread tid < RP / 2 keeps the Philox blocks of A rows
-  // 2 tid and 2 tid + 1 for this 256-column block.
-  uint64_t sw0[4] = {0, 0, 0, 0}, sw1[4] = {0, 0, 0, 0};
-  const int ra = 2 * tid, rb = 2 * tid + 1;
-  if (!GAUSS && tid < RP / 2) {
-    if (ra < r) {
-      const Words4 b = sign_block(seed, stream, (uint64_t)cb, (uint64_t)ra);
+  // Sign basis: thread tid < RP / 2 draws the Philox blocks of A rows 2 tid
+  // and 2 tid + 1 for this 256-column block and parks their words in LDS,
+  // word-major (sgn[q * RP + i] = word q of row i: columns 64 q .. 64 q + 63).
+  auto sign_words = [&]() {
+    if (!GAUSS && tid < RP / 2) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sw0[q] = b.w[q];
-    }
-    if (rb < r) {
-      const Words4 b = sign_block(seed, stream, (uint64_t)cb, (uint64_t)rb);
+      for (int h = 0; h < 2; ++h) {
+        const int i = 2 * tid + h;
+        Words4 b = {{0, 0, 0, 0}};
+        if (i < r) b = sign_block(seed, stream, (uint64_t)cb, (uint64_t)i);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sw1[q] = b.w[q];
+        for (int q = 0; q < 4; ++q) sgn[q * RP + i] = b.w[q];
+      }
     }
-  }
+  };
 
   // A slice of pass p into LDS: buf[col * LDA + i] = A[i][col0 + 64 p + col].
+  // Sign basis: every thread takes (8-row group G, column c) jobs: it reads the
+  // eight words of rows 8G .. 8G + 7 (one broadcast read per wave), gathers
+  // their bit c into one byte and expands it to eight +-1 bf16 (rows >= r: 0).
   auto build_A = [&](int pass, uint16_t* buf) {
     const int c0 = col0 + pass * kPassCols;
     if (GAUSS) {
-      for (int job = tid; job < RP * (kPassCols / 4); job += 256) {
+      for (int job = tid; job < RP * (kPassCols / 4); job += 64 * kWaves) {
         const int i = job / (kPassCols / 4);
         const int cc = 4 * (job % (kPassCols / 4));
         uint16_t v[4] = {0, 0, 0, 0};
@@ -127,17 +130,29 @@ __global__ __launch_bounds__(256) void merge_kernel(
 #pragma unroll
         for (int a = 0; a < 4; ++a) buf[(cc + a) * LDA + i] = v[a];
       }
-    } else if (tid < RP / 2) {
-      // word `pass` of each block holds columns 64 pass .. 64 pass + 63
-      const uint64_t wa = pass == 0 ? sw0[0] : pass == 1 ? sw0[1] : pass == 2 ? sw0[2] : sw0[3];
-      const uint64_t wb = pass == 0 ? sw1[0] : pass == 1 ? sw1[1] : pass == 2 ? sw1[2] : sw1[3];
-      const uint32_t one = 0x3F80u, neg = 0xBF80u;
-      uint32_t* b32 = reinterpret_cast<uint32_t*>(buf);
-#pragma unroll 8
-      for (int cc = 0; cc < kPassCols; ++cc) {
-        const uint32_t lo = ra < r ? (((wa >> cc) & 1u) ? neg : one) : 0u;
-        const uint32_t hi = rb < r ? (((wb >> cc) & 1u) ? neg : one) : 0u;
-        b32[(cc * LDA) / 2 + tid] = lo | (hi << 16);
+    } else {
+      constexpr int kJobs = kPassCols * (RP / 8);
+#pragma unroll
+      for (int job = tid; job < kJobs; job += 64 * kWaves) {
+        const int c = job & (kPassCols - 1);
+        const int grp = job / kPassCols;
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(&sgn[pass * RP + 8 * grp]);
+        const int half = c >> 5;           // which dword of each 64-bit word
+        const int bit = c & 31;
+        uint32_t byte = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) byte |= ((wp[2 * e + half] >> bit) & 1u) << e;
+        u32x4 v = signs_to_bf16x8(byte);
+        const int valid = r - 8 * grp;     // rows of this group below r
+        if (valid < 8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t keep = (2 * q < valid ? 0x0000FFFFu : 0u) |
+                                  (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
+            v[q] &= keep;
+          }
+        }
+        *reinterpret_cast<u32x4*>(&buf[c * LDA + 8 * grp]) = v;
       }
     }
   };
@@ -257,25 +272,49 @@ __global__ __launch_bounds__(256) void merge_kernel(
     }
   };
 
+  // Prologue: start the loads first (S rows, then the W elements of pass 0),
+  // regenerate the signs and the first A slice while they are in flight, and
+  // only then wait for S.
   u32x4 wa[4][2], wb[4][2];
-  build_A(0, buf0);
+  float sraw[4][kHoistS ? NKS : 1][8];
+  if constexpr (kHoistS) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) s_raw(nt, ks, sraw[nt][ks]);
+  }
   load_W(0, wa);
+  __builtin_amdgcn_sched_barrier(0);
+  sign_words();
+  __syncthreads();
+  build_A(0, buf0);
+  if constexpr (kHoistS) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) s_split(sraw[nt][ks], sh[nt][ks], sl[nt][ks]);
+  }
   do_pass(0, wa, wb);
   if (n_pass > 1) do_pass(1, wb, wa);
   if (n_pass > 2) do_pass(2, wa, wb);
   if (n_pass > 3) do_pass(3, wb, wa);
 }
 
+// Four waves (256 rows) per work-group: measured faster than two at the
+// 4096 x 4096 layer shape.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeRows = 64 * kMergeWaves;
+
 template <int NKS, bool MASKED>
 void launch_merge_m(uint16_t* W, int64_t ldw, const float* S, int d, int k, int r,
                     uint64_t seed, uint64_t stream, bool gauss, float scale,
                     float cr, hipStream_t s, dim3 grid) {
   if (gauss) {
-    hipLaunchKernelGGL((merge_kernel<NKS, true, MASKED>), grid, dim3(256), 0, s, W,
-                       ldw, S, d, k, r, seed, stream, scale, cr);
+    hipLaunchKernelGGL((merge_kernel<NKS, true, MASKED, kMergeWaves>), grid,
+                       dim3(kMergeRows), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
   } else {
-    hipLaunchKernelGGL((merge_kernel<NKS, false, MASKED>), grid, dim3(256), 0, s, W,
-                       ldw, S, d, k, r, seed, stream, scale, cr);
+    hipLaunchKernelGGL((merge_kernel<NKS, false, MASKED, kMergeWaves>), grid,
+                       dim3(kMergeRows), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
   }
 }
 
