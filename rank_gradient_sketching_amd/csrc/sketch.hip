@@ -9,15 +9,17 @@
 // Kernels on the caller's stream (no cross-work-group synchronisation inside
 // any of them: on this part an agent-scope fence per work-group costs far more
 // than an extra launch):
-//   project    P = c * X A^T (T x r).  One work-group per 32 tokens; its eight
-//              waves split k in 256-column chunks.  For the sign basis each
-//              lane regenerates the sign bits of its A row in registers from
-//              Philox (one block per row and chunk) and expands them to bf16
-//              +-1 MFMA operands, so A never touches memory.  Products with
-//              +-1 are exact; 32x32x16 bf16 MFMA accumulates in fp32; the
-//              waves' partial sums meet in LDS in a fixed order.  P is stored
-//              as a hi/lo bf16 pair in the accumulate kernel's operand order
-//              (one contiguous 1 KB block per 32 tokens x 16 r columns).
+//   project    P = c * X A^T (T x r).  One work-group per 32 tokens; its
+//              waves split k in 256-column chunks, which reach LDS through
+//              direct global->LDS loads (whole cache lines per instruction)
+//              while the previous chunk is multiplied.  For the sign basis
+//              each lane regenerates the sign bits of its A row in registers
+//              from Philox (one block per row and chunk) and expands them to
+//              bf16 +-1 MFMA operands, so A never touches memory.  Products
+//              with +-1 are exact; 32x32x16 bf16 MFMA accumulates in fp32;
+//              the waves' partial sums meet in LDS in a fixed order.  P is
+//              stored as a hi/lo bf16 pair in the accumulate kernel's operand
+//              order (one contiguous 1 KB block per 32 tokens x 16 r columns).
 //   accumulate S += dY^T P.  A work-group owns 16*Q columns of d and a range
 //              of 32-token steps.  Each lane loads an 8-token x Q-column block
 //              of dY with row-contiguous loads and transposes it in registers
@@ -37,8 +39,8 @@ namespace logra {
 
 namespace {
 
-// Waves per project work-group: eight (two per SIMD) unless the accumulators
-// of a large rank need the bigger per-wave register budget.
+// Waves per project work-group: eight (two per SIMD, 128 KB of X staging)
+// unless the accumulators of a large rank need the larger register budget.
 constexpr int proj_waves(int nb) { return nb <= 4 ? 8 : 4; }
 
 // Waves per accumulate work-group: eight (two per SIMD) while the
@@ -46,22 +48,17 @@ constexpr int proj_waves(int nb) { return nb <= 4 ? 8 : 4; }
 constexpr int acc_waves(int q, int nb16) { return q * nb16 * 4 <= 64 ? 8 : 4; }
 
 // ------------------------------------------------------------------ project
-// X tile of one 256-column chunk for lane (m, h): row t0 + m, columns
-// 256 ch + 128 h + 8 s, s = 0..15 (rows >= T and columns >= k read as zero).
-// `full` (uniform across the wave) selects plain loads for interior tiles.
-__device__ __forceinline__ void load_x_chunk(const uint16_t* xrow, bool trow,
-                                             bool full, int ch, int h, int k,
-                                             u32x4 xv[16]) {
-  const int cbase = ch * 256 + h * 128;
-  if (full) {
-#pragma unroll
-    for (int s = 0; s < 16; ++s) xv[s] = load_bf16x8(xrow, cbase + 8 * s);
-  } else {
-    const uint32_t keep = trow ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) xv[s] = load_bf16x8_masked(xrow, cbase + 8 * s, k) & keep;
-  }
-}
+// X reaches LDS by direct global->LDS loads (global_load_lds_dwordx4): each
+// instruction moves 1 KB, four token rows x 256 contiguous bytes, so every
+// cache line is fetched by one instruction (register loads in MFMA operand
+// order would touch 32 rows per instruction and refetch each line 8 times).
+// A wave stages one 256-column chunk as two 128-column halves of 8 KB, each
+// 32 rows x 16 pieces of 16 bytes; piece j of row t sits at slot j ^ (t % 16)
+// so the MFMA operand reads (row = lane % 32) hit distinct banks.
+constexpr int kHalfCols = 128;
+constexpr int kHalfBytes = 32 * kHalfCols * 2;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Element offset of the P operand block (step, 16-column block nb, half hl)
 // in the tiled P buffer.  Inside a block, lane slot l = 16 g4 + n holds the
@@ -75,14 +72,19 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int T, int k, int rp,
     uint64_t seed, uint64_t stream, float c, const uint16_t* __restrict__ Ab,
     int64_t lda, uint16_t* __restrict__ Pt) {
-  __shared__ float red[kProjWaves][32 * 33];
+  __shared__ __attribute__((aligned(16))) unsigned char stage0[kProjWaves][kHalfBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char stage1[kProjWaves][kHalfBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int m = lane & 31;  // A-operand row (token) and B-operand column (A row)
-  const int h = lane >> 5;  // which half of each 256-column chunk this lane feeds
+  const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
   const int step = blockIdx.x;
   const int t0 = step * 32;
+  const bool trow = !MASKED || t0 + m < T;
+  const int n_chunks = (k + 255) >> 8;
+  unsigned char* buf0 = stage0[wave];
+  unsigned char* buf1 = stage1[wave];
 
   f32x16 acc[NB];
 #pragma unroll
@@ -91,86 +93,106 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
     for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
   }
 
-  const int t = t0 + m;
-  const bool trow = t < T;
-  const uint16_t* xrow = X + (int64_t)(trow ? t : T - 1) * ldx;
-  const int n_chunks = (k + 255) >> 8;
-
-  // Ping-pong pipeline over this wave's chunks (ch, ch + W, ...): one buffer's
-  // loads are in flight while the other buffer's signs are generated and
-  // multiplied.  Rows of A at or past r are generated like any other row; they
-  // only reach sketch columns >= r, which are never written back.
-  // MASKED is false when T % 32 == 0 and k % 256 == 0: every tile is interior.
-  auto load = [&](int cnk, u32x4 xv[16]) {
-    const int cc = cnk < n_chunks ? cnk : n_chunks - 1;   // past the end: re-read
-    load_x_chunk(xrow, trow, !MASKED, cc, h, k, xv);
-  };
-  // Sign words of A row 32 nb + m for this lane's half of chunk ch: words
-  // 2h and 2h+1 of the row's Philox block.  With two or more 32-row blocks the
-  // two lane halves generate different rows (half h makes block nb = 2j + h)
-  // and swap the words the other half needs, so no block is generated twice.
-  auto mfma_signs = [&](int nb, uint64_t w0, uint64_t w1, const u32x4 xv[16]) {
+  // Half hc of chunk cnk -> dst.  Instruction i: lane l brings piece
+  // (l % 16) ^ (row % 16) of row 4 i + l / 16.  Rows >= T re-read row T - 1
+  // and pieces past k re-read the row's first piece; both are cleared when
+  // read back.
+  auto issue = [&](int cnk, int hc, unsigned char* dst) {
+    const int colbase = cnk * 256 + hc * kHalfCols;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const uint64_t w = s < 8 ? w0 : w1;
-      const uint32_t byte = (uint32_t)(w >> (8 * (s & 7))) & 0xFFu;
-      acc[nb] = mfma32(xv[s], signs_to_bf16x8(byte), acc[nb]);
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      const int j = (lane & 15) ^ (row & 15);
+      int t = t0 + row;
+      int col = colbase + 8 * j;
+      if (MASKED) {
+        t = t < T ? t : T - 1;
+        col = col < k ? col : 0;
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(X + (int64_t)t * ldx + col),
+          (lds_void*)(dst + i * 1024), 16, 0, 0);
     }
   };
-  auto compute = [&](int ch, const u32x4 xv[16]) {
-    // K assignment: in step s, lane half h carries columns
-    // 256 ch + 128 h + 8 s + (0..7).
-    if (GAUSS) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const uint16_t* arow = Ab + (int64_t)(nb * 32 + m) * lda + ch * 256 + h * 128;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          const u32x4 b = *reinterpret_cast<const u32x4*>(arow + 8 * s);
-          acc[nb] = mfma32(xv[s], b, acc[nb]);
-        }
-      }
-    } else if (NB == 1) {
+
+  // Sign words of A row 32 nb + m for chunk ch: word 2 hc + h feeds half hc.
+  // With two or more 32-row blocks the lane halves draw different blocks
+  // (half h draws block 2 j + h) and swap the words the other half needs, so
+  // no Philox block is computed twice.
+  uint64_t sw[NB][2];
+  auto sign_words = [&](int ch) {
+    if constexpr (NB == 1) {
       const Words4 blk = sign_block(seed, stream, (uint64_t)ch, (uint64_t)m);
-      mfma_signs(0, h ? blk.w[2] : blk.w[0], h ? blk.w[3] : blk.w[1], xv);
+      sw[0][0] = h ? blk.w[1] : blk.w[0];
+      sw[0][1] = h ? blk.w[3] : blk.w[2];
     } else {
 #pragma unroll
       for (int j = 0; j < NB / 2; ++j) {
         const Words4 blk =
             sign_block(seed, stream, (uint64_t)ch, (uint64_t)((2 * j + h) * 32 + m));
-        // half 0 needs words 0,1 of both blocks; half 1 needs words 2,3
-        const uint64_t r0 = swap_halves64(h ? blk.w[0] : blk.w[2]);
-        const uint64_t r1 = swap_halves64(h ? blk.w[1] : blk.w[3]);
-        mfma_signs(2 * j, h ? r0 : blk.w[0], h ? r1 : blk.w[1], xv);
-        mfma_signs(2 * j + 1, h ? blk.w[2] : r0, h ? blk.w[3] : r1, xv);
+        const uint64_t r0 = swap_halves64(h ? blk.w[0] : blk.w[1]);
+        const uint64_t r2 = swap_halves64(h ? blk.w[2] : blk.w[3]);
+        sw[2 * j][0] = h ? r0 : blk.w[0];
+        sw[2 * j][1] = h ? r2 : blk.w[2];
+        sw[2 * j + 1][0] = h ? blk.w[1] : r0;
+        sw[2 * j + 1][1] = h ? blk.w[3] : r2;
       }
     }
   };
-  u32x4 xa[16], xb[16];
+
+  // K assignment: in step s of half hc, lane half h carries columns
+  // 256 ch + 128 hc + 64 h + 8 s + (0..7) - byte s of sign word 2 hc + h.
+  auto compute = [&](int ch, int hc, const unsigned char* buf) {
+    const int colq = ch * 256 + hc * kHalfCols + 64 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int slot = (8 * h + s) ^ (m & 15);
+      u32x4 a = *reinterpret_cast<const u32x4*>(buf + m * (kHalfCols * 2) + slot * 16);
+      if (MASKED) a &= keep_mask8(trow ? k - (colq + 8 * s) : 0);
+      if constexpr (GAUSS) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const u32x4 b = *reinterpret_cast<const u32x4*>(
+              Ab + (int64_t)(nb * 32 + m) * lda + colq + 8 * s);
+          acc[nb] = mfma32(a, b, acc[nb]);
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t byte = (uint32_t)(sw[nb][hc] >> (8 * s)) & 0xFFu;
+          acc[nb] = mfma32(a, signs_to_bf16x8(byte), acc[nb]);
+        }
+      }
+    }
+  };
+
+  // Per wave: chunks wave, wave + W, ...; the two halves of the next chunk
+  // load while the current one is multiplied.
   int ch = wave;
   if (ch < n_chunks) {
-    load(ch, xa);
-    load(ch + kProjWaves, xb);
-    __builtin_amdgcn_sched_barrier(0);
-    for (; ch < n_chunks; ch += 2 * kProjWaves) {
-      compute(ch, xa);
-      __builtin_amdgcn_sched_barrier(0);
-      load(ch + 2 * kProjWaves, xa);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ch + kProjWaves < n_chunks) compute(ch + kProjWaves, xb);
-      __builtin_amdgcn_sched_barrier(0);
-      load(ch + 3 * kProjWaves, xb);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    issue(ch, 0, buf0);
+    issue(ch, 1, buf1);
+  }
+  for (; ch < n_chunks; ch += kProjWaves) {
+    if constexpr (!GAUSS) sign_words(ch);
+    const bool more = ch + kProjWaves < n_chunks;
+    compute(ch, 0, buf0);
+    if (more) issue(ch + kProjWaves, 0, buf0);
+    compute(ch, 1, buf1);
+    if (more) issue(ch + kProjWaves, 1, buf1);
   }
 
   // Sum the waves' partial P in a fixed order (w0 + w1 + ...) and store the
   // hi/lo pair in the tiled layout.  Thread (n_out, tg) owns the TPT tokens
-  // TPT tg .. TPT tg + TPT - 1 of A row 32 nb + n_out.
+  // TPT tg .. TPT tg + TPT - 1 of A row 32 nb + n_out.  The staging buffers
+  // are free (every load was consumed above) and hold the partial sums.
   constexpr int TPT = 16 / kProjWaves;     // tokens per thread: 2 or 4
+  static_assert(kProjWaves * 32 * 33 * 4 <= kProjWaves * kHalfBytes, "red fits");
+  float (*red)[32 * 33] = reinterpret_cast<float (*)[32 * 33]>(&stage0[0][0]);
   const int n_out = tid & 31;
   const int tg = tid >> 5;
   const int nb16 = rp >> 4;
+  __syncthreads();
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -420,9 +442,6 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   const int64_t per_split = (int64_t)n_dgroups * TILE;
   if (idx4 * 4 >= per_split) return;
   const int64_t flat = idx4 * 4;
-  f32x4 sum = *reinterpret_cast<const f32x4*>(part + flat);
-  for (int s = 1; s < n_split; ++s)
-    sum += *reinterpret_cast<const f32x4*>(part + (int64_t)s * per_split + flat);
   const int dg = (int)(flat / TILE);
   const int within = (int)(flat % TILE);
   const int i = within >> 6;
@@ -431,9 +450,29 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   const int rc = acc_rcol<NB16>(i, ln);
   if (drow >= d) return;
   float* srow = S + (int64_t)drow * r;
-  if (s_vec4 && rc + 4 <= r) {     // r % 4 == 0 and S 16-byte aligned
-    f32x4* p = reinterpret_cast<f32x4*>(srow + rc);
-    *p += sum;
+  const bool vec = s_vec4 && rc + 4 <= r;   // r % 4 == 0 and S 16-byte aligned
+  // Loads go out four splits at a time (with S in the first group), so one
+  // memory latency covers each group; the adds still run in split order.
+  // Slots past the last split re-read it and add an exact zero.
+  f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+  if (vec) sv = *reinterpret_cast<const f32x4*>(srow + rc);
+  const float* pp = part + flat;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < n_split; sp += 4) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int su = sp + u < n_split ? sp + u : n_split - 1;
+      v[u] = *reinterpret_cast<const f32x4*>(pp + (int64_t)su * per_split);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float keep = sp + u < n_split ? 1.0f : 0.0f;
+      sum += v[u] * keep;
+    }
+  }
+  if (vec) {
+    *reinterpret_cast<f32x4*>(srow + rc) = sv + sum;
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
