@@ -105,7 +105,8 @@ size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r);
  * scale is already inside dY).
  *
  * X:  device bf16[T x ldx], row-major, ldx >= k, ldx % 8 == 0, 16-B aligned.
- * dY: device bf16[T x ldd], row-major, ldd >= d, ldd % 8 == 0, 16-B aligned.
+ * dY: device bf16[T x ldd], row-major, ldd >= d, ldd % 8 == 0, ldd < 2^26,
+ *     16-B aligned.
  * S:  device float[d x r], contiguous, in/out, 4-B aligned.
  * seed, stream, kind: select A as in logra_regen_A.
  * ws: device scratch of at least logra_sketch_ws_bytes(T, d, k, r) bytes,

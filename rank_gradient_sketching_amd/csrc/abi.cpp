@@ -25,6 +25,7 @@ bool aligned(const void* p, uintptr_t a) {
 }
 
 constexpr int64_t kDimLimit = int64_t(1) << 31;
+constexpr int64_t kDyStrideLimit = int64_t(1) << 26;
 
 bool dim_ok(int64_t x) { return x >= 1 && x < kDimLimit; }
 bool rank_ok(int32_t r) { return r >= 1 && r <= LOGRA_MAX_RANK; }
@@ -76,6 +77,8 @@ int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
   if (X == nullptr || dY == nullptr || S == nullptr) return LOGRA_EINVAL;
   if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(S, 4)) return LOGRA_EINVAL;
   if (!ld_ok(ldx, k) || !ld_ok(ldd, d)) return LOGRA_EINVAL;
+  // dY is read through 32-bit buffer offsets spanning 32 rows of 2 * ldd bytes
+  if (ldd >= kDyStrideLimit) return LOGRA_EINVAL;
   logra::SketchPlan p;
   if (!logra::make_sketch_plan(T, d, k, r, &p)) return LOGRA_EINVAL;
   if (ws == nullptr || ws_bytes < p.total || !aligned(ws, 256)) return LOGRA_EWORKSPACE;

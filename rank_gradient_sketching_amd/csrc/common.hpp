@@ -226,4 +226,41 @@ __device__ __forceinline__ u32x4 load_bf16x8(const uint16_t* row, int col) {
   return *reinterpret_cast<const u32x4*>(row + col);
 }
 
+// ---------------------------------------------------------------- LDS DMA
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Byte address inside LDS of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes from `src` land at LDS byte address lds_base + 16 l.
+// lds_base must be the same in every lane of the wave.  Written as inline
+// assembly so that the compiler's wait-count pass, which does not see it,
+// does not make every later LDS read wait for all outstanding vector loads;
+// the caller orders its LDS reads after the copy with vm_wait<N>() and its
+// LDS reads before a re-fill with lgkm_wait0().  M0 is saved and restored.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+// Wait until at most N vector-memory instructions of this wave are in
+// flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lgkm_wait0() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 }  // namespace logra

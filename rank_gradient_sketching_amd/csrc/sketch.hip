@@ -43,9 +43,15 @@ namespace {
 // unless the accumulators of a large rank need the larger register budget.
 constexpr int proj_waves(int nb) { return nb <= 4 ? 8 : 4; }
 
-// Waves per accumulate work-group: eight (two per SIMD) while the
-// accumulators are small, four when they need the larger register budget.
-constexpr int acc_waves(int q, int nb16) { return q * nb16 * 4 <= 64 ? 8 : 4; }
+// P operands go through LDS for r <= 64 (the two-slot ring of eight waves
+// fits in 128 KB); larger ranks stage them in registers.
+constexpr bool acc_plds(int nb16) { return nb16 <= 4; }
+
+// Waves per accumulate work-group: eight (two per SIMD) unless register-
+// staged P operands of a large rank need the larger per-wave budget.
+constexpr int acc_waves(int q, int nb16) {
+  return (q * nb16 * 4 <= 64 || acc_plds(nb16)) ? 8 : 4;
+}
 
 // ------------------------------------------------------------------ project
 // X reaches LDS by direct global->LDS loads (global_load_lds_dwordx4): each
@@ -251,61 +257,62 @@ __global__ __launch_bounds__(256) void gauss_basis_kernel(
 }
 
 // --------------------------------------------------------------- accumulate
-// One pipeline stage of the accumulate kernel for lane (m, g4): eight dY rows
-// (tokens tb .. tb + 7) x Q columns from `col`, and the P_hi / P_lo operands
-// (16 r-columns per block, the same eight tokens).
-template <int Q, int NB16>
-struct AccStage {
+// dY rows of one 32-token step for lane (m, g4): tokens tb .. tb + 7 x Q
+// columns from `col` (tb = 32 step + 8 g4).
+template <int Q>
+struct DyStage {
   uint32_t R[8][Q / 2];
+};
+
+// P_hi / P_lo operands of one step held in registers (16 r-columns per block,
+// the lane's eight tokens).
+template <int NB16>
+struct PStage {
   u32x4 bh[NB16], bl[NB16];
 };
 
-template <int Q, bool MASKED>
-__device__ __forceinline__ void load_dy_row(const uint16_t* row, int col, int d,
-                                            bool tok_ok, uint32_t out[Q / 2]) {
-  const int valid = d - col;
-  const uint16_t* p = row + (!MASKED || valid > 0 ? col : 0);
-  uint32_t v[Q / 2];
-  if constexpr (Q == 8) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = x[i];
-  } else if constexpr (Q == 4) {
-    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
-    v[0] = x[0];
-    v[1] = x[1];
-  } else {
-    v[0] = *reinterpret_cast<const uint32_t*>(p);
-  }
-  if constexpr (!MASKED) {
-#pragma unroll
-    for (int i = 0; i < Q / 2; ++i) out[i] = v[i];
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < Q / 2; ++i) {
-    const int left = valid - 2 * i;
-    const uint32_t keep = left >= 2 ? 0xFFFFFFFFu : left == 1 ? 0x0000FFFFu : 0u;
-    out[i] = tok_ok ? (v[i] & keep) : 0u;
-  }
+// dY loads go through a buffer resource over the step's rows: the row offset
+// e * ldd rides in the scalar offset and the lane's own offset in one 32-bit
+// register (the caller guarantees 64 * ldd < 2^32), and rows at or past T
+// fall outside the resource and read as zero.  Columns at or past d read the
+// row's first group; the kernel zeroes their A operands.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data (gfx9)
+
+// The lane's fixed part of the offset: row 8 g4 of the step, column col
+// (the row's first group when col is past d).
+__device__ __forceinline__ int dy_lane_offset(int64_t ldd, int d, int col, int g4) {
+  const int c = col < d ? col : 0;
+  return (int)(((uint32_t)(8 * g4) * (uint32_t)ldd + (uint32_t)c) * 2u);
 }
 
-template <int Q, int NB16, bool MASKED>
-__device__ __forceinline__ void load_acc_stage(
-    const uint16_t* __restrict__ dY, int64_t ldd, int T, int d, int col, int step,
-    int g4, int lane, const uint16_t* __restrict__ Pt, AccStage<Q, NB16>& st) {
-  const int tb = step * 32 + 8 * g4;
+template <int Q>
+__device__ __forceinline__ void load_dy_stage(const uint16_t* __restrict__ dY,
+                                              int64_t ldd, int T, int vo, int step,
+                                              DyStage<Q>& st) {
+  const int64_t row0 = (int64_t)step * 32;
+  const int64_t rows = T - row0 < 32 ? T - row0 : 32;
+  const uint32_t bytes = (uint32_t)rows * (uint32_t)ldd * 2u;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(dY + row0 * ldd), (short)0, (int)bytes, kBufferDword3);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int t = tb + e;
-    const bool ok = !MASKED || t < T;
-    load_dy_row<Q, MASKED>(dY + (int64_t)(ok ? t : T - 1) * ldd, col, d, ok, st.R[e]);
-  }
-  // one contiguous 1 KB block per (16 r columns, half): lane l reads slot l
+    const int so = (int)((uint32_t)e * (uint32_t)ldd * 2u);
+    uint32_t v[Q / 2];
+    if constexpr (Q == 8) {
+      const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, 0);
 #pragma unroll
-  for (int nb = 0; nb < NB16; ++nb) {
-    st.bh[nb] = *reinterpret_cast<const u32x4*>(Pt + p_block(step, nb, 0, NB16) + 8 * lane);
-    st.bl[nb] = *reinterpret_cast<const u32x4*>(Pt + p_block(step, nb, 1, NB16) + 8 * lane);
+      for (int u = 0; u < 4; ++u) v[u] = (uint32_t)x[u];
+    } else if constexpr (Q == 4) {
+      const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, 0);
+      v[0] = (uint32_t)x[0];
+      v[1] = (uint32_t)x[1];
+    } else {
+      v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < Q / 2; ++u) st.R[e][u] = v[u];
   }
 }
 
@@ -320,19 +327,38 @@ __device__ __forceinline__ int acc_rcol(int i, int ln) {
   return 16 * ((i >> 2) % NB16) + (ln & 15);
 }
 
-template <int Q, int NB16, int kAccWaves, bool MASKED>
+// LDS bytes of the accumulate kernel: the P ring (PLDS) and the reduction
+// buffer share one array.
+template <int NB16, int kAccWaves, bool PLDS>
+constexpr int acc_lds_bytes() {
+  constexpr int ring = PLDS ? kAccWaves * 2 * (NB16 * 2 * 1024) : 0;
+  constexpr int red = kAccWaves * 32 * 64 * 4;
+  return ring > red ? ring : red;
+}
+
+// S += dY^T P over a range of 32-token steps for 16 Q columns of d.
+// PLDS: the P operands of each step reach a per-wave two-slot LDS ring by
+// direct global->LDS loads issued from inline assembly, so the compiler's
+// wait-count pass (which would wait for every outstanding vector load before
+// any LDS read) keeps the dY prefetch in flight; the kernel waits for each P
+// slot itself with an exact vmcnt.  Otherwise P is staged in registers.
+template <int Q, int NB16, int kAccWaves, bool MASKED, bool PLDS>
 __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
     const uint16_t* __restrict__ dY, int64_t ldd, int T, int d, int r,
     const uint16_t* __restrict__ Pt, int steps_total, int steps_per_split,
     float* __restrict__ S, float* __restrict__ part) {
   constexpr int DC = 16 * Q;            // d columns per work-group
   constexpr int NREG = Q * NB16 * 4;    // accumulator floats per lane
-  constexpr int CH = NREG < 32 ? NREG : 32;  // registers per LDS round
-  __shared__ float red[(kAccWaves - 1) * CH * 64];
+  constexpr int CH = NREG < 32 ? NREG : 32;  // registers per reduction round
+  constexpr int kSlot = NB16 * 2 * 1024;     // P bytes of one step
+  // vector-memory instructions issued after a P slot's loads before it is
+  // read: the stage's 8 dY loads, then the other slot's P and dY loads
+  constexpr int kAfterP = 8 + 2 * NB16 + 8;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[acc_lds_bytes<NB16, kAccWaves, PLDS>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int m = lane & 15;   // A-operand row group (d columns)
   const int g4 = lane >> 4;  // which 8 tokens of the 32-token step
   const int dg = blockIdx.x;
@@ -345,87 +371,145 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   float acc[NREG];
 #pragma unroll
   for (int i = 0; i < NREG; ++i) acc[i] = 0.0f;
+  const int vo = dy_lane_offset(ldd, d, col, g4);
+  const int qvalid = d - col;     // columns col + q < d are real (MASKED)
 
-  // Ping-pong pipeline over this wave's steps (st, st + W, st + 2W, ...):
-  // the loads of one buffer are in flight while the other buffer is
-  // multiplied.  sched_barrier keeps the scheduler from sinking the loads
-  // back next to their consumers.
-  auto compute = [&](const AccStage<Q, NB16>& cs) {
+  unsigned char* ring = lds + wave * 2 * kSlot;   // PLDS only
+  auto p_issue = [&](int step, int slot) {
+#pragma unroll
+    for (int blk = 0; blk < 2 * NB16; ++blk) {
+      const uint16_t* src = Pt + p_block(step, blk >> 1, blk & 1, NB16) + 8 * lane;
+      lds_dma16(src, lds_addr(ring + slot * kSlot + blk * 1024));
+    }
+  };
+  // One step: Q A operands (d rows x tokens, transposed in registers with
+  // v_perm from the row loads) against NB16 hi/lo pairs of P operands.
+  auto mfma_step = [&](const DyStage<Q>& ds, const u32x4* bh, const u32x4* bl, int nb) {
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       // K assignment: lane group g4, element e <-> token tb + e.
       u32x4 a;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        a[u] = __builtin_amdgcn_perm(cs.R[2 * u + 1][q >> 1], cs.R[2 * u][q >> 1],
+        a[u] = __builtin_amdgcn_perm(ds.R[2 * u + 1][q >> 1], ds.R[2 * u][q >> 1],
                                      (q & 1) ? 0x07060302u : 0x05040100u);
       }
+      if (MASKED && q >= qvalid) a = u32x4{0u, 0u, 0u, 0u};   // column past d
+      const int i0 = (q * NB16 + nb) * 4;
+      f32x4 c4 = {acc[i0], acc[i0 + 1], acc[i0 + 2], acc[i0 + 3]};
+      c4 = mfma16(a, *bh, c4);
+      c4 = mfma16(a, *bl, c4);
 #pragma unroll
-      for (int nb = 0; nb < NB16; ++nb) {
-        f32x4 c4 = {acc[(q * NB16 + nb) * 4 + 0], acc[(q * NB16 + nb) * 4 + 1],
-                    acc[(q * NB16 + nb) * 4 + 2], acc[(q * NB16 + nb) * 4 + 3]};
-        c4 = mfma16(a, cs.bh[nb], c4);
-        c4 = mfma16(a, cs.bl[nb], c4);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[(q * NB16 + nb) * 4 + v] = c4[v];
-      }
+      for (int v = 0; v < 4; ++v) acc[i0 + v] = c4[v];
     }
   };
-  auto load = [&](int step, AccStage<Q, NB16>& ls) {
-    // steps past the end re-read the last step of the range (never used)
-    const int sc = step < s_end ? step : s_end - 1;
-    load_acc_stage<Q, NB16, MASKED>(dY, ldd, T, d, col, sc, g4, lane, Pt, ls);
+  auto compute_lds = [&](const DyStage<Q>& ds, int slot) {
+    const unsigned char* base = ring + slot * kSlot + 16 * lane;
+#pragma unroll
+    for (int nb = 0; nb < NB16; ++nb) {
+      const u32x4 bh = *reinterpret_cast<const u32x4*>(base + (2 * nb) * 1024);
+      const u32x4 bl = *reinterpret_cast<const u32x4*>(base + (2 * nb + 1) * 1024);
+      mfma_step(ds, &bh, &bl, nb);
+    }
   };
-  AccStage<Q, NB16> b0, b1;
+  auto compute_reg = [&](const DyStage<Q>& ds, const PStage<NB16>& ps) {
+#pragma unroll
+    for (int nb = 0; nb < NB16; ++nb) mfma_step(ds, &ps.bh[nb], &ps.bl[nb], nb);
+  };
+  auto p_load = [&](int step, PStage<NB16>& ps) {
+#pragma unroll
+    for (int nb = 0; nb < NB16; ++nb) {
+      ps.bh[nb] = *reinterpret_cast<const u32x4*>(Pt + p_block(step, nb, 0, NB16) + 8 * lane);
+      ps.bl[nb] = *reinterpret_cast<const u32x4*>(Pt + p_block(step, nb, 1, NB16) + 8 * lane);
+    }
+  };
+
+  // Ping-pong pipeline over this wave's steps (st, st + W, st + 2W, ...):
+  // the loads of one stage are in flight while the other is multiplied.
+  // Steps past the end re-read the last step of the range (never used), so
+  // every stage issues the same number of loads.  sched_barrier keeps the
+  // scheduler from sinking loads back next to their consumers.
+  auto clampst = [&](int step) { return step < s_end ? step : s_end - 1; };
   int st = s_begin + wave;
   if (st < s_end) {
-    load(st, b0);
-    load(st + kAccWaves, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    for (; st < s_end; st += 2 * kAccWaves) {
-      compute(b0);
+    DyStage<Q> y0, y1;
+    if constexpr (PLDS) {
+      p_issue(clampst(st), 0);
+      load_dy_stage<Q>(dY, ldd, T, vo, clampst(st), y0);
+      p_issue(clampst(st + kAccWaves), 1);
+      load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + kAccWaves), y1);
       __builtin_amdgcn_sched_barrier(0);
-      load(st + 2 * kAccWaves, b0);
+      for (; st < s_end; st += 2 * kAccWaves) {
+        vm_wait<kAfterP>();
+        compute_lds(y0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        lgkm_wait0();
+        p_issue(clampst(st + 2 * kAccWaves), 0);
+        load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + 2 * kAccWaves), y0);
+        __builtin_amdgcn_sched_barrier(0);
+        vm_wait<kAfterP>();
+        if (st + kAccWaves < s_end) compute_lds(y1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        lgkm_wait0();
+        p_issue(clampst(st + 3 * kAccWaves), 1);
+        load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + 3 * kAccWaves), y1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      vm_wait<0>();   // the ring is reused below
+    } else {
+      PStage<NB16> p0, p1;
+      load_dy_stage<Q>(dY, ldd, T, vo, clampst(st), y0);
+      p_load(clampst(st), p0);
+      load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + kAccWaves), y1);
+      p_load(clampst(st + kAccWaves), p1);
       __builtin_amdgcn_sched_barrier(0);
-      if (st + kAccWaves < s_end) compute(b1);
-      __builtin_amdgcn_sched_barrier(0);
-      load(st + 3 * kAccWaves, b1);
-      __builtin_amdgcn_sched_barrier(0);
+      for (; st < s_end; st += 2 * kAccWaves) {
+        compute_reg(y0, p0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + 2 * kAccWaves), y0);
+        p_load(clampst(st + 2 * kAccWaves), p0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + kAccWaves < s_end) compute_reg(y1, p1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + 3 * kAccWaves), y1);
+        p_load(clampst(st + 3 * kAccWaves), p1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
-  // Fixed-order sum of the waves into wave 0: (((w0 + w1) + w2) + ...),
-  // CH registers per round through LDS.
+  // Sum of the waves in a fixed order (((w0 + w1) + w2) + ...), CH registers
+  // per round through LDS; wave w sums registers c0 + w CH/W .. and writes
+  // them out (the partial tile of this split, register-major and coalesced,
+  // or straight into S when there is a single split).
+  float* red = reinterpret_cast<float*>(lds);
+  constexpr int kPer = CH / kAccWaves > 0 ? CH / kAccWaves : 1;
+  float* my = part ? part + ((int64_t)sp * gridDim.x + dg) * (NREG * 64) : nullptr;
+  __syncthreads();
 #pragma unroll
   for (int c0 = 0; c0 < NREG; c0 += CH) {
-    if (wave > 0) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i) red[((wave - 1) * CH + i) * 64 + lane] = acc[c0 + i];
-    }
+    for (int i = 0; i < CH; ++i) red[(wave * CH + i) * 64 + lane] = acc[c0 + i];
     __syncthreads();
-    if (wave == 0) {
 #pragma unroll
-      for (int w = 0; w < kAccWaves - 1; ++w)
+    for (int u = 0; u < kPer; ++u) {
+      const int il = wave * kPer + u;        // register within the round
+      if (il < CH) {
+        float v = red[il * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) acc[c0 + i] += red[(w * CH + i) * 64 + lane];
+        for (int w = 1; w < kAccWaves; ++w) v += red[(w * CH + il) * 64 + lane];
+        const int i = c0 + il;
+        if (my) {
+          my[i * 64 + lane] = v;
+        } else {
+          const int drow = acc_drow<Q, NB16>(dc0, i, lane);
+          const int rc = acc_rcol<NB16>(i, lane);
+          if (drow < d && rc < r) S[(int64_t)drow * r + rc] += v;
+        }
+      }
     }
     __syncthreads();
   }
-  if (wave != 0) return;
-
-  if (part == nullptr) {          // a single split: add straight into S
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int drow = acc_drow<Q, NB16>(dc0, i, lane);
-      const int rc = acc_rcol<NB16>(i, lane);
-      if (drow < d && rc < r) S[(int64_t)drow * r + rc] += acc[i];
-    }
-    return;
-  }
-  // Partial tile of this split, stored register-major ([i][lane], coalesced).
-  float* my = part + ((int64_t)sp * gridDim.x + dg) * (NREG * 64);
-#pragma unroll
-  for (int i = 0; i < NREG; ++i) my[i * 64 + lane] = acc[i];
 }
 
 // S += sum over splits of the partial tiles, in split order.  One thread per
@@ -510,15 +594,16 @@ hipError_t launch_accumulate(const SketchPlan& p, const uint16_t* dY, int64_t ld
                              int T, int d, int r, const uint16_t* Pt, float* S,
                              float* part, hipStream_t s) {
   constexpr int kAccWaves = acc_waves(Q, NB16);
+  constexpr bool kPlds = acc_plds(NB16);
   const dim3 grid((unsigned)p.n_dgroups, (unsigned)p.n_split);
   float* pp = p.n_split > 1 ? part : nullptr;
   const bool masked = (T % 32) != 0 || (d % (16 * Q)) != 0;
   if (masked) {
-    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, true>), grid,
+    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, true, kPlds>), grid,
                        dim3(64 * kAccWaves), 0, s, dY, ldd, T, d, r, Pt, p.steps,
                        p.steps_per_split, S, pp);
   } else {
-    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, false>), grid,
+    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, false, kPlds>), grid,
                        dim3(64 * kAccWaves), 0, s, dY, ldd, T, d, r, Pt, p.steps,
                        p.steps_per_split, S, pp);
   }
@@ -542,7 +627,7 @@ bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p) {
   q.rp = r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : r <= 128 ? 128 : 256;
   q.p_rows = q.rp < 32 ? 32 : q.rp;
   q.nb32 = q.p_rows / 32;
-  q.q_cols = q.rp <= 32 ? 8 : q.rp <= 128 ? 4 : 2;
+  q.q_cols = q.rp <= 64 ? 8 : q.rp <= 128 ? 4 : 2;
   q.t_pad = round_up(T > 0 ? T : 1, 32);
   q.k_pad = round_up(k, 256);
   q.steps = (int)(q.t_pad / 32);
@@ -599,7 +684,7 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
   switch (p.rp) {
     case 16: return launch_accumulate<8, 1>(p, dY, ldd, T, d, r, Pt, S, part, s);
     case 32: return launch_accumulate<8, 2>(p, dY, ldd, T, d, r, Pt, S, part, s);
-    case 64: return launch_accumulate<4, 4>(p, dY, ldd, T, d, r, Pt, S, part, s);
+    case 64: return launch_accumulate<8, 4>(p, dY, ldd, T, d, r, Pt, S, part, s);
     case 128: return launch_accumulate<4, 8>(p, dY, ldd, T, d, r, Pt, S, part, s);
     default: return launch_accumulate<2, 16>(p, dY, ldd, T, d, r, Pt, S, part, s);
   }

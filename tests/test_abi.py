@@ -64,7 +64,7 @@ def _sketch(L, **kw):
     (dict(ldx=255), EINVAL), (dict(ldx=260), EINVAL), (dict(ldd=100), EINVAL),
     (dict(kind=2), EINVAL), (dict(kind=-1), EINVAL),
     (dict(X=MIS), EINVAL), (dict(dY=MIS), EINVAL), (dict(S=P + 1), EINVAL),
-    (dict(d=1 << 31), EINVAL), (dict(T=1 << 31), EINVAL),
+    (dict(d=1 << 31), EINVAL), (dict(T=1 << 31), EINVAL), (dict(ldd=1 << 26), EINVAL),
     (dict(ws=None), EWS), (dict(ws_bytes=16), EWS), (dict(ws=P + 16), EWS),
 ])
 def test_sketch_rejects(L, kw, status):
