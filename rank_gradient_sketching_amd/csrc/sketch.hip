@@ -424,56 +424,79 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
     }
   };
 
-  // Ping-pong pipeline over this wave's steps (st, st + W, st + 2W, ...):
-  // the loads of one stage are in flight while the other is multiplied.
-  // Steps past the end re-read the last step of the range (never used), so
-  // every stage issues the same number of loads.  sched_barrier keeps the
+  // Ping-pong pipeline over this wave's n steps s_begin + wave + W j: the
+  // loads of step j + 1 are in flight while step j is multiplied, and step
+  // j + 2 is issued into the stage step j frees.  Nothing is loaded past the
+  // wave's last step, so before reading a P slot the kernel waits for every
+  // load older than the next step's (8 dY loads behind it, and the 2 NB16 + 8
+  // loads of step j + 1 when that step exists).  sched_barrier keeps the
   // scheduler from sinking loads back next to their consumers.
-  auto clampst = [&](int step) { return step < s_end ? step : s_end - 1; };
-  int st = s_begin + wave;
-  if (st < s_end) {
+  const int first = s_begin + wave;
+  const int n = first < s_end ? (s_end - first + kAccWaves - 1) / kAccWaves : 0;
+  auto step_of = [&](int jj) { return first + kAccWaves * jj; };
+  if (n > 0) {
     DyStage<Q> y0, y1;
     if constexpr (PLDS) {
-      p_issue(clampst(st), 0);
-      load_dy_stage<Q>(dY, ldd, T, vo, clampst(st), y0);
-      p_issue(clampst(st + kAccWaves), 1);
-      load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + kAccWaves), y1);
+      auto wait_slot = [&](int jj) {
+        if (jj + 1 < n) vm_wait<kAfterP>();
+        else vm_wait<8>();
+      };
+      p_issue(step_of(0), 0);
+      load_dy_stage<Q>(dY, ldd, T, vo, step_of(0), y0);
+      if (n > 1) {
+        p_issue(step_of(1), 1);
+        load_dy_stage<Q>(dY, ldd, T, vo, step_of(1), y1);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      for (; st < s_end; st += 2 * kAccWaves) {
-        vm_wait<kAfterP>();
+      for (int jj = 0; jj < n; jj += 2) {
+        wait_slot(jj);
         compute_lds(y0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        lgkm_wait0();
-        p_issue(clampst(st + 2 * kAccWaves), 0);
-        load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + 2 * kAccWaves), y0);
+        if (jj + 2 < n) {
+          lgkm_wait0();
+          p_issue(step_of(jj + 2), 0);
+          load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 2), y0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        vm_wait<kAfterP>();
-        if (st + kAccWaves < s_end) compute_lds(y1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        lgkm_wait0();
-        p_issue(clampst(st + 3 * kAccWaves), 1);
-        load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + 3 * kAccWaves), y1);
-        __builtin_amdgcn_sched_barrier(0);
+        if (jj + 1 < n) {
+          wait_slot(jj + 1);
+          compute_lds(y1, 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (jj + 3 < n) {
+            lgkm_wait0();
+            p_issue(step_of(jj + 3), 1);
+            load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 3), y1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       vm_wait<0>();   // the ring is reused below
     } else {
       PStage<NB16> p0, p1;
-      load_dy_stage<Q>(dY, ldd, T, vo, clampst(st), y0);
-      p_load(clampst(st), p0);
-      load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + kAccWaves), y1);
-      p_load(clampst(st + kAccWaves), p1);
+      load_dy_stage<Q>(dY, ldd, T, vo, step_of(0), y0);
+      p_load(step_of(0), p0);
+      if (n > 1) {
+        load_dy_stage<Q>(dY, ldd, T, vo, step_of(1), y1);
+        p_load(step_of(1), p1);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      for (; st < s_end; st += 2 * kAccWaves) {
+      for (int jj = 0; jj < n; jj += 2) {
         compute_reg(y0, p0);
         __builtin_amdgcn_sched_barrier(0);
-        load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + 2 * kAccWaves), y0);
-        p_load(clampst(st + 2 * kAccWaves), p0);
+        if (jj + 2 < n) {
+          load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 2), y0);
+          p_load(step_of(jj + 2), p0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        if (st + kAccWaves < s_end) compute_reg(y1, p1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_dy_stage<Q>(dY, ldd, T, vo, clampst(st + 3 * kAccWaves), y1);
-        p_load(clampst(st + 3 * kAccWaves), p1);
-        __builtin_amdgcn_sched_barrier(0);
+        if (jj + 1 < n) {
+          compute_reg(y1, p1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (jj + 3 < n) {
+            load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 3), y1);
+            p_load(step_of(jj + 3), p1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
