@@ -172,20 +172,27 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
     }
   };
 
-  // Per wave: chunks wave, wave + W, ...; the two halves of the next chunk
-  // load while the current one is multiplied.
+  // Per wave: logical chunks wave, wave + W, ...; the two halves of the next
+  // chunk load while the current one is multiplied.  Each work-group starts
+  // its walk along k at a different chunk (physical chunk = logical + step,
+  // mod n_chunks): work-groups that run in lock step would otherwise all read
+  // the same byte range of their rows at the same time, and HBM channels are
+  // interleaved by address within a row, so half of them would sit idle.
+  const int rot = step % n_chunks;
+  auto phys = [&](int c) { c += rot; return c < n_chunks ? c : c - n_chunks; };
   int ch = wave;
   if (ch < n_chunks) {
-    issue(ch, 0, buf0);
-    issue(ch, 1, buf1);
+    issue(phys(ch), 0, buf0);
+    issue(phys(ch), 1, buf1);
   }
   for (; ch < n_chunks; ch += kProjWaves) {
-    if constexpr (!GAUSS) sign_words(ch);
+    const int pc = phys(ch);
+    if constexpr (!GAUSS) sign_words(pc);
     const bool more = ch + kProjWaves < n_chunks;
-    compute(ch, 0, buf0);
-    if (more) issue(ch + kProjWaves, 0, buf0);
-    compute(ch, 1, buf1);
-    if (more) issue(ch + kProjWaves, 1, buf1);
+    compute(pc, 0, buf0);
+    if (more) issue(phys(ch + kProjWaves), 0, buf0);
+    compute(pc, 1, buf1);
+    if (more) issue(phys(ch + kProjWaves), 1, buf1);
   }
 
   // Sum the waves' partial P in a fixed order (w0 + w1 + ...) and store the
