@@ -226,6 +226,18 @@ __device__ __forceinline__ u32x4 load_bf16x8(const uint16_t* row, int col) {
   return *reinterpret_cast<const u32x4*>(row + col);
 }
 
+// ---------------------------------------------------------------- grid order
+// Work-groups are dispatched round-robin over the 8 XCDs, so with a plain
+// index -> tile map XCD x only ever gets tiles whose index is x mod 8.  On
+// this part such tiles sit in the same slice of HBM address space (token
+// blocks 256 KB apart, W column strips 512 B apart), and each XCD then streams
+// from one slice while the others idle.  xcd_spread rotates the low three
+// bits of `i` by `salt` inside every complete aligned group of 8 (a bijection
+// on [0, n)), so each XCD's work-groups cover all residues.
+__device__ __forceinline__ int xcd_spread(int i, int salt, int n) {
+  return i < (n & ~7) ? ((i & ~7) | ((i + salt) & 7)) : i;
+}
+
 // ---------------------------------------------------------------- LDS DMA
 typedef __attribute__((address_space(3))) void lds_void;
 

@@ -47,8 +47,8 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   const int g = lane >> 4;   // K group for operands, row group for D
   // flat grid: column block fastest, so neighbouring work-groups share rows
   const int n_cb = (k + kMergeCols - 1) / kMergeCols;
-  const int cb = (int)(blockIdx.x % (unsigned)n_cb);
   const int rblk = (int)(blockIdx.x / (unsigned)n_cb);
+  const int cb = xcd_spread((int)(blockIdx.x % (unsigned)n_cb), rblk, n_cb);
   const int col0 = cb * kMergeCols;
   const int row0 = rblk * (64 * kWaves) + wave * 64;
   const int n_pass = min(kMergeCols / kPassCols, (k - col0 + kPassCols - 1) / kPassCols);

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
   const int wave = tid >> 6;
   const int m = lane & 31;  // A-operand row (token) and B-operand column (A row)
   const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
-  const int step = blockIdx.x;
+  const int step = xcd_spread((int)blockIdx.x, (int)blockIdx.x >> 3, (int)gridDim.x);
   const int t0 = step * 32;
   const bool trow = !MASKED || t0 + m < T;
   const int n_chunks = (k + 255) >> 8;
@@ -368,8 +368,8 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int m = lane & 15;   // A-operand row group (d columns)
   const int g4 = lane >> 4;  // which 8 tokens of the 32-token step
-  const int dg = blockIdx.x;
   const int sp = blockIdx.y;
+  const int dg = xcd_spread((int)blockIdx.x, sp, (int)gridDim.x);
   const int dc0 = dg * DC;
   const int col = dc0 + Q * m;
   const int s_begin = sp * steps_per_split;
