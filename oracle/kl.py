@@ -49,3 +49,33 @@ def step_size(q, kl_budget, alpha_max):
     if q <= 0.0:
         return float(alpha_max)
     return float(min(float(alpha_max), np.sqrt(float(kl_budget) / q)))
+
+
+# --------------------------------------------------------------------------
+# Direction-form sweep (the KL at several step multipliers in one call).
+#
+# [LoGRA] PKL: the proposal is the current model moved along the update
+# direction; the predicted KL is quadratic in the step multiplier alpha.
+# Here the proposed logits are z + alpha * delta, formed exactly (fp64, no
+# rounding to bf16), so the alpha^2 law holds on the inputs as given.
+# Readings: the weighted mean uses non-negative per-row weights (None means
+# equal weights); a token mask or per-response averaging is a choice of
+# weights.  A zero weight sum gives NaN.
+
+def kl_sweep_rows(z, delta, alphas, tau):
+    """(n_alpha, n_tok) array: row t, multiplier a -> KL(p(z_t) || p(z_t + a delta_t))."""
+    z = np.asarray(z, np.float64)
+    delta = np.asarray(delta, np.float64)
+    return np.stack([kl_rows(z, z + float(a) * delta, tau) for a in alphas])
+
+
+def predicted_kl_sweep(z, delta, alphas, tau, weights=None):
+    """Weighted mean over rows of kl_sweep_rows, one value per multiplier."""
+    rows = kl_sweep_rows(z, delta, alphas, tau)
+    if weights is None:
+        return rows.mean(axis=1)
+    w = np.asarray(weights, np.float64)
+    tot = w.sum()
+    if tot == 0.0:
+        return np.full(rows.shape[0], np.nan)
+    return (rows * w[None, :]).sum(axis=1) / tot

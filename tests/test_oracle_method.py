@@ -321,3 +321,85 @@ def test_step_controller(golden):
     a1 = kl.step_size(3e-3, delta, 4.0)
     a4 = kl.step_size(12e-3, delta, 4.0)
     assert abs(a1 / a4 - 2.0) < 1e-12
+
+
+# ------------------------------------------------------ KL sweep (direction form)
+
+def test_kl_sweep_matches_scipy_for_every_multiplier():
+    rng = np.random.default_rng(21)
+    z = rng.standard_normal((6, 400)) * 3
+    delta = rng.standard_normal(z.shape) * 0.2
+    alphas = [-1.5, 0.25, 1.0, 3.0]
+    for tau in (1.0, 0.8):
+        rows = kl.kl_sweep_rows(z, delta, alphas, tau)
+        assert rows.shape == (4, 6)
+        p = scipy.special.softmax(z / tau, axis=1)
+        for i, a in enumerate(alphas):
+            q = scipy.special.softmax((z + a * delta) / tau, axis=1)
+            np.testing.assert_allclose(rows[i], scipy.stats.entropy(p, q, axis=1),
+                                       rtol=1e-10, atol=1e-15)
+
+
+def test_kl_sweep_special_cases():
+    rng = np.random.default_rng(22)
+    z = rng.standard_normal((3, 500)) * 3
+    delta = rng.standard_normal(z.shape) * 0.1
+    rows = kl.kl_sweep_rows(z, delta, [0.0, 1.0], 1.0)
+    assert np.all(rows[0] == 0.0)                       # alpha = 0: no move
+    shift = np.ones_like(z) * np.array([[0.5], [-2.0], [7.0]])
+    assert np.all(np.abs(kl.kl_sweep_rows(z, shift, [1.0, 4.0], 1.0)) < 1e-12)   # row shift
+    # V = 2: Bernoulli KL in closed form at each multiplier
+    z2 = np.array([[0.3, 1.7]])
+    d2 = np.array([[0.6, -2.1]])
+    for a in (0.5, 2.0):
+        p = 1 / (1 + np.exp(z2[0, 0] - z2[0, 1]))
+        zq = z2 + a * d2
+        q = 1 / (1 + np.exp(zq[0, 0] - zq[0, 1]))
+        ref = p * np.log(p / q) + (1 - p) * np.log((1 - p) / (1 - q))
+        np.testing.assert_allclose(kl.kl_sweep_rows(z2, d2, [a], 1.0)[0, 0], ref, rtol=1e-12)
+
+
+def test_kl_sweep_small_step_limit_is_half_the_variance():
+    # KL(alpha) = alpha^2 Var_p(delta / tau) / 2 + O(alpha^3)
+    rng = np.random.default_rng(23)
+    z = rng.standard_normal((4, 2000)) * 3
+    delta = rng.standard_normal(z.shape) * 0.5
+    tau = 1.3
+    p = scipy.special.softmax(z / tau, axis=1)
+    dd = delta / tau
+    var = (p * dd * dd).sum(1) - (p * dd).sum(1) ** 2
+    for a in (1e-2, 1e-3):
+        ratio = kl.kl_sweep_rows(z, delta, [a], tau)[0] / (0.5 * a * a * var)
+        assert np.all(np.abs(ratio - 1) < 5 * a)
+
+
+def test_kl_sweep_weighted_mean():
+    rng = np.random.default_rng(24)
+    z = rng.standard_normal((5, 300)) * 3
+    delta = rng.standard_normal(z.shape) * 0.1
+    alphas = [0.5, 2.0]
+    rows = kl.kl_sweep_rows(z, delta, alphas, 1.0)
+    np.testing.assert_allclose(kl.predicted_kl_sweep(z, delta, alphas, 1.0), rows.mean(1), rtol=1e-14)
+    one_hot = np.zeros(5)
+    one_hot[3] = 2.5
+    np.testing.assert_allclose(kl.predicted_kl_sweep(z, delta, alphas, 1.0, one_hot), rows[:, 3],
+                               rtol=1e-14)
+    mask = np.array([1.0, 0.0, 1.0, 0.0, 1.0])        # a token mask
+    np.testing.assert_allclose(kl.predicted_kl_sweep(z, delta, alphas, 1.0, mask),
+                               rows[:, [0, 2, 4]].mean(1), rtol=1e-14)
+    assert np.all(np.isnan(kl.predicted_kl_sweep(z, delta, alphas, 1.0, np.zeros(5))))
+
+
+def test_kl_sweep_restores_the_alpha_squared_law(golden):
+    # The direction form keeps z + alpha delta unrounded, so KL(alpha)/alpha^2
+    # stays constant across the sweep (halving alpha quarters the KL).
+    rng = np.random.default_rng(25)
+    z = bf16.round_f64(rng.standard_normal((8, 32768)) * 3.0)
+    delta = bf16.round_f64(rng.standard_normal(z.shape) * 0.05)
+    alphas = np.array([0.25, 0.5, 1.0, 2.0])
+    vals = kl.predicted_kl_sweep(z, delta, alphas, 1.0)
+    ratios = vals / alphas ** 2
+    assert ratios.max() / ratios.min() - 1 < 3e-3
+    div = golden["controller"]["kl_divisor"]
+    for lo, hi in zip(vals[:-1], vals[1:]):
+        assert abs(hi / lo / div - 1) < 3e-3
