@@ -171,7 +171,6 @@ def run_kl(lg, synth, reps=5):
     z = synth.device_normal_bf16((n, V), synth.Z_ID, "kl_vocab152064")
     dirn = synth.device_normal_bf16((n, V), synth.DIR_ID, "kl_vocab152064")
     zp = synth.proposal_logits(z, dirn, 1.0)
-    del dirn
     kl_tok = torch.empty(n, device="cuda")
     out = torch.empty(2, device="cuda")
     lg.predicted_kl(z, zp, cfg["tau"], cfg["kl_budget"], cfg["alpha_max"], out=out, kl_tok=kl_tok)
@@ -196,8 +195,40 @@ def run_kl(lg, synth, reps=5):
                q=q, alpha=alpha, sampled_row_max_rel_err=row_err,
                q_vs_row_mean_rel=abs(q / q_mean - 1))
     res["frac_hbm"] = res["GBps"] / HBM_PEAK_GBPS
-    del z, zp
+    del zp
+    res["sweep"] = run_kl_sweep(lg, synth, cfg, z, dirn, rows, reps, ms)
+    del z, dirn
     torch.cuda.empty_cache()
+    return res
+
+
+def run_kl_sweep(lg, synth, cfg, z, dirn, rows, reps, ms_single):
+    """Direction-form sweep over the controller workload's multipliers: one
+    pass over (z, delta) for all of them; sampled rows against the oracle."""
+    alphas = list(cfg["alphas"])
+    n = z.shape[0]
+    out = torch.empty(len(alphas), device="cuda")
+    kl_tok = torch.empty(len(alphas), n, device="cuda")
+    lg.predicted_kl_sweep(z, dirn, alphas, cfg["tau"], out=out, kl_tok=kl_tok)
+    torch.cuda.synchronize()
+    tm = Timer()
+    for _ in range(reps):
+        tm.start()
+        lg.predicted_kl_sweep(z, dirn, alphas, cfg["tau"], out=out, kl_tok=kl_tok)
+        tm.stop()
+    torch.cuda.synchronize()
+    ms = float(np.mean(tm.times_ms()))
+    nbytes = 2 * 2 * n * z.shape[1]
+    from oracle import kl as okl
+    ref = okl.kl_sweep_rows(synth.bf16_to_f64(z[rows]), synth.bf16_to_f64(dirn[rows]), alphas,
+                            cfg["tau"])
+    got = kl_tok[:, rows].cpu().numpy().astype(np.float64)
+    kl = out.cpu().numpy().astype(np.float64)
+    res = dict(alphas=alphas, ms=ms, bytes=nbytes, GBps=nbytes / (ms * 1e-3) / 1e9,
+               kl=kl.tolist(), kl_over_alpha2=(kl / np.array(alphas) ** 2).tolist(),
+               sampled_row_max_rel_err=float(np.max(np.abs(got / ref - 1))),
+               speedup_vs_one_call_per_alpha=len(alphas) * ms_single / ms)
+    res["frac_hbm"] = res["GBps"] / HBM_PEAK_GBPS
     return res
 
 

@@ -174,6 +174,48 @@ int logra_predicted_kl(const uint16_t* z_cur, const uint16_t* z_prop,
                        float kl_budget, float alpha_max, float* q_alpha_out,
                        float* kl_tok, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* Largest number of step multipliers one logra_predicted_kl_sweep call takes. */
+#define LOGRA_MAX_SWEEP 8
+
+/* Bytes of workspace logra_predicted_kl_sweep needs when kl_tok is NULL (0
+ * when kl_tok is given).  Returns 0 for invalid sizes. */
+size_t logra_kl_sweep_ws_bytes(int64_t n_tok, int32_t n_alpha);
+
+/*
+ * logra_predicted_kl_sweep - the predicted KL at several step multipliers,
+ * in one pass over the current logits and the update direction.
+ * [LoGRA] PKL: the current and the proposed model's vocabulary distributions
+ * are compared at one common temperature, and the mean predicted KL grows as
+ * alpha^2 q(D).  Here the proposal at multiplier alpha_i is z + alpha_i delta,
+ * formed in fp32 and never rounded to bf16, so the alpha^2 law holds on the
+ * inputs as given.
+ *
+ * Computed: for every row t and multiplier i,
+ *   KL_t(alpha_i) = KL(softmax(z[t] / tau) || softmax((z[t] + alpha_i delta[t]) / tau))
+ * (forward KL), and kl_mean[i] = sum_t w_t KL_t(alpha_i) / sum_t w_t in fp64
+ * (w_t = weight[t], or 1 when weight is NULL; a token mask or per-response
+ * averaging is a choice of weights; a zero weight sum gives NaN).
+ * Per element the cost does not depend on n_alpha: the multipliers enter
+ * through weighted moments of delta (see kl_sweep.hip); the relative
+ * truncation of that expansion is below 1.1e-5.
+ *
+ * z, delta: device bf16[n_tok x ld], ld >= vocab, ld % 8 == 0, 16-B aligned.
+ * alphas: host float[n_alpha], 1 <= n_alpha <= LOGRA_MAX_SWEEP, finite.
+ * weight: device float[n_tok] (>= 0), 4-B aligned, or NULL.
+ * kl_mean: device float[n_alpha] <- the weighted means.
+ * kl_tok: device float[n_alpha x n_tok] (multiplier-major) <- KL_t(alpha_i),
+ *     or NULL.
+ * ws: device scratch of logra_kl_sweep_ws_bytes(n_tok, n_alpha) bytes (256-B
+ *     aligned) when kl_tok is NULL; ignored otherwise.
+ * tau > 0 and finite; n_tok, vocab >= 1.
+ * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
+ */
+int logra_predicted_kl_sweep(const uint16_t* z, const uint16_t* delta, int64_t n_tok,
+                             int64_t vocab, int64_t ld, const float* alphas,
+                             int32_t n_alpha, float tau, const float* weight,
+                             float* kl_mean, float* kl_tok, void* ws, size_t ws_bytes,
+                             hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,11 @@ SIGNATURES = {
                                           ctypes.c_int64, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_float, c_vp, c_vp, c_vp, ctypes.c_size_t,
                                           c_vp]),
+    "logra_kl_sweep_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
+    "logra_predicted_kl_sweep": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_int32, ctypes.c_float, c_vp, c_vp, c_vp,
+                                                c_vp, ctypes.c_size_t, c_vp]),
 }
 
 OK, EINVAL, EWORKSPACE, EHIP = 0, -1, -2, -3

@@ -8,6 +8,8 @@ Names follow the pages' notation: X (T x k inputs), dY (T x d output
 gradients), S (d x r fp32 sketch), W (d x k bf16 weights), A (r x k
 projection), q and alpha of the predicted-KL controller.
 """
+import ctypes
+
 import torch
 
 from . import _lib
@@ -133,3 +135,63 @@ def predicted_kl(z_cur, z_prop, tau, kl_budget, alpha_max, out=None, kl_tok=None
                                        out.data_ptr(), kl_ptr, ws_ptr, ws_n, _stream(z_cur))
     _lib.check(st, "logra_predicted_kl")
     return out
+
+
+MAX_SWEEP = 8
+
+
+def kl_sweep_ws_bytes(n_tok, n_alpha):
+    return int(_lib.lib().logra_kl_sweep_ws_bytes(n_tok, n_alpha))
+
+
+def predicted_kl_sweep(z, delta, alphas, tau, weight=None, out=None, kl_tok=None, ws=None):
+    """Device tensor [n_alpha] of weighted mean KL(p(z) || p(z + alpha_i delta));
+    per-row values go to kl_tok ([n_alpha, n_tok], multiplier-major) when given."""
+    _require(z, "z", torch.bfloat16, 2)
+    _require(delta, "delta", torch.bfloat16, 2)
+    n, V, ld = _rows(z, "z")
+    if _rows(delta, "delta") != (n, V, ld):
+        raise ValueError("z and delta must have the same shape and row stride")
+    al = [float(a) for a in alphas]
+    if not 1 <= len(al) <= MAX_SWEEP:
+        raise ValueError(f"between 1 and {MAX_SWEEP} multipliers")
+    c_al = (ctypes.c_float * len(al))(*al)
+    if out is None:
+        out = torch.empty(len(al), dtype=torch.float32, device=z.device)
+    _require(out, "out", torch.float32, 1)
+    w_ptr = None
+    if weight is not None:
+        _require(weight, "weight", torch.float32, 1)
+        if weight.numel() != n or not weight.is_contiguous():
+            raise ValueError("weight must be a contiguous float32 vector of n_tok entries")
+        w_ptr = weight.data_ptr()
+    kl_ptr = None
+    if kl_tok is not None:
+        _require(kl_tok, "kl_tok", torch.float32, 2)
+        if tuple(kl_tok.shape) != (len(al), n) or not kl_tok.is_contiguous():
+            raise ValueError("kl_tok must be a contiguous float32 [n_alpha, n_tok] tensor")
+        kl_ptr = kl_tok.data_ptr()
+    ws_ptr, ws_n = None, 0
+    if kl_tok is None:
+        if ws is None:
+            ws = torch.empty(max(kl_sweep_ws_bytes(n, len(al)), 256), dtype=torch.uint8,
+                             device=z.device)
+        ws_ptr, ws_n = ws.data_ptr(), ws.numel() * ws.element_size()
+    st = _lib.lib().logra_predicted_kl_sweep(z.data_ptr(), delta.data_ptr(), n, V, ld, c_al,
+                                             len(al), float(tau), w_ptr, out.data_ptr(), kl_ptr,
+                                             ws_ptr, ws_n, _stream(z))
+    _lib.check(st, "logra_predicted_kl_sweep")
+    return out
+
+
+def kl_budget_schedule(step, n_steps, start=2e-4, end=2e-5):
+    """KL budget at `step` of an annealed run: linear from `start` (step 0) to
+    `end` (step n_steps - 1), constant afterwards.  [LoGRA] PKL: the budget may
+    be constant or annealed downward (2e-4 to 2e-5 in the pages' LoRA
+    comparison); the pages do not give the shape, so it is linear here."""
+    if n_steps <= 1 or step >= n_steps - 1:
+        return float(end) if n_steps > 1 else float(start)
+    if step <= 0:
+        return float(start)
+    f = step / (n_steps - 1)
+    return float(start + (end - start) * f)

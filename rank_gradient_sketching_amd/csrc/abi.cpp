@@ -127,4 +127,36 @@ int logra_predicted_kl(const uint16_t* z_cur, const uint16_t* z_prop,
                                      kl_budget, alpha_max, q_alpha_out, rows, s));
 }
 
+size_t logra_kl_sweep_ws_bytes(int64_t n_tok, int32_t n_alpha) {
+  if (!dim_ok(n_tok) || n_alpha < 1 || n_alpha > LOGRA_MAX_SWEEP) return 0;
+  return (size_t)logra::round_up(n_tok * 4 * (int64_t)n_alpha, 256);
+}
+
+int logra_predicted_kl_sweep(const uint16_t* z, const uint16_t* delta, int64_t n_tok,
+                             int64_t vocab, int64_t ld, const float* alphas,
+                             int32_t n_alpha, float tau, const float* weight,
+                             float* kl_mean, float* kl_tok, void* ws, size_t ws_bytes,
+                             hipStream_t s) {
+  if (z == nullptr || delta == nullptr || alphas == nullptr || kl_mean == nullptr)
+    return LOGRA_EINVAL;
+  if (!dim_ok(n_tok) || !dim_ok(vocab) || !ld_ok(ld, vocab)) return LOGRA_EINVAL;
+  if (n_alpha < 1 || n_alpha > LOGRA_MAX_SWEEP) return LOGRA_EINVAL;
+  // the multiplier-major per-row buffer is indexed with 32-bit row counts
+  if ((int64_t)n_alpha * n_tok >= kDimLimit) return LOGRA_EINVAL;
+  if (!aligned(z, 16) || !aligned(delta, 16) || !aligned(kl_mean, 4)) return LOGRA_EINVAL;
+  if (weight != nullptr && !aligned(weight, 4)) return LOGRA_EINVAL;
+  if (kl_tok != nullptr && !aligned(kl_tok, 4)) return LOGRA_EINVAL;
+  if (!isfinite(tau) || !(tau > 0.0f)) return LOGRA_EINVAL;
+  for (int i = 0; i < n_alpha; ++i)
+    if (!isfinite(alphas[i])) return LOGRA_EINVAL;
+  float* rows = kl_tok;
+  if (rows == nullptr) {
+    if (ws == nullptr || ws_bytes < logra_kl_sweep_ws_bytes(n_tok, n_alpha) || !aligned(ws, 256))
+      return LOGRA_EWORKSPACE;
+    rows = static_cast<float*>(ws);
+  }
+  return hip_status(logra::launch_kl_sweep(z, delta, (int)n_tok, (int)vocab, ld, alphas,
+                                           n_alpha, tau, weight, kl_mean, rows, s));
+}
+
 }  // extern "C"

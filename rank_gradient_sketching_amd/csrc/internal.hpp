@@ -49,4 +49,11 @@ hipError_t launch_kl(const uint16_t* zc, const uint16_t* zp, int n_tok,
                      float alpha_max, float* q_alpha, float* kl_tok,
                      hipStream_t s);
 
+// alphas: host array of n_alpha (1..LOGRA_MAX_SWEEP) multipliers; kl_tok:
+// device float[n_alpha x n_tok] (written), kl_mean: device float[n_alpha].
+hipError_t launch_kl_sweep(const uint16_t* z, const uint16_t* dz, int n_tok, int vocab,
+                           int64_t ld, const float* alphas, int n_alpha, float tau,
+                           const float* weight, float* kl_mean, float* kl_tok,
+                           hipStream_t s);
+
 }  // namespace logra

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = _lib.header_symbols()
-    assert len(declared) == 8
+    assert len(declared) == 10
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -132,3 +132,47 @@ def test_binding_refuses_cpu_tensors():
         lg.sketch_accumulate(X, X, S, seed=1)
     with pytest.raises(ValueError, match="GPU"):
         lg.merge(X, S, seed=1)
+
+
+def _sweep(L, **kw):
+    import ctypes
+    al = kw.pop("alphas", [0.5, 1.0])
+    a = dict(z=P, delta=P, n_tok=16, vocab=1000, ld=1000, n_alpha=len(al or [0.0]), tau=1.0,
+             weight=None,
+             kl_mean=P, kl_tok=None, ws=P, ws_bytes=1 << 20, s=None)
+    a.update(kw)
+    c_al = None if al is None else (ctypes.c_float * max(1, len(al)))(*al)
+    return L.logra_predicted_kl_sweep(a["z"], a["delta"], a["n_tok"], a["vocab"], a["ld"], c_al,
+                                      a["n_alpha"], a["tau"], a["weight"], a["kl_mean"],
+                                      a["kl_tok"], a["ws"], a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=None), EINVAL), (dict(delta=None), EINVAL), (dict(kl_mean=None), EINVAL),
+    (dict(alphas=None), EINVAL), (dict(n_alpha=0), EINVAL), (dict(n_alpha=9), EINVAL),
+    (dict(alphas=[float("nan")]), EINVAL), (dict(alphas=[1.0, float("inf")]), EINVAL),
+    (dict(tau=0.0), EINVAL), (dict(tau=float("nan")), EINVAL), (dict(n_tok=0), EINVAL),
+    (dict(vocab=0), EINVAL), (dict(ld=999), EINVAL), (dict(ld=1004), EINVAL),
+    (dict(z=MIS), EINVAL), (dict(weight=P + 2), EINVAL), (dict(kl_tok=P + 1), EINVAL),
+    (dict(kl_mean=P + 3), EINVAL),
+    (dict(ws=None), EWS), (dict(ws_bytes=64), EWS), (dict(ws=P + 16), EWS),
+])
+def test_kl_sweep_rejects(L, kw, status):
+    assert _sweep(L, **kw) == status
+
+
+def test_kl_sweep_ws_bytes(L):
+    assert L.logra_kl_sweep_ws_bytes(65536, 4) >= 65536 * 4 * 4
+    assert L.logra_kl_sweep_ws_bytes(10, 0) == 0
+    assert L.logra_kl_sweep_ws_bytes(10, 9) == 0
+    assert L.logra_kl_sweep_ws_bytes(0, 2) == 0
+
+
+def test_kl_budget_schedule():
+    from rank_gradient_sketching_amd import kl_budget_schedule as sched
+    assert sched(0, 300) == 2e-4
+    assert sched(299, 300) == 2e-5
+    assert sched(5000, 300) == 2e-5
+    vals = [sched(s, 300) for s in range(300)]
+    assert all(a > b for a, b in zip(vals, vals[1:]))
+    assert abs(sched(149.5, 300) - 1.1e-4) < 1e-12

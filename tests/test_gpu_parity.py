@@ -293,3 +293,72 @@ def test_kl_controller_edges(lg):
     zn[0, 0] = float("nan")
     q, a = lg.predicted_kl(zn, zp, 1.0, 2e-4, 4.0).cpu().tolist()
     assert np.isnan(q) and np.isnan(a)
+
+
+# ------------------------------------------------------- predicted-KL sweep
+
+SWEEP_CASES = [
+    # n, V, tau, sigma_dir, multipliers, weighted
+    (64, 1000, 1.0, 0.05, [0.25, 0.5, 1.0, 2.0], False),
+    (7, 152064, 1.0, 0.05, [0.25, 0.5, 1.0, 2.0], True),
+    (3, 1001, 0.7, 0.05, [1.0], False),
+    (5, 2, 1.0, 0.5, [-1.0, 0.5, 3.0], False),
+    # |amax * delta / tau| > 1 for about a quarter of the elements: the exact path
+    (9, 4099, 1.3, 0.3, [0.5, 1.0, 2.0, 4.0, -2.0], True),
+    (300, 32000, 1.0, 0.01, [0.0, 0.1, 1.0, 2.0, 3.0, 4.0, 6.0, 8.0], True),
+]
+
+
+@pytest.mark.parametrize("n,V,tau,sig,alphas,weighted", SWEEP_CASES)
+def test_predicted_kl_sweep_matches_oracle(lg, n, V, tau, sig, alphas, weighted):
+    say("kl sweep", n, V, tau, sig, alphas, weighted)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V)
+    dirn = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V, sigma=sig)
+    ld = -(-V // 8) * 8
+    z_g, d_g = padded_bf16(z, ld), padded_bf16(dirn, ld)
+    w = None
+    if weighted:
+        rng = np.random.default_rng(n * 131 + V)
+        w = rng.uniform(0.0, 2.0, n)
+        w[rng.uniform(size=n) < 0.3] = 0.0          # a token mask
+        w[0] = 1.0
+    w_g = None if w is None else torch.tensor(w, dtype=torch.float32, device="cuda")
+    m = len(alphas)
+    kl_tok = torch.empty(m, n, device="cuda")
+    out = lg.predicted_kl_sweep(z_g, d_g, alphas, tau, weight=w_g, kl_tok=kl_tok)
+    out_ws = lg.predicted_kl_sweep(z_g, d_g, alphas, tau, weight=w_g)
+    torch.cuda.synchronize()
+    zf, df = synth.bf16_to_f64(z), synth.bf16_to_f64(dirn)
+    ref_rows = okl.kl_sweep_rows(zf, df, alphas, tau)
+    ref = okl.predicted_kl_sweep(zf, df, alphas, tau, None if w is None else np.float32(w))
+    got_rows = kl_tok.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got_rows, ref_rows, rtol=1e-3, atol=1e-9)
+    got = out.cpu().numpy().astype(np.float64)
+    for i, a in enumerate(alphas):
+        if a == 0.0:
+            assert got[i] == 0.0 and np.all(got_rows[i] == 0.0)
+        else:
+            assert abs(got[i] / ref[i] - 1) < Q_TOL, (a, got[i], ref[i])
+    assert torch.equal(out, out_ws)
+
+
+def test_kl_sweep_alpha_squared_law_and_edges(lg):
+    say("kl sweep alpha^2 law")
+    n, V = 16, 32768
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=77)
+    dirn = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=77, sigma=0.05)
+    z_g, d_g = z.cuda(), dirn.cuda()
+    alphas = np.array([0.25, 0.5, 1.0, 2.0])
+    kl = lg.predicted_kl_sweep(z_g, d_g, alphas, 1.0).cpu().numpy().astype(np.float64)
+    ratios = kl / alphas ** 2
+    assert ratios.max() / ratios.min() - 1 < 3e-3
+    # the rounded-proposal entry point on the same direction does not keep the law
+    zp = synth.proposal_logits(z, dirn, 0.25).cuda()
+    q_rounded = lg.predicted_kl(z_g, zp, 1.0, 2e-4, 4.0)[0].item()
+    assert abs(q_rounded / 0.25 ** 2 / ratios[2] - 1) > 0.05
+    # zero weights everywhere: NaN means; a shift of every row: zero KL
+    zero_w = torch.zeros(n, device="cuda")
+    assert torch.isnan(lg.predicted_kl_sweep(z_g, d_g, [1.0, 2.0], 1.0, weight=zero_w)).all()
+    shift = torch.full((n, V), 0.75, dtype=torch.bfloat16, device="cuda")
+    flat = lg.predicted_kl_sweep(z_g, shift, [1.0, 4.0], 1.0).cpu().numpy()
+    assert np.all(np.abs(flat) < 1e-6)
