@@ -232,6 +232,77 @@ def run_kl_sweep(lg, synth, cfg, z, dirn, rows, reps, ms_single):
     return res
 
 
+def run_layer_set(lg, synth, reps=10, r=64):
+    """One decoder layer of the 1.5B-shaped layer set (hidden 1536, KV 256, MLP
+    8960) at T = 16384, r = 64: the seven projections sketched with one call
+    each, against q/k/v and gate/up sharing their input and A (four calls).
+    Same inputs and accumulators; the two results are compared."""
+    cfg = synth.QWEN1P5B
+    T = cfg["T"]
+    wl = "qwen1p5b_layers"
+    proj = {n: (d, k) for n, d, k in cfg["projections"]}
+    groups = [("attn", ["q", "k", "v"]), ("o", ["o"]), ("mlp", ["gate", "up"]), ("down", ["down"])]
+    log(f"[bench] generating one 1.5B-shaped layer at T = {T}")
+    X = {g: synth.device_normal_bf16((T, proj[names[0]][1]), synth.X_ID, wl, salt=gi)
+         for gi, (g, names) in enumerate(groups)}
+    dY = {n: synth.device_normal_bf16((T, proj[n][0]), synth.DY_ID, wl, salt=i)
+          for i, n in enumerate(proj)}
+    S_sep = {n: torch.zeros(proj[n][0], r, device="cuda") for n in proj}
+    S_sh = {n: torch.zeros(proj[n][0], r, device="cuda") for n in proj}
+    seed = 1234
+    ws_sep = {n: lg.sketch_workspace(T, proj[n][0], proj[n][1], r) for n in proj}
+    ws_sh = {}
+    for g, names in groups:
+        n_b = lg.sketch_shared_ws_bytes(T, proj[names[0]][1], r, [proj[n][0] for n in names])
+        ws_sh[g] = torch.empty(max(n_b, 256), dtype=torch.uint8, device="cuda")
+
+    def separate():
+        for g, names in groups:
+            for n in names:
+                lg.sketch_accumulate(X[g], dY[n], S_sep[n], seed, ws=ws_sep[n])
+
+    def shared():
+        for g, names in groups:
+            lg.sketch_accumulate_shared(X[g], [dY[n] for n in names], [S_sh[n] for n in names],
+                                        seed, ws=ws_sh[g])
+
+    separate()
+    shared()
+    torch.cuda.synchronize()
+    def rel_fro(a, b):
+        a, b = a.astype(np.float64), b.astype(np.float64)
+        return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+    err = max(rel_fro(S_sh[n].cpu().numpy(), S_sep[n].cpu().numpy()) for n in proj)
+    times = {}
+    for name, fn in (("separate", separate), ("shared", shared)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        times[name] = t0.elapsed_time(t1) / reps
+    b_sep = sum(2 * T * (proj[n][0] + proj[n][1]) + 8 * proj[n][0] * r for n in proj)
+    b_sh = sum(2 * T * proj[names[0]][1] for _, names in groups) + \
+        sum(2 * T * proj[n][0] + 8 * proj[n][0] * r for n in proj)
+    res = dict(workload="qwen1p5b_layers (one layer, 7 projections)", T=T, r=r,
+               us_separate=times["separate"] * 1e3, us_shared=times["shared"] * 1e3,
+               tokens_per_s_separate=T / (times["separate"] * 1e-3),
+               tokens_per_s_shared=T / (times["shared"] * 1e-3),
+               bytes_separate=b_sep, bytes_shared=b_sh,
+               GBps_separate=b_sep / (times["separate"] * 1e-3) / 1e9,
+               GBps_shared=b_sh / (times["shared"] * 1e-3) / 1e9,
+               speedup=times["separate"] / times["shared"],
+               shared_vs_separate_rel_fro=err)
+    del X, dY, ws_sep, ws_sh
+    torch.cuda.empty_cache()
+    return res
+
+
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "sketch_merge_d4096_r64_traffic.md")
 
 
@@ -318,6 +389,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-calib", action="store_true")
+    ap.add_argument("--no-layerset", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU leg "
@@ -332,14 +404,13 @@ def main():
 
     layer, data = run_layer(lg, synth, args.steps, args.warmup)
     kl = None if args.no_kl else run_kl(lg, synth)
+    layer_set = None if args.no_layerset else run_layer_set(lg, synth)
     calib = None if args.no_calib else run_copy_calibration()
     cpu = None if args.no_cpu else cpu_baseline(synth, data, args.cpu_budget)
 
     cfg = layer["cfg"]
     sk, mg = layer["sketch"], layer["merge"]
     tokens_per_s = layer["tokens_per_step"] / (layer["step_ms"] * 1e-3)
-    # dominant entry point: the sketch call (4 per step) - its two kernels
-    # (project, accumulate) run back to back on the stream
     # dominant entry point: the sketch call (4 per step); its kernels
     # (project, accumulate, finalize) run back to back on the library's stream
     sketch_kernels = ["project_kernel", "accumulate_kernel", "finalize_kernel"]
@@ -374,6 +445,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": layer["parity"],
         "kl": kl,
+        "layer_set": layer_set,
         "copy_calibration": calib,
     }
     print(json.dumps(out), flush=True)

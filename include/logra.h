@@ -121,6 +121,40 @@ int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
                             int32_t r, uint64_t seed, uint64_t stream, int kind,
                             float* S, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* Largest number of outputs one logra_sketch_accumulate_shared call takes. */
+#define LOGRA_MAX_SHARED 4
+
+/* Bytes of workspace logra_sketch_accumulate_shared needs for these sizes
+ * (d: host int64[n_out]).  Returns 0 for invalid sizes. */
+size_t logra_sketch_shared_ws_bytes(int64_t T, int64_t k, int32_t r, int32_t n_out,
+                                    const int64_t* d);
+
+/*
+ * logra_sketch_accumulate_shared - S_o += dY_o^T (X A^T) for up to
+ * LOGRA_MAX_SHARED outputs o that share the input X and the projection A.
+ * [LoGRA] Sketch: the inputs used in the weight-gradient computation are
+ * projected before they meet the backward derivatives, so projections of
+ * one layer that read the same input (q/k/v, or gate/up) and use the same A
+ * (same seed, stream, kind and k) need X A^T only once; each output then
+ * streams its own dY.  One projection pass and one accumulate launch over
+ * the d groups of every output.  Equal to n_out logra_sketch_accumulate
+ * calls up to fp32 summation order.
+ *
+ * X, ldx, T, k, r, seed, stream, kind: as in logra_sketch_accumulate.
+ * dY, ldd, d, S: host arrays of n_out entries (1 <= n_out <= LOGRA_MAX_SHARED);
+ *     dY[o] device bf16[T x ldd[o]] (same rules as dY above), S[o] device
+ *     float[d[o] x r], distinct.
+ * ws: device scratch of logra_sketch_shared_ws_bytes(T, k, r, n_out, d)
+ *     bytes, 256-B aligned.
+ * T == 0 is a no-op (device pointers are not inspected).
+ * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
+ */
+int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, int64_t k,
+                                   int32_t r, uint64_t seed, uint64_t stream, int kind,
+                                   int32_t n_out, const uint16_t* const* dY,
+                                   const int64_t* ldd, const int64_t* d, float* const* S,
+                                   void* ws, size_t ws_bytes, hipStream_t s);
+
 /*
  * logra_merge - W <- RNE_bf16(W - alpha * eta * S A), in place.
  * [LoGRA] Sketch: the update is W <- W - alpha eta U A with U = S in the basic

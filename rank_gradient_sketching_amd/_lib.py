@@ -36,6 +36,18 @@ SIGNATURES = {
                                           ctypes.c_int64, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_float, c_vp, c_vp, c_vp, ctypes.c_size_t,
                                           c_vp]),
+    "logra_sketch_shared_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.POINTER(ctypes.c_int64)]),
+    "logra_sketch_accumulate_shared": (ctypes.c_int, [c_vp, ctypes.c_int64, ctypes.c_int64,
+                                                      ctypes.c_int64, ctypes.c_int32,
+                                                      ctypes.c_uint64, ctypes.c_uint64,
+                                                      ctypes.c_int, ctypes.c_int32,
+                                                      ctypes.POINTER(c_vp),
+                                                      ctypes.POINTER(ctypes.c_int64),
+                                                      ctypes.POINTER(ctypes.c_int64),
+                                                      ctypes.POINTER(c_vp), c_vp,
+                                                      ctypes.c_size_t, c_vp]),
     "logra_kl_sweep_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
     "logra_predicted_kl_sweep": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_int64, ctypes.POINTER(ctypes.c_float),

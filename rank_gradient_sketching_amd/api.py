@@ -90,6 +90,51 @@ def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None):
     return S
 
 
+MAX_SHARED = 4
+
+
+def sketch_shared_ws_bytes(T, k, r, ds):
+    ds = [int(x) for x in ds]
+    arr = (ctypes.c_int64 * max(1, len(ds)))(*ds)
+    return int(_lib.lib().logra_sketch_shared_ws_bytes(T, k, r, len(ds), arr))
+
+
+def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=None):
+    """S_o += dY_o^T (X A^T) in place for outputs sharing the input X and A
+    (e.g. q/k/v or gate/up of one layer); returns the list of S."""
+    _require(X, "X", torch.bfloat16, 2)
+    T, k, ldx = _rows(X, "X")
+    if not 1 <= len(dYs) <= MAX_SHARED or len(dYs) != len(Ss):
+        raise ValueError(f"between 1 and {MAX_SHARED} (dY, S) pairs")
+    ptr_dy, ldds, ds, ptr_s = [], [], [], []
+    r = None
+    for dY, S in zip(dYs, Ss):
+        _require(dY, "dY", torch.bfloat16, 2)
+        _require(S, "S", torch.float32, 2)
+        T2, d, ldd = _rows(dY, "dY")
+        if T2 != T:
+            raise ValueError(f"X has {T} rows but a dY has {T2}")
+        if S.shape[0] != d or not S.is_contiguous():
+            raise ValueError("each S must be a contiguous (d, r) float32 tensor")
+        if r is not None and S.shape[1] != r:
+            raise ValueError("every S must have the same rank r")
+        r = S.shape[1]
+        ptr_dy.append(dY.data_ptr())
+        ldds.append(ldd)
+        ds.append(d)
+        ptr_s.append(S.data_ptr())
+    n = len(dYs)
+    if ws is None:
+        ws = torch.empty(max(sketch_shared_ws_bytes(T, k, r, ds), 256), dtype=torch.uint8,
+                         device=X.device)
+    st = _lib.lib().logra_sketch_accumulate_shared(
+        X.data_ptr(), ldx, T, k, r, seed, stream, kind, n, (ctypes.c_void_p * n)(*ptr_dy),
+        (ctypes.c_int64 * n)(*ldds), (ctypes.c_int64 * n)(*ds), (ctypes.c_void_p * n)(*ptr_s),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(X))
+    _lib.check(st, "logra_sketch_accumulate_shared")
+    return list(Ss)
+
+
 def merge(W, S, seed, stream=0, kind=RADEMACHER, alpha=1.0, eta=1.0):
     """W <- RNE_bf16(W - alpha * eta * S A) in place; returns W."""
     _require(W, "W", torch.bfloat16, 2)

@@ -10,8 +10,22 @@ namespace logra {
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Tiling of one logra_sketch_accumulate call.  Both the workspace-size query
-// and the launcher derive everything from this one function, so they agree.
+// Projections that share the layer input X (and so, with the same seed, the
+// same A) can be sketched together: one projection pass, one accumulate
+// launch over all of their d groups.
+constexpr int kMaxShared = 4;
+
+// One output of a sketch call: S (d x r, fp32) += dY^T P.
+struct SketchOut {
+  const uint16_t* dY;
+  int64_t ldd;
+  int64_t d;
+  float* S;
+};
+
+// Tiling of one sketch call (one or several outputs sharing X).  Both the
+// workspace-size query and the launcher derive everything from this one
+// function, so they agree.
 struct SketchPlan {
   int rp;           // r padded to the accumulate kernel's N tiling (16..256)
   int p_rows;       // rows of the projected-input buffers (>= 32, >= rp)
@@ -20,14 +34,17 @@ struct SketchPlan {
   int64_t t_pad;    // T rounded up to 32 (one MFMA K step of tokens)
   int64_t k_pad;    // k rounded up to 256 (one sign block)
   int steps;        // t_pad / 32
-  int n_dgroups;    // accumulate work-groups along d
+  int n_out;        // outputs sharing X
+  int dg_off[kMaxShared + 1];  // first d group of each output (prefix sums)
+  int n_dgroups;    // accumulate work-groups along d, all outputs together
   int n_split;      // accumulate work-groups along T
   int steps_per_split;
   int64_t d_pad;    // n_dgroups * 16 * q_cols
   size_t off_pt, off_part, off_gauss, total;
 };
 
-bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p);
+bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
+                      SketchPlan* p);
 
 // c = 1/sqrt(r) computed in double and rounded once to float.
 float sign_scale(int r);
@@ -36,9 +53,8 @@ hipError_t launch_regen(uint64_t seed, uint64_t stream, int kind, int r,
                         int64_t k, float* A, hipStream_t s);
 
 hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
-                         const uint16_t* dY, int64_t ldd, int T, int d, int k,
-                         int r, uint64_t seed, uint64_t stream, int kind,
-                         float* S, char* ws, hipStream_t s);
+                         const SketchOut* outs, int T, int k, int r, uint64_t seed,
+                         uint64_t stream, int kind, char* ws, hipStream_t s);
 
 hipError_t launch_merge(uint16_t* W, int64_t ldw, const float* S, int d, int k,
                         int r, uint64_t seed, uint64_t stream, int kind,

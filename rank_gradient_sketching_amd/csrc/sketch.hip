@@ -343,6 +343,39 @@ constexpr int acc_lds_bytes() {
   return ring > red ? ring : red;
 }
 
+// The outputs of one call as a kernel argument.  Work-group d groups are
+// numbered across all outputs; output o owns groups dg_off[o] .. dg_off[o+1].
+struct OutTable {
+  int n;
+  int dg_off[kMaxShared + 1];
+  const uint16_t* dY[kMaxShared];
+  int64_t ldd[kMaxShared];
+  int d[kMaxShared];
+  float* S[kMaxShared];
+};
+
+// Output of a (wave-uniform) global d group, chosen with compares and selects
+// on the kernel argument's fields (constant indices only: taking the
+// argument's address would copy the table to scratch memory).
+struct OutSel {
+  int dg;
+  const uint16_t* dY;
+  int64_t ldd;
+  int d;
+  float* S;
+};
+#define LOGRA_SELECT_OUT(tab, dgg, out)                                    \
+  OutSel out{(dgg), (tab).dY[0], (tab).ldd[0], (tab).d[0], (tab).S[0]};   \
+  _Pragma("unroll") for (int i_ = 1; i_ < kMaxShared; ++i_) {              \
+    if (i_ < (tab).n && (dgg) >= (tab).dg_off[i_]) {                       \
+      out.dg = (dgg) - (tab).dg_off[i_];                                   \
+      out.dY = (tab).dY[i_];                                               \
+      out.ldd = (tab).ldd[i_];                                             \
+      out.d = (tab).d[i_];                                                 \
+      out.S = (tab).S[i_];                                                 \
+    }                                                                      \
+  }
+
 // S += dY^T P over a range of 32-token steps for 16 Q columns of d.
 // PLDS: the P operands of each step reach a per-wave two-slot LDS ring by
 // direct global->LDS loads issued from inline assembly, so the compiler's
@@ -351,9 +384,8 @@ constexpr int acc_lds_bytes() {
 // slot itself with an exact vmcnt.  Otherwise P is staged in registers.
 template <int Q, int NB16, int kAccWaves, bool MASKED, bool PLDS>
 __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
-    const uint16_t* __restrict__ dY, int64_t ldd, int T, int d, int r,
-    const uint16_t* __restrict__ Pt, int steps_total, int steps_per_split,
-    float* __restrict__ S, float* __restrict__ part) {
+    OutTable tab, int T, int r, const uint16_t* __restrict__ Pt, int steps_total,
+    int steps_per_split, float* __restrict__ part) {
   constexpr int DC = 16 * Q;            // d columns per work-group
   constexpr int NREG = Q * NB16 * 4;    // accumulator floats per lane
   constexpr int CH = NREG < 32 ? NREG : 32;  // registers per reduction round
@@ -369,7 +401,13 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   const int m = lane & 15;   // A-operand row group (d columns)
   const int g4 = lane >> 4;  // which 8 tokens of the 32-token step
   const int sp = blockIdx.y;
-  const int dg = xcd_spread((int)blockIdx.x, sp, (int)gridDim.x);
+  const int dgg = xcd_spread((int)blockIdx.x, sp, (int)gridDim.x);   // across outputs
+  LOGRA_SELECT_OUT(tab, dgg, out);
+  const uint16_t* __restrict__ dY = out.dY;
+  const int64_t ldd = out.ldd;
+  const int d = out.d;
+  float* __restrict__ S = out.S;
+  const int dg = out.dg;                                             // within the output
   const int dc0 = dg * DC;
   const int col = dc0 + Q * m;
   const int s_begin = sp * steps_per_split;
@@ -514,7 +552,7 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   // or straight into S when there is a single split).
   float* red = reinterpret_cast<float*>(lds);
   constexpr int kPer = CH / kAccWaves > 0 ? CH / kAccWaves : 1;
-  float* my = part ? part + ((int64_t)sp * gridDim.x + dg) * (NREG * 64) : nullptr;
+  float* my = part ? part + ((int64_t)sp * gridDim.x + dgg) * (NREG * 64) : nullptr;
   __syncthreads();
 #pragma unroll
   for (int c0 = 0; c0 < NREG; c0 += CH) {
@@ -548,23 +586,24 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
 template <int Q, int NB16>
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part,
                                                        int n_split, int n_dgroups,
-                                                       int d, int r, bool s_vec4,
-                                                       float* __restrict__ S) {
+                                                       OutTable tab, int r) {
   constexpr int NREG = Q * NB16 * 4;
   constexpr int TILE = NREG * 64;
   const int64_t idx4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_split = (int64_t)n_dgroups * TILE;
   if (idx4 * 4 >= per_split) return;
   const int64_t flat = idx4 * 4;
-  const int dg = (int)(flat / TILE);
+  const int dgg = (int)(flat / TILE);
+  LOGRA_SELECT_OUT(tab, dgg, out);
   const int within = (int)(flat % TILE);
   const int i = within >> 6;
   const int ln = within & 63;       // multiple of 4
-  const int drow = acc_drow<Q, NB16>(dg * 16 * Q, i, ln);
+  const int drow = acc_drow<Q, NB16>(out.dg * 16 * Q, i, ln);
   const int rc = acc_rcol<NB16>(i, ln);
-  if (drow >= d) return;
-  float* srow = S + (int64_t)drow * r;
-  const bool vec = s_vec4 && rc + 4 <= r;   // r % 4 == 0 and S 16-byte aligned
+  if (drow >= out.d) return;
+  float* srow = out.S + (int64_t)drow * r;
+  // float4 access when r % 4 == 0 and S is 16-byte aligned
+  const bool vec = (r % 4) == 0 && (reinterpret_cast<uintptr_t>(out.S) & 15) == 0 && rc + 4 <= r;
   // Loads go out four splits at a time (with S in the first group), so one
   // memory latency covers each group; the adds still run in split order.
   // Slots past the last split re-read it and add an exact zero.
@@ -620,39 +659,37 @@ hipError_t launch_project(const SketchPlan& p, const uint16_t* X, int64_t ldx,
 }
 
 template <int Q, int NB16>
-hipError_t launch_accumulate(const SketchPlan& p, const uint16_t* dY, int64_t ldd,
-                             int T, int d, int r, const uint16_t* Pt, float* S,
-                             float* part, hipStream_t s) {
+hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, int r,
+                             const uint16_t* Pt, float* part, hipStream_t s) {
   constexpr int kAccWaves = acc_waves(Q, NB16);
   constexpr bool kPlds = acc_plds(NB16);
   const dim3 grid((unsigned)p.n_dgroups, (unsigned)p.n_split);
   float* pp = p.n_split > 1 ? part : nullptr;
-  const bool masked = (T % 32) != 0 || (d % (16 * Q)) != 0;
+  bool masked = (T % 32) != 0;
+  for (int o = 0; o < tab.n; ++o) masked = masked || (tab.d[o] % (16 * Q)) != 0;
   if (masked) {
     hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, true, kPlds>), grid,
-                       dim3(64 * kAccWaves), 0, s, dY, ldd, T, d, r, Pt, p.steps,
-                       p.steps_per_split, S, pp);
+                       dim3(64 * kAccWaves), 0, s, tab, T, r, Pt, p.steps,
+                       p.steps_per_split, pp);
   } else {
     hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, false, kPlds>), grid,
-                       dim3(64 * kAccWaves), 0, s, dY, ldd, T, d, r, Pt, p.steps,
-                       p.steps_per_split, S, pp);
+                       dim3(64 * kAccWaves), 0, s, tab, T, r, Pt, p.steps,
+                       p.steps_per_split, pp);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const int64_t quads = (int64_t)p.n_dgroups * Q * NB16 * 4 * 64 / 4;
-  const bool s_vec4 = (r % 4) == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0;
   hipLaunchKernelGGL((finalize_kernel<Q, NB16>), dim3((unsigned)((quads + 255) / 256)),
-                     dim3(256), 0, s, part, p.n_split, p.n_dgroups, d, r, s_vec4, S);
+                     dim3(256), 0, s, part, p.n_split, p.n_dgroups, tab, r);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p) {
-  if (T < 0 || d < 1 || k < 1 || r < 1 || r > 256) return false;
-  if (T >= (int64_t(1) << 31) || d >= (int64_t(1) << 31) ||
-      k >= (int64_t(1) << 31))
-    return false;
+bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
+                      SketchPlan* p) {
+  if (T < 0 || k < 1 || r < 1 || r > 256 || n_out < 1 || n_out > kMaxShared) return false;
+  if (T >= (int64_t(1) << 31) || k >= (int64_t(1) << 31)) return false;
   SketchPlan q{};
   q.rp = r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : r <= 128 ? 128 : 256;
   q.p_rows = q.rp < 32 ? 32 : q.rp;
@@ -662,7 +699,16 @@ bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p) {
   q.k_pad = round_up(k, 256);
   q.steps = (int)(q.t_pad / 32);
   const int dc = 16 * q.q_cols;
-  q.n_dgroups = (int)((d + dc - 1) / dc);
+  q.n_out = n_out;
+  int64_t groups = 0;
+  for (int o = 0; o < n_out; ++o) {
+    if (d[o] < 1 || d[o] >= (int64_t(1) << 31)) return false;
+    q.dg_off[o] = (int)groups;
+    groups += (d[o] + dc - 1) / dc;
+  }
+  if (groups >= (int64_t(1) << 27)) return false;   // finalize grid: 8 per group
+  q.dg_off[n_out] = (int)groups;
+  q.n_dgroups = (int)groups;
   // Enough work-groups to cover the chip (256 CUs) while each wave keeps at
   // least two 32-token steps.
   const int waves = acc_waves(q.q_cols, q.rp / 16);
@@ -688,9 +734,8 @@ bool make_sketch_plan(int64_t T, int64_t d, int64_t k, int r, SketchPlan* p) {
 }
 
 hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
-                         const uint16_t* dY, int64_t ldd, int T, int d, int k,
-                         int r, uint64_t seed, uint64_t stream, int kind,
-                         float* S, char* ws, hipStream_t s) {
+                         const SketchOut* outs, int T, int k, int r, uint64_t seed,
+                         uint64_t stream, int kind, char* ws, hipStream_t s) {
   uint16_t* Pt = reinterpret_cast<uint16_t*>(ws + p.off_pt);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   uint16_t* Ab = reinterpret_cast<uint16_t*>(ws + p.off_gauss);
@@ -711,12 +756,21 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
     default: e = launch_project<8>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
   }
   if (e != hipSuccess) return e;
+  OutTable tab{};
+  tab.n = p.n_out;
+  for (int o = 0; o <= p.n_out; ++o) tab.dg_off[o] = p.dg_off[o];
+  for (int o = 0; o < p.n_out; ++o) {
+    tab.dY[o] = outs[o].dY;
+    tab.ldd[o] = outs[o].ldd;
+    tab.d[o] = (int)outs[o].d;
+    tab.S[o] = outs[o].S;
+  }
   switch (p.rp) {
-    case 16: return launch_accumulate<8, 1>(p, dY, ldd, T, d, r, Pt, S, part, s);
-    case 32: return launch_accumulate<8, 2>(p, dY, ldd, T, d, r, Pt, S, part, s);
-    case 64: return launch_accumulate<8, 4>(p, dY, ldd, T, d, r, Pt, S, part, s);
-    case 128: return launch_accumulate<4, 8>(p, dY, ldd, T, d, r, Pt, S, part, s);
-    default: return launch_accumulate<2, 16>(p, dY, ldd, T, d, r, Pt, S, part, s);
+    case 16: return launch_accumulate<8, 1>(p, tab, T, r, Pt, part, s);
+    case 32: return launch_accumulate<8, 2>(p, tab, T, r, Pt, part, s);
+    case 64: return launch_accumulate<8, 4>(p, tab, T, r, Pt, part, s);
+    case 128: return launch_accumulate<4, 8>(p, tab, T, r, Pt, part, s);
+    default: return launch_accumulate<2, 16>(p, tab, T, r, Pt, part, s);
   }
 }
 

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = _lib.header_symbols()
-    assert len(declared) == 10
+    assert len(declared) == 12
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -176,3 +176,45 @@ def test_kl_budget_schedule():
     vals = [sched(s, 300) for s in range(300)]
     assert all(a > b for a, b in zip(vals, vals[1:]))
     assert abs(sched(149.5, 300) - 1.1e-4) < 1e-12
+
+
+def _shared(L, n_out=2, **kw):
+    import ctypes
+    a = dict(X=P, ldx=256, T=128, k=256, r=4, seed=1, stream=0, kind=0,
+             dY=[P] * n_out, ldd=[256] * n_out, d=[256] * n_out,
+             S=[P + 4096 * (o + 1) for o in range(n_out)], ws=P, ws_bytes=1 << 30, s=None)
+    a.update(kw)
+    n = kw.get("n_out_arg", n_out)
+    arr = lambda t, xs: None if xs is None else (t * max(1, len(xs)))(*xs)
+    return L.logra_sketch_accumulate_shared(
+        a["X"], a["ldx"], a["T"], a["k"], a["r"], a["seed"], a["stream"], a["kind"], n,
+        arr(ctypes.c_void_p, a["dY"]), arr(ctypes.c_int64, a["ldd"]), arr(ctypes.c_int64, a["d"]),
+        arr(ctypes.c_void_p, a["S"]), a["ws"], a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_out_arg=0), EINVAL), (dict(n_out_arg=5), EINVAL), (dict(dY=None), EINVAL),
+    (dict(ldd=None), EINVAL), (dict(d=None), EINVAL), (dict(S=None), EINVAL),
+    (dict(X=None), EINVAL), (dict(dY=[P, None]), EINVAL), (dict(S=[P, None]), EINVAL),
+    (dict(S=[P, P]), EINVAL),                                  # one accumulator per output
+    (dict(d=[256, 0]), EINVAL), (dict(ldd=[256, 100]), EINVAL), (dict(ldd=[256, 1 << 26]), EINVAL),
+    (dict(dY=[P, MIS]), EINVAL), (dict(S=[P, P + 2]), EINVAL), (dict(ldx=255), EINVAL),
+    (dict(r=0), EINVAL), (dict(kind=5), EINVAL),
+    (dict(ws=None), EWS), (dict(ws_bytes=16), EWS),
+])
+def test_sketch_shared_rejects(L, kw, status):
+    assert _shared(L, **kw) == status
+
+
+def test_sketch_shared_T0_and_sizes(L):
+    import ctypes
+    assert _shared(L, T=0, X=None, dY=[None, None], S=[None, None], ws=None, ws_bytes=0) == 0
+    d3 = (ctypes.c_int64 * 3)(1536, 256, 256)
+    shared = L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 3, d3)
+    assert shared >= 2 * 64 * 16384 * 2                       # at least the P buffer
+    d1 = (ctypes.c_int64 * 1)(1536)
+    assert L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 1, d1) == \
+        L.logra_sketch_ws_bytes(16384, 1536, 1536, 64)
+    assert L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 0, d3) == 0
+    assert L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 5, d3) == 0
+    assert L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 3, None) == 0

@@ -123,6 +123,55 @@ def test_sketch_matches_oracle(lg, T, d, k, r, kind, n_mb):
     assert err_total < S_TOL, err_total
 
 
+SHARED_CASES = [
+    # T, k, ds (outputs sharing X), r, kind
+    (512, 256, (256, 64, 64), 64, 0),          # q/k/v-shaped
+    (1000, 520, (300, 1030), 16, 0),           # gate/up-shaped, ragged
+    (77, 264, (17, 256, 129, 8), 4, 0),        # four outputs, tiny and ragged
+    (2048, 512, (512, 128), 100, 0),           # split path, padded rank
+    (129, 1000, (256, 100), 256, 1),           # Gaussian basis, maximum rank
+]
+
+
+@pytest.mark.parametrize("T,k,ds,r,kind", SHARED_CASES)
+def test_sketch_shared_matches_oracle_and_single_calls(lg, T, k, ds, r, kind):
+    say("sketch shared", T, k, ds, r, kind)
+    X = synth.host_normal_bf16((T, k), synth.X_ID, salt=k)
+    dYs = [synth.host_normal_bf16((T, d), synth.DY_ID, mb=o, salt=d) for o, d in enumerate(ds)]
+    S0 = [synth.host_normal_f32((d, r), synth.S_ID, mb=o, salt=T) for o, d in enumerate(ds)]
+    ldx = -(-k // 8) * 8
+    Xg = padded_bf16(X, ldx)
+    dYg = [padded_bf16(dY, -(-dY.shape[1] // 8) * 8 + 8) for dY in dYs]
+    Ss = [s0.clone().cuda() for s0 in S0]
+    lg.sketch_accumulate_shared(Xg, dYg, Ss, 1234, 0, kind)
+    singles = [s0.clone().cuda() for s0 in S0]
+    for dY, S in zip(dYg, singles):
+        lg.sketch_accumulate(Xg, dY, S, 1234, 0, kind)
+    torch.cuda.synchronize()
+    A = oproj.projection(1234, 0, kind, r, k)
+    Xf = synth.bf16_to_f64(X)
+    for o in range(len(ds)):
+        ref = osketch.accumulate(S0[o].numpy().astype(np.float64),
+                                 [(Xf, synth.bf16_to_f64(dYs[o]))], A)
+        base = S0[o].numpy().astype(np.float64)
+        got = Ss[o].cpu().numpy().astype(np.float64)
+        assert rel_fro(got - base, ref - base) < S_TOL, o
+        one = singles[o].cpu().numpy().astype(np.float64)
+        assert rel_fro(got - base, one - base) < 1e-5, o
+
+
+def test_sketch_shared_one_output_is_the_single_call_bitwise(lg):
+    say("sketch shared n_out = 1")
+    T, d, k, r = 2048, 384, 512, 64
+    X = synth.host_normal_bf16((T, k), synth.X_ID, salt=5).cuda()
+    dY = synth.host_normal_bf16((T, d), synth.DY_ID, salt=5).cuda()
+    a = torch.zeros(d, r, device="cuda")
+    b = torch.zeros(d, r, device="cuda")
+    lg.sketch_accumulate(X, dY, a, 99)
+    lg.sketch_accumulate_shared(X, [dY], [b], 99)
+    assert torch.equal(a, b)
+
+
 def test_sketch_padded_strides(lg):
     say("sketch padded strides")
     _, e1, _ = _sketch_case(lg, 300, 100, 120, 16, 0, 2, ld_pad=24)
