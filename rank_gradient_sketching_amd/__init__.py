@@ -7,3 +7,4 @@ from .api import (GAUSSIAN, MAX_SHARED, MAX_SWEEP, RADEMACHER,  # noqa: F401
                   kl_budget_schedule, kl_sweep_ws_bytes, kl_ws_bytes, merge, predicted_kl,
                   predicted_kl_sweep, regen_A, sketch_accumulate, sketch_accumulate_shared,
                   sketch_shared_ws_bytes, sketch_ws_bytes, sketch_workspace)
+from . import sync  # noqa: F401,E402

@@ -411,3 +411,18 @@ def test_kl_sweep_alpha_squared_law_and_edges(lg):
     shift = torch.full((n, V), 0.75, dtype=torch.bfloat16, device="cuda")
     flat = lg.predicted_kl_sweep(z_g, shift, [1.0, 4.0], 1.0).cpu().numpy()
     assert np.all(np.abs(flat) < 1e-6)
+
+
+def test_rollout_payload_apply_is_bitwise_the_trainer_merge(lg):
+    """[LoGRA] Sync: the rollout side rebuilds A from the seed and applies the
+    received factor; with (U, alpha, eta, seed) in the payload it runs the same
+    merge and its weights equal the trainer's bit for bit."""
+    say("rollout payload")
+    from rank_gradient_sketching_amd import sync
+    for kind, (d, k, r) in ((0, (512, 768, 64)), (1, (300, 1000, 17))):
+        W0 = synth.host_normal_bf16((d, k), synth.W_ID, salt=d).cuda()
+        S = synth.host_normal_f32((d, r), synth.S_ID, salt=d, sigma=15.0).cuda()
+        W_train = lg.merge(W0.clone(), S, 4321, 3, kind, 0.75, 2e-4)
+        payload = sync.pack_update(S, 4321, 3, kind, 0.75, 2e-4, k)
+        W_roll = sync.apply_update(W0.clone(), payload)
+        assert torch.equal(W_train, W_roll)
