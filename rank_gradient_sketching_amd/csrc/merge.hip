@@ -39,6 +39,10 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   constexpr bool kDouble = NKS <= 4;  // two A slices fit in 64 KB of LDS
   __shared__ __attribute__((aligned(16))) uint16_t At[(kDouble ? 2 : 1) * kPassCols * LDA];
   __shared__ __attribute__((aligned(16))) uint64_t sgn[GAUSS ? 1 : 4 * RP];
+  // Per-wave staging of one pass's results (64 rows x 64 columns, row stride
+  // kStRow bf16) for row-contiguous stores (interior tiles only).
+  constexpr int kStRow = kPassCols + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t stage[MASKED ? 1 : kWaves * 64 * kStRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -251,7 +255,11 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
           out[hh][p] = pack_bf16x2(n0, n1);
         }
       }
-      if (!MASKED || row < d) {
+      if constexpr (!MASKED) {
+        uint16_t* stg = stage + (wave * 64 + 16 * nt + m) * kStRow + 16 * g;
+        *reinterpret_cast<u32x4*>(stg) = out[0];
+        *reinterpret_cast<u32x4*>(stg + 8) = out[1];
+      } else if (row < d) {
         uint16_t* wr = W + (int64_t)row * ldw;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -268,6 +276,20 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
             }
           }
         }
+      }
+    }
+    // Interior tiles: the wave reads its 64 x 64 results back row by row,
+    // eight lanes per row, so every store writes whole 128-byte lines (stores
+    // of half lines, as the MFMA layout gives them, measured ~10 % slower).
+    // A wave only touches its own staging rows and LDS operations of a wave
+    // complete in order, so no barrier is needed.
+    if constexpr (!MASKED) {
+      const int pc = lane & 7;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = 8 * i + (lane >> 3);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (wave * 64 + rr) * kStRow + 8 * pc);
+        *reinterpret_cast<u32x4*>(W + (int64_t)(row0 + rr) * ldw + col0 + pass * kPassCols + 8 * pc) = v;
       }
     }
   };
