@@ -43,20 +43,22 @@ def kernel_source_hash():
 
 
 def short_name(name):
-    """'void logra::(anon)::accumulate_kernel<4, 4, 8, false>(...)' -> 'accumulate_kernel<4, 4, 8, false>'."""
-    base = name.split("(")[0] if "(anonymous" not in name else name
-    if "logra::" in name:
-        base = name.split("logra::")[-1]
-        base = base.replace("(anonymous namespace)::", "")
-        depth, out = 0, []
-        for ch in base:
-            if ch == "(" and depth == 0:
-                break
-            depth += ch == "<"
-            depth -= ch == ">"
-            out.append(ch)
-        return "".join(out).strip()
-    return base.replace("void ", "").strip()[:80]
+    """'void logra::(anonymous namespace)::accumulate_kernel<4, 4, 8, false>(...)'
+    -> 'accumulate_kernel<4, 4, 8, false>' (parameter types may name logra:: too)."""
+    base = name.replace("(anonymous namespace)::", "")
+    if base.startswith("void "):
+        base = base[5:]
+    depth, out = 0, []
+    for ch in base:
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    base = "".join(out).strip()
+    if base.startswith("logra::"):
+        return base[len("logra::"):]
+    return base[:80]
 
 
 def stats_table(stats_csv):
