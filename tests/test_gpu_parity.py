@@ -93,6 +93,12 @@ SKETCH_CASES = [
     (4096, 1536, 256, 64, 0, 1),    # narrow k, many splits
     (200, 300, 520, 16, 1, 2),      # Gaussian basis
     (129, 256, 1000, 256, 1, 1),
+    # many d groups along with several splits
+    (4096, 1024, 1024, 64, 0, 2),   # 8 d groups x 8 splits
+    (3000, 4096, 512, 16, 0, 1),    # 32 d groups, 5 splits, ragged T
+    (1000, 4000, 256, 64, 0, 1),    # ragged d (masked columns), 2 splits
+    (1024, 4224, 256, 32, 0, 1),    # 33 d groups
+    (2048, 1024, 768, 64, 1, 1),    # Gaussian basis
 ]
 
 
