@@ -37,6 +37,9 @@ Parity status per function:
   projection (Gaussian): the generator's statistics are pinned; its exact
       element values are "parity unpinned" (fp64 Box-Muller here vs fp32
       hardware transcendentals on the GPU, compared to within one bf16 ulp).
+  optim (stateful sketch update rules): "parity unpinned" - the pages name
+      stateful sketch optimizers without defining one; the textbook momentum
+      and Adam rules used here are pinned against closed forms only.
 """
 
-from . import bf16, philox, projection, sketch, merge, kl  # noqa: F401
+from . import bf16, philox, projection, sketch, merge, kl, optim  # noqa: F401
