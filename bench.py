@@ -303,6 +303,30 @@ def run_layer_set(lg, synth, reps=10, r=64):
     return res
 
 
+def run_update(lg, synth, d=4096, r=64, reps=200):
+    """The sketch-space Adam and momentum updates on the layer's d x r sketch
+    (24 and 16 bytes per entry); the merge would then read U."""
+    S = synth.host_normal_f32((d, r), synth.S_ID, sigma=15.0).cuda()
+    m = torch.zeros(d, r, device="cuda")
+    v = torch.zeros(d, r, device="cuda")
+    U = torch.empty(d, r, device="cuda")
+    res = {}
+    for name, rule, nbytes in (("adam", lg.UPDATE_ADAM, 24), ("momentum", lg.UPDATE_MOMENTUM, 16)):
+        for t in range(1, 4):
+            lg.sketch_update(rule, S, U, m, v, step=t)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for t in range(reps):
+            lg.sketch_update(rule, S, U, m, v, step=4 + t)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / reps * 1e3
+        res[name] = dict(us_per_call=us, GBps=nbytes * d * r / (us * 1e-6) / 1e9)
+    res["shape"] = [d, r]
+    return res
+
+
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "sketch_merge_d4096_r64_traffic.md")
 
 
@@ -405,6 +429,7 @@ def main():
     layer, data = run_layer(lg, synth, args.steps, args.warmup)
     kl = None if args.no_kl else run_kl(lg, synth)
     layer_set = None if args.no_layerset else run_layer_set(lg, synth)
+    update = run_update(lg, synth)
     calib = None if args.no_calib else run_copy_calibration()
     cpu = None if args.no_cpu else cpu_baseline(synth, data, args.cpu_budget)
 
@@ -446,6 +471,7 @@ def main():
         "parity": layer["parity"],
         "kl": kl,
         "layer_set": layer_set,
+        "sketch_update": update,
         "copy_calibration": calib,
     }
     print(json.dumps(out), flush=True)

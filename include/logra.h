@@ -176,6 +176,42 @@ int logra_merge(uint16_t* W, int64_t ldw, const float* S, int64_t d, int64_t k,
                 int32_t r, uint64_t seed, uint64_t stream, int kind,
                 float alpha, float eta, hipStream_t s);
 
+/* Sketch-space update rules for logra_sketch_update. */
+#define LOGRA_UPDATE_SGD 0      /* U = S */
+#define LOGRA_UPDATE_MOMENTUM 1 /* m <- beta1 m + S; U = m */
+#define LOGRA_UPDATE_ADAM 2     /* Adam on the sketch (see below) */
+
+/*
+ * logra_sketch_update - the update factor U from the sketch S and the state
+ * of a sketch-space optimizer, entrywise over d x r.
+ * [LoGRA] Sketch: the update is W <- W - alpha eta U A, with U = S in the
+ * basic SGD variant; stateful sketch optimizers keep state of their own
+ * (the pages do not define one).  The stateful rules are the textbook ones on
+ * the d x r sketch instead of the d x k gradient:
+ *   LOGRA_UPDATE_SGD       U = S
+ *   LOGRA_UPDATE_MOMENTUM  m <- beta1 m + S;  U = m          (heavy ball)
+ *   LOGRA_UPDATE_ADAM      m <- beta1 m + (1 - beta1) S
+ *                          v <- beta2 v + (1 - beta2) S^2
+ *                          U = (m / b1) / (sqrt(v / b2) + eps)
+ *                          b1 = 1 - beta1^step, b2 = 1 - beta2^step
+ *                          (Kingma & Ba, ICLR 2015, Algorithm 1)
+ * U then goes to logra_merge in place of S (and to the rollout payload).
+ * Arithmetic is fp32 per entry; b1, b2 are formed in double on the host and
+ * rounded to float.  With eps = 0 an entry whose m and v are both 0 gives NaN.
+ *
+ * S: device float[d x r] (read only).  m, v: device float[d x r] state,
+ *     in/out (m for MOMENTUM and ADAM, v for ADAM; otherwise ignored and may
+ *     be NULL); start them at zero.  U: device float[d x r], written.
+ * U may be S itself, and for MOMENTUM also m itself; no other pair of the
+ * arrays may overlap.  All arrays contiguous and 4-byte aligned.
+ * beta1, beta2 in [0, 1); eps >= 0 and finite; step >= 1 (ADAM: the 1-based
+ * step number).  d >= 1, 1 <= r <= LOGRA_MAX_RANK.
+ * Returns LOGRA_OK, LOGRA_EINVAL or LOGRA_EHIP.
+ */
+int logra_sketch_update(int rule, const float* S, float* m, float* v, float* U,
+                        int64_t d, int32_t r, float beta1, float beta2, float eps,
+                        int64_t step, hipStream_t s);
+
 /* Bytes of workspace logra_predicted_kl needs when kl_tok is NULL (0 when
  * kl_tok is given).  Returns 0 for invalid sizes. */
 size_t logra_kl_ws_bytes(int64_t n_tok, int64_t vocab);

@@ -15,7 +15,9 @@ closed forms (tests/test_oracle_optim.py), not against the pages.
                     v <- beta2 v + (1 - beta2) S^2
                     U = (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
                     t = 1, 2, ... the step number            [KINGMA15]
-All arithmetic is fp64.  State arrays are updated in place.
+All arithmetic is fp64 on the beta / eps values as given (a caller comparing
+with an fp32 interface passes the fp32-rounded values).  State arrays are
+updated in place.
 
 [KINGMA15] Kingma & Ba, "Adam: A Method for Stochastic Optimization", ICLR 2015,
            Algorithm 1.

@@ -31,6 +31,9 @@ SIGNATURES = {
     "logra_merge": (ctypes.c_int, [c_vp, ctypes.c_int64, c_vp, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_float, c_vp]),
+    "logra_sketch_update": (ctypes.c_int, [ctypes.c_int, c_vp, c_vp, c_vp, c_vp, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_int64, c_vp]),
     "logra_kl_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "logra_predicted_kl": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_float, ctypes.c_float,

@@ -149,6 +149,40 @@ def merge(W, S, seed, stream=0, kind=RADEMACHER, alpha=1.0, eta=1.0):
     return W
 
 
+UPDATE_SGD = 0
+UPDATE_MOMENTUM = 1
+UPDATE_ADAM = 2
+
+
+def sketch_update(rule, S, U=None, m=None, v=None, beta1=0.9, beta2=0.999, eps=1e-8, step=1):
+    """U from the sketch S and the sketch-space optimizer state (m, v updated in
+    place): UPDATE_SGD U = S; UPDATE_MOMENTUM m <- beta1 m + S, U = m;
+    UPDATE_ADAM bias-corrected Adam on S.  U defaults to a new tensor; returns U."""
+    _require(S, "S", torch.float32, 2)
+    if not S.is_contiguous():
+        raise ValueError("S must be a contiguous (d, r) float32 tensor")
+    d, r = S.shape
+    if U is None:
+        U = torch.empty_like(S)
+    ptrs = []
+    for name, t, need in (("U", U, True), ("m", m, rule in (UPDATE_MOMENTUM, UPDATE_ADAM)),
+                          ("v", v, rule == UPDATE_ADAM)):
+        if t is None:
+            if need:
+                raise ValueError(f"rule {rule} needs the state tensor {name}")
+            ptrs.append(None)
+            continue
+        _require(t, name, torch.float32, 2)
+        if tuple(t.shape) != (d, r) or not t.is_contiguous() or t.device != S.device:
+            raise ValueError(f"{name} must be a contiguous ({d}, {r}) float32 tensor on {S.device}")
+        ptrs.append(t.data_ptr())
+    st = _lib.lib().logra_sketch_update(rule, S.data_ptr(), ptrs[1], ptrs[2], ptrs[0], d, r,
+                                        float(beta1), float(beta2), float(eps), int(step),
+                                        _stream(S))
+    _lib.check(st, "logra_sketch_update")
+    return U
+
+
 def kl_ws_bytes(n_tok, vocab):
     return int(_lib.lib().logra_kl_ws_bytes(n_tok, vocab))
 

@@ -155,6 +155,45 @@ int logra_merge(uint16_t* W, int64_t ldw, const float* S, int64_t d, int64_t k,
                                         kind, alpha, eta, s));
 }
 
+int logra_sketch_update(int rule, const float* S, float* m, float* v, float* U,
+                        int64_t d, int32_t r, float beta1, float beta2, float eps,
+                        int64_t step, hipStream_t s) {
+  if (rule != LOGRA_UPDATE_SGD && rule != LOGRA_UPDATE_MOMENTUM && rule != LOGRA_UPDATE_ADAM)
+    return LOGRA_EINVAL;
+  if (!dim_ok(d) || !rank_ok(r) || S == nullptr || U == nullptr) return LOGRA_EINVAL;
+  const bool use_m = rule != LOGRA_UPDATE_SGD;
+  const bool use_v = rule == LOGRA_UPDATE_ADAM;
+  if ((use_m && m == nullptr) || (use_v && v == nullptr)) return LOGRA_EINVAL;
+  const float* arr[4] = {S, use_m ? m : nullptr, use_v ? v : nullptr, U};
+  for (const float* a : arr)
+    if (a != nullptr && !aligned(a, 4)) return LOGRA_EINVAL;
+  auto beta_ok = [](float b) { return isfinite(b) && b >= 0.0f && b < 1.0f; };
+  if (use_m && !beta_ok(beta1)) return LOGRA_EINVAL;
+  if (use_v && (!beta_ok(beta2) || !isfinite(eps) || eps < 0.0f || step < 1)) return LOGRA_EINVAL;
+  // Overlaps: U may be S itself, and for momentum m itself; any other overlap
+  // of the four d x r arrays (or a partial one) is rejected.
+  const int64_t n = d * (int64_t)r;
+  auto lo = [](const float* a) { return reinterpret_cast<uintptr_t>(a); };
+  auto overlap = [&](const float* a, const float* b) {
+    return a != nullptr && b != nullptr && lo(a) < lo(b) + 4 * (uintptr_t)n &&
+           lo(b) < lo(a) + 4 * (uintptr_t)n;
+  };
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j) {
+      if (!overlap(arr[i], arr[j])) continue;
+      const bool same = arr[i] == arr[j];
+      const bool allowed = (j == 3 && i == 0) || (j == 3 && i == 1 && rule == LOGRA_UPDATE_MOMENTUM);
+      if (!same || !allowed) return LOGRA_EINVAL;
+    }
+  double bc1 = 1.0, bc2 = 1.0;
+  if (use_v) {
+    bc1 = 1.0 - pow((double)beta1, (double)step);
+    bc2 = 1.0 - pow((double)beta2, (double)step);
+  }
+  return hip_status(logra::launch_sketch_update(rule, S, m, v, U, n, beta1, beta2, eps,
+                                                bc1, bc2, s));
+}
+
 size_t logra_kl_ws_bytes(int64_t n_tok, int64_t vocab) {
   if (!dim_ok(n_tok) || !dim_ok(vocab)) return 0;
   return (size_t)logra::round_up(n_tok * 4, 256);

@@ -72,4 +72,14 @@ hipError_t launch_kl_sweep(const uint16_t* z, const uint16_t* dz, int n_tok, int
                            const float* weight, float* kl_mean, float* kl_tok,
                            hipStream_t s);
 
+// Sketch-space update rules (U from S and the optimizer state).
+constexpr int kUpdateSgd = 0;
+constexpr int kUpdateMomentum = 1;
+constexpr int kUpdateAdam = 2;
+
+// n = d r entries; bc1, bc2 = 1 - beta^t (Adam only).
+hipError_t launch_sketch_update(int rule, const float* S, float* m, float* v, float* U,
+                                int64_t n, float beta1, float beta2, float eps,
+                                double bc1, double bc2, hipStream_t s);
+
 }  // namespace logra

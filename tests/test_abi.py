@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = _lib.header_symbols()
-    assert len(declared) == 12
+    assert len(declared) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -218,3 +218,43 @@ def test_sketch_shared_T0_and_sizes(L):
     assert L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 0, d3) == 0
     assert L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 5, d3) == 0
     assert L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 3, None) == 0
+
+
+def _update(L, **kw):
+    n4 = 64 * 16 * 4                       # bytes of one d x r array below
+    a = dict(rule=2, S=P, m=P + n4, v=P + 2 * n4, U=P + 3 * n4, d=64, r=16, b1=0.9, b2=0.999,
+             eps=1e-8, step=1, s=None)
+    a.update(kw)
+    return L.logra_sketch_update(a["rule"], a["S"], a["m"], a["v"], a["U"], a["d"], a["r"],
+                                 a["b1"], a["b2"], a["eps"], a["step"], a["s"])
+
+
+N4 = 64 * 16 * 4
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rule=3), dict(rule=-1), dict(S=None), dict(U=None), dict(rule=1, m=None), dict(v=None),
+    dict(d=0), dict(r=0), dict(r=300), dict(S=P + 2), dict(U=P + 3 * N4 + 2), dict(m=P + N4 + 1),
+    dict(b1=1.0), dict(b1=-0.1), dict(b1=float("nan")), dict(b2=1.0), dict(b2=float("inf")),
+    dict(eps=-1e-8), dict(eps=float("inf")), dict(step=0), dict(step=-3),
+    dict(rule=1, m=P),                     # momentum state aliasing S
+    dict(U=P + 2 * N4),                    # U aliasing Adam's v
+    dict(U=P + N4),                        # U aliasing Adam's m
+    dict(U=P + 4),                         # U partially overlapping S
+    dict(v=P + N4 + 64),                   # v partially overlapping m
+    dict(rule=0, U=P + 16),                # SGD: U partially overlapping S
+])
+def test_sketch_update_rejects(L, kw):
+    assert _update(L, **kw) == EINVAL
+
+
+def test_sketch_update_ignores_unused_state_arguments(L):
+    # SGD and momentum never look at v (nor SGD at m), so their validity does not
+    # depend on them; a valid call then fails only at the launch (no GPU here).
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a valid call would launch on placeholder pointers")
+    st = _update(L, rule=0, m=None, v=None, b1=7.0, b2=-1.0, eps=-1.0, step=0)
+    assert st != EINVAL
+    st = _update(L, rule=1, v=None, b2=9.0, eps=float("nan"), step=0)
+    assert st != EINVAL
