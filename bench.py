@@ -303,6 +303,116 @@ def run_layer_set(lg, synth, reps=10, r=64):
     return res
 
 
+def _time_ms(fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def _layer_set_step(lg, synth, wl, cfg, r, kind, stream, n_mb, salt=0):
+    """One decoder layer of a layer-set workload: every projection sketched over
+    n_mb microbatches (q/k/v and gate/up sharing their input) and merged.
+    Returns (fn, algorithmic bytes, tokens) for one optimizer step of the layer."""
+    T = cfg["T"]
+    proj = {n: (d, k) for n, d, k in cfg["projections"]}
+    groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+    seed = 1234 + salt
+    X = [synth.device_normal_bf16((T, proj[g[0]][1]), synth.X_ID, wl, salt=gi)
+         for gi, g in enumerate(groups)]
+    dY = {n: synth.device_normal_bf16((T, proj[n][0]), synth.DY_ID, wl, salt=i)
+          for i, n in enumerate(proj)}
+    W = {n: synth.device_normal_bf16(proj[n], synth.W_ID, wl, salt=i) for i, n in enumerate(proj)}
+    S = {n: torch.zeros(proj[n][0], r, device="cuda") for n in proj}
+    ws = []
+    for g in groups:
+        nb = lg.sketch_shared_ws_bytes(T, proj[g[0]][1], r, [proj[n][0] for n in g])
+        ws.append(torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"))
+
+    def step():
+        for n in proj:
+            S[n].zero_()
+        for _ in range(n_mb):   # the microbatches' tensors are reused: each is far above the MALL
+            for gi, g in enumerate(groups):
+                lg.sketch_accumulate_shared(X[gi], [dY[n] for n in g], [S[n] for n in g], seed,
+                                            stream, kind, ws=ws[gi])
+        for n in proj:
+            lg.merge(W[n], S[n], seed, stream, kind, 1.0, 2e-4)
+
+    nbytes = n_mb * (sum(2 * T * proj[g[0]][1] for g in groups) +
+                     sum(2 * T * proj[n][0] + 8 * proj[n][0] * r for n in proj)) + \
+        sum(merge_bytes(proj[n][0], proj[n][1], r) for n in proj)
+    return step, nbytes, n_mb * T
+
+
+def run_other_configs(lg, synth):
+    """Throughput of the other workloads at one GPU: the d = k = 256 layer, one
+    layer of the 1.5B-shaped set at each rank and basis, one layer of the
+    7B-shaped set at r = 256, and the wide layer (d = 5120, k = 25600,
+    r = 256, T = 16384).  Each: one optimizer step (every microbatch sketched,
+    then merged), algorithmic bytes / time."""
+    out = {}
+
+    def report(name, ms, nbytes, tokens, **extra):
+        out[name] = dict(us_per_step=ms * 1e3, tokens_per_s=tokens / (ms * 1e-3),
+                         GBps=nbytes / (ms * 1e-3) / 1e9,
+                         frac_hbm=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, bytes=nbytes, **extra)
+        log(f"[bench] {name}: {ms * 1e3:.1f} us/step, {out[name]['GBps']:.0f} GB/s")
+
+    # d = k = 256, r = 4, two microbatches of T = 128 (latency bound)
+    c = synth.WORKLOADS["layer_d256_r4"]
+    d, k, r, T = c["d"], c["k"], c["r"], c["T"]
+    Xs = [synth.device_normal_bf16((T, k), synth.X_ID, "layer_d256_r4", mb) for mb in range(2)]
+    dYs = [synth.device_normal_bf16((T, d), synth.DY_ID, "layer_d256_r4", mb) for mb in range(2)]
+    W = synth.device_normal_bf16((d, k), synth.W_ID, "layer_d256_r4")
+    S = torch.zeros(d, r, device="cuda")
+    ws = lg.sketch_workspace(T, d, k, r)
+
+    def small():
+        S.zero_()
+        for X, dY in zip(Xs, dYs):
+            lg.sketch_accumulate(X, dY, S, 1234, ws=ws)
+        lg.merge(W, S, 1234, 0, 0, c["alpha"], c["eta"])
+    report("layer_d256_r4", _time_ms(small, 50), 2 * sketch_bytes(T, d, k, r) + merge_bytes(d, k, r),
+           2 * T)
+
+    for r, kind, stream, label in ((4, 0, 0, "r4"), (16, 0, 0, "r16"), (64, 0, 0, "r64"),
+                                   (64, 0, 1, "r64_refreshed"), (64, 1, 0, "r64_gaussian"),
+                                   (256, 0, 0, "r256")):
+        fn, nbytes, tokens = _layer_set_step(lg, synth, "qwen1p5b_layers", synth.QWEN1P5B, r, kind,
+                                             stream, synth.QWEN1P5B["n_mb"])
+        report(f"qwen1p5b_layer_{label}", _time_ms(fn, 3), nbytes, tokens)
+        del fn
+        torch.cuda.empty_cache()
+
+    fn, nbytes, tokens = _layer_set_step(lg, synth, "qwen7b_layers", synth.QWEN7B, 256, 0, 0,
+                                         synth.QWEN7B["n_mb"])
+    report("qwen7b_layer_r256", _time_ms(fn, 2), nbytes, tokens)
+    del fn
+    torch.cuda.empty_cache()
+
+    wide = synth.WORKLOADS["kl_vocab152064"]["wide"]
+    d, k, r, T = wide["d"], wide["k"], wide["r"], wide["T"]
+    X = synth.device_normal_bf16((T, k), synth.X_ID, "kl_vocab152064")
+    dY = synth.device_normal_bf16((T, d), synth.DY_ID, "kl_vocab152064")
+    W = synth.device_normal_bf16((d, k), synth.W_ID, "kl_vocab152064")
+    S = torch.zeros(d, r, device="cuda")
+    ws = lg.sketch_workspace(T, d, k, r)
+    sk_ms = _time_ms(lambda: lg.sketch_accumulate(X, dY, S, 1234, ws=ws), 5)
+    mg_ms = _time_ms(lambda: lg.merge(W, S, 1234, 0, 0, 1.0, 2e-4), 5)
+    report("wide_layer_d5120_k25600_r256", sk_ms + mg_ms, sketch_bytes(T, d, k, r) + merge_bytes(d, k, r),
+           T, sketch_us=sk_ms * 1e3, sketch_GBps=sketch_bytes(T, d, k, r) / (sk_ms * 1e-3) / 1e9,
+           merge_us=mg_ms * 1e3, merge_GBps=merge_bytes(d, k, r) / (mg_ms * 1e-3) / 1e9)
+    del X, dY, W
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_update(lg, synth, d=4096, r=64, reps=200):
     """The sketch-space Adam and momentum updates on the layer's d x r sketch
     (24 and 16 bytes per entry); the merge would then read U."""
@@ -414,6 +524,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-calib", action="store_true")
     ap.add_argument("--no-layerset", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU leg "
@@ -430,6 +541,7 @@ def main():
     kl = None if args.no_kl else run_kl(lg, synth)
     layer_set = None if args.no_layerset else run_layer_set(lg, synth)
     update = run_update(lg, synth)
+    others = None if args.no_configs else run_other_configs(lg, synth)
     calib = None if args.no_calib else run_copy_calibration()
     cpu = None if args.no_cpu else cpu_baseline(synth, data, args.cpu_budget)
 
@@ -472,6 +584,7 @@ def main():
         "kl": kl,
         "layer_set": layer_set,
         "sketch_update": update,
+        "other_configs": others,
         "copy_calibration": calib,
     }
     print(json.dumps(out), flush=True)

@@ -24,9 +24,9 @@
 //              of 32-token steps.  Each lane loads an 8-token x Q-column block
 //              of dY with row-contiguous loads and transposes it in registers
 //              (v_perm_b32), giving K = token operands for 16x16x32 MFMA
-//              against P_hi and P_lo.  Waves split the steps and are summed in
-//              LDS in a fixed order; with several work-groups along T each
-//              writes its partial tile, and
+//              against P_hi and P_lo.  Waves split the steps (and, above
+//              r = 64, the rank) and are summed in LDS in a fixed order; with
+//              several work-groups along T each writes its partial tile, and
 //   finalize   adds the partial tiles to S in split order.  S is therefore
 //              bit-reproducible.
 // The Gaussian basis is first written once per call as a bf16 r x k matrix in
@@ -43,15 +43,15 @@ namespace {
 // unless the accumulators of a large rank need the larger register budget.
 constexpr int proj_waves(int nb) { return nb <= 4 ? 8 : 4; }
 
-// P operands go through LDS for r <= 64 (the two-slot ring of eight waves
-// fits in 128 KB); larger ranks stage them in registers.
-constexpr bool acc_plds(int nb16) { return nb16 <= 4; }
-
-// Waves per accumulate work-group: eight (two per SIMD) unless register-
-// staged P operands of a large rank need the larger per-wave budget.
-constexpr int acc_waves(int q, int nb16) {
-  return (q * nb16 * 4 <= 64 || acc_plds(nb16)) ? 8 : 4;
-}
+// Accumulate work-groups: eight waves (two per SIMD), each holding a tile of
+// 128 d columns x up to 64 r columns (NB16 blocks of 16) of the sketch, with
+// its steps' P operands in a per-wave two-slot LDS ring (8 waves x 16 KB).
+// Ranks above 64 split r across the waves (2 or 4 ways) rather than shrink
+// the d tile, so every P byte brought to a CU still meets 128 d columns.
+constexpr int kAccWaves = 8;
+constexpr int kAccQ = 8;                                      // d columns per lane / 16
+constexpr int acc_nbw(int nb16) { return nb16 < 4 ? nb16 : 4; }   // r blocks per wave
+constexpr int acc_rsplit(int nb16) { return nb16 / acc_nbw(nb16); }
 
 // ------------------------------------------------------------------ project
 // X reaches LDS by direct global->LDS loads (global_load_lds_dwordx4): each
@@ -271,13 +271,6 @@ struct DyStage {
   uint32_t R[8][Q / 2];
 };
 
-// P_hi / P_lo operands of one step held in registers (16 r-columns per block,
-// the lane's eight tokens).
-template <int NB16>
-struct PStage {
-  u32x4 bh[NB16], bl[NB16];
-};
-
 // dY loads go through a buffer resource over the step's rows: the row offset
 // e * ldd rides in the scalar offset and the lane's own offset in one 32-bit
 // register (the caller guarantees 64 * ldd < 2^32), and rows at or past T
@@ -334,12 +327,18 @@ __device__ __forceinline__ int acc_rcol(int i, int ln) {
   return 16 * ((i >> 2) % NB16) + (ln & 15);
 }
 
-// LDS bytes of the accumulate kernel: the P ring (PLDS) and the reduction
-// buffer share one array.
-template <int NB16, int kAccWaves, bool PLDS>
+// Registers per round of the cross-wave sum: 32 when every wave holds the
+// whole tile, 64 (or all) when r is split across the waves.
+constexpr int acc_round(int nb16) {
+  return acc_rsplit(nb16) == 1 ? 32 : (kAccQ * acc_nbw(nb16) * 4 < 64 ? kAccQ * acc_nbw(nb16) * 4 : 64);
+}
+
+// LDS bytes of the accumulate kernel: the P ring and the reduction buffer
+// share one array.
+template <int NB16>
 constexpr int acc_lds_bytes() {
-  constexpr int ring = PLDS ? kAccWaves * 2 * (NB16 * 2 * 1024) : 0;
-  constexpr int red = kAccWaves * 32 * 64 * 4;
+  constexpr int ring = kAccWaves * 2 * (acc_nbw(NB16) * 2 * 1024);
+  constexpr int red = kAccWaves * acc_round(NB16) * 64 * 4;
   return ring > red ? ring : red;
 }
 
@@ -377,27 +376,36 @@ struct OutSel {
   }
 
 // S += dY^T P over a range of 32-token steps for 16 Q columns of d.
-// PLDS: the P operands of each step reach a per-wave two-slot LDS ring by
-// direct global->LDS loads issued from inline assembly, so the compiler's
-// wait-count pass (which would wait for every outstanding vector load before
-// any LDS read) keeps the dY prefetch in flight; the kernel waits for each P
-// slot itself with an exact vmcnt.  Otherwise P is staged in registers.
-template <int Q, int NB16, int kAccWaves, bool MASKED, bool PLDS>
+// The P operands of each step reach a per-wave two-slot LDS ring by direct
+// global->LDS loads issued from inline assembly, so the compiler's wait-count
+// pass (which would wait for every outstanding vector load before any LDS
+// read) keeps the dY prefetch in flight; the kernel waits for each P slot
+// itself with an exact vmcnt.  With r split RS ways, wave w takes r blocks
+// NBW (w / L) .. and steps s_begin + (w % L) + L j (L = 8 / RS waves along
+// the steps); waves of one r part load the same dY rows (cache hits after
+// the first).
+template <int Q, int NB16, bool MASKED>
 __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
     OutTable tab, int T, int r, const uint16_t* __restrict__ Pt, int steps_total,
     int steps_per_split, float* __restrict__ part) {
   constexpr int DC = 16 * Q;            // d columns per work-group
-  constexpr int NREG = Q * NB16 * 4;    // accumulator floats per lane
-  constexpr int CH = NREG < 32 ? NREG : 32;  // registers per reduction round
-  constexpr int kSlot = NB16 * 2 * 1024;     // P bytes of one step
+  constexpr int NREG = Q * NB16 * 4;    // accumulator floats of the tile per lane
+  constexpr int NBW = acc_nbw(NB16);    // 16-column r blocks per wave
+  constexpr int RS = NB16 / NBW;        // ways r is split across the waves
+  constexpr int NREGW = Q * NBW * 4;    // accumulator floats per lane of one wave
+  constexpr int kLanes = kAccWaves / RS;     // waves along the steps
+  constexpr int CH = acc_round(NB16);        // registers per reduction round
+  constexpr int kSlot = NBW * 2 * 1024;      // P bytes of one step for one wave
   // vector-memory instructions issued after a P slot's loads before it is
   // read: the stage's 8 dY loads, then the other slot's P and dY loads
-  constexpr int kAfterP = 8 + 2 * NB16 + 8;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[acc_lds_bytes<NB16, kAccWaves, PLDS>()];
+  constexpr int kAfterP = 8 + 2 * NBW + 8;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[acc_lds_bytes<NB16>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int rpart = wave / kLanes;  // r part of this wave
+  const int wl = wave % kLanes;     // step lane of this wave
   const int m = lane & 15;   // A-operand row group (d columns)
   const int g4 = lane >> 4;  // which 8 tokens of the 32-token step
   const int sp = blockIdx.y;
@@ -413,23 +421,24 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   const int s_begin = sp * steps_per_split;
   const int s_end = min(steps_total, s_begin + steps_per_split);
 
-  float acc[NREG];
+  float acc[NREGW];
 #pragma unroll
-  for (int i = 0; i < NREG; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < NREGW; ++i) acc[i] = 0.0f;
   const int vo = dy_lane_offset(ldd, d, col, g4);
   const int qvalid = d - col;     // columns col + q < d are real (MASKED)
 
-  unsigned char* ring = lds + wave * 2 * kSlot;   // PLDS only
+  unsigned char* ring = lds + wave * 2 * kSlot;
   auto p_issue = [&](int step, int slot) {
 #pragma unroll
-    for (int blk = 0; blk < 2 * NB16; ++blk) {
-      const uint16_t* src = Pt + p_block(step, blk >> 1, blk & 1, NB16) + 8 * lane;
+    for (int blk = 0; blk < 2 * NBW; ++blk) {
+      const uint16_t* src =
+          Pt + p_block(step, rpart * NBW + (blk >> 1), blk & 1, NB16) + 8 * lane;
       lds_dma16(src, lds_addr(ring + slot * kSlot + blk * 1024));
     }
   };
   // One step: Q A operands (d rows x tokens, transposed in registers with
-  // v_perm from the row loads) against NB16 hi/lo pairs of P operands.
-  auto mfma_step = [&](const DyStage<Q>& ds, const u32x4* bh, const u32x4* bl, int nb) {
+  // v_perm from the row loads) against NBW hi/lo pairs of P operands.
+  auto mfma_step = [&](const DyStage<Q>& ds, const u32x4& bh, const u32x4& bl, int nb) {
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       // K assignment: lane group g4, element e <-> token tb + e.
@@ -440,10 +449,10 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
                                      (q & 1) ? 0x07060302u : 0x05040100u);
       }
       if (MASKED && q >= qvalid) a = u32x4{0u, 0u, 0u, 0u};   // column past d
-      const int i0 = (q * NB16 + nb) * 4;
+      const int i0 = (q * NBW + nb) * 4;
       f32x4 c4 = {acc[i0], acc[i0 + 1], acc[i0 + 2], acc[i0 + 3]};
-      c4 = mfma16(a, *bh, c4);
-      c4 = mfma16(a, *bl, c4);
+      c4 = mfma16(a, bh, c4);
+      c4 = mfma16(a, bl, c4);
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i0 + v] = c4[v];
     }
@@ -451,122 +460,87 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   auto compute_lds = [&](const DyStage<Q>& ds, int slot) {
     const unsigned char* base = ring + slot * kSlot + 16 * lane;
 #pragma unroll
-    for (int nb = 0; nb < NB16; ++nb) {
+    for (int nb = 0; nb < NBW; ++nb) {
       const u32x4 bh = *reinterpret_cast<const u32x4*>(base + (2 * nb) * 1024);
       const u32x4 bl = *reinterpret_cast<const u32x4*>(base + (2 * nb + 1) * 1024);
-      mfma_step(ds, &bh, &bl, nb);
-    }
-  };
-  auto compute_reg = [&](const DyStage<Q>& ds, const PStage<NB16>& ps) {
-#pragma unroll
-    for (int nb = 0; nb < NB16; ++nb) mfma_step(ds, &ps.bh[nb], &ps.bl[nb], nb);
-  };
-  auto p_load = [&](int step, PStage<NB16>& ps) {
-#pragma unroll
-    for (int nb = 0; nb < NB16; ++nb) {
-      ps.bh[nb] = *reinterpret_cast<const u32x4*>(Pt + p_block(step, nb, 0, NB16) + 8 * lane);
-      ps.bl[nb] = *reinterpret_cast<const u32x4*>(Pt + p_block(step, nb, 1, NB16) + 8 * lane);
+      mfma_step(ds, bh, bl, nb);
     }
   };
 
-  // Ping-pong pipeline over this wave's n steps s_begin + wave + W j: the
-  // loads of step j + 1 are in flight while step j is multiplied, and step
-  // j + 2 is issued into the stage step j frees.  Nothing is loaded past the
-  // wave's last step, so before reading a P slot the kernel waits for every
-  // load older than the next step's (8 dY loads behind it, and the 2 NB16 + 8
-  // loads of step j + 1 when that step exists).  sched_barrier keeps the
-  // scheduler from sinking loads back next to their consumers.
-  const int first = s_begin + wave;
-  const int n = first < s_end ? (s_end - first + kAccWaves - 1) / kAccWaves : 0;
-  auto step_of = [&](int jj) { return first + kAccWaves * jj; };
+  // Ping-pong pipeline over this wave's n steps: the loads of step j + 1 are
+  // in flight while step j is multiplied, and step j + 2 is issued into the
+  // stage step j frees.  Nothing is loaded past the wave's last step, so
+  // before reading a P slot the kernel waits for every load older than the
+  // next step's (8 dY loads behind it, and the 2 NBW + 8 loads of step j + 1
+  // when that step exists).  sched_barrier keeps the scheduler from sinking
+  // loads back next to their consumers.
+  const int first = s_begin + wl;
+  const int n = first < s_end ? (s_end - first + kLanes - 1) / kLanes : 0;
+  auto step_of = [&](int jj) { return first + kLanes * jj; };
   if (n > 0) {
     DyStage<Q> y0, y1;
-    if constexpr (PLDS) {
-      auto wait_slot = [&](int jj) {
-        if (jj + 1 < n) vm_wait<kAfterP>();
-        else vm_wait<8>();
-      };
-      p_issue(step_of(0), 0);
-      load_dy_stage<Q>(dY, ldd, T, vo, step_of(0), y0);
-      if (n > 1) {
-        p_issue(step_of(1), 1);
-        load_dy_stage<Q>(dY, ldd, T, vo, step_of(1), y1);
+    auto wait_slot = [&](int jj) {
+      if (jj + 1 < n) vm_wait<kAfterP>();
+      else vm_wait<8>();
+    };
+    p_issue(step_of(0), 0);
+    load_dy_stage<Q>(dY, ldd, T, vo, step_of(0), y0);
+    if (n > 1) {
+      p_issue(step_of(1), 1);
+      load_dy_stage<Q>(dY, ldd, T, vo, step_of(1), y1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    for (int jj = 0; jj < n; jj += 2) {
+      wait_slot(jj);
+      compute_lds(y0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (jj + 2 < n) {
+        lgkm_wait0();
+        p_issue(step_of(jj + 2), 0);
+        load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 2), y0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      for (int jj = 0; jj < n; jj += 2) {
-        wait_slot(jj);
-        compute_lds(y0, 0);
+      if (jj + 1 < n) {
+        wait_slot(jj + 1);
+        compute_lds(y1, 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (jj + 2 < n) {
+        if (jj + 3 < n) {
           lgkm_wait0();
-          p_issue(step_of(jj + 2), 0);
-          load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 2), y0);
+          p_issue(step_of(jj + 3), 1);
+          load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 3), y1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (jj + 1 < n) {
-          wait_slot(jj + 1);
-          compute_lds(y1, 1);
-          __builtin_amdgcn_sched_barrier(0);
-          if (jj + 3 < n) {
-            lgkm_wait0();
-            p_issue(step_of(jj + 3), 1);
-            load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 3), y1);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      vm_wait<0>();   // the ring is reused below
-    } else {
-      PStage<NB16> p0, p1;
-      load_dy_stage<Q>(dY, ldd, T, vo, step_of(0), y0);
-      p_load(step_of(0), p0);
-      if (n > 1) {
-        load_dy_stage<Q>(dY, ldd, T, vo, step_of(1), y1);
-        p_load(step_of(1), p1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      for (int jj = 0; jj < n; jj += 2) {
-        compute_reg(y0, p0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (jj + 2 < n) {
-          load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 2), y0);
-          p_load(step_of(jj + 2), p0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (jj + 1 < n) {
-          compute_reg(y1, p1);
-          __builtin_amdgcn_sched_barrier(0);
-          if (jj + 3 < n) {
-            load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 3), y1);
-            p_load(step_of(jj + 3), p1);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
     }
+    vm_wait<0>();   // the ring is reused below
   }
 
-  // Sum of the waves in a fixed order (((w0 + w1) + w2) + ...), CH registers
-  // per round through LDS; wave w sums registers c0 + w CH/W .. and writes
-  // them out (the partial tile of this split, register-major and coalesced,
-  // or straight into S when there is a single split).
+  // Sum over the waves that share an r part, in a fixed order (((l0 + l1) +
+  // l2) + ...), CH registers per round through LDS; each wave sums its share
+  // of the round and writes it out: to the partial tile of this split
+  // (register-major, coalesced) or, with a single split, into S.
   float* red = reinterpret_cast<float*>(lds);
-  constexpr int kPer = CH / kAccWaves > 0 ? CH / kAccWaves : 1;
   float* my = part ? part + ((int64_t)sp * gridDim.x + dgg) * (NREG * 64) : nullptr;
+  constexpr int kPer = CH / kLanes > 0 ? CH / kLanes : 1;
   __syncthreads();
 #pragma unroll
-  for (int c0 = 0; c0 < NREG; c0 += CH) {
+  for (int c0 = 0; c0 < NREGW; c0 += CH) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) red[(wave * CH + i) * 64 + lane] = acc[c0 + i];
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int il = wave * kPer + u;        // register within the round
+      const int il = wl * kPer + u;            // register within the round
       if (il < CH) {
-        float v = red[il * 64 + lane];
+        const int base = rpart * kLanes;       // first wave of this r part
+        float v = red[(base * CH + il) * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kAccWaves; ++w) v += red[(w * CH + il) * 64 + lane];
-        const int i = c0 + il;
+        for (int w = 1; w < kLanes; ++w) v += red[((base + w) * CH + il) * 64 + lane];
+        // wave register c0 + il = (q NBW + nb) 4 + e -> tile register
+        const int lr = c0 + il;
+        const int q = lr / (NBW * 4);
+        const int rem = lr % (NBW * 4);
+        const int i = (q * NB16 + rpart * NBW + (rem >> 2)) * 4 + (rem & 3);
         if (my) {
           my[i * 64 + lane] = v;
         } else {
@@ -661,20 +635,16 @@ hipError_t launch_project(const SketchPlan& p, const uint16_t* X, int64_t ldx,
 template <int Q, int NB16>
 hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, int r,
                              const uint16_t* Pt, float* part, hipStream_t s) {
-  constexpr int kAccWaves = acc_waves(Q, NB16);
-  constexpr bool kPlds = acc_plds(NB16);
   const dim3 grid((unsigned)p.n_dgroups, (unsigned)p.n_split);
   float* pp = p.n_split > 1 ? part : nullptr;
   bool masked = (T % 32) != 0;
   for (int o = 0; o < tab.n; ++o) masked = masked || (tab.d[o] % (16 * Q)) != 0;
   if (masked) {
-    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, true, kPlds>), grid,
-                       dim3(64 * kAccWaves), 0, s, tab, T, r, Pt, p.steps,
-                       p.steps_per_split, pp);
+    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, true>), grid, dim3(64 * kAccWaves), 0, s,
+                       tab, T, r, Pt, p.steps, p.steps_per_split, pp);
   } else {
-    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, kAccWaves, false, kPlds>), grid,
-                       dim3(64 * kAccWaves), 0, s, tab, T, r, Pt, p.steps,
-                       p.steps_per_split, pp);
+    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, false>), grid, dim3(64 * kAccWaves), 0, s,
+                       tab, T, r, Pt, p.steps, p.steps_per_split, pp);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
@@ -694,7 +664,7 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
   q.rp = r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : r <= 128 ? 128 : 256;
   q.p_rows = q.rp < 32 ? 32 : q.rp;
   q.nb32 = q.p_rows / 32;
-  q.q_cols = q.rp <= 64 ? 8 : q.rp <= 128 ? 4 : 2;
+  q.q_cols = kAccQ;
   q.t_pad = round_up(T > 0 ? T : 1, 32);
   q.k_pad = round_up(k, 256);
   q.steps = (int)(q.t_pad / 32);
@@ -709,13 +679,26 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
   if (groups >= (int64_t(1) << 27)) return false;   // finalize grid: 8 per group
   q.dg_off[n_out] = (int)groups;
   q.n_dgroups = (int)groups;
-  // Enough work-groups to cover the chip (256 CUs) while each wave keeps at
-  // least two 32-token steps.
-  const int waves = acc_waves(q.q_cols, q.rp / 16);
-  const int want = (256 + q.n_dgroups - 1) / q.n_dgroups;
-  const int max_split = q.steps / (2 * waves) > 0 ? q.steps / (2 * waves) : 1;
-  int n_split = want < max_split ? want : max_split;
-  if (n_split < 1) n_split = 1;
+  // Work-groups along T: at most so many that each wave keeps two 32-token
+  // steps; among those counts, the one with the least modelled cost: the dY
+  // stream slowed by the share of the 256 CUs that the work-groups' rounds
+  // leave idle (one work-group per CU), plus writing and reading the split
+  // partial tiles and the split-reduction launch (~25 MB of streaming).
+  const int lanes = kAccWaves / acc_rsplit(q.rp / 16);   // waves along the steps
+  const int max_split = q.steps / (2 * lanes) > 0 ? q.steps / (2 * lanes) : 1;
+  const double dy_bytes = 2.0 * (double)q.t_pad * (double)groups * dc;
+  int n_split = 1;
+  double best = 0.0;
+  for (int ns = 1; ns <= max_split && ns <= 64; ++ns) {
+    const int64_t wgs = groups * ns;
+    const double eff = (double)wgs / (double)(((wgs + 255) / 256) * 256);
+    const double cost = dy_bytes / eff +
+                        (ns > 1 ? 8.0 * ns * (double)groups * dc * q.rp + 25e6 : 0.0);
+    if (ns == 1 || cost < best * 0.999) {
+      best = cost;
+      n_split = ns;
+    }
+  }
   q.steps_per_split = (q.steps + n_split - 1) / n_split;
   q.n_split = (q.steps + q.steps_per_split - 1) / q.steps_per_split;
   q.d_pad = (int64_t)q.n_dgroups * dc;
@@ -766,11 +749,11 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
     tab.S[o] = outs[o].S;
   }
   switch (p.rp) {
-    case 16: return launch_accumulate<8, 1>(p, tab, T, r, Pt, part, s);
-    case 32: return launch_accumulate<8, 2>(p, tab, T, r, Pt, part, s);
-    case 64: return launch_accumulate<8, 4>(p, tab, T, r, Pt, part, s);
-    case 128: return launch_accumulate<4, 8>(p, tab, T, r, Pt, part, s);
-    default: return launch_accumulate<2, 16>(p, tab, T, r, Pt, part, s);
+    case 16: return launch_accumulate<kAccQ, 1>(p, tab, T, r, Pt, part, s);
+    case 32: return launch_accumulate<kAccQ, 2>(p, tab, T, r, Pt, part, s);
+    case 64: return launch_accumulate<kAccQ, 4>(p, tab, T, r, Pt, part, s);
+    case 128: return launch_accumulate<kAccQ, 8>(p, tab, T, r, Pt, part, s);
+    default: return launch_accumulate<kAccQ, 16>(p, tab, T, r, Pt, part, s);
   }
 }
 
