@@ -7,7 +7,8 @@
 // applies the same merge after rebuilding A from the seed.
 //
 // One work-group owns 256 rows x 256 columns of W (one sign block wide); its
-// four waves own 64 rows each.  Columns are processed in four passes of 64:
+// four waves own 64 rows each (eight waves of 32 rows above r = 64).  Columns
+// are processed in four passes of 64:
 //   1. the pass's slice of A (r x 64) is regenerated into LDS as bf16,
 //      transposed (column-major, r contiguous) by all threads - signs from
 //      the Philox words of the block's A rows (drawn once per work-group and
@@ -30,19 +31,21 @@ namespace {
 constexpr int kMergeCols = 256;
 constexpr int kPassCols = 64;
 
-template <int NKS, bool GAUSS, bool MASKED, int kWaves>
+template <int NKS, bool GAUSS, bool MASKED, int kWaves, int NT>
 __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
     uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ S, int d,
     int k, int r, uint64_t seed, uint64_t stream, float scale, float cr) {
   constexpr int RP = 32 * NKS;    // r padded to whole K steps
   constexpr int LDA = RP + 8;     // bf16 per LDS column (+16 B against conflicts)
-  constexpr bool kDouble = NKS <= 4;  // two A slices fit in 64 KB of LDS
+  constexpr int WR = 16 * NT;     // W rows per wave
+  // two A slices fit next to the other buffers (up to 112 KB in all)
+  constexpr bool kDouble = NKS <= 4 || NT <= 2;
   __shared__ __attribute__((aligned(16))) uint16_t At[(kDouble ? 2 : 1) * kPassCols * LDA];
   __shared__ __attribute__((aligned(16))) uint64_t sgn[GAUSS ? 1 : 4 * RP];
-  // Per-wave staging of one pass's results (64 rows x 64 columns, row stride
+  // Per-wave staging of one pass's results (WR rows x 64 columns, row stride
   // kStRow bf16) for row-contiguous stores (interior tiles only).
   constexpr int kStRow = kPassCols + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t stage[MASKED ? 1 : kWaves * 64 * kStRow];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[MASKED ? 1 : kWaves * WR * kStRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -54,13 +57,14 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   const int rblk = (int)(blockIdx.x / (unsigned)n_cb);
   const int cb = xcd_spread((int)(blockIdx.x % (unsigned)n_cb), rblk, n_cb);
   const int col0 = cb * kMergeCols;
-  const int row0 = rblk * (64 * kWaves) + wave * 64;
+  const int row0 = rblk * (WR * kWaves) + wave * WR;
   const int n_pass = min(kMergeCols / kPassCols, (k - col0 + kPassCols - 1) / kPassCols);
 
   // S operands: rows row0 + 16 nt + m, K = r columns 32 ks + 8 g + (0..7),
-  // as hi/lo bf16.  They do not depend on the column pass, so for small r
-  // they stay in registers; for large r they are rebuilt per pass (L2 hits).
-  constexpr bool kHoistS = NKS <= 2;
+  // as hi/lo bf16.  They do not depend on the column pass and stay in
+  // registers (4 NT NKS u32x4 per lane: large ranks use NT = 2 to fit); with
+  // NT = 4 and r > 64 they are rebuilt per pass (L2 hits).
+  constexpr bool kHoistS = NKS <= 2 || NT <= 2;
   // rows of this wave all inside d and r a multiple of 32: plain float4 loads
   const bool s_fast = !MASKED;
   auto s_raw = [&](int nt, int ks, float v[8]) {
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
     s_raw(nt, ks, v);
     s_split(v, hi, lo);
   };
-  u32x4 sh[4][kHoistS ? NKS : 1], sl[4][kHoistS ? NKS : 1];
+  u32x4 sh[NT][kHoistS ? NKS : 1], sl[NT][kHoistS ? NKS : 1];
 
   // Sign basis: thread tid < RP / 2 draws the Philox blocks of A rows 2 tid
   // and 2 tid + 1 for this 256-column block and parks their words in LDS,
@@ -164,19 +168,19 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   // This lane's W elements of pass p: rows row0 + 16 nt + m, columns
   // col0 + 64 p + 16 g + (0..15).  Rows past d are read from row d - 1 and
   // never stored; columns past k read as zero.
-  auto load_W = [&](int pass, u32x4 wv[4][2]) {
+  auto load_W = [&](int pass, u32x4 wv[NT][2]) {
     const int c0 = col0 + pass * kPassCols;
     const int wc = c0 + 16 * g;
     if (!MASKED) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const uint16_t* wr = W + (int64_t)(row0 + 16 * nt + m) * ldw;
         wv[nt][0] = load_bf16x8(wr, wc);
         wv[nt][1] = load_bf16x8(wr, wc + 8);
       }
     } else {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const int row = min(row0 + 16 * nt + m, d - 1);
         const uint16_t* wr = W + (int64_t)row * ldw;
         wv[nt][0] = load_bf16x8_masked(wr, wc, k);
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   // One column pass: multiply the A slice, update the W elements loaded one
   // pass earlier (wcur) and, before that, start the loads of the next pass
   // (wnxt) so they overlap this pass's work.
-  auto do_pass = [&](int pass, u32x4 (&wcur)[4][2], u32x4 (&wnxt)[4][2]) {
+  auto do_pass = [&](int pass, u32x4 (&wcur)[NT][2], u32x4 (&wnxt)[NT][2]) {
     if (!kDouble && pass > 0) {
       __syncthreads();          // every wave is done reading the previous slice
       build_A(pass, buf0);
@@ -205,16 +209,16 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
     const uint16_t* cur_buf = (kDouble && (pass & 1)) ? buf1 : buf0;
 
     // MFMA: acc[t][nt] rows m' = 4 g' + v map to columns c0 + 16 g' + 4 t + v.
-    f32x4 acc[4][4];
+    f32x4 acc[4][NT];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 bh[4], bl[4];
+      u32x4 bh[NT], bl[NT];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         if constexpr (kHoistS) {
           bh[nt] = sh[nt][ks];
           bl[nt] = sl[nt][ks];
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
         const u32x4 a =
             *reinterpret_cast<const u32x4*>(&cur_buf[cc * LDA + 32 * ks + 8 * g]);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           acc[t][nt] = mfma16(a, bh[nt], acc[t][nt]);
           acc[t][nt] = mfma16(a, bl[nt], acc[t][nt]);
         }
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
     // Update and store.
     const int wc = col0 + pass * kPassCols + 16 * g;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const int row = row0 + 16 * nt + m;
       u32x4 out[2];
 #pragma unroll
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
         }
       }
       if constexpr (!MASKED) {
-        uint16_t* stg = stage + (wave * 64 + 16 * nt + m) * kStRow + 16 * g;
+        uint16_t* stg = stage + (wave * WR + 16 * nt + m) * kStRow + 16 * g;
         *reinterpret_cast<u32x4*>(stg) = out[0];
         *reinterpret_cast<u32x4*>(stg + 8) = out[1];
       } else if (row < d) {
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
         }
       }
     }
-    // Interior tiles: the wave reads its 64 x 64 results back row by row,
+    // Interior tiles: the wave reads its WR x 64 results back row by row,
     // eight lanes per row, so every store writes whole 128-byte lines (stores
     // of half lines, as the MFMA layout gives them, measured ~10 % slower).
     // A wave only touches its own staging rows and LDS operations of a wave
@@ -286,9 +290,9 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
     if constexpr (!MASKED) {
       const int pc = lane & 7;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < WR / 8; ++i) {
         const int rr = 8 * i + (lane >> 3);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (wave * 64 + rr) * kStRow + 8 * pc);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (wave * WR + rr) * kStRow + 8 * pc);
         *reinterpret_cast<u32x4*>(W + (int64_t)(row0 + rr) * ldw + col0 + pass * kPassCols + 8 * pc) = v;
       }
     }
@@ -297,11 +301,11 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   // Prologue: start the loads first (S rows, then the W elements of pass 0),
   // regenerate the signs and the first A slice while they are in flight, and
   // only then wait for S.
-  u32x4 wa[4][2], wb[4][2];
-  float sraw[4][kHoistS ? NKS : 1][8];
+  u32x4 wa[NT][2], wb[NT][2];
+  float sraw[NT][kHoistS ? NKS : 1][8];
   if constexpr (kHoistS) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) s_raw(nt, ks, sraw[nt][ks]);
   }
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   build_A(0, buf0);
   if constexpr (kHoistS) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) s_split(sraw[nt][ks], sh[nt][ks], sl[nt][ks]);
   }
@@ -322,21 +326,26 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   if (n_pass > 3) do_pass(3, wb, wa);
 }
 
-// Four waves (256 rows) per work-group: measured faster than two at the
-// 4096 x 4096 layer shape.
-constexpr int kMergeWaves = 4;
-constexpr int kMergeRows = 64 * kMergeWaves;
+// 256 rows per work-group.  Up to r = 64: four waves of 64 rows (measured
+// faster than two at the 4096 x 4096 layer shape).  Larger ranks: eight waves
+// of 32 rows, so each lane's S operands (4 NT NKS u32x4) stay in registers
+// for all four column passes instead of being re-read and re-split per pass.
+constexpr int kMergeRows = 256;
+constexpr int merge_nt(int nks) { return nks <= 2 ? 4 : 2; }
+constexpr int merge_waves(int nks) { return kMergeRows / (16 * merge_nt(nks)); }
 
 template <int NKS, bool MASKED>
 void launch_merge_m(uint16_t* W, int64_t ldw, const float* S, int d, int k, int r,
                     uint64_t seed, uint64_t stream, bool gauss, float scale,
                     float cr, hipStream_t s, dim3 grid) {
+  constexpr int kW = merge_waves(NKS);
+  constexpr int kNT = merge_nt(NKS);
   if (gauss) {
-    hipLaunchKernelGGL((merge_kernel<NKS, true, MASKED, kMergeWaves>), grid,
-                       dim3(kMergeRows), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
+    hipLaunchKernelGGL((merge_kernel<NKS, true, MASKED, kW, kNT>), grid,
+                       dim3(64 * kW), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
   } else {
-    hipLaunchKernelGGL((merge_kernel<NKS, false, MASKED, kMergeWaves>), grid,
-                       dim3(kMergeRows), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
+    hipLaunchKernelGGL((merge_kernel<NKS, false, MASKED, kW, kNT>), grid,
+                       dim3(64 * kW), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
   }
 }
 
