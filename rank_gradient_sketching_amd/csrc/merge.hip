@@ -356,8 +356,10 @@ hipError_t launch_merge_t(uint16_t* W, int64_t ldw, const float* S, int d, int k
   const int64_t blocks = (int64_t)((k + kMergeCols - 1) / kMergeCols) *
                          ((d + kMergeRows - 1) / kMergeRows);
   const dim3 grid((unsigned)blocks);
-  // unmasked when every tile is interior and S rows are whole K steps
-  const bool masked = (d % kMergeRows) != 0 || (k % kMergeCols) != 0 || (r % 32) != 0;
+  // unmasked when every row block is whole, every 64-column pass is whole (a
+  // short last column block just runs fewer passes) and S rows are whole K
+  // steps
+  const bool masked = (d % kMergeRows) != 0 || (k % kPassCols) != 0 || (r % 32) != 0;
   if (masked) launch_merge_m<NKS, true>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
   else launch_merge_m<NKS, false>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
   return hipGetLastError();

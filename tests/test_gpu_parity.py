@@ -234,6 +234,11 @@ MERGE_CASES = [
     (512, 1000, 256, 0, 0.5, 1e-3),
     (300, 520, 16, 1, 1.0, 1e-3),
     (256, 1000, 256, 1, 1.0, 1e-3),
+    # whole row blocks and 64-column passes, short last column block
+    (512, 832, 64, 0, 1.0, 1e-3),
+    (256, 1344, 256, 0, 1.0, 1e-3),
+    (512, 1536, 128, 0, 0.5, 1e-3),
+    (256, 1280, 256, 1, 1.0, 1e-3),
 ]
 
 
