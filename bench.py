@@ -44,6 +44,20 @@ def sketch_bytes(T, d, k, r):
     return 2 * T * (d + k) + 8 * d * r
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix cores
+
+
+def sketch_mfma(T, d, k, r, us):
+    """Matrix-core rate of one sketch call: algorithmic FLOP 2 T r (k + d) (the
+    projection and the contraction), executed 2 T r (k + 2 d) (P enters the
+    contraction as a hi/lo bf16 pair), over the call time."""
+    alg = 2.0 * T * r * (k + d)
+    exe = 2.0 * T * r * (k + 2 * d)
+    t = us * 1e-6
+    return dict(TFLOPs_algorithmic=alg / t / 1e12, TFLOPs_executed=exe / t / 1e12,
+                frac_bf16_mfma_peak=exe / t / 1e12 / BF16_MFMA_PEAK_TFLOPS)
+
+
 def merge_bytes(d, k, r):
     """Algorithmic bytes of one merge: W read + write, S read once."""
     return 4 * d * k + 4 * d * r
@@ -407,7 +421,9 @@ def run_other_configs(lg, synth):
     mg_ms = _time_ms(lambda: lg.merge(W, S, 1234, 0, 0, 1.0, 2e-4), 5)
     report("wide_layer_d5120_k25600_r256", sk_ms + mg_ms, sketch_bytes(T, d, k, r) + merge_bytes(d, k, r),
            T, sketch_us=sk_ms * 1e3, sketch_GBps=sketch_bytes(T, d, k, r) / (sk_ms * 1e-3) / 1e9,
-           merge_us=mg_ms * 1e3, merge_GBps=merge_bytes(d, k, r) / (mg_ms * 1e-3) / 1e9)
+           merge_us=mg_ms * 1e3, merge_GBps=merge_bytes(d, k, r) / (mg_ms * 1e-3) / 1e9,
+           sketch_mfma=sketch_mfma(T, d, k, r, sk_ms * 1e3),
+           merge_TFLOPs_executed=4.0 * d * k * r / (mg_ms * 1e-3) / 1e12)
     del X, dY, W
     torch.cuda.empty_cache()
     return out
@@ -575,7 +591,8 @@ def main():
                    "parallelism": "single-gpu"},
         "sketch": {"tokens_per_s": sk["tokens_per_s"], "GBps": sk["GBps"],
                    "frac_hbm": sk["frac_hbm"], "us_per_call": sk["us_per_call"],
-                   "min_us": sk["min_us"]},
+                   "min_us": sk["min_us"], **sketch_mfma(cfg["T"], cfg["d"], cfg["k"], cfg["r"],
+                                                          sk["us_per_call"])},
         "merge": {"GBps": mg["GBps"], "frac_hbm": mg["frac_hbm"], "us_per_call": mg["us_per_call"],
                   "min_us": mg["min_us"]},
         "roofline": roof,

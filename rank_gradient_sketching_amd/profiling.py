@@ -9,6 +9,10 @@ Two commands, both reading the CSV files rocprofv3 writes with
            `*_counter_collection.csv`) -> HBM bytes per dispatch of each
            kernel, scaled by what the same counters read for a plain device
            copy of known size (the largest `copyBuffer` dispatch of the run).
+  mfma     one counter run (`--pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES
+           SQ_BUSY_CU_CYCLES SQ_INSTS_VALU`) -> per kernel and grid size: MFMA
+           and VALU instructions per dispatch and the matrix-core busy share,
+           SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES).
 
 `traffic` also records a hash of the kernel sources, so a consumer can tell
 whether the counters still describe the code being run.
@@ -17,6 +21,7 @@ Usage:
   python -m rank_gradient_sketching_amd.profiling stats STATS_CSV --out F.md --cmd "..."
   python -m rank_gradient_sketching_amd.profiling traffic FETCH_DIR WRITE_DIR \
       --copy-bytes N --out F.md --cmd "..."
+  python -m rank_gradient_sketching_amd.profiling mfma PMC_DIR --out F.md --cmd "..."
 """
 import argparse
 import collections
@@ -104,6 +109,25 @@ def traffic(fetch_dir, write_dir, copy_bytes):
                 source_hash=kernel_source_hash())
 
 
+MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU")
+
+
+def mfma_table(run_dir):
+    """[(kernel, grid, dispatches, {counter: median per dispatch})] of the library's kernels."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if "logra" not in r["Kernel_Name"] or r["Counter_Name"] not in MFMA_COUNTERS:
+                continue
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+            vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    rows = []
+    for (kn, grid), cs in sorted(vals.items()):
+        med = {c: statistics.median(v) for c, v in cs.items()}
+        rows.append((kn, grid, max(len(v) for v in cs.values()), med))
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -118,7 +142,28 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--cmd", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_dir")
+    m.add_argument("--out", required=True)
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--title", default="Matrix-core and VALU counters")
     a = ap.parse_args()
+    if a.cmd_name == "mfma":
+        lines = [f"# {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
+                 f"Kernel sources: `{kernel_source_hash()}`", "",
+                 "Per dispatch (median over dispatches of the same kernel and grid size). "
+                 "MFMA busy share = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES).", "",
+                 "| kernel | grid (threads) | dispatches | MFMA instr | VALU instr | VALU / MFMA | MFMA busy share |",
+                 "|---|---|---|---|---|---|---|"]
+        for kn, grid, n, c in mfma_table(a.pmc_dir):
+            mf = c.get("SQ_INSTS_MFMA", 0.0)
+            va = c.get("SQ_INSTS_VALU", 0.0)
+            busy = c.get("SQ_BUSY_CU_CYCLES", 0.0)
+            share = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4.0 * busy) if busy else 0.0
+            ratio = f"{va / mf:.1f}" if mf else "-"
+            lines.append(f"| `{kn}` | {grid} | {n} | {mf:.0f} | {va:.0f} | {ratio} | {share:.3f} |")
+        open(a.out, "w").write("\n".join(lines) + "\n")
+        return
     if a.cmd_name == "stats":
         rows = stats_table(a.stats_csv)
         lines = [f"# {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
