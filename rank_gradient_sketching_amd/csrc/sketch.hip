@@ -32,6 +32,8 @@
 // The Gaussian basis is first written once per call as a bf16 r x k matrix in
 // the workspace (Box-Muller per entry is too costly to repeat per token
 // block) and the project kernel reads its operand tiles from there.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -236,6 +238,196 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
       }
     }
     __syncthreads();
+  }
+}
+
+// Projection with 64 tokens per work-group, for r >= 64 (chosen by
+// use_tile_projection below).  Waves 0-3 and 4-7 take the two halves of r (NBW 32-row blocks
+// of A each) over the same 256-column chunks of k (chunk lane = wave mod 4),
+// and each chunk lane's X rows reach LDS once for both halves, 32 rows from
+// each of its two waves.  A wave multiplies every sign (or Gaussian) operand
+// it builds with both 32-token blocks, so the Philox words and the +-1
+// expansion cost half as much per product as in project_kernel, whose waves
+// cover one 32-token block (at r = 256 that kernel issues ~24 VALU
+// instructions per MFMA).  The half-chunk steps of all lanes run in lock step
+// with one barrier each: after it, a wave's own copy and its partner's have
+// landed and every wave is done reading the other buffer, which is refilled
+// while this step is multiplied.
+constexpr int kTileTokens = 64;
+constexpr int kTileLanes = 4;
+
+template <int NBW, bool GAUSS, bool MASKED>
+__global__ __launch_bounds__(512) void project_tile_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, int T, int k, int rp, int steps_total,
+    uint64_t seed, uint64_t stream, float c, const uint16_t* __restrict__ Ab,
+    int64_t lda, uint16_t* __restrict__ Pt) {
+  static_assert(NBW % 2 == 0 || NBW == 1, "sign words pair 32-row blocks");
+  // [chunk lane][half][64 rows x 128 columns bf16], 16-byte pieces swizzled by row
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kTileLanes][2][2 * kHalfBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rpart = wave / kTileLanes;   // which half of r
+  const int cl = wave % kTileLanes;      // chunk lane
+  const int m = lane & 31;  // A-operand row (token) and B-operand column (A row)
+  const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
+  const int blk = xcd_spread((int)blockIdx.x, (int)blockIdx.x >> 3, (int)gridDim.x);
+  const int t0 = blk * kTileTokens;
+  const bool trow0 = !MASKED || t0 + m < T;
+  const bool trow1 = !MASKED || t0 + 32 + m < T;
+  const int n_chunks = (k + 255) >> 8;
+  const int row_base = rpart * NBW * 32;   // first A row of this wave
+
+  f32x16 acc[2][NBW];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tb][nb][v] = 0.0f;
+
+  // This wave's 32 rows (32 rpart ..) of half hc of chunk cnk -> dst, eight
+  // direct global->LDS copies of 4 rows x 256 bytes.  Rows >= T re-read row
+  // T - 1 and pieces past k re-read the row's first piece; both are cleared
+  // when read back.
+  auto issue = [&](int cnk, int hc, unsigned char* dst) {
+    const int colbase = cnk * 256 + hc * kHalfCols;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 32 * rpart + 4 * i + (lane >> 4);
+      const int j = (lane & 15) ^ (row & 15);
+      int t = t0 + row;
+      int col = colbase + 8 * j;
+      if (MASKED) {
+        t = t < T ? t : T - 1;
+        col = col < k ? col : 0;
+      }
+      lds_dma16((const void*)(X + (int64_t)t * ldx + col),
+                lds_addr(dst + (32 * rpart + 4 * i) * (kHalfCols * 2)));
+    }
+  };
+
+  // Sign words of A rows row_base + 32 nb + m for chunk ch (word 2 hc + h
+  // feeds half hc); the lane halves draw different row blocks and swap the
+  // words the other half needs, as in project_kernel.
+  uint64_t sw[NBW][2];
+  auto sign_words = [&](int ch) {
+    if constexpr (NBW == 1) {
+      const Words4 b = sign_block(seed, stream, (uint64_t)ch, (uint64_t)(row_base + m));
+      sw[0][0] = h ? b.w[1] : b.w[0];
+      sw[0][1] = h ? b.w[3] : b.w[2];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NBW / 2; ++j) {
+        const Words4 b =
+            sign_block(seed, stream, (uint64_t)ch, (uint64_t)(row_base + (2 * j + h) * 32 + m));
+        const uint64_t r0 = swap_halves64(h ? b.w[0] : b.w[1]);
+        const uint64_t r2 = swap_halves64(h ? b.w[2] : b.w[3]);
+        sw[2 * j][0] = h ? r0 : b.w[0];
+        sw[2 * j][1] = h ? r2 : b.w[2];
+        sw[2 * j + 1][0] = h ? b.w[1] : r0;
+        sw[2 * j + 1][1] = h ? b.w[3] : r2;
+      }
+    }
+  };
+
+  auto compute = [&](int ch, int hc, const unsigned char* buf) {
+    const int colq = ch * 256 + hc * kHalfCols + 64 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int slot = (8 * h + s) ^ (m & 15);
+      u32x4 a0 = *reinterpret_cast<const u32x4*>(buf + m * (kHalfCols * 2) + slot * 16);
+      u32x4 a1 = *reinterpret_cast<const u32x4*>(buf + (32 + m) * (kHalfCols * 2) + slot * 16);
+      if (MASKED) {
+        const int valid = k - (colq + 8 * s);
+        a0 &= keep_mask8(trow0 ? valid : 0);
+        a1 &= keep_mask8(trow1 ? valid : 0);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        u32x4 b;
+        if constexpr (GAUSS) {
+          b = *reinterpret_cast<const u32x4*>(Ab + (int64_t)(row_base + nb * 32 + m) * lda +
+                                              colq + 8 * s);
+        } else {
+          b = signs_to_bf16x8((uint32_t)(sw[nb][hc] >> (8 * s)) & 0xFFu);
+        }
+        acc[0][nb] = mfma32(a0, b, acc[0][nb]);
+        acc[1][nb] = mfma32(a1, b, acc[1][nb]);
+      }
+    }
+  };
+
+  // Lane cl takes chunks cl, cl + 4, ... (physical chunk = logical + block,
+  // mod n_chunks, as in project_kernel); every lane runs 2 ceil(n / 4) steps
+  // so the barriers match, idling past its last chunk.
+  const int rot = blk % n_chunks;
+  auto phys = [&](int cc) { cc += rot; return cc < n_chunks ? cc : cc - n_chunks; };
+  const int n_mine = cl < n_chunks ? (n_chunks - cl + kTileLanes - 1) / kTileLanes : 0;
+  const int n_steps = 2 * ((n_chunks + kTileLanes - 1) / kTileLanes);
+  if (n_mine > 0) issue(phys(cl), 0, stage[cl][0]);
+  for (int step = 0; step < n_steps; ++step) {
+    const int jc = step >> 1;
+    const int hc = step & 1;
+    vm_wait<0>();       // this wave's copies for the step have landed
+    __syncthreads();    // ... and its partner's; the other buffer is free
+    const int nj = (step + 1) >> 1;
+    if (nj < n_mine) issue(phys(cl + kTileLanes * nj), (step + 1) & 1, stage[cl][(step + 1) & 1]);
+    if (jc < n_mine) {
+      const int pc = phys(cl + kTileLanes * jc);
+      if constexpr (!GAUSS) {
+        if (hc == 0) sign_words(pc);
+      }
+      lgkm_wait0();
+      compute(pc, hc, stage[cl][hc]);
+    }
+  }
+  vm_wait<0>();
+
+  // Sum the four chunk lanes of each r half in a fixed order (l0 + l1 + l2 +
+  // l3), one (token block, r block) at a time through LDS, and store the hi/lo
+  // pair in the tiled layout.  Thread t: r half t / 256, r column n_out of the
+  // block, tokens 4 tg .. 4 tg + 3.
+  float (*red)[32 * 33] = reinterpret_cast<float (*)[32 * 33]>(&stage[0][0][0]);
+  const int rh = tid >> 8;
+  const int n_out = tid & 31;
+  const int tg = (tid >> 5) & 7;
+  const int nb16 = rp >> 4;
+  __syncthreads();
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+        red[wave][row * 33 + m] = acc[tb][nb][v];
+      }
+      __syncthreads();
+      const int step = 2 * blk + tb;
+      const int i = (rh * NBW + nb) * 32 + n_out;   // A row / P column
+      if (step < steps_total && i < rp) {
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = (4 * tg + u) * 33 + n_out;
+          float p = red[rh * kTileLanes][idx];
+#pragma unroll
+          for (int w = 1; w < kTileLanes; ++w) p += red[rh * kTileLanes + w][idx];
+          split_bf16(p * c, hi[u], lo[u]);
+        }
+        const int u0 = 4 * tg;
+        const int64_t slot = (int64_t)(((u0 >> 3) * 16 + (i & 15)) * 8 + (u0 & 7));
+        uint16_t* ph = Pt + p_block(step, i >> 4, 0, nb16) + slot;
+        uint16_t* pl = Pt + p_block(step, i >> 4, 1, nb16) + slot;
+#pragma unroll
+        for (int u = 0; u < 4; u += 2) {
+          *reinterpret_cast<uint32_t*>(ph + u) = (uint32_t)hi[u] | ((uint32_t)hi[u + 1] << 16);
+          *reinterpret_cast<uint32_t*>(pl + u) = (uint32_t)lo[u] | ((uint32_t)lo[u + 1] << 16);
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -607,6 +799,21 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   }
 }
 
+// Whether launch_project takes project_tile_kernel (only from two 32-row
+// blocks of A up).  It builds each basis operand for two token blocks, which
+// pays wherever operand building bounds project_kernel: always for the
+// Gaussian basis, and for the sign basis once its 64-token work-groups still
+// fill all 256 CUs (below that, project_kernel's twice as many work-groups
+// are worth more).  LOGRA_PROJECT_TILE in the environment overrides the
+// choice, read at every launch: 0 never, 2 always.
+bool use_tile_projection(const SketchPlan& p, int nb32, bool gauss) {
+  if (nb32 < 2) return false;
+  const char* env = getenv("LOGRA_PROJECT_TILE");
+  if (env != nullptr && env[0] == '0') return false;
+  if (env != nullptr && env[0] == '2') return true;
+  return gauss || p.t_pad / kTileTokens >= 256;
+}
+
 template <int NB, bool GAUSS, bool MASKED>
 void launch_project_t(const SketchPlan& p, const uint16_t* X, int64_t ldx, int T,
                       int k, uint64_t seed, uint64_t stream, float c,
@@ -621,6 +828,25 @@ template <int NB>
 hipError_t launch_project(const SketchPlan& p, const uint16_t* X, int64_t ldx,
                           int T, int k, uint64_t seed, uint64_t stream, bool gauss,
                           float c, const uint16_t* Ab, uint16_t* Pt, hipStream_t s) {
+  if constexpr (NB >= 2) {
+    if (use_tile_projection(p, NB, gauss)) {
+      const bool tmask = (T % kTileTokens) != 0 || (k % 256) != 0;
+      const dim3 grid((unsigned)((p.t_pad + kTileTokens - 1) / kTileTokens));
+      const float cc = gauss ? 1.0f : c;
+#define LOGRA_TILE(G, M)                                                                  \
+  hipLaunchKernelGGL((project_tile_kernel<NB / 2, G, M>), grid, dim3(512), 0, s, X, ldx, T, \
+                     k, p.rp, p.steps, seed, stream, cc, Ab, p.k_pad, Pt)
+      if (gauss) {
+        if (tmask) LOGRA_TILE(true, true);
+        else LOGRA_TILE(true, false);
+      } else {
+        if (tmask) LOGRA_TILE(false, true);
+        else LOGRA_TILE(false, false);
+      }
+#undef LOGRA_TILE
+      return hipGetLastError();
+    }
+  }
   const bool masked = (T % 32) != 0 || (k % 256) != 0;
   if (gauss) {
     if (masked) launch_project_t<NB, true, true>(p, X, ldx, T, k, seed, stream, 1.0f, Ab, Pt, s);

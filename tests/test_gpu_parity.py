@@ -129,6 +129,31 @@ def test_sketch_matches_oracle(lg, T, d, k, r, kind, n_mb):
     assert err_total < S_TOL, err_total
 
 
+# Both projection kernels on each case (LOGRA_PROJECT_TILE: 0 = the 32-token
+# kernel, 2 = the 64-token tile kernel), ragged and whole tiles alike.
+PROJECTION_CASES = [
+    # T, d, k, r, kind, n_mb
+    (77, 1030, 264, 64, 0, 1),      # 3 steps: the last tile's second block is empty
+    (300, 200, 700, 100, 0, 2),     # padded rank, ragged k
+    (64, 128, 512, 256, 0, 1),      # one whole tile, maximum rank
+    (129, 256, 1000, 256, 1, 1),    # Gaussian basis, ragged
+    (1056, 384, 1280, 128, 0, 1),   # odd step count, five chunks over four lanes
+    (640, 256, 2304, 256, 0, 1),    # whole tiles and chunks (unmasked), nine chunks
+    (1024, 512, 4096, 64, 0, 1),    # unmasked, one 32-row block per wave
+    (2048, 1024, 768, 64, 1, 1),    # Gaussian basis, unmasked tiles
+]
+
+
+@pytest.mark.parametrize("mode", ["0", "2"])
+@pytest.mark.parametrize("T,d,k,r,kind,n_mb", PROJECTION_CASES)
+def test_sketch_both_projection_kernels(lg, monkeypatch, mode, T, d, k, r, kind, n_mb):
+    say("sketch projection kernel", mode, T, d, k, r, kind, n_mb)
+    monkeypatch.setenv("LOGRA_PROJECT_TILE", mode)
+    _, err_delta, err_total = _sketch_case(lg, T, d, k, r, kind, n_mb)
+    assert err_delta < S_TOL, err_delta
+    assert err_total < S_TOL, err_total
+
+
 SHARED_CASES = [
     # T, k, ds (outputs sharing X), r, kind
     (512, 256, (256, 64, 64), 64, 0),          # q/k/v-shaped
