@@ -6,9 +6,9 @@
 // into the weights with no adapter branch; section Sync: the rollout engine
 // applies the same merge after rebuilding A from the seed.
 //
-// One work-group owns 256 rows x 256 columns of W (one sign block wide); its
-// four waves own 64 rows each (eight waves of 32 rows above r = 64).  Columns
-// are processed in four passes of 64:
+// One work-group owns a block of rows x 256 columns of W (one sign block
+// wide) and each of its waves 16 or 32 of those rows (the shapes are chosen
+// per rank and basis below).  Columns are processed in four passes of 64:
 //   1. the pass's slice of A (r x 64) is regenerated into LDS as bf16,
 //      transposed (column-major, r contiguous) by all threads - signs from
 //      the Philox words of the block's A rows (drawn once per work-group and
@@ -326,24 +326,32 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   if (n_pass > 3) do_pass(3, wb, wa);
 }
 
-// 256 rows per work-group.  Up to r = 64: four waves of 64 rows (measured
-// faster than two at the 4096 x 4096 layer shape).  Larger ranks: eight waves
-// of 32 rows, so each lane's S operands (4 NT NKS u32x4) stay in registers
-// for all four column passes instead of being re-read and re-split per pass.
-constexpr int kMergeRows = 256;
-constexpr int merge_nt(int nks) { return nks <= 2 ? 4 : 2; }
-constexpr int merge_waves(int nks) { return kMergeRows / (16 * merge_nt(nks)); }
+// Rows per work-group and per wave (16 NT).  Up to r = 64 with the sign
+// basis: 128 rows, eight waves of 16.  A work-group of the d = k = 4096 layer
+// then moves 64 KB of W each way and two of them share a CU, so 16 waves per
+// CU keep W loads in flight (measured 16.9 -> 12.9 us against 256 rows in four
+// waves of 64, about the rate of a device copy).  The Gaussian basis rebuilds
+// its A slices from Philox and Box-Muller per work-group, so it keeps 256 rows
+// and runs them as sixteen waves of 16 (27.4 -> 21.6 us).  Larger ranks: 256
+// rows, eight waves of 32, so each lane's S operands (4 NT NKS u32x4) stay in
+// registers for all four column passes instead of being re-read and re-split
+// per pass (16 waves of 16 rows spill and ran 15-20 % slower at r = 256; at
+// r = 128 the small-rank shapes measured the same).
+constexpr int merge_rows(int nks, bool gauss) { return nks <= 2 && !gauss ? 128 : 256; }
+constexpr int merge_nt(int nks) { return nks <= 2 ? 1 : 2; }
+constexpr int merge_waves(int nks, bool gauss) { return merge_rows(nks, gauss) / (16 * merge_nt(nks)); }
 
 template <int NKS, bool MASKED>
 void launch_merge_m(uint16_t* W, int64_t ldw, const float* S, int d, int k, int r,
                     uint64_t seed, uint64_t stream, bool gauss, float scale,
                     float cr, hipStream_t s, dim3 grid) {
-  constexpr int kW = merge_waves(NKS);
   constexpr int kNT = merge_nt(NKS);
   if (gauss) {
+    constexpr int kW = merge_waves(NKS, true);
     hipLaunchKernelGGL((merge_kernel<NKS, true, MASKED, kW, kNT>), grid,
                        dim3(64 * kW), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
   } else {
+    constexpr int kW = merge_waves(NKS, false);
     hipLaunchKernelGGL((merge_kernel<NKS, false, MASKED, kW, kNT>), grid,
                        dim3(64 * kW), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
   }
@@ -353,13 +361,13 @@ template <int NKS>
 hipError_t launch_merge_t(uint16_t* W, int64_t ldw, const float* S, int d, int k,
                           int r, uint64_t seed, uint64_t stream, bool gauss,
                           float scale, float cr, hipStream_t s) {
-  const int64_t blocks = (int64_t)((k + kMergeCols - 1) / kMergeCols) *
-                         ((d + kMergeRows - 1) / kMergeRows);
+  const int rows = merge_rows(NKS, gauss);
+  const int64_t blocks = (int64_t)((k + kMergeCols - 1) / kMergeCols) * ((d + rows - 1) / rows);
   const dim3 grid((unsigned)blocks);
   // unmasked when every row block is whole, every 64-column pass is whole (a
   // short last column block just runs fewer passes) and S rows are whole K
   // steps
-  const bool masked = (d % kMergeRows) != 0 || (k % kPassCols) != 0 || (r % 32) != 0;
+  const bool masked = (d % rows) != 0 || (k % kPassCols) != 0 || (r % 32) != 0;
   if (masked) launch_merge_m<NKS, true>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
   else launch_merge_m<NKS, false>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
   return hipGetLastError();

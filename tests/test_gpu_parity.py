@@ -264,6 +264,13 @@ MERGE_CASES = [
     (256, 1344, 256, 0, 1.0, 1e-3),
     (512, 1536, 128, 0, 0.5, 1e-3),
     (256, 1280, 256, 1, 1.0, 1e-3),
+    # 128-row blocks of the small-rank sign basis, 256-row blocks of 16-row
+    # waves for the small-rank Gaussian basis
+    (384, 576, 32, 0, 1.0, 1e-3),
+    (128, 256, 16, 0, 1.0, 1e-3),
+    (200, 300, 64, 0, 1.0, 1e-3),
+    (512, 768, 64, 1, 1.0, 1e-3),
+    (640, 512, 64, 1, 0.5, 1e-3),
 ]
 
 
