@@ -10,8 +10,9 @@ streamed in turn, so nothing is re-read from the 256 MB Infinity Cache.
 
 Printed: one JSON line.  `value` is tokens sketched and merged per second for
 the whole step.  Extra objects report the sketch and merge bandwidth against
-the 8 TB/s HBM peak, the roofline of the dominant entry point (timed with
-events on the library's stream), full-size parity against the CPU oracle,
+the 8 TB/s HBM peak, the roofline of the dominant entry point (its calls
+run back to back after the timed steps, one event pair around the batch on
+the library's stream), full-size parity against the CPU oracle,
 the predicted-KL leg at 64 x 1024 rows x 152064 vocab, and the CPU oracle's
 own throughput on the host cores.
 
@@ -105,53 +106,57 @@ def run_layer(lg, synth, steps, warmup):
     parity = check_layer_parity(synth, Xs, dYs, W0, W, S, cfg)
     log(f"[bench] parity {parity}")
 
-    # ---- timed steps
-    sk, mg, st = Timer(), Timer(), Timer()
-
-    def one_step(timed):
+    # ---- timed steps: back to back, one event pair around all of them (an
+    # event recorded between calls would sit inside the step)
+    def one_step():
         S.zero_()
-        if timed:
-            st.start()
         for X, dY in zip(Xs, dYs):
-            if timed:
-                sk.start()
             lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws)
-            if timed:
-                sk.stop()
-        if timed:
-            mg.start()
         lg.merge(W, S, seed, stream, kind, alpha, eta)
-        if timed:
-            mg.stop()
-            st.stop()
 
     for _ in range(warmup):
-        one_step(False)
+        one_step()
     torch.cuda.synchronize()
     log(f"[bench] timing {steps} steps")
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
     t0.record()
     for _ in range(steps):
-        one_step(True)
+        one_step()
     t1.record()
     torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3
     total_ms = t0.elapsed_time(t1)
-    # the S.zero_() fill kernel sits inside the bracket but outside the step
-    step_ms = float(np.mean(st.times_ms()))
-    sk_us = float(np.mean(sk.times_ms())) * 1e3
-    sk_min_us = float(np.min(sk.times_ms())) * 1e3
-    mg_us = float(np.mean(mg.times_ms())) * 1e3
-    mg_min_us = float(np.min(mg.times_ms())) * 1e3
+    step_ms = total_ms / steps
+
+    # ---- average duration of each entry point: the same calls back to back
+    # (sketches cycling over the microbatches, merges of the same W), one
+    # event pair around each batch, outside the timed steps
+    reps = max(steps, 20)
+
+    def batch_us(fn, n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    sk_us = batch_us(lambda i: lg.sketch_accumulate(Xs[i % n_mb], dYs[i % n_mb], S, seed, stream,
+                                                    kind, ws=ws), reps * n_mb)
+    mg_us = batch_us(lambda i: lg.merge(W, S, seed, stream, kind, alpha, eta), reps)
     sb = sketch_bytes(T, d, k, r)
     mb_ = merge_bytes(d, k, r)
     res = dict(
-        cfg=cfg, total_ms=total_ms, step_ms=step_ms,
+        cfg=cfg, total_ms=total_ms, step_ms=step_ms, wall_ms=wall_ms,
         tokens_per_step=T * n_mb,
-        sketch=dict(us_per_call=sk_us, min_us=sk_min_us, bytes_per_call=sb,
+        sketch=dict(us_per_call=sk_us, bytes_per_call=sb,
                     GBps=sb / (sk_us * 1e-6) / 1e9,
                     tokens_per_s=T / (sk_us * 1e-6)),
-        merge=dict(us_per_call=mg_us, min_us=mg_min_us, bytes_per_call=mb_,
+        merge=dict(us_per_call=mg_us, bytes_per_call=mb_,
                    GBps=mb_ / (mg_us * 1e-6) / 1e9),
         parity=parity)
     res["sketch"]["frac_hbm"] = res["sketch"]["GBps"] / HBM_PEAK_GBPS
@@ -591,10 +596,9 @@ def main():
                    "parallelism": "single-gpu"},
         "sketch": {"tokens_per_s": sk["tokens_per_s"], "GBps": sk["GBps"],
                    "frac_hbm": sk["frac_hbm"], "us_per_call": sk["us_per_call"],
-                   "min_us": sk["min_us"], **sketch_mfma(cfg["T"], cfg["d"], cfg["k"], cfg["r"],
-                                                          sk["us_per_call"])},
-        "merge": {"GBps": mg["GBps"], "frac_hbm": mg["frac_hbm"], "us_per_call": mg["us_per_call"],
-                  "min_us": mg["min_us"]},
+                   **sketch_mfma(cfg["T"], cfg["d"], cfg["k"], cfg["r"], sk["us_per_call"])},
+        "merge": {"GBps": mg["GBps"], "frac_hbm": mg["frac_hbm"], "us_per_call": mg["us_per_call"]},
+        "wall_ms_timed_steps": layer["wall_ms"],
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": layer["parity"],
