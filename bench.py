@@ -97,10 +97,12 @@ def run_layer(lg, synth, steps, warmup):
     ws = lg.sketch_workspace(T, d, k, r)
     torch.cuda.synchronize()
 
-    # ---- full-size parity of one step against the CPU oracle
+    # ---- full-size parity of one step against the CPU oracle (S starts as
+    # NaN: the first microbatch overwrites it, as in the timed steps)
     log("[bench] parity step")
-    for X, dY in zip(Xs, dYs):
-        lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws)
+    S.fill_(float("nan"))
+    for mb, (X, dY) in enumerate(zip(Xs, dYs)):
+        lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws, overwrite=mb == 0)
     lg.merge(W, S, seed, stream, kind, alpha, eta)
     torch.cuda.synchronize()
     parity = check_layer_parity(synth, Xs, dYs, W0, W, S, cfg)
@@ -109,9 +111,9 @@ def run_layer(lg, synth, steps, warmup):
     # ---- timed steps: back to back, one event pair around all of them (an
     # event recorded between calls would sit inside the step)
     def one_step():
-        S.zero_()
-        for X, dY in zip(Xs, dYs):
-            lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws)
+        # the first microbatch starts S (overwrite): no separate zero fill
+        for mb, (X, dY) in enumerate(zip(Xs, dYs)):
+            lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws, overwrite=mb == 0)
         lg.merge(W, S, seed, stream, kind, alpha, eta)
 
     for _ in range(warmup):
@@ -354,12 +356,12 @@ def _layer_set_step(lg, synth, wl, cfg, r, kind, stream, n_mb, salt=0):
         ws.append(torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"))
 
     def step():
-        for n in proj:
-            S[n].zero_()
-        for _ in range(n_mb):   # the microbatches' tensors are reused: each is far above the MALL
+        # the first microbatch starts each S (overwrite); the others add.  The
+        # microbatches' tensors are reused: each is far above the MALL.
+        for mb in range(n_mb):
             for gi, g in enumerate(groups):
                 lg.sketch_accumulate_shared(X[gi], [dY[n] for n in g], [S[n] for n in g], seed,
-                                            stream, kind, ws=ws[gi])
+                                            stream, kind, ws=ws[gi], overwrite=mb == 0)
         for n in proj:
             lg.merge(W[n], S[n], seed, stream, kind, 1.0, 2e-4)
 
@@ -393,9 +395,8 @@ def run_other_configs(lg, synth):
     ws = lg.sketch_workspace(T, d, k, r)
 
     def small():
-        S.zero_()
-        for X, dY in zip(Xs, dYs):
-            lg.sketch_accumulate(X, dY, S, 1234, ws=ws)
+        for mb, (X, dY) in enumerate(zip(Xs, dYs)):
+            lg.sketch_accumulate(X, dY, S, 1234, ws=ws, overwrite=mb == 0)
         lg.merge(W, S, 1234, 0, 0, c["alpha"], c["eta"])
     report("layer_d256_r4", _time_ms(small, 50), 2 * sketch_bytes(T, d, k, r) + merge_bytes(d, k, r),
            2 * T)

@@ -96,6 +96,9 @@ int logra_regen_A(uint64_t seed, uint64_t stream, int kind, int32_t r,
  * projection kind).  Returns 0 for invalid sizes. */
 size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r);
 
+/* Flags of the sketch entry points. */
+#define LOGRA_SKETCH_OVERWRITE 1 /* S = dY^T (X A^T): start the accumulation */
+
 /*
  * logra_sketch_accumulate - S += dY^T (X A^T), one microbatch.
  * [LoGRA] Sketch: each microbatch's contribution to S = G A^T is accumulated
@@ -109,17 +112,23 @@ size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r);
  *     16-B aligned.
  * S:  device float[d x r], contiguous, in/out, 4-B aligned.
  * seed, stream, kind: select A as in logra_regen_A.
+ * flags: 0, or LOGRA_SKETCH_OVERWRITE for the first microbatch of an
+ *     optimizer step: S = dY^T (X A^T), S's contents on entry are ignored
+ *     (they need not be initialised), which spares the caller a zero fill of
+ *     S and the kernels a read of it.  Other bits: LOGRA_EINVAL.
  * ws: device scratch of at least logra_sketch_ws_bytes(T, d, k, r) bytes,
  *     256-B aligned, owned by the caller; its contents on entry do not
  *     matter.  The result is deterministic (fixed summation order).
- * T == 0 is a no-op (returns LOGRA_OK; pointers are not inspected).
+ * T == 0 is a no-op (returns LOGRA_OK; X, dY and ws are not inspected);
+ *     with LOGRA_SKETCH_OVERWRITE it sets S to zero.
  * Constraints: d, k >= 1, T >= 0, 1 <= r <= 256, d, k, T < 2^31.
  * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
  */
 int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
                             int64_t ldd, int64_t T, int64_t d, int64_t k,
                             int32_t r, uint64_t seed, uint64_t stream, int kind,
-                            float* S, void* ws, size_t ws_bytes, hipStream_t s);
+                            int32_t flags, float* S, void* ws, size_t ws_bytes,
+                            hipStream_t s);
 
 /* Largest number of outputs one logra_sketch_accumulate_shared call takes. */
 #define LOGRA_MAX_SHARED 4
@@ -140,18 +149,20 @@ size_t logra_sketch_shared_ws_bytes(int64_t T, int64_t k, int32_t r, int32_t n_o
  * the d groups of every output.  Equal to n_out logra_sketch_accumulate
  * calls up to fp32 summation order.
  *
- * X, ldx, T, k, r, seed, stream, kind: as in logra_sketch_accumulate.
+ * X, ldx, T, k, r, seed, stream, kind, flags: as in logra_sketch_accumulate
+ *     (LOGRA_SKETCH_OVERWRITE applies to every S[o]).
  * dY, ldd, d, S: host arrays of n_out entries (1 <= n_out <= LOGRA_MAX_SHARED);
  *     dY[o] device bf16[T x ldd[o]] (same rules as dY above), S[o] device
  *     float[d[o] x r], distinct.
  * ws: device scratch of logra_sketch_shared_ws_bytes(T, k, r, n_out, d)
  *     bytes, 256-B aligned.
- * T == 0 is a no-op (device pointers are not inspected).
+ * T == 0 is a no-op (X, dY and ws are not inspected); with
+ *     LOGRA_SKETCH_OVERWRITE it sets every S[o] to zero.
  * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
  */
 int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, int64_t k,
                                    int32_t r, uint64_t seed, uint64_t stream, int kind,
-                                   int32_t n_out, const uint16_t* const* dY,
+                                   int32_t flags, int32_t n_out, const uint16_t* const* dY,
                                    const int64_t* ldd, const int64_t* d, float* const* S,
                                    void* ws, size_t ws_bytes, hipStream_t s);
 

@@ -3,7 +3,7 @@
 The work runs in liblogra.so (hand-written HIP for gfx950) behind a C ABI
 (include/logra.h); this package only marshals torch tensors into it.
 """
-from .api import (GAUSSIAN, MAX_SHARED, MAX_SWEEP, RADEMACHER,  # noqa: F401
+from .api import (GAUSSIAN, MAX_SHARED, MAX_SWEEP, RADEMACHER, SKETCH_OVERWRITE,  # noqa: F401
                   UPDATE_ADAM, UPDATE_MOMENTUM, UPDATE_SGD,
                   kl_budget_schedule, kl_sweep_ws_bytes, kl_ws_bytes, merge, predicted_kl,
                   predicted_kl_sweep, regen_A, sketch_accumulate, sketch_accumulate_shared,

@@ -27,7 +27,8 @@ SIGNATURES = {
     "logra_sketch_accumulate": (ctypes.c_int, [c_vp, ctypes.c_int64, c_vp, ctypes.c_int64,
                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64,
-                                               ctypes.c_int, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+                                               ctypes.c_int, ctypes.c_int32, c_vp, c_vp,
+                                               ctypes.c_size_t, c_vp]),
     "logra_merge": (ctypes.c_int, [c_vp, ctypes.c_int64, c_vp, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_float, c_vp]),
@@ -46,7 +47,7 @@ SIGNATURES = {
                                                       ctypes.c_int64, ctypes.c_int32,
                                                       ctypes.c_uint64, ctypes.c_uint64,
                                                       ctypes.c_int, ctypes.c_int32,
-                                                      ctypes.POINTER(c_vp),
+                                                      ctypes.c_int32, ctypes.POINTER(c_vp),
                                                       ctypes.POINTER(ctypes.c_int64),
                                                       ctypes.POINTER(ctypes.c_int64),
                                                       ctypes.POINTER(c_vp), c_vp,

@@ -16,6 +16,7 @@ from . import _lib
 
 RADEMACHER = 0
 GAUSSIAN = 1
+SKETCH_OVERWRITE = 1      # LOGRA_SKETCH_OVERWRITE: S = ... instead of S += ...
 
 
 def _stream(t):
@@ -69,8 +70,10 @@ def sketch_workspace(T, d, k, r, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None):
-    """S += dY^T (X A^T) in place for one microbatch; returns S."""
+def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None, overwrite=False):
+    """S += dY^T (X A^T) in place for one microbatch; returns S.  With
+    overwrite=True (the first microbatch of a step) S = dY^T (X A^T) and S's
+    previous contents are ignored."""
     _require(X, "X", torch.bfloat16, 2)
     _require(dY, "dY", torch.bfloat16, 2)
     _require(S, "S", torch.float32, 2)
@@ -85,7 +88,8 @@ def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None):
         ws = sketch_workspace(T, d, k, r, X.device)
     st = _lib.lib().logra_sketch_accumulate(
         X.data_ptr(), ldx, dY.data_ptr(), ldd, T, d, k, r, seed, stream, kind,
-        S.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(X))
+        SKETCH_OVERWRITE if overwrite else 0, S.data_ptr(), ws.data_ptr(),
+        ws.numel() * ws.element_size(), _stream(X))
     _lib.check(st, "logra_sketch_accumulate")
     return S
 
@@ -99,9 +103,11 @@ def sketch_shared_ws_bytes(T, k, r, ds):
     return int(_lib.lib().logra_sketch_shared_ws_bytes(T, k, r, len(ds), arr))
 
 
-def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=None):
+def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=None,
+                             overwrite=False):
     """S_o += dY_o^T (X A^T) in place for outputs sharing the input X and A
-    (e.g. q/k/v or gate/up of one layer); returns the list of S."""
+    (e.g. q/k/v or gate/up of one layer); returns the list of S.  overwrite
+    as in sketch_accumulate, for every S_o."""
     _require(X, "X", torch.bfloat16, 2)
     T, k, ldx = _rows(X, "X")
     if not 1 <= len(dYs) <= MAX_SHARED or len(dYs) != len(Ss):
@@ -128,7 +134,8 @@ def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=Non
         ws = torch.empty(max(sketch_shared_ws_bytes(T, k, r, ds), 256), dtype=torch.uint8,
                          device=X.device)
     st = _lib.lib().logra_sketch_accumulate_shared(
-        X.data_ptr(), ldx, T, k, r, seed, stream, kind, n, (ctypes.c_void_p * n)(*ptr_dy),
+        X.data_ptr(), ldx, T, k, r, seed, stream, kind, SKETCH_OVERWRITE if overwrite else 0, n,
+        (ctypes.c_void_p * n)(*ptr_dy),
         (ctypes.c_int64 * n)(*ldds), (ctypes.c_int64 * n)(*ds), (ctypes.c_void_p * n)(*ptr_s),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(X))
     _lib.check(st, "logra_sketch_accumulate_shared")

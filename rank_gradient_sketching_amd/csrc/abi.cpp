@@ -82,27 +82,36 @@ namespace {
 // Checks shared by the single- and multi-output sketch entry points; fills
 // the plan.  T == 0 is reported as LOGRA_OK with *run = false.
 int sketch_checks(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t r,
-                  int kind, int32_t n_out, const logra::SketchOut* outs, void* ws,
-                  size_t ws_bytes, logra::SketchPlan* plan, bool* run) {
+                  int kind, int32_t flags, int32_t n_out, const logra::SketchOut* outs,
+                  void* ws, size_t ws_bytes, logra::SketchPlan* plan, bool* run) {
   *run = false;
   if (n_out < 1 || n_out > LOGRA_MAX_SHARED) return LOGRA_EINVAL;
   if (!dim_ok(k) || !rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
+  if ((flags & ~LOGRA_SKETCH_OVERWRITE) != 0) return LOGRA_EINVAL;
   int64_t d[LOGRA_MAX_SHARED];
   for (int o = 0; o < n_out; ++o) {
     if (!dim_ok(outs[o].d)) return LOGRA_EINVAL;
     d[o] = outs[o].d;
   }
   if (T < 0 || T >= kDimLimit) return LOGRA_EINVAL;
-  if (T == 0) return LOGRA_OK;
+  if (T == 0 && (flags & LOGRA_SKETCH_OVERWRITE) == 0) return LOGRA_OK;
+  // S of every output: needed by the kernels, and by the zero fill at T == 0
+  for (int o = 0; o < n_out; ++o) {
+    if (outs[o].S == nullptr || !aligned(outs[o].S, 4)) return LOGRA_EINVAL;
+    for (int o2 = 0; o2 < o; ++o2)
+      if (outs[o2].S == outs[o].S) return LOGRA_EINVAL;   // one accumulator per output
+  }
+  if (T == 0) {
+    *run = true;
+    return LOGRA_OK;
+  }
   if (X == nullptr || !aligned(X, 16) || !ld_ok(ldx, k)) return LOGRA_EINVAL;
   for (int o = 0; o < n_out; ++o) {
     const logra::SketchOut& q = outs[o];
-    if (q.dY == nullptr || q.S == nullptr) return LOGRA_EINVAL;
-    if (!aligned(q.dY, 16) || !aligned(q.S, 4) || !ld_ok(q.ldd, q.d)) return LOGRA_EINVAL;
+    if (q.dY == nullptr) return LOGRA_EINVAL;
+    if (!aligned(q.dY, 16) || !ld_ok(q.ldd, q.d)) return LOGRA_EINVAL;
     // dY is read through 32-bit buffer offsets spanning 32 rows of 2 * ldd bytes
     if (q.ldd >= kDyStrideLimit) return LOGRA_EINVAL;
-    for (int o2 = 0; o2 < o; ++o2)
-      if (outs[o2].S == q.S) return LOGRA_EINVAL;   // one accumulator per output
   }
   if (!logra::make_sketch_plan(T, n_out, d, k, r, plan)) return LOGRA_EINVAL;
   if (ws == nullptr || ws_bytes < plan->total || !aligned(ws, 256)) return LOGRA_EWORKSPACE;
@@ -115,19 +124,22 @@ int sketch_checks(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t 
 int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
                             int64_t ldd, int64_t T, int64_t d, int64_t k,
                             int32_t r, uint64_t seed, uint64_t stream, int kind,
-                            float* S, void* ws, size_t ws_bytes, hipStream_t s) {
+                            int32_t flags, float* S, void* ws, size_t ws_bytes,
+                            hipStream_t s) {
   const logra::SketchOut out{dY, ldd, d, S};
   logra::SketchPlan p;
   bool run = false;
-  const int st = sketch_checks(X, ldx, T, k, r, kind, 1, &out, ws, ws_bytes, &p, &run);
+  const int st = sketch_checks(X, ldx, T, k, r, kind, flags, 1, &out, ws, ws_bytes, &p, &run);
   if (st != LOGRA_OK || !run) return st;
+  if (T == 0) return hip_status(logra::launch_zero_outputs(&out, 1, r, s));
   return hip_status(logra::launch_sketch(p, X, ldx, &out, (int)T, (int)k, r, seed, stream,
-                                         kind, static_cast<char*>(ws), s));
+                                         kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
+                                         static_cast<char*>(ws), s));
 }
 
 int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, int64_t k,
                                    int32_t r, uint64_t seed, uint64_t stream, int kind,
-                                   int32_t n_out, const uint16_t* const* dY,
+                                   int32_t flags, int32_t n_out, const uint16_t* const* dY,
                                    const int64_t* ldd, const int64_t* d, float* const* S,
                                    void* ws, size_t ws_bytes, hipStream_t s) {
   if (n_out < 1 || n_out > LOGRA_MAX_SHARED) return LOGRA_EINVAL;
@@ -136,10 +148,13 @@ int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, in
   for (int o = 0; o < n_out; ++o) outs[o] = logra::SketchOut{dY[o], ldd[o], d[o], S[o]};
   logra::SketchPlan p;
   bool run = false;
-  const int st = sketch_checks(X, ldx, T, k, r, kind, n_out, outs, ws, ws_bytes, &p, &run);
+  const int st = sketch_checks(X, ldx, T, k, r, kind, flags, n_out, outs, ws, ws_bytes, &p,
+                               &run);
   if (st != LOGRA_OK || !run) return st;
+  if (T == 0) return hip_status(logra::launch_zero_outputs(outs, n_out, r, s));
   return hip_status(logra::launch_sketch(p, X, ldx, outs, (int)T, (int)k, r, seed, stream,
-                                         kind, static_cast<char*>(ws), s));
+                                         kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
+                                         static_cast<char*>(ws), s));
 }
 
 int logra_merge(uint16_t* W, int64_t ldw, const float* S, int64_t d, int64_t k,

@@ -52,9 +52,14 @@ float sign_scale(int r);
 hipError_t launch_regen(uint64_t seed, uint64_t stream, int kind, int r,
                         int64_t k, float* A, hipStream_t s);
 
+// overwrite: S = dY^T (X A^T) instead of S += (S is not read).
 hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
                          const SketchOut* outs, int T, int k, int r, uint64_t seed,
-                         uint64_t stream, int kind, char* ws, hipStream_t s);
+                         uint64_t stream, int kind, bool overwrite, char* ws,
+                         hipStream_t s);
+
+// S = 0 for n_out outputs of d x r floats (a fill kernel, no memset node).
+hipError_t launch_zero_outputs(const SketchOut* outs, int n_out, int r, hipStream_t s);
 
 hipError_t launch_merge(uint16_t* W, int64_t ldw, const float* S, int d, int k,
                         int r, uint64_t seed, uint64_t stream, int kind,

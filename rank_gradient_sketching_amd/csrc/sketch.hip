@@ -538,6 +538,7 @@ constexpr int acc_lds_bytes() {
 // numbered across all outputs; output o owns groups dg_off[o] .. dg_off[o+1].
 struct OutTable {
   int n;
+  int overwrite;   // S = result instead of S += result (S is not read)
   int dg_off[kMaxShared + 1];
   const uint16_t* dY[kMaxShared];
   int64_t ldd[kMaxShared];
@@ -738,7 +739,10 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
         } else {
           const int drow = acc_drow<Q, NB16>(dc0, i, lane);
           const int rc = acc_rcol<NB16>(i, lane);
-          if (drow < d && rc < r) S[(int64_t)drow * r + rc] += v;
+          if (drow < d && rc < r) {
+            float* sp_ = S + (int64_t)drow * r + rc;
+            *sp_ = tab.overwrite ? v : *sp_ + v;
+          }
         }
       }
     }
@@ -773,8 +777,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   // Loads go out four splits at a time (with S in the first group), so one
   // memory latency covers each group; the adds still run in split order.
   // Slots past the last split re-read it and add an exact zero.
+  const bool add = !tab.overwrite;
   f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-  if (vec) sv = *reinterpret_cast<const f32x4*>(srow + rc);
+  if (vec && add) sv = *reinterpret_cast<const f32x4*>(srow + rc);
   const float* pp = part + flat;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < n_split; sp += 4) {
@@ -795,7 +800,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (rc + e < r) srow[rc + e] += sum[e];
+      if (rc + e < r) srow[rc + e] = add ? srow[rc + e] + sum[e] : sum[e];
   }
 }
 
@@ -944,7 +949,8 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
 
 hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
                          const SketchOut* outs, int T, int k, int r, uint64_t seed,
-                         uint64_t stream, int kind, char* ws, hipStream_t s) {
+                         uint64_t stream, int kind, bool overwrite, char* ws,
+                         hipStream_t s) {
   uint16_t* Pt = reinterpret_cast<uint16_t*>(ws + p.off_pt);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   uint16_t* Ab = reinterpret_cast<uint16_t*>(ws + p.off_gauss);
@@ -967,6 +973,7 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
   if (e != hipSuccess) return e;
   OutTable tab{};
   tab.n = p.n_out;
+  tab.overwrite = overwrite ? 1 : 0;
   for (int o = 0; o <= p.n_out; ++o) tab.dg_off[o] = p.dg_off[o];
   for (int o = 0; o < p.n_out; ++o) {
     tab.dY[o] = outs[o].dY;
@@ -981,6 +988,28 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
     case 128: return launch_accumulate<kAccQ, 8>(p, tab, T, r, Pt, part, s);
     default: return launch_accumulate<kAccQ, 16>(p, tab, T, r, Pt, part, s);
   }
+}
+
+// S = 0, four floats per thread where the row allows (S of every output is
+// a contiguous d x r array; its base is only 4-byte aligned).
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ S, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n && (reinterpret_cast<uintptr_t>(S) & 15) == 0) {
+    *reinterpret_cast<f32x4*>(S + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    for (int64_t j = i; j < i + 4 && j < n; ++j) S[j] = 0.0f;
+  }
+}
+
+hipError_t launch_zero_outputs(const SketchOut* outs, int n_out, int r, hipStream_t s) {
+  for (int o = 0; o < n_out; ++o) {
+    const int64_t n = outs[o].d * (int64_t)r;
+    const int64_t blocks = (n + 1023) / 1024;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, outs[o].S, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace logra

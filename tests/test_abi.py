@@ -50,11 +50,11 @@ def test_workspace_queries(L):
 
 def _sketch(L, **kw):
     a = dict(X=P, ldx=256, dY=P, ldd=256, T=128, d=256, k=256, r=4, seed=1234, stream=0,
-             kind=0, S=P, ws=P, ws_bytes=1 << 30, s=None)
+             kind=0, flags=0, S=P, ws=P, ws_bytes=1 << 30, s=None)
     a.update(kw)
     return L.logra_sketch_accumulate(a["X"], a["ldx"], a["dY"], a["ldd"], a["T"], a["d"],
                                      a["k"], a["r"], a["seed"], a["stream"], a["kind"],
-                                     a["S"], a["ws"], a["ws_bytes"], a["s"])
+                                     a["flags"], a["S"], a["ws"], a["ws_bytes"], a["s"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -66,6 +66,11 @@ def _sketch(L, **kw):
     (dict(X=MIS), EINVAL), (dict(dY=MIS), EINVAL), (dict(S=P + 1), EINVAL),
     (dict(d=1 << 31), EINVAL), (dict(T=1 << 31), EINVAL), (dict(ldd=1 << 26), EINVAL),
     (dict(ws=None), EWS), (dict(ws_bytes=16), EWS), (dict(ws=P + 16), EWS),
+    (dict(flags=2), EINVAL), (dict(flags=-1), EINVAL), (dict(flags=3), EINVAL),
+    (dict(flags=1, S=None), EINVAL),
+    # the zero fill of an empty first microbatch still needs a valid S
+    (dict(flags=1, T=0, S=None), EINVAL), (dict(flags=1, T=0, S=P + 2), EINVAL),
+    (dict(flags=2, T=0), EINVAL),
 ])
 def test_sketch_rejects(L, kw, status):
     assert _sketch(L, **kw) == status
@@ -180,14 +185,14 @@ def test_kl_budget_schedule():
 
 def _shared(L, n_out=2, **kw):
     import ctypes
-    a = dict(X=P, ldx=256, T=128, k=256, r=4, seed=1, stream=0, kind=0,
+    a = dict(X=P, ldx=256, T=128, k=256, r=4, seed=1, stream=0, kind=0, flags=0,
              dY=[P] * n_out, ldd=[256] * n_out, d=[256] * n_out,
              S=[P + 4096 * (o + 1) for o in range(n_out)], ws=P, ws_bytes=1 << 30, s=None)
     a.update(kw)
     n = kw.get("n_out_arg", n_out)
     arr = lambda t, xs: None if xs is None else (t * max(1, len(xs)))(*xs)
     return L.logra_sketch_accumulate_shared(
-        a["X"], a["ldx"], a["T"], a["k"], a["r"], a["seed"], a["stream"], a["kind"], n,
+        a["X"], a["ldx"], a["T"], a["k"], a["r"], a["seed"], a["stream"], a["kind"], a["flags"], n,
         arr(ctypes.c_void_p, a["dY"]), arr(ctypes.c_int64, a["ldd"]), arr(ctypes.c_int64, a["d"]),
         arr(ctypes.c_void_p, a["S"]), a["ws"], a["ws_bytes"], a["s"])
 
@@ -201,6 +206,8 @@ def _shared(L, n_out=2, **kw):
     (dict(dY=[P, MIS]), EINVAL), (dict(S=[P, P + 2]), EINVAL), (dict(ldx=255), EINVAL),
     (dict(r=0), EINVAL), (dict(kind=5), EINVAL),
     (dict(ws=None), EWS), (dict(ws_bytes=16), EWS),
+    (dict(flags=4), EINVAL), (dict(flags=1, T=0, S=[P, None]), EINVAL),
+    (dict(flags=1, T=0, S=[P, P]), EINVAL),
 ])
 def test_sketch_shared_rejects(L, kw, status):
     assert _shared(L, **kw) == status

@@ -203,6 +203,74 @@ def test_sketch_shared_one_output_is_the_single_call_bitwise(lg):
     assert torch.equal(a, b)
 
 
+OVERWRITE_CASES = [
+    # T, d, k, r, kind: one split (S written by the accumulate kernel), several
+    # splits (S written by the finalize kernel), a rank that is not a multiple
+    # of four (scalar finalize stores), the Gaussian basis at maximum rank
+    (128, 256, 256, 4, 0),
+    (2048, 512, 1024, 64, 0),
+    (2048, 300, 520, 3, 0),
+    (1000, 1536, 512, 256, 1),
+]
+
+
+@pytest.mark.parametrize("T,d,k,r,kind", OVERWRITE_CASES)
+def test_sketch_overwrite_is_zero_then_add(lg, T, d, k, r, kind):
+    say("sketch overwrite", T, d, k, r, kind)
+    mbs = [(padded_bf16(synth.host_normal_bf16((T, k), synth.X_ID, mb=mb, salt=d), -(-k // 8) * 8),
+            padded_bf16(synth.host_normal_bf16((T, d), synth.DY_ID, mb=mb, salt=d), -(-d // 8) * 8))
+           for mb in range(2)]
+    ref = torch.zeros(d, r, device="cuda")
+    got = torch.full((d, r), float("nan"), device="cuda")
+    for mb, (X, dY) in enumerate(mbs):
+        lg.sketch_accumulate(X, dY, ref, 1234, 0, kind)
+        lg.sketch_accumulate(X, dY, got, 1234, 0, kind, overwrite=mb == 0)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), mb
+    # overwriting again discards everything accumulated so far
+    lg.sketch_accumulate(mbs[1][0], mbs[1][1], got, 1234, 0, kind, overwrite=True)
+    one = torch.zeros(d, r, device="cuda")
+    lg.sketch_accumulate(mbs[1][0], mbs[1][1], one, 1234, 0, kind)
+    torch.cuda.synchronize()
+    assert torch.equal(got, one)
+
+
+def test_sketch_overwrite_empty_microbatch_zeroes_S(lg):
+    say("sketch overwrite T = 0")
+    for d, r in ((256, 4), (300, 3), (1, 1), (4097, 256)):
+        S = torch.full((d, r), float("nan"), device="cuda")
+        X = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+        dY = torch.zeros(0, d, dtype=torch.bfloat16, device="cuda")
+        lg.sketch_accumulate(X, dY, S, 1234, overwrite=True)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(S).item() == 0 and not torch.isnan(S).any()
+    # an empty microbatch without the flag leaves S as it is
+    S = torch.full((64, 8), 3.0, device="cuda")
+    lg.sketch_accumulate(torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda"),
+                         torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda"), S, 1234)
+    torch.cuda.synchronize()
+    assert torch.all(S == 3.0)
+
+
+def test_sketch_shared_overwrite(lg):
+    say("sketch shared overwrite")
+    T, k, ds, r = 512, 256, (256, 64, 136), 64
+    X = synth.host_normal_bf16((T, k), synth.X_ID, salt=3).cuda()
+    dYs = [synth.host_normal_bf16((T, d), synth.DY_ID, mb=o, salt=d).cuda() for o, d in enumerate(ds)]
+    ref = [torch.zeros(d, r, device="cuda") for d in ds]
+    got = [torch.full((d, r), float("nan"), device="cuda") for d in ds]
+    lg.sketch_accumulate_shared(X, dYs, ref, 1234)
+    lg.sketch_accumulate_shared(X, dYs, got, 1234, overwrite=True)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+    empty = [torch.full((d, r), float("nan"), device="cuda") for d in ds]
+    lg.sketch_accumulate_shared(X[:0], [dY[:0] for dY in dYs], empty, 1234, overwrite=True)
+    torch.cuda.synchronize()
+    for e in empty:
+        assert torch.count_nonzero(e).item() == 0 and not torch.isnan(e).any()
+
+
 def test_sketch_padded_strides(lg):
     say("sketch padded strides")
     _, e1, _ = _sketch_case(lg, 300, 100, 120, 16, 0, 2, ld_pad=24)
