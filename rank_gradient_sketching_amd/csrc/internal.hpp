@@ -36,7 +36,11 @@ struct SketchPlan {
   int steps;        // t_pad / 32
   int n_out;        // outputs sharing X
   int dg_off[kMaxShared + 1];  // first d group of each output (prefix sums)
-  int n_dgroups;    // accumulate work-groups along d, all outputs together
+  int n_dgroups;    // 128-column d groups, all outputs together
+  bool acc_wide;    // accumulate_wide_kernel (r >= 128) instead of accumulate_kernel
+  int wg_groups;    // d groups per accumulate work-group (1, or 8 / (rp / 64) when wide)
+  int wg_off[kMaxShared + 1];  // first accumulate work-group along d of each output
+  int n_wg;         // accumulate work-groups along d, all outputs together
   int n_split;      // accumulate work-groups along T
   int steps_per_split;
   int64_t d_pad;    // n_dgroups * 16 * q_cols

@@ -540,6 +540,7 @@ struct OutTable {
   int n;
   int overwrite;   // S = result instead of S += result (S is not read)
   int dg_off[kMaxShared + 1];
+  int wg_off[kMaxShared + 1];   // first accumulate_wide_kernel work-group of each output
   const uint16_t* dY[kMaxShared];
   int64_t ldd[kMaxShared];
   int d[kMaxShared];
@@ -750,6 +751,187 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   }
 }
 
+// S += dY^T P for r = 128 and 256, where accumulate_kernel's waves split r
+// and each loads the same dY rows and its own P tiles: at r = 256 that moves
+// ~128 KB through a CU's vector-memory path per 2048 matrix-core cycles, about
+// all it takes, and the matrix cores sat ~50 % busy.  Here a work-group owns
+// DP = 8 / (r / 64) d groups of 128 columns and all of r over a range of
+// 32-token steps; wave w takes d group w % DP and r columns 64 (w / DP) ..
+// + 63 (128 x 64 accumulators, as in accumulate_kernel).  Per step the dY
+// rows of all DP groups (32 x 128 DP bf16) and the P tile of all r reach LDS
+// once, by direct global->LDS copies spread over the waves, and every wave
+// reads its operands from there: 48 KB per step per work-group for 2048
+// matrix-core cycles per SIMD.  Three stages: a step's copies are issued two
+// steps ahead, one barrier per step.  No cross-wave sum: each wave writes its
+// own 128 x 64 block (partial tile or S).
+template <int NB16, bool MASKED>
+__global__ __launch_bounds__(512) void accumulate_wide_kernel(
+    OutTable tab, int T, int r, const uint16_t* __restrict__ Pt, int steps_total,
+    int steps_per_split, int n_dgroups, float* __restrict__ part) {
+  constexpr int Q = 8;
+  constexpr int NBW = 4;                     // 16-column r blocks per wave
+  constexpr int RPW = NB16 / NBW;            // waves along r
+  constexpr int DP = kAccWaves / RPW;        // d groups per work-group
+  constexpr int NREG = Q * NB16 * 4;         // registers of a d group's tile
+  constexpr int NREGW = Q * NBW * 4;         // accumulators per lane
+  constexpr int kDyRow = DP * 16 * Q * 2;    // bytes of one token row of the dY tile
+  constexpr int kDyBytes = 32 * kDyRow;
+  constexpr int kPBytes = NB16 * 2 * 1024;   // one step of P, every r block, hi and lo
+  constexpr int kStage = kDyBytes + kPBytes;
+  constexpr int kStages = 3;
+  constexpr int kCopies = kStage / 1024;     // 1 KB copies per step
+  constexpr int kCopiesW = kCopies / kAccWaves;
+  static_assert(kCopies % kAccWaves == 0, "copies spread evenly over the waves");
+  static_assert(kStages * kStage <= 160 * 1024, "stages fit in LDS");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kStages * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dpart = wave % DP;
+  const int rpart = wave / DP;
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+  const int sp = blockIdx.y;
+  const int wg = xcd_spread((int)blockIdx.x, sp, (int)gridDim.x);
+  // output of this work-group (wave-uniform compares on the table)
+  int o_sel = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxShared; ++i)
+    if (i < tab.n && wg >= tab.wg_off[i]) o_sel = i;
+  const uint16_t* dY = tab.dY[0];
+  int64_t ldd = tab.ldd[0];
+  int d = tab.d[0];
+  float* S = tab.S[0];
+  int dg_first = tab.dg_off[0], dg_end = tab.dg_off[1], wg_first = tab.wg_off[0];
+#pragma unroll
+  for (int i = 1; i < kMaxShared; ++i) {
+    if (i == o_sel) {
+      dY = tab.dY[i];
+      ldd = tab.ldd[i];
+      d = tab.d[i];
+      S = tab.S[i];
+      dg_first = tab.dg_off[i];
+      dg_end = tab.dg_off[i + 1];
+      wg_first = tab.wg_off[i];
+    }
+  }
+  const int col_wg = (wg - wg_first) * DP * 16 * Q;   // first d column of the work-group
+  const int dg_local = (wg - wg_first) * DP + dpart;   // this wave's d group in the output
+  const bool group_ok = dg_first + dg_local < dg_end;
+  const int dc0 = dg_local * 16 * Q;
+  const int qvalid = d - (dc0 + Q * m);   // columns dc0 + Q m + q < d are real
+  const int s_begin = sp * steps_per_split;
+  const int s_end = min(steps_total, s_begin + steps_per_split);
+  const int n = s_end - s_begin;
+
+  // Copies of step `step` into stage st: copy c = j * 8 + wave; the first
+  // kDyBytes / 1 KB copies bring dY (row-major, kDyRow bytes per token row;
+  // rows past T re-read row T - 1 and columns past d the row's first 8, both
+  // cleared when read back), the rest the step's P blocks (contiguous).
+  auto issue = [&](int step, int st) {
+    unsigned char* base = lds + st * kStage;
+#pragma unroll
+    for (int j = 0; j < kCopiesW; ++j) {
+      const int c = j * kAccWaves + wave;
+      if (c < kDyBytes / 1024) {
+        const int b = c * 1024 + 16 * lane;
+        int t = step * 32 + b / kDyRow;
+        int col = col_wg + (b % kDyRow) / 2;
+        if (MASKED) {
+          t = t < T ? t : T - 1;
+          col = col < d ? col : 0;
+        }
+        lds_dma16((const void*)(dY + (int64_t)t * ldd + col), lds_addr(base + c * 1024));
+      } else {
+        const int cp = c - kDyBytes / 1024;
+        lds_dma16((const void*)(Pt + p_block(step, 0, 0, NB16) + cp * 512 + 8 * lane),
+                  lds_addr(base + kDyBytes + cp * 1024));
+      }
+    }
+  };
+
+  float acc[NREGW];
+#pragma unroll
+  for (int i = 0; i < NREGW; ++i) acc[i] = 0.0f;
+
+  auto compute = [&](int step, int st) {
+    const unsigned char* base = lds + st * kStage;
+    // dY rows 8 g4 + e of the step, columns dc0 + Q m .. + 7 (as
+    // load_dy_stage gives them), and the wave's P operands
+    u32x4 row[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      row[e] = *reinterpret_cast<const u32x4*>(base + (8 * g4 + e) * kDyRow + dpart * 256 +
+                                               16 * m);
+      if (MASKED && step * 32 + 8 * g4 + e >= T) row[e] = u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x4 bh[NBW], bl[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int nbg = rpart * NBW + nb;
+      bh[nb] = *reinterpret_cast<const u32x4*>(base + kDyBytes + (2 * nbg) * 1024 + 16 * lane);
+      bl[nb] = *reinterpret_cast<const u32x4*>(base + kDyBytes + (2 * nbg + 1) * 1024 + 16 * lane);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      u32x4 a;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        a[u] = __builtin_amdgcn_perm(row[2 * u + 1][q >> 1], row[2 * u][q >> 1],
+                                     (q & 1) ? 0x07060302u : 0x05040100u);
+      if (MASKED && q >= qvalid) a = u32x4{0u, 0u, 0u, 0u};   // column past d
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int i0 = (q * NBW + nb) * 4;
+        f32x4 c4 = {acc[i0], acc[i0 + 1], acc[i0 + 2], acc[i0 + 3]};
+        c4 = mfma16(a, bh[nb], c4);
+        c4 = mfma16(a, bl[nb], c4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i0 + v] = c4[v];
+      }
+    }
+  };
+
+  if (n > 0) {
+    issue(s_begin, 0);
+    if (n > 1) issue(s_begin + 1, 1);
+    for (int j = 0; j < n; ++j) {
+      // this wave's copies of step j are done (only step j + 1's may be
+      // outstanding), then everybody's; stage (j + 2) % 3 was last read in
+      // step j - 1, which every wave has finished
+      if (j + 1 < n) vm_wait<kCopiesW>();
+      else vm_wait<0>();
+      __syncthreads();
+      if (j + 2 < n) issue(s_begin + j + 2, (j + 2) % kStages);
+      lgkm_wait0();
+      compute(s_begin + j, j % kStages);
+    }
+  }
+  if (!group_ok) return;
+
+  // Wave register il = (q NBW + nb) 4 + e -> tile register of its d group.
+  const int dgg = dg_first + dg_local;
+  float* my = part ? part + ((int64_t)sp * n_dgroups + dgg) * (NREG * 64) : nullptr;
+#pragma unroll
+  for (int il = 0; il < NREGW; ++il) {
+    const int q = il / (NBW * 4);
+    const int rem = il % (NBW * 4);
+    const int i = (q * NB16 + rpart * NBW + (rem >> 2)) * 4 + (rem & 3);
+    const float v = acc[il];
+    if (my) {
+      my[i * 64 + lane] = v;
+    } else {
+      const int drow = acc_drow<Q, NB16>(dc0, i, lane);
+      const int rc = acc_rcol<NB16>(i, lane);
+      if (drow < d && rc < r) {
+        float* sp_ = S + (int64_t)drow * r + rc;
+        *sp_ = tab.overwrite ? v : *sp_ + v;
+      }
+    }
+  }
+}
+
 // S += sum over splits of the partial tiles, in split order.  One thread per
 // four consecutive floats of a tile (four lanes with the same d row and four
 // consecutive r columns).
@@ -864,6 +1046,15 @@ hipError_t launch_project(const SketchPlan& p, const uint16_t* X, int64_t ldx,
 }
 
 template <int Q, int NB16>
+hipError_t launch_finalize(const SketchPlan& p, const OutTable& tab, int r, float* part,
+                           hipStream_t s) {
+  const int64_t quads = (int64_t)p.n_dgroups * Q * NB16 * 4 * 64 / 4;
+  hipLaunchKernelGGL((finalize_kernel<Q, NB16>), dim3((unsigned)((quads + 255) / 256)),
+                     dim3(256), 0, s, part, p.n_split, p.n_dgroups, tab, r);
+  return hipGetLastError();
+}
+
+template <int Q, int NB16>
 hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, int r,
                              const uint16_t* Pt, float* part, hipStream_t s) {
   const dim3 grid((unsigned)p.n_dgroups, (unsigned)p.n_split);
@@ -879,10 +1070,38 @@ hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, in
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
-  const int64_t quads = (int64_t)p.n_dgroups * Q * NB16 * 4 * 64 / 4;
-  hipLaunchKernelGGL((finalize_kernel<Q, NB16>), dim3((unsigned)((quads + 255) / 256)),
-                     dim3(256), 0, s, part, p.n_split, p.n_dgroups, tab, r);
-  return hipGetLastError();
+  return launch_finalize<Q, NB16>(p, tab, r, part, s);
+}
+
+template <int NB16>
+hipError_t launch_accumulate_wide(const SketchPlan& p, const OutTable& tab, int T, int r,
+                                  const uint16_t* Pt, float* part, hipStream_t s) {
+  constexpr int DP = kAccWaves / (NB16 / 4);
+  const dim3 grid((unsigned)p.n_wg, (unsigned)p.n_split);
+  float* pp = p.n_split > 1 ? part : nullptr;
+  // masked: a ragged step, a ragged d group, or a work-group whose last d
+  // groups lie past its output (their columns must not be read)
+  bool masked = (T % 32) != 0;
+  for (int o = 0; o < tab.n; ++o)
+    masked = masked || (tab.d[o] % (16 * kAccQ)) != 0 ||
+             ((tab.dg_off[o + 1] - tab.dg_off[o]) % DP) != 0;
+  if (masked) {
+    hipLaunchKernelGGL((accumulate_wide_kernel<NB16, true>), grid, dim3(64 * kAccWaves), 0, s,
+                       tab, T, r, Pt, p.steps, p.steps_per_split, p.n_dgroups, pp);
+  } else {
+    hipLaunchKernelGGL((accumulate_wide_kernel<NB16, false>), grid, dim3(64 * kAccWaves), 0, s,
+                       tab, T, r, Pt, p.steps, p.steps_per_split, p.n_dgroups, pp);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_split == 1) return e;
+  return launch_finalize<kAccQ, NB16>(p, tab, r, part, s);
+}
+
+// LOGRA_ACC_WIDE in the environment overrides the choice of the accumulate
+// kernel for r >= 128: 0 never the wide kernel, 2 always (any T).
+int wide_accumulate_mode() {
+  const char* env = getenv("LOGRA_ACC_WIDE");
+  return env == nullptr ? 1 : env[0] - '0';
 }
 
 }  // namespace
@@ -901,27 +1120,41 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
   q.steps = (int)(q.t_pad / 32);
   const int dc = 16 * q.q_cols;
   q.n_out = n_out;
-  int64_t groups = 0;
+  // The wide kernel from r = 128 once T gives each work-group enough steps
+  // (T >= 16384): at T = 8192 it left CUs idle and measured slower.
+  const int wide_mode = wide_accumulate_mode();
+  q.acc_wide = q.rp >= 128 && wide_mode != 0 && (q.steps >= 512 || wide_mode == 2);
+  q.wg_groups = q.acc_wide ? kAccWaves / (q.rp / 64) : 1;
+  int64_t groups = 0, wgs_d = 0;
   for (int o = 0; o < n_out; ++o) {
     if (d[o] < 1 || d[o] >= (int64_t(1) << 31)) return false;
     q.dg_off[o] = (int)groups;
-    groups += (d[o] + dc - 1) / dc;
+    q.wg_off[o] = (int)wgs_d;
+    const int64_t g = (d[o] + dc - 1) / dc;
+    groups += g;
+    wgs_d += (g + q.wg_groups - 1) / q.wg_groups;
   }
   if (groups >= (int64_t(1) << 27)) return false;   // finalize grid: 8 per group
   q.dg_off[n_out] = (int)groups;
+  q.wg_off[n_out] = (int)wgs_d;
   q.n_dgroups = (int)groups;
+  q.n_wg = (int)wgs_d;
   // Work-groups along T: at most so many that each wave keeps two 32-token
   // steps; among those counts, the one with the least modelled cost: the dY
   // stream slowed by the share of the 256 CUs that the work-groups' rounds
   // leave idle (one work-group per CU), plus writing and reading the split
   // partial tiles and the split-reduction launch (~25 MB of streaming).
+  // (The wide kernel's waves all take every step of their split: at least
+  // four steps each, so the three-stage copy ring fills.)
   const int lanes = kAccWaves / acc_rsplit(q.rp / 16);   // waves along the steps
-  const int max_split = q.steps / (2 * lanes) > 0 ? q.steps / (2 * lanes) : 1;
+  const int min_steps = q.acc_wide ? 4 : 2 * lanes;
+  const int max_split = q.steps / min_steps > 0 ? q.steps / min_steps : 1;
   const double dy_bytes = 2.0 * (double)q.t_pad * (double)groups * dc;
+  const int64_t wgs_along_d = q.acc_wide ? wgs_d : groups;
   int n_split = 1;
   double best = 0.0;
   for (int ns = 1; ns <= max_split && ns <= 64; ++ns) {
-    const int64_t wgs = groups * ns;
+    const int64_t wgs = wgs_along_d * ns;
     const double eff = (double)wgs / (double)(((wgs + 255) / 256) * 256);
     const double cost = dy_bytes / eff +
                         (ns > 1 ? 8.0 * ns * (double)groups * dc * q.rp + 25e6 : 0.0);
@@ -974,12 +1207,19 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
   OutTable tab{};
   tab.n = p.n_out;
   tab.overwrite = overwrite ? 1 : 0;
-  for (int o = 0; o <= p.n_out; ++o) tab.dg_off[o] = p.dg_off[o];
+  for (int o = 0; o <= p.n_out; ++o) {
+    tab.dg_off[o] = p.dg_off[o];
+    tab.wg_off[o] = p.wg_off[o];
+  }
   for (int o = 0; o < p.n_out; ++o) {
     tab.dY[o] = outs[o].dY;
     tab.ldd[o] = outs[o].ldd;
     tab.d[o] = (int)outs[o].d;
     tab.S[o] = outs[o].S;
+  }
+  if (p.acc_wide) {
+    if (p.rp == 128) return launch_accumulate_wide<8>(p, tab, T, r, Pt, part, s);
+    return launch_accumulate_wide<16>(p, tab, T, r, Pt, part, s);
   }
   switch (p.rp) {
     case 16: return launch_accumulate<kAccQ, 1>(p, tab, T, r, Pt, part, s);

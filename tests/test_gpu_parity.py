@@ -154,6 +154,31 @@ def test_sketch_both_projection_kernels(lg, monkeypatch, mode, T, d, k, r, kind,
     assert err_total < S_TOL, err_total
 
 
+# Both accumulate kernels at r = 128 and 256 (LOGRA_ACC_WIDE: 0 = the kernel
+# whose waves split r and T, 2 = the work-group-wide tile of 2 or 4 d groups,
+# which by default serves only T >= 16384).
+WIDE_CASES = [
+    # T, d, k, r, kind, n_mb
+    (77, 1030, 264, 256, 0, 1),     # ragged T and d, nine d groups (the last work-group half empty)
+    (256, 384, 256, 256, 0, 2),     # three d groups: a work-group with a group past d
+    (512, 512, 512, 256, 0, 1),     # whole tiles (unmasked)
+    (2048, 1024, 512, 128, 0, 1),   # r = 128: four d groups per work-group, several splits
+    (1000, 640, 300, 100, 0, 2),    # padded rank, five d groups over two work-groups
+    (129, 256, 1000, 256, 1, 1),    # Gaussian basis
+    (4096, 256, 256, 256, 0, 1),    # many splits of one work-group column
+]
+
+
+@pytest.mark.parametrize("mode", ["0", "2"])
+@pytest.mark.parametrize("T,d,k,r,kind,n_mb", WIDE_CASES)
+def test_sketch_both_accumulate_kernels(lg, monkeypatch, mode, T, d, k, r, kind, n_mb):
+    say("sketch accumulate kernel", mode, T, d, k, r, kind, n_mb)
+    monkeypatch.setenv("LOGRA_ACC_WIDE", mode)
+    _, err_delta, err_total = _sketch_case(lg, T, d, k, r, kind, n_mb)
+    assert err_delta < S_TOL, err_delta
+    assert err_total < S_TOL, err_total
+
+
 SHARED_CASES = [
     # T, k, ds (outputs sharing X), r, kind
     (512, 256, (256, 64, 64), 64, 0),          # q/k/v-shaped
