@@ -956,25 +956,25 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   float* srow = out.S + (int64_t)drow * r;
   // float4 access when r % 4 == 0 and S is 16-byte aligned
   const bool vec = (r % 4) == 0 && (reinterpret_cast<uintptr_t>(out.S) & 15) == 0 && rc + 4 <= r;
-  // Loads go out four splits at a time (with S in the first group), so one
+  // Loads go out eight splits at a time (with S in the first group), so one
   // memory latency covers each group; the adds still run in split order.
-  // Slots past the last split re-read it and add an exact zero.
+  // Slots past the last split re-read it and are not added.
+  constexpr int G = 8;
   const bool add = !tab.overwrite;
   f32x4 sv = {0.f, 0.f, 0.f, 0.f};
   if (vec && add) sv = *reinterpret_cast<const f32x4*>(srow + rc);
   const float* pp = part + flat;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < n_split; sp += 4) {
-    f32x4 v[4];
+  for (int sp = 0; sp < n_split; sp += G) {
+    f32x4 v[G];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < G; ++u) {
       const int su = sp + u < n_split ? sp + u : n_split - 1;
       v[u] = *reinterpret_cast<const f32x4*>(pp + (int64_t)su * per_split);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float keep = sp + u < n_split ? 1.0f : 0.0f;
-      sum += v[u] * keep;
+    for (int u = 0; u < G; ++u) {
+      if (sp + u < n_split) sum += v[u];
     }
   }
   if (vec) {

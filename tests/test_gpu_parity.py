@@ -296,6 +296,27 @@ def test_sketch_shared_overwrite(lg):
         assert torch.count_nonzero(e).item() == 0 and not torch.isnan(e).any()
 
 
+@pytest.mark.parametrize("T,d,k,r", [(2048, 1536, 256, 64), (3000, 4096, 512, 16), (4096, 1536, 256, 64),
+                                     (1000, 4000, 256, 64)])
+def test_sketch_overflow_stays_infinite(lg, T, d, k, r):
+    # One token of dY near the bf16 maximum in the last split: that split's
+    # partial overflows to +-inf, which must reach S as inf (never NaN) whatever
+    # the split count.
+    say("sketch overflow", T, d, k, r)
+    X = synth.host_normal_bf16((T, k), synth.X_ID, salt=11)
+    dY = synth.host_normal_bf16((T, d), synth.DY_ID, salt=11)
+    col = d // 3
+    dY[T - 1, col] = 3.0e38
+    S = torch.zeros(d, r, device="cuda")
+    lg.sketch_accumulate(padded_bf16(X, -(-k // 8) * 8), padded_bf16(dY, -(-d // 8) * 8), S, 1234)
+    torch.cuda.synchronize()
+    got = S.cpu()
+    assert not torch.isnan(got).any()
+    assert torch.isinf(got[col]).sum().item() > r // 2
+    others = torch.cat([got[:col], got[col + 1:]])
+    assert torch.isfinite(others).all()
+
+
 def test_sketch_padded_strides(lg):
     say("sketch padded strides")
     _, e1, _ = _sketch_case(lg, 300, 100, 120, 16, 0, 2, ld_pad=24)
