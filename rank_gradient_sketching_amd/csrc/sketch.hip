@@ -9,8 +9,10 @@
 // Kernels on the caller's stream (no cross-work-group synchronisation inside
 // any of them: on this part an agent-scope fence per work-group costs far more
 // than an extra launch):
-//   project    P = c * X A^T (T x r).  One work-group per 32 tokens; its
-//              waves split k in 256-column chunks, which reach LDS through
+//   project    P = c * X A^T (T x r).  One work-group per 32 tokens
+//              (project_kernel), or per 64 tokens from r = 64 when that still
+//              fills the chip or the basis is Gaussian (project_tile_kernel);
+//              its waves split k in 256-column chunks, which reach LDS through
 //              direct global->LDS loads (whole cache lines per instruction)
 //              while the previous chunk is multiplied.  For the sign basis
 //              each lane regenerates the sign bits of its A row in registers
@@ -21,14 +23,19 @@
 //              stored as a hi/lo bf16 pair in the accumulate kernel's operand
 //              order (one contiguous 1 KB block per 32 tokens x 16 r columns).
 //   accumulate S += dY^T P.  A work-group owns 16*Q columns of d and a range
-//              of 32-token steps.  Each lane loads an 8-token x Q-column block
-//              of dY with row-contiguous loads and transposes it in registers
-//              (v_perm_b32), giving K = token operands for 16x16x32 MFMA
-//              against P_hi and P_lo.  Waves split the steps (and, above
-//              r = 64, the rank) and are summed in LDS in a fixed order; with
-//              several work-groups along T each writes its partial tile, and
+//              of 32-token steps (accumulate_kernel).  Each lane loads an
+//              8-token x Q-column block of dY with row-contiguous loads and
+//              transposes it in registers (v_perm_b32), giving K = token
+//              operands for 16x16x32 MFMA against P_hi and P_lo.  Waves split
+//              the steps (and, above r = 64, the rank) and are summed in LDS
+//              in a fixed order.  From r = 128 at T >= 16384 a work-group
+//              instead owns 2 or 4 such column groups and all of r, with dY
+//              and P staged once per step in LDS for all its waves
+//              (accumulate_wide_kernel).  With several work-groups along T
+//              each writes its partial tile, and
 //   finalize   adds the partial tiles to S in split order.  S is therefore
-//              bit-reproducible.
+//              bit-reproducible.  With the overwrite flag the kernel that
+//              writes S stores the result instead of adding it.
 // The Gaussian basis is first written once per call as a bf16 r x k matrix in
 // the workspace (Box-Muller per entry is too costly to repeat per token
 // block) and the project kernel reads its operand tiles from there.
