@@ -150,8 +150,14 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 // an MFMA operand (element 2p in the low half of dword p).  With
 // x = b | (b << 15), bit 2p of b sits at 2p and bit 2p+1 at 2p+16; shifting
 // left by 15 - 2p moves them to bits 15 and 31, the two bf16 sign positions.
+// x passes through an empty asm statement so the compiler no longer knows
+// that b < 256: with that knowledge it rewrites each shift of x as a
+// multiply of b by 2^n + 2^(n + 15), a quarter-rate v_mul_lo_u32 in place of
+// a full-rate shift (measured neutral in the kernels, which are not bound by
+// VALU issue, but never slower).
 __device__ __forceinline__ u32x4 signs_to_bf16x8(uint32_t byte) {
-  const uint32_t x = byte | (byte << 15);
+  uint32_t x = byte | (byte << 15);
+  asm("" : "+v"(x));
   u32x4 v;
   v[0] = ((x << 15) & 0x80008000u) | 0x3F803F80u;
   v[1] = ((x << 13) & 0x80008000u) | 0x3F803F80u;
