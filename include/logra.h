@@ -32,6 +32,13 @@
  *   - Calls that share an output buffer (S, W) must be ordered by the caller
  *     (same stream or events).  Two concurrent calls must not share a
  *     workspace.
+ *   - Two environment variables, read at every call, override the choice
+ *     among equivalent kernels (results agree to fp32 rounding; meant for
+ *     testing): LOGRA_PROJECT_TILE=0/2 never/always uses the 64-token
+ *     projection tile, LOGRA_ACC_WIDE=0/2 never/always uses the
+ *     work-group-wide accumulate kernel at r > 64.  The latter changes the
+ *     workspace size, so it must not change between logra_sketch_ws_bytes
+ *     (or logra_sketch_shared_ws_bytes) and the call the workspace serves.
  */
 #ifndef LOGRA_H
 #define LOGRA_H
