@@ -189,6 +189,21 @@ SHARED_CASES = [
 ]
 
 
+SHARED_WIDE_CASES = [
+    # outputs with odd and even d-group counts, so work-groups of the wide
+    # accumulate kernel stop at each output's last group
+    (512, 256, (256, 64, 136), 256, 0),      # 2, 1, 2 groups at 2 per work-group
+    (300, 520, (300, 1030), 128, 0),         # 3 and 9 groups at 4 per work-group, ragged T
+    (129, 1000, (256, 100, 384, 17), 256, 1),
+]
+
+
+@pytest.mark.parametrize("T,k,ds,r,kind", SHARED_WIDE_CASES)
+def test_sketch_shared_wide_accumulate(lg, monkeypatch, T, k, ds, r, kind):
+    monkeypatch.setenv("LOGRA_ACC_WIDE", "2")
+    test_sketch_shared_matches_oracle_and_single_calls(lg, T, k, ds, r, kind)
+
+
 @pytest.mark.parametrize("T,k,ds,r,kind", SHARED_CASES)
 def test_sketch_shared_matches_oracle_and_single_calls(lg, T, k, ds, r, kind):
     say("sketch shared", T, k, ds, r, kind)
