@@ -65,8 +65,11 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   // registers (4 NT NKS u32x4 per lane: large ranks use NT = 2 to fit); with
   // NT = 4 and r > 64 they are rebuilt per pass (L2 hits).
   constexpr bool kHoistS = NKS <= 2 || NT <= 2;
-  // rows of this wave all inside d and r a multiple of 32: plain float4 loads
-  const bool s_fast = !MASKED;
+  // rows of this wave all inside d and r a multiple of 32: plain float4 loads.
+  // A rank that is not a multiple of 32 needs only these loads to clear its
+  // K tail; they run once, before the passes, so such ranks still take the
+  // unmasked kernel.
+  const bool s_fast = !MASKED && (r % 32) == 0;
   auto s_raw = [&](int nt, int ks, float v[8]) {
     const int row = row0 + 16 * nt + m;
     if (s_fast) {
@@ -364,10 +367,9 @@ hipError_t launch_merge_t(uint16_t* W, int64_t ldw, const float* S, int d, int k
   const int rows = merge_rows(NKS, gauss);
   const int64_t blocks = (int64_t)((k + kMergeCols - 1) / kMergeCols) * ((d + rows - 1) / rows);
   const dim3 grid((unsigned)blocks);
-  // unmasked when every row block is whole, every 64-column pass is whole (a
-  // short last column block just runs fewer passes) and S rows are whole K
-  // steps
-  const bool masked = (d % rows) != 0 || (k % kPassCols) != 0 || (r % 32) != 0;
+  // unmasked when every row block is whole and every 64-column pass is whole
+  // (a short last column block just runs fewer passes)
+  const bool masked = (d % rows) != 0 || (k % kPassCols) != 0;
   if (masked) launch_merge_m<NKS, true>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
   else launch_merge_m<NKS, false>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
   return hipGetLastError();

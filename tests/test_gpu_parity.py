@@ -400,6 +400,12 @@ MERGE_CASES = [
     (200, 300, 64, 0, 1.0, 1e-3),
     (512, 768, 64, 1, 1.0, 1e-3),
     (640, 512, 64, 1, 0.5, 1e-3),
+    # whole tiles with a rank that is not a multiple of 32 (unmasked kernel,
+    # K tail cleared in the S loads)
+    (384, 1024, 24, 0, 1.0, 1e-3),
+    (512, 768, 100, 0, 1.0, 1e-3),
+    (256, 512, 200, 1, 1.0, 1e-3),
+    (128, 64, 1, 0, 1.0, 1e-2),
 ]
 
 
