@@ -41,6 +41,8 @@
 // block) and the project kernel reads its operand tiles from there.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -96,7 +98,6 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
   const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
   const int step = xcd_spread((int)blockIdx.x, (int)blockIdx.x >> 3, (int)gridDim.x);
   const int t0 = step * 32;
-  const bool trow = !MASKED || t0 + m < T;
   const int n_chunks = (k + 255) >> 8;
   unsigned char* buf0 = stage0[wave];
   unsigned char* buf1 = stage1[wave];
@@ -120,10 +121,8 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
       const int j = (lane & 15) ^ (row & 15);
       int t = t0 + row;
       int col = colbase + 8 * j;
-      if (MASKED) {
-        t = t < T ? t : T - 1;
-        col = col < k ? col : 0;
-      }
+      if (t0 + 32 > T) t = t < T ? t : T - 1;                       // ragged block only
+      if (MASKED && (cnk + 1) * 256 > k) col = col < k ? col : 0;   // ragged chunk only
       __builtin_amdgcn_global_load_lds(
           (const void*)(X + (int64_t)t * ldx + col),
           (lds_void*)(dst + i * 1024), 16, 0, 0);
@@ -157,13 +156,17 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
 
   // K assignment: in step s of half hc, lane half h carries columns
   // 256 ch + 128 hc + 64 h + 8 s + (0..7) - byte s of sign word 2 hc + h.
+  // Columns past k (ragged k only, MASKED) are cleared in the last chunk.
+  // Token rows past T need no mask: their copies re-read row T - 1 and the
+  // store below writes zeros for them.
   auto compute = [&](int ch, int hc, const unsigned char* buf) {
     const int colq = ch * 256 + hc * kHalfCols + 64 * h;
+    const bool edge = MASKED && (ch + 1) * 256 > k;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int slot = (8 * h + s) ^ (m & 15);
       u32x4 a = *reinterpret_cast<const u32x4*>(buf + m * (kHalfCols * 2) + slot * 16);
-      if (MASKED) a &= keep_mask8(trow ? k - (colq + 8 * s) : 0);
+      if (edge) a &= keep_mask8(k - (colq + 8 * s));
       if constexpr (GAUSS) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -232,6 +235,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
         float p = red[0][idx];
 #pragma unroll
         for (int w = 1; w < kProjWaves; ++w) p += red[w][idx];
+        if (t0 + TPT * tg + u >= T) p = 0.0f;      // token past T
         split_bf16(p * c, hi[u], lo[u]);
       }
       const int u0 = TPT * tg;                 // first token within the step
@@ -280,8 +284,6 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
   const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
   const int blk = xcd_spread((int)blockIdx.x, (int)blockIdx.x >> 3, (int)gridDim.x);
   const int t0 = blk * kTileTokens;
-  const bool trow0 = !MASKED || t0 + m < T;
-  const bool trow1 = !MASKED || t0 + 32 + m < T;
   const int n_chunks = (k + 255) >> 8;
   const int row_base = rpart * NBW * 32;   // first A row of this wave
 
@@ -305,10 +307,8 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
       const int j = (lane & 15) ^ (row & 15);
       int t = t0 + row;
       int col = colbase + 8 * j;
-      if (MASKED) {
-        t = t < T ? t : T - 1;
-        col = col < k ? col : 0;
-      }
+      if (t0 + kTileTokens > T) t = t < T ? t : T - 1;              // ragged tile only
+      if (MASKED && (cnk + 1) * 256 > k) col = col < k ? col : 0;  // ragged chunk only
       lds_dma16((const void*)(X + (int64_t)t * ldx + col),
                 lds_addr(dst + (32 * rpart + 4 * i) * (kHalfCols * 2)));
     }
@@ -338,17 +338,21 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
     }
   };
 
+  // Columns past k cleared in the ragged last chunk only (MASKED); token
+  // rows past T re-read row T - 1 and are zeroed at the store, as in
+  // project_kernel.
   auto compute = [&](int ch, int hc, const unsigned char* buf) {
     const int colq = ch * 256 + hc * kHalfCols + 64 * h;
+    const bool edge = MASKED && (ch + 1) * 256 > k;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int slot = (8 * h + s) ^ (m & 15);
       u32x4 a0 = *reinterpret_cast<const u32x4*>(buf + m * (kHalfCols * 2) + slot * 16);
       u32x4 a1 = *reinterpret_cast<const u32x4*>(buf + (32 + m) * (kHalfCols * 2) + slot * 16);
-      if (MASKED) {
-        const int valid = k - (colq + 8 * s);
-        a0 &= keep_mask8(trow0 ? valid : 0);
-        a1 &= keep_mask8(trow1 ? valid : 0);
+      if (edge) {
+        const u32x4 keep = keep_mask8(k - (colq + 8 * s));
+        a0 &= keep;
+        a1 &= keep;
       }
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
@@ -421,6 +425,7 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
           float p = red[rh * kTileLanes][idx];
 #pragma unroll
           for (int w = 1; w < kTileLanes; ++w) p += red[rh * kTileLanes + w][idx];
+          if (t0 + 32 * tb + 4 * tg + u >= T) p = 0.0f;   // token past T
           split_bf16(p * c, hi[u], lo[u]);
         }
         const int u0 = 4 * tg;
@@ -639,7 +644,12 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   };
   // One step: Q A operands (d rows x tokens, transposed in registers with
   // v_perm from the row loads) against NBW hi/lo pairs of P operands.
-  auto mfma_step = [&](const DyStage<Q>& ds, const u32x4& bh, const u32x4& bl, int nb) {
+  // mc: std::true_type in a work-group whose d group is ragged (the column
+  // masks), std::false_type elsewhere; the pipeline below is instantiated
+  // for both and each work-group runs one.
+  auto mfma_step = [&](auto mc, const DyStage<Q>& ds, const u32x4& bh, const u32x4& bl,
+                       int nb) {
+    constexpr bool MC = decltype(mc)::value;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       // K assignment: lane group g4, element e <-> token tb + e.
@@ -649,7 +659,9 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
         a[u] = __builtin_amdgcn_perm(ds.R[2 * u + 1][q >> 1], ds.R[2 * u][q >> 1],
                                      (q & 1) ? 0x07060302u : 0x05040100u);
       }
-      if (MASKED && q >= qvalid) a = u32x4{0u, 0u, 0u, 0u};   // column past d
+      if constexpr (MC) {
+        if (q >= qvalid) a = u32x4{0u, 0u, 0u, 0u};   // column past d
+      }
       const int i0 = (q * NBW + nb) * 4;
       f32x4 c4 = {acc[i0], acc[i0 + 1], acc[i0 + 2], acc[i0 + 3]};
       c4 = mfma16(a, bh, c4);
@@ -658,13 +670,13 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
       for (int v = 0; v < 4; ++v) acc[i0 + v] = c4[v];
     }
   };
-  auto compute_lds = [&](const DyStage<Q>& ds, int slot) {
+  auto compute_lds = [&](auto mc, const DyStage<Q>& ds, int slot) {
     const unsigned char* base = ring + slot * kSlot + 16 * lane;
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       const u32x4 bh = *reinterpret_cast<const u32x4*>(base + (2 * nb) * 1024);
       const u32x4 bl = *reinterpret_cast<const u32x4*>(base + (2 * nb + 1) * 1024);
-      mfma_step(ds, bh, bl, nb);
+      mfma_step(mc, ds, bh, bl, nb);
     }
   };
 
@@ -678,7 +690,7 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   const int first = s_begin + wl;
   const int n = first < s_end ? (s_end - first + kLanes - 1) / kLanes : 0;
   auto step_of = [&](int jj) { return first + kLanes * jj; };
-  if (n > 0) {
+  auto pipeline = [&](auto mc) {
     DyStage<Q> y0, y1;
     auto wait_slot = [&](int jj) {
       if (jj + 1 < n) vm_wait<kAfterP>();
@@ -693,7 +705,7 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
     __builtin_amdgcn_sched_barrier(0);
     for (int jj = 0; jj < n; jj += 2) {
       wait_slot(jj);
-      compute_lds(y0, 0);
+      compute_lds(mc, y0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (jj + 2 < n) {
         lgkm_wait0();
@@ -703,7 +715,7 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
       __builtin_amdgcn_sched_barrier(0);
       if (jj + 1 < n) {
         wait_slot(jj + 1);
-        compute_lds(y1, 1);
+        compute_lds(mc, y1, 1);
         __builtin_amdgcn_sched_barrier(0);
         if (jj + 3 < n) {
           lgkm_wait0();
@@ -714,6 +726,12 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
       }
     }
     vm_wait<0>();   // the ring is reused below
+  };
+  if (n > 0) {
+    if (MASKED && dc0 + DC > d)
+      pipeline(std::true_type{});
+    else
+      pipeline(std::false_type{});
   }
 
   // Sum over the waves that share an r part, in a fixed order (((l0 + l1) +
@@ -827,15 +845,17 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
   const int dg_local = (wg - wg_first) * DP + dpart;   // this wave's d group in the output
   const bool group_ok = dg_first + dg_local < dg_end;
   const int dc0 = dg_local * 16 * Q;
-  const int qvalid = d - (dc0 + Q * m);   // columns dc0 + Q m + q < d are real
   const int s_begin = sp * steps_per_split;
   const int s_end = min(steps_total, s_begin + steps_per_split);
   const int n = s_end - s_begin;
+  // the masks and clamps matter only on the ragged last step and in
+  // work-groups that reach past d
+  const bool cols_edge = MASKED && col_wg + DP * 16 * Q > d;
 
   // Copies of step `step` into stage st: copy c = j * 8 + wave; the first
   // kDyBytes / 1 KB copies bring dY (row-major, kDyRow bytes per token row;
   // rows past T re-read row T - 1 and columns past d the row's first 8, both
-  // cleared when read back), the rest the step's P blocks (contiguous).
+  // cleared by clear_edges), the rest the step's P blocks (contiguous).
   auto issue = [&](int step, int st) {
     unsigned char* base = lds + st * kStage;
 #pragma unroll
@@ -845,10 +865,8 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
         const int b = c * 1024 + 16 * lane;
         int t = step * 32 + b / kDyRow;
         int col = col_wg + (b % kDyRow) / 2;
-        if (MASKED) {
-          t = t < T ? t : T - 1;
-          col = col < d ? col : 0;
-        }
+        if (MASKED && (step + 1) * 32 > T) t = t < T ? t : T - 1;   // ragged last step only
+        if (cols_edge) col = col < d ? col : 0;
         lds_dma16((const void*)(dY + (int64_t)t * ldd + col), lds_addr(base + c * 1024));
       } else {
         const int cp = c - kDyBytes / 1024;
@@ -862,17 +880,32 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
 #pragma unroll
   for (int i = 0; i < NREGW; ++i) acc[i] = 0.0f;
 
+  // On an edge step (the ragged last step, or any step of a work-group that
+  // reaches past d) the staged dY tile gets its rows past T and columns past
+  // d cleared in LDS, by all threads between two barriers, so compute never
+  // masks.  Pieces wholly inside are left alone.
+  auto clear_edges = [&](int step, int st) {
+    unsigned char* base = lds + st * kStage;
+    for (int p = tid; p < kDyBytes / 16; p += 64 * kAccWaves) {
+      const int row = p / (kDyRow / 16);
+      const int piece = p % (kDyRow / 16);
+      const int valid = step * 32 + row < T ? d - (col_wg + 8 * piece) : 0;
+      if (valid < 8) {
+        u32x4* q4 = reinterpret_cast<u32x4*>(base + p * 16);
+        *q4 = *q4 & keep_mask8(valid);
+      }
+    }
+  };
+
   auto compute = [&](int step, int st) {
     const unsigned char* base = lds + st * kStage;
     // dY rows 8 g4 + e of the step, columns dc0 + Q m .. + 7 (as
     // load_dy_stage gives them), and the wave's P operands
     u32x4 row[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 8; ++e)
       row[e] = *reinterpret_cast<const u32x4*>(base + (8 * g4 + e) * kDyRow + dpart * 256 +
                                                16 * m);
-      if (MASKED && step * 32 + 8 * g4 + e >= T) row[e] = u32x4{0u, 0u, 0u, 0u};
-    }
     u32x4 bh[NBW], bl[NBW];
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
@@ -887,7 +920,6 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
       for (int u = 0; u < 4; ++u)
         a[u] = __builtin_amdgcn_perm(row[2 * u + 1][q >> 1], row[2 * u][q >> 1],
                                      (q & 1) ? 0x07060302u : 0x05040100u);
-      if (MASKED && q >= qvalid) a = u32x4{0u, 0u, 0u, 0u};   // column past d
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         const int i0 = (q * NBW + nb) * 4;
@@ -910,6 +942,10 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
       if (j + 1 < n) vm_wait<kCopiesW>();
       else vm_wait<0>();
       __syncthreads();
+      if (MASKED && (cols_edge || (s_begin + j + 1) * 32 > T)) {   // work-group uniform
+        clear_edges(s_begin + j, j % kStages);
+        __syncthreads();
+      }
       if (j + 2 < n) issue(s_begin + j + 2, (j + 2) % kStages);
       lgkm_wait0();
       compute(s_begin + j, j % kStages);
@@ -1024,7 +1060,7 @@ hipError_t launch_project(const SketchPlan& p, const uint16_t* X, int64_t ldx,
                           float c, const uint16_t* Ab, uint16_t* Pt, hipStream_t s) {
   if constexpr (NB >= 2) {
     if (use_tile_projection(p, NB, gauss)) {
-      const bool tmask = (T % kTileTokens) != 0 || (k % 256) != 0;
+      const bool tmask = (k % 256) != 0;   // ragged T needs no mask (see the kernel)
       const dim3 grid((unsigned)((p.t_pad + kTileTokens - 1) / kTileTokens));
       const float cc = gauss ? 1.0f : c;
 #define LOGRA_TILE(G, M)                                                                  \
@@ -1041,7 +1077,7 @@ hipError_t launch_project(const SketchPlan& p, const uint16_t* X, int64_t ldx,
       return hipGetLastError();
     }
   }
-  const bool masked = (T % 32) != 0 || (k % 256) != 0;
+  const bool masked = (k % 256) != 0;   // ragged T needs no mask (see the kernel)
   if (gauss) {
     if (masked) launch_project_t<NB, true, true>(p, X, ldx, T, k, seed, stream, 1.0f, Ab, Pt, s);
     else launch_project_t<NB, true, false>(p, X, ldx, T, k, seed, stream, 1.0f, Ab, Pt, s);
@@ -1066,7 +1102,9 @@ hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, in
                              const uint16_t* Pt, float* part, hipStream_t s) {
   const dim3 grid((unsigned)p.n_dgroups, (unsigned)p.n_split);
   float* pp = p.n_split > 1 ? part : nullptr;
-  bool masked = (T % 32) != 0;
+  // masked for a ragged d group only: rows past T read as zero through the
+  // buffer loads whatever the template
+  bool masked = false;
   for (int o = 0; o < tab.n; ++o) masked = masked || (tab.d[o] % (16 * Q)) != 0;
   if (masked) {
     hipLaunchKernelGGL((accumulate_kernel<Q, NB16, true>), grid, dim3(64 * kAccWaves), 0, s,
