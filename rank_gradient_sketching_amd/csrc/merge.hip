@@ -21,6 +21,8 @@
 //      fp32 and rounds once to bf16 (v_cvt_pk_bf16_f32, ties to even).
 // The M -> column map (m / 4) * 16 + 4 t + m % 4 makes each lane's 16
 // accumulator values land on 16 consecutive columns of one row.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   // Per-wave staging of one pass's results (WR rows x 64 columns, row stride
   // kStRow bf16) for row-contiguous stores (interior tiles only).
   constexpr int kStRow = kPassCols + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t stage[MASKED ? 1 : kWaves * WR * kStRow];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[kWaves * WR * kStRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -59,274 +61,299 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   const int col0 = cb * kMergeCols;
   const int row0 = rblk * (WR * kWaves) + wave * WR;
   const int n_pass = min(kMergeCols / kPassCols, (k - col0 + kPassCols - 1) / kPassCols);
+  // Work-groups holding the ragged last row block or a ragged last column
+  // pass run the masked body; all others the plain one (both are
+  // instantiated in a MASKED kernel, so one ragged edge no longer slows
+  // every work-group).
+  auto body = [&](auto masked_c) {
+    constexpr bool M = decltype(masked_c)::value;
 
-  // S operands: rows row0 + 16 nt + m, K = r columns 32 ks + 8 g + (0..7),
-  // as hi/lo bf16.  They do not depend on the column pass and stay in
-  // registers (4 NT NKS u32x4 per lane: large ranks use NT = 2 to fit); with
-  // NT = 4 and r > 64 they are rebuilt per pass (L2 hits).
-  constexpr bool kHoistS = NKS <= 2 || NT <= 2;
-  // rows of this wave all inside d and r a multiple of 32: plain float4 loads.
-  // A rank that is not a multiple of 32 needs only these loads to clear its
-  // K tail; they run once, before the passes, so such ranks still take the
-  // unmasked kernel.
-  const bool s_fast = !MASKED && (r % 32) == 0;
-  auto s_raw = [&](int nt, int ks, float v[8]) {
-    const int row = row0 + 16 * nt + m;
-    if (s_fast) {
-      const f32x4* sp = reinterpret_cast<const f32x4*>(S + (int64_t)row * r + 32 * ks + 8 * g);
-      const f32x4 a = sp[0], b = sp[1];
+    // S operands: rows row0 + 16 nt + m, K = r columns 32 ks + 8 g + (0..7),
+    // as hi/lo bf16.  They do not depend on the column pass and stay in
+    // registers (4 NT NKS u32x4 per lane: large ranks use NT = 2 to fit); with
+    // NT = 4 and r > 64 they are rebuilt per pass (L2 hits).
+    constexpr bool kHoistS = NKS <= 2 || NT <= 2;
+    // rows of this wave all inside d and r a multiple of 32: plain float4 loads.
+    // A rank that is not a multiple of 32 needs only these loads to clear its
+    // K tail; they run once, before the passes, so such ranks still take the
+    // unmasked kernel.
+    const bool s_fast = !M && (r % 32) == 0;
+    auto s_raw = [&](int nt, int ks, float v[8]) {
+      const int row = row0 + 16 * nt + m;
+      if (s_fast) {
+        const f32x4* sp = reinterpret_cast<const f32x4*>(S + (int64_t)row * r + 32 * ks + 8 * g);
+        const f32x4 a = sp[0], b = sp[1];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = a[e];
-        v[4 + e] = b[e];
-      }
-    } else {
-      const int rr = row < d ? row : d - 1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int rc = 32 * ks + 8 * g + e;
-        const float x = S[(int64_t)rr * r + (rc < r ? rc : r - 1)];
-        v[e] = (row < d && rc < r) ? x : 0.0f;
-      }
-    }
-  };
-  auto s_split = [&](const float v[8], u32x4& hi, u32x4& lo) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint16_t h0, l0, h1, l1;
-      split_bf16(v[2 * p], h0, l0);
-      split_bf16(v[2 * p + 1], h1, l1);
-      hi[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      lo[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
-  };
-  auto s_operands = [&](int nt, int ks, u32x4& hi, u32x4& lo) {
-    float v[8];
-    s_raw(nt, ks, v);
-    s_split(v, hi, lo);
-  };
-  u32x4 sh[NT][kHoistS ? NKS : 1], sl[NT][kHoistS ? NKS : 1];
-
-  // Sign basis: thread tid < RP / 2 draws the Philox blocks of A rows 2 tid
-  // and 2 tid + 1 for this 256-column block and parks their words in LDS,
-  // word-major (sgn[q * RP + i] = word q of row i: columns 64 q .. 64 q + 63).
-  auto sign_words = [&]() {
-    if (!GAUSS && tid < RP / 2) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int i = 2 * tid + h;
-        Words4 b = {{0, 0, 0, 0}};
-        if (i < r) b = sign_block(seed, stream, (uint64_t)cb, (uint64_t)i);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sgn[q * RP + i] = b.w[q];
-      }
-    }
-  };
-
-  // A slice of pass p into LDS: buf[col * LDA + i] = A[i][col0 + 64 p + col].
-  // Sign basis: every thread takes (8-row group G, column c) jobs: it reads the
-  // eight words of rows 8G .. 8G + 7 (one broadcast read per wave), gathers
-  // their bit c into one byte and expands it to eight +-1 bf16 (rows >= r: 0).
-  auto build_A = [&](int pass, uint16_t* buf) {
-    const int c0 = col0 + pass * kPassCols;
-    if (GAUSS) {
-      for (int job = tid; job < RP * (kPassCols / 4); job += 64 * kWaves) {
-        const int i = job / (kPassCols / 4);
-        const int cc = 4 * (job % (kPassCols / 4));
-        uint16_t v[4] = {0, 0, 0, 0};
-        if (i < r && c0 + cc < k) {
-          gaussian_entries_bf16(seed, stream, (uint64_t)((c0 + cc) >> 2),
-                                (uint64_t)i, cr, v);
+        for (int e = 0; e < 4; ++e) {
+          v[e] = a[e];
+          v[4 + e] = b[e];
+        }
+      } else if ((r % 32) == 0) {   // only rows past d to clear
+        f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+        if (row < d) {
+          const f32x4* sp = reinterpret_cast<const f32x4*>(S + (int64_t)row * r + 32 * ks + 8 * g);
+          a = sp[0];
+          b = sp[1];
         }
 #pragma unroll
-        for (int a = 0; a < 4; ++a) buf[(cc + a) * LDA + i] = v[a];
+        for (int e = 0; e < 4; ++e) {
+          v[e] = a[e];
+          v[4 + e] = b[e];
+        }
+      } else {
+        const int rr = row < d ? row : d - 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int rc = 32 * ks + 8 * g + e;
+          const float x = S[(int64_t)rr * r + (rc < r ? rc : r - 1)];
+          v[e] = (row < d && rc < r) ? x : 0.0f;
+        }
       }
-    } else {
-      constexpr int kJobs = kPassCols * (RP / 8);
+    };
+    auto s_split = [&](const float v[8], u32x4& hi, u32x4& lo) {
 #pragma unroll
-      for (int job = tid; job < kJobs; job += 64 * kWaves) {
-        const int c = job & (kPassCols - 1);
-        const int grp = job / kPassCols;
-        const uint32_t* wp = reinterpret_cast<const uint32_t*>(&sgn[pass * RP + 8 * grp]);
-        const int half = c >> 5;           // which dword of each 64-bit word
-        const int bit = c & 31;
-        uint32_t byte = 0;
+      for (int p = 0; p < 4; ++p) {
+        uint16_t h0, l0, h1, l1;
+        split_bf16(v[2 * p], h0, l0);
+        split_bf16(v[2 * p + 1], h1, l1);
+        hi[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+    };
+    auto s_operands = [&](int nt, int ks, u32x4& hi, u32x4& lo) {
+      float v[8];
+      s_raw(nt, ks, v);
+      s_split(v, hi, lo);
+    };
+    u32x4 sh[NT][kHoistS ? NKS : 1], sl[NT][kHoistS ? NKS : 1];
+
+    // Sign basis: thread tid < RP / 2 draws the Philox blocks of A rows 2 tid
+    // and 2 tid + 1 for this 256-column block and parks their words in LDS,
+    // word-major (sgn[q * RP + i] = word q of row i: columns 64 q .. 64 q + 63).
+    auto sign_words = [&]() {
+      if (!GAUSS && tid < RP / 2) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) byte |= ((wp[2 * e + half] >> bit) & 1u) << e;
-        u32x4 v = signs_to_bf16x8(byte);
-        const int valid = r - 8 * grp;     // rows of this group below r
-        if (valid < 8) {
+        for (int h = 0; h < 2; ++h) {
+          const int i = 2 * tid + h;
+          Words4 b = {{0, 0, 0, 0}};
+          if (i < r) b = sign_block(seed, stream, (uint64_t)cb, (uint64_t)i);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t keep = (2 * q < valid ? 0x0000FFFFu : 0u) |
-                                  (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
-            v[q] &= keep;
+          for (int q = 0; q < 4; ++q) sgn[q * RP + i] = b.w[q];
+        }
+      }
+    };
+
+    // A slice of pass p into LDS: buf[col * LDA + i] = A[i][col0 + 64 p + col].
+    // Sign basis: every thread takes (8-row group G, column c) jobs: it reads the
+    // eight words of rows 8G .. 8G + 7 (one broadcast read per wave), gathers
+    // their bit c into one byte and expands it to eight +-1 bf16 (rows >= r: 0).
+    auto build_A = [&](int pass, uint16_t* buf) {
+      const int c0 = col0 + pass * kPassCols;
+      if (GAUSS) {
+        for (int job = tid; job < RP * (kPassCols / 4); job += 64 * kWaves) {
+          const int i = job / (kPassCols / 4);
+          const int cc = 4 * (job % (kPassCols / 4));
+          uint16_t v[4] = {0, 0, 0, 0};
+          if (i < r && c0 + cc < k) {
+            gaussian_entries_bf16(seed, stream, (uint64_t)((c0 + cc) >> 2),
+                                  (uint64_t)i, cr, v);
           }
+#pragma unroll
+          for (int a = 0; a < 4; ++a) buf[(cc + a) * LDA + i] = v[a];
         }
-        *reinterpret_cast<u32x4*>(&buf[c * LDA + 8 * grp]) = v;
-      }
-    }
-  };
-
-  // This lane's W elements of pass p: rows row0 + 16 nt + m, columns
-  // col0 + 64 p + 16 g + (0..15).  Rows past d are read from row d - 1 and
-  // never stored; columns past k read as zero.
-  auto load_W = [&](int pass, u32x4 wv[NT][2]) {
-    const int c0 = col0 + pass * kPassCols;
-    const int wc = c0 + 16 * g;
-    if (!MASKED) {
+      } else {
+        constexpr int kJobs = kPassCols * (RP / 8);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const uint16_t* wr = W + (int64_t)(row0 + 16 * nt + m) * ldw;
-        wv[nt][0] = load_bf16x8(wr, wc);
-        wv[nt][1] = load_bf16x8(wr, wc + 8);
-      }
-    } else {
+        for (int job = tid; job < kJobs; job += 64 * kWaves) {
+          const int c = job & (kPassCols - 1);
+          const int grp = job / kPassCols;
+          const uint32_t* wp = reinterpret_cast<const uint32_t*>(&sgn[pass * RP + 8 * grp]);
+          const int half = c >> 5;           // which dword of each 64-bit word
+          const int bit = c & 31;
+          uint32_t byte = 0;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int row = min(row0 + 16 * nt + m, d - 1);
-        const uint16_t* wr = W + (int64_t)row * ldw;
-        wv[nt][0] = load_bf16x8_masked(wr, wc, k);
-        wv[nt][1] = load_bf16x8_masked(wr, wc + 8, k);
-      }
-    }
-  };
-
-  uint16_t* buf0 = At;
-  uint16_t* buf1 = At + (kDouble ? kPassCols * LDA : 0);
-
-  // One column pass: multiply the A slice, update the W elements loaded one
-  // pass earlier (wcur) and, before that, start the loads of the next pass
-  // (wnxt) so they overlap this pass's work.
-  auto do_pass = [&](int pass, u32x4 (&wcur)[NT][2], u32x4 (&wnxt)[NT][2]) {
-    if (!kDouble && pass > 0) {
-      __syncthreads();          // every wave is done reading the previous slice
-      build_A(pass, buf0);
-    }
-    __syncthreads();            // slice `pass` is complete
-    if (pass + 1 < n_pass) {
-      load_W(pass + 1, wnxt);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kDouble) build_A(pass + 1, (pass & 1) ? buf0 : buf1);
-    }
-    const uint16_t* cur_buf = (kDouble && (pass & 1)) ? buf1 : buf0;
-
-    // MFMA: acc[t][nt] rows m' = 4 g' + v map to columns c0 + 16 g' + 4 t + v.
-    f32x4 acc[4][NT];
+          for (int e = 0; e < 8; ++e) byte |= ((wp[2 * e + half] >> bit) & 1u) << e;
+          u32x4 v = signs_to_bf16x8(byte);
+          const int valid = r - 8 * grp;     // rows of this group below r
+          if (valid < 8) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 bh[NT], bl[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if constexpr (kHoistS) {
-          bh[nt] = sh[nt][ks];
-          bl[nt] = sl[nt][ks];
-        } else {
-          s_operands(nt, ks, bh[nt], bl[nt]);
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t keep = (2 * q < valid ? 0x0000FFFFu : 0u) |
+                                    (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
+              v[q] &= keep;
+            }
+          }
+          *reinterpret_cast<u32x4*>(&buf[c * LDA + 8 * grp]) = v;
         }
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int cc = (m >> 2) * 16 + 4 * t + (m & 3);
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(&cur_buf[cc * LDA + 32 * ks + 8 * g]);
+    };
+
+    // This lane's W elements of pass p: rows row0 + 16 nt + m, columns
+    // col0 + 64 p + 16 g + (0..15).  Rows past d are read from row d - 1 and
+    // never stored; columns past k read as zero.
+    auto load_W = [&](int pass, u32x4 wv[NT][2]) {
+      const int c0 = col0 + pass * kPassCols;
+      const int wc = c0 + 16 * g;
+      if (!M) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          acc[t][nt] = mfma16(a, bh[nt], acc[t][nt]);
-          acc[t][nt] = mfma16(a, bl[nt], acc[t][nt]);
+          const uint16_t* wr = W + (int64_t)(row0 + 16 * nt + m) * ldw;
+          wv[nt][0] = load_bf16x8(wr, wc);
+          wv[nt][1] = load_bf16x8(wr, wc + 8);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int row = min(row0 + 16 * nt + m, d - 1);
+          const uint16_t* wr = W + (int64_t)row * ldw;
+          wv[nt][0] = load_bf16x8_masked(wr, wc, k);
+          wv[nt][1] = load_bf16x8_masked(wr, wc + 8, k);
         }
       }
-    }
+    };
 
-    // Update and store.
-    const int wc = col0 + pass * kPassCols + 16 * g;
+    uint16_t* buf0 = At;
+    uint16_t* buf1 = At + (kDouble ? kPassCols * LDA : 0);
+
+    // One column pass: multiply the A slice, update the W elements loaded one
+    // pass earlier (wcur) and, before that, start the loads of the next pass
+    // (wnxt) so they overlap this pass's work.
+    auto do_pass = [&](int pass, u32x4 (&wcur)[NT][2], u32x4 (&wnxt)[NT][2]) {
+      if (!kDouble && pass > 0) {
+        __syncthreads();          // every wave is done reading the previous slice
+        build_A(pass, buf0);
+      }
+      __syncthreads();            // slice `pass` is complete
+      if (pass + 1 < n_pass) {
+        load_W(pass + 1, wnxt);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kDouble) build_A(pass + 1, (pass & 1) ? buf0 : buf1);
+      }
+      const uint16_t* cur_buf = (kDouble && (pass & 1)) ? buf1 : buf0;
+
+      // MFMA: acc[t][nt] rows m' = 4 g' + v map to columns c0 + 16 g' + 4 t + v.
+      f32x4 acc[4][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int row = row0 + 16 * nt + m;
-      u32x4 out[2];
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+        for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          // element e = 8 hh + 2 p (+1) of the lane's 16 columns = 4 t + v
-          const int e0 = 8 * hh + 2 * p;
-          const int e1 = e0 + 1;
-          const float w0 = bf16_lo(wcur[nt][hh][p]);
-          const float w1 = bf16_hi(wcur[nt][hh][p]);
-          const float n0 = w0 - scale * acc[e0 >> 2][nt][e0 & 3];
-          const float n1 = w1 - scale * acc[e1 >> 2][nt][e1 & 3];
-          out[hh][p] = pack_bf16x2(n0, n1);
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 bh[NT], bl[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if constexpr (kHoistS) {
+            bh[nt] = sh[nt][ks];
+            bl[nt] = sl[nt][ks];
+          } else {
+            s_operands(nt, ks, bh[nt], bl[nt]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int cc = (m >> 2) * 16 + 4 * t + (m & 3);
+          const u32x4 a =
+              *reinterpret_cast<const u32x4*>(&cur_buf[cc * LDA + 32 * ks + 8 * g]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc[t][nt] = mfma16(a, bh[nt], acc[t][nt]);
+            acc[t][nt] = mfma16(a, bl[nt], acc[t][nt]);
+          }
         }
       }
-      if constexpr (!MASKED) {
-        uint16_t* stg = stage + (wave * WR + 16 * nt + m) * kStRow + 16 * g;
-        *reinterpret_cast<u32x4*>(stg) = out[0];
-        *reinterpret_cast<u32x4*>(stg + 8) = out[1];
-      } else if (row < d) {
-        uint16_t* wr = W + (int64_t)row * ldw;
+
+      // Update and store.
+      const int wc = col0 + pass * kPassCols + 16 * g;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int row = row0 + 16 * nt + m;
+        u32x4 out[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int cbeg = wc + 8 * hh;
-          if (!MASKED || cbeg + 8 <= k) {
-            *reinterpret_cast<u32x4*>(wr + cbeg) = out[hh];
-          } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (cbeg + e < k) {
-                const uint32_t dw = out[hh][e >> 1];
-                wr[cbeg + e] = (uint16_t)((e & 1) ? (dw >> 16) : (dw & 0xFFFFu));
+          for (int p = 0; p < 4; ++p) {
+            // element e = 8 hh + 2 p (+1) of the lane's 16 columns = 4 t + v
+            const int e0 = 8 * hh + 2 * p;
+            const int e1 = e0 + 1;
+            const float w0 = bf16_lo(wcur[nt][hh][p]);
+            const float w1 = bf16_hi(wcur[nt][hh][p]);
+            const float n0 = w0 - scale * acc[e0 >> 2][nt][e0 & 3];
+            const float n1 = w1 - scale * acc[e1 >> 2][nt][e1 & 3];
+            out[hh][p] = pack_bf16x2(n0, n1);
+          }
+        }
+        if constexpr (!M) {
+          uint16_t* stg = stage + (wave * WR + 16 * nt + m) * kStRow + 16 * g;
+          *reinterpret_cast<u32x4*>(stg) = out[0];
+          *reinterpret_cast<u32x4*>(stg + 8) = out[1];
+        } else if (row < d) {
+          uint16_t* wr = W + (int64_t)row * ldw;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int cbeg = wc + 8 * hh;
+            if (!M || cbeg + 8 <= k) {
+              *reinterpret_cast<u32x4*>(wr + cbeg) = out[hh];
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                if (cbeg + e < k) {
+                  const uint32_t dw = out[hh][e >> 1];
+                  wr[cbeg + e] = (uint16_t)((e & 1) ? (dw >> 16) : (dw & 0xFFFFu));
+                }
               }
             }
           }
         }
       }
-    }
-    // Interior tiles: the wave reads its WR x 64 results back row by row,
-    // eight lanes per row, so every store writes whole 128-byte lines (stores
-    // of half lines, as the MFMA layout gives them, measured ~10 % slower).
-    // A wave only touches its own staging rows and LDS operations of a wave
-    // complete in order, so no barrier is needed.
-    if constexpr (!MASKED) {
-      const int pc = lane & 7;
+      // Interior tiles: the wave reads its WR x 64 results back row by row,
+      // eight lanes per row, so every store writes whole 128-byte lines (stores
+      // of half lines, as the MFMA layout gives them, measured ~10 % slower).
+      // A wave only touches its own staging rows and LDS operations of a wave
+      // complete in order, so no barrier is needed.
+      if constexpr (!M) {
+        const int pc = lane & 7;
 #pragma unroll
-      for (int i = 0; i < WR / 8; ++i) {
-        const int rr = 8 * i + (lane >> 3);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (wave * WR + rr) * kStRow + 8 * pc);
-        *reinterpret_cast<u32x4*>(W + (int64_t)(row0 + rr) * ldw + col0 + pass * kPassCols + 8 * pc) = v;
+        for (int i = 0; i < WR / 8; ++i) {
+          const int rr = 8 * i + (lane >> 3);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (wave * WR + rr) * kStRow + 8 * pc);
+          *reinterpret_cast<u32x4*>(W + (int64_t)(row0 + rr) * ldw + col0 + pass * kPassCols + 8 * pc) = v;
+        }
       }
-    }
-  };
+    };
 
-  // Prologue: start the loads first (S rows, then the W elements of pass 0),
-  // regenerate the signs and the first A slice while they are in flight, and
-  // only then wait for S.
-  u32x4 wa[NT][2], wb[NT][2];
-  float sraw[NT][kHoistS ? NKS : 1][8];
-  if constexpr (kHoistS) {
+    // Prologue: start the loads first (S rows, then the W elements of pass 0),
+    // regenerate the signs and the first A slice while they are in flight, and
+    // only then wait for S.
+    u32x4 wa[NT][2], wb[NT][2];
+    float sraw[NT][kHoistS ? NKS : 1][8];
+    if constexpr (kHoistS) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) s_raw(nt, ks, sraw[nt][ks]);
-  }
-  load_W(0, wa);
-  __builtin_amdgcn_sched_barrier(0);
-  sign_words();
-  __syncthreads();
-  build_A(0, buf0);
-  if constexpr (kHoistS) {
+        for (int ks = 0; ks < NKS; ++ks) s_raw(nt, ks, sraw[nt][ks]);
+    }
+    load_W(0, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    sign_words();
+    __syncthreads();
+    build_A(0, buf0);
+    if constexpr (kHoistS) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) s_split(sraw[nt][ks], sh[nt][ks], sl[nt][ks]);
-  }
-  do_pass(0, wa, wb);
-  if (n_pass > 1) do_pass(1, wb, wa);
-  if (n_pass > 2) do_pass(2, wa, wb);
-  if (n_pass > 3) do_pass(3, wb, wa);
+        for (int ks = 0; ks < NKS; ++ks) s_split(sraw[nt][ks], sh[nt][ks], sl[nt][ks]);
+    }
+    do_pass(0, wa, wb);
+    if (n_pass > 1) do_pass(1, wb, wa);
+    if (n_pass > 2) do_pass(2, wa, wb);
+    if (n_pass > 3) do_pass(3, wb, wa);
+  };
+  const bool edge = MASKED && ((rblk + 1) * (WR * kWaves) > d ||
+                               col0 + n_pass * kPassCols > k);
+  if (edge)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
 }
 
 // Rows per work-group and per wave (16 NT).  Up to r = 64 with the sign
