@@ -33,7 +33,7 @@ def common_flags():
             f"-I{INCLUDE}", f"-I{CSRC}",
             # packed fp32 VALU ops stay disabled in every kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument"]
+            "-Wall", "-Wextra", "-Wno-unused-command-line-argument"]
 
 
 def _compile(src):

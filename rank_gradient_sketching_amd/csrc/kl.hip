@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
     kl_group(st, z, zq, 8, l2t, inv_tau);
   }
   const int tail = V - 8 * nfull;
-  if (tail > 0 && threadIdx.x == (nfull % kKlThreads)) {
+  if (tail > 0 && (int)threadIdx.x == nfull % kKlThreads) {
     float z[8], zq[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
     sw_group(st, zz, dd, 8, l2t, inv_tau, thr, al);
   }
   const int tail = V - 8 * nfull;
-  if (tail > 0 && threadIdx.x == (nfull % kSwThreads)) {
+  if (tail > 0 && (int)threadIdx.x == nfull % kSwThreads) {
     float zz[8], dd[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

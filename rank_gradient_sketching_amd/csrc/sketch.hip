@@ -897,7 +897,7 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
     }
   };
 
-  auto compute = [&](int step, int st) {
+  auto compute = [&](int st) {
     const unsigned char* base = lds + st * kStage;
     // dY rows 8 g4 + e of the step, columns dc0 + Q m .. + 7 (as
     // load_dy_stage gives them), and the wave's P operands
@@ -948,7 +948,7 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
       }
       // multiply first, then issue step j + 2's copies (measured 1-4 %
       // faster than issuing them ahead of the MFMAs)
-      compute(s_begin + j, j % kStages);
+      compute(j % kStages);
       if (j + 2 < n) issue(s_begin + j + 2, (j + 2) % kStages);
     }
   }
