@@ -341,7 +341,20 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
   // Columns past k cleared in the ragged last chunk only (MASKED); token
   // rows past T re-read row T - 1 and are zeroed at the store, as in
   // project_kernel.
-  auto compute = [&](int ch, int hc, const unsigned char* buf) {
+  // Gaussian basis with one 32-row block per wave (r = 64): the half-step's
+  // eight operands come from L2, loaded one half-step ahead into one of two
+  // register sets (gb_a / gb_b below) so their latency hides behind the
+  // previous half-step's MFMAs; wider Gaussian ranks load them in place.
+  constexpr bool kPrefetchB = GAUSS && NBW == 1;
+  typedef u32x4 GbSet[kPrefetchB ? 8 : 1];
+  auto load_gb = [&](int ch, int hc, GbSet& dst) {
+    if constexpr (kPrefetchB) {
+      const uint16_t* src = Ab + (int64_t)(row_base + m) * lda + ch * 256 + hc * kHalfCols + 64 * h;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const u32x4*>(src + 8 * s);
+    }
+  };
+  auto compute = [&](int ch, int hc, const unsigned char* buf, const GbSet& gbc) {
     const int colq = ch * 256 + hc * kHalfCols + 64 * h;
     const bool edge = MASKED && (ch + 1) * 256 > k;
 #pragma unroll
@@ -357,7 +370,9 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         u32x4 b;
-        if constexpr (GAUSS) {
+        if constexpr (kPrefetchB) {
+          b = gbc[s];
+        } else if constexpr (GAUSS) {
           b = *reinterpret_cast<const u32x4*>(Ab + (int64_t)(row_base + nb * 32 + m) * lda +
                                               colq + 8 * s);
         } else {
@@ -376,22 +391,41 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
   auto phys = [&](int cc) { cc += rot; return cc < n_chunks ? cc : cc - n_chunks; };
   const int n_mine = cl < n_chunks ? (n_chunks - cl + kTileLanes - 1) / kTileLanes : 0;
   const int n_steps = 2 * ((n_chunks + kTileLanes - 1) / kTileLanes);
-  if (n_mine > 0) issue(phys(cl), 0, stage[cl][0]);
-  for (int step = 0; step < n_steps; ++step) {
+  // One half-step; with the prefetch the loop below runs them in pairs
+  // (n_steps is even) so the two operand sets swap roles at compile time.
+  GbSet gb_a, gb_b;
+  auto half_step = [&](int step, const GbSet& cur, GbSet& nxt) {
     const int jc = step >> 1;
     const int hc = step & 1;
-    vm_wait<0>();       // this wave's copies for the step have landed
+    vm_wait<0>();       // this wave's copies (and operand loads) for the step have landed
     __syncthreads();    // ... and its partner's; the other buffer is free
     const int nj = (step + 1) >> 1;
-    if (nj < n_mine) issue(phys(cl + kTileLanes * nj), (step + 1) & 1, stage[cl][(step + 1) & 1]);
+    if (nj < n_mine) {
+      issue(phys(cl + kTileLanes * nj), (step + 1) & 1, stage[cl][(step + 1) & 1]);
+      load_gb(phys(cl + kTileLanes * nj), (step + 1) & 1, nxt);
+    }
     if (jc < n_mine) {
       const int pc = phys(cl + kTileLanes * jc);
       if constexpr (!GAUSS) {
         if (hc == 0) sign_words(pc);
       }
       lgkm_wait0();
-      compute(pc, hc, stage[cl][hc]);
+      compute(pc, hc, stage[cl][hc], cur);
     }
+  };
+  if (n_mine > 0) {
+    issue(phys(cl), 0, stage[cl][0]);
+    load_gb(phys(cl), 0, gb_a);
+  }
+  if constexpr (kPrefetchB) {
+    for (int step = 0; step < n_steps; step += 2) {
+      half_step(step, gb_a, gb_b);
+      half_step(step + 1, gb_b, gb_a);
+    }
+  } else {
+    // (unrolled by two, the other variants ran out of registers: the
+    // Gaussian r = 256 tile measured 128 -> 164 us)
+    for (int step = 0; step < n_steps; ++step) half_step(step, gb_a, gb_b);
   }
   vm_wait<0>();
 
