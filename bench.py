@@ -19,6 +19,7 @@ own throughput on the host cores.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-kl] [--no-cpu]
 """
 import argparse
+import gc
 import json
 import os
 import sys
@@ -324,16 +325,22 @@ def run_layer_set(lg, synth, reps=10, r=64):
     return res
 
 
-def _time_ms(fn, reps):
+def _time_ms(fn, reps, batches=5):
+    """Median over `batches` of the mean time of `reps` back-to-back calls, one
+    event pair per batch: a host stall that lets the GPU run dry moves one
+    batch, not the figure."""
     fn()
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        fn()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / reps
+    per = []
+    for _ in range(batches):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) / reps)
+    return float(np.median(per))
 
 
 def _layer_set_step(lg, synth, wl, cfg, r, kind, stream, n_mb, salt=0):
@@ -559,6 +566,9 @@ def main():
     import rank_gradient_sketching_amd as lg
     from rank_gradient_sketching_amd import synth
 
+    # no cyclic garbage collection inside the timed regions (the bench makes
+    # few objects; tensors are freed by reference count)
+    gc.disable()
     layer, data = run_layer(lg, synth, args.steps, args.warmup)
     kl = None if args.no_kl else run_kl(lg, synth)
     layer_set = None if args.no_layerset else run_layer_set(lg, synth)

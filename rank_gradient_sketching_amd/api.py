@@ -19,12 +19,17 @@ GAUSSIAN = 1
 SKETCH_OVERWRITE = 1      # LOGRA_SKETCH_OVERWRITE: S = ... instead of S += ...
 
 
+# torch's raw current-stream lookup costs well under a microsecond per call; the
+# public torch.cuda.current_stream(device) builds a Stream object (a few us,
+# a quarter of a sketch call's host time at small sizes)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t):
-    return ctypes_stream(torch.cuda.current_stream(t.device))
-
-
-def ctypes_stream(s):
-    return s.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index if t.device.index is not None
+                           else torch.cuda.current_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _require(t, name, dtype, ndim=None):
