@@ -244,6 +244,17 @@ __device__ __forceinline__ int xcd_spread(int i, int salt, int n) {
   return i < (n & ~7) ? ((i & ~7) | ((i + salt) & 7)) : i;
 }
 
+// Work-group L of a launch of n runs on XCD L mod 8.  xcd_runs gives it task
+// (L mod 8) (n8 / 8) + L / 8, n8 = n rounded down to a multiple of 8 (the
+// tail keeps its own index): each XCD takes one contiguous run of tasks.  With
+// tasks numbered split-major (split s, d group g -> s groups + g) the
+// work-groups of an XCD share one or two token splits, and their L2 fetches
+// only those splits' P tiles instead of all of P.
+__device__ __forceinline__ int xcd_runs(int L, int n) {
+  const int n8 = n & ~7;
+  return L < n8 ? (L & 7) * (n8 >> 3) + (L >> 3) : L;
+}
+
 // ---------------------------------------------------------------- LDS DMA
 typedef __attribute__((address_space(3))) void lds_void;
 

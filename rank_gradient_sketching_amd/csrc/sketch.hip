@@ -648,8 +648,10 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   const int wl = wave % kLanes;     // step lane of this wave
   const int m = lane & 15;   // A-operand row group (d columns)
   const int g4 = lane >> 4;  // which 8 tokens of the 32-token step
-  const int sp = blockIdx.y;
-  const int dgg = xcd_spread((int)blockIdx.x, sp, (int)gridDim.x);   // across outputs
+  const int task = xcd_runs((int)(blockIdx.y * gridDim.x + blockIdx.x),
+                            (int)(gridDim.x * gridDim.y));
+  const int sp = task / (int)gridDim.x;
+  const int dgg = task % (int)gridDim.x;   // d group across outputs
   LOGRA_SELECT_OUT(tab, dgg, out);
   const uint16_t* __restrict__ dY = out.dY;
   const int64_t ldd = out.ldd;
@@ -851,8 +853,10 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
   const int rpart = wave / DP;
   const int m = lane & 15;
   const int g4 = lane >> 4;
-  const int sp = blockIdx.y;
-  const int wg = xcd_spread((int)blockIdx.x, sp, (int)gridDim.x);
+  const int task = xcd_runs((int)(blockIdx.y * gridDim.x + blockIdx.x),
+                            (int)(gridDim.x * gridDim.y));
+  const int sp = task / (int)gridDim.x;
+  const int wg = task % (int)gridDim.x;
   // output of this work-group (wave-uniform compares on the table)
   int o_sel = 0;
 #pragma unroll
