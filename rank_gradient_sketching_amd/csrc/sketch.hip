@@ -565,10 +565,11 @@ __device__ __forceinline__ int acc_rcol(int i, int ln) {
   return 16 * ((i >> 2) % NB16) + (ln & 15);
 }
 
-// Registers per round of the cross-wave sum: 32 when every wave holds the
-// whole tile, 64 (or all) when r is split across the waves.
+// Registers per round of the cross-wave sum: 64 when r is split across the
+// waves or when a wave holds four r blocks (the P ring then already takes the
+// 128 KiB that 64 registers of eight waves need), else 32.
 constexpr int acc_round(int nb16) {
-  return acc_rsplit(nb16) == 1 ? 32 : (kAccQ * acc_nbw(nb16) * 4 < 64 ? kAccQ * acc_nbw(nb16) * 4 : 64);
+  return (acc_rsplit(nb16) > 1 || acc_nbw(nb16) == 4) ? 64 : 32;
 }
 
 // LDS bytes of the accumulate kernel: the P ring and the reduction buffer
@@ -771,44 +772,52 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   }
 
   // Sum over the waves that share an r part, in a fixed order (((l0 + l1) +
-  // l2) + ...), CH registers per round through LDS; each wave sums its share
-  // of the round and writes it out: to the partial tile of this split
-  // (register-major, coalesced) or, with a single split, into S.
-  float* red = reinterpret_cast<float*>(lds);
+  // l2) + ...), CH registers per round through LDS as 16-byte quads (four
+  // registers of one lane); each wave sums its share of the round's quads
+  // and writes them out: to the partial tile of this split (register-major,
+  // coalesced) or, with a single split, into S.
+  static_assert(CH % 4 == 0 && NREGW % CH == 0, "whole quads and rounds");
+  constexpr int CQ = CH / 4;                                   // quads per round
+  constexpr int kPerQ = CQ / kLanes > 0 ? CQ / kLanes : 1;     // quads per wave
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
   float* my = part ? part + ((int64_t)sp * gridDim.x + dgg) * (NREG * 64) : nullptr;
-  constexpr int kPer = CH / kLanes > 0 ? CH / kLanes : 1;
   __syncthreads();
 #pragma unroll
   for (int c0 = 0; c0 < NREGW; c0 += CH) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) red[(wave * CH + i) * 64 + lane] = acc[c0 + i];
+    for (int j = 0; j < CQ; ++j)
+      red[(wave * CQ + j) * 64 + lane] =
+          f32x4{acc[c0 + 4 * j], acc[c0 + 4 * j + 1], acc[c0 + 4 * j + 2], acc[c0 + 4 * j + 3]};
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int il = wl * kPer + u;            // register within the round
-      if (il < CH) {
+    for (int u = 0; u < kPerQ; ++u) {
+      const int jq = wl * kPerQ + u;           // quad within the round
+      if (jq < CQ) {
         const int base = rpart * kLanes;       // first wave of this r part
-        float v = red[(base * CH + il) * 64 + lane];
+        f32x4 v = red[(base * CQ + jq) * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kLanes; ++w) v += red[((base + w) * CH + il) * 64 + lane];
-        // wave register c0 + il = (q NBW + nb) 4 + e -> tile register
-        const int lr = c0 + il;
-        const int q = lr / (NBW * 4);
-        const int rem = lr % (NBW * 4);
-        const int i = (q * NB16 + rpart * NBW + (rem >> 2)) * 4 + (rem & 3);
-        if (my) {
-          my[i * 64 + lane] = v;
-        } else {
-          const int drow = acc_drow<Q, NB16>(dc0, i, lane);
-          const int rc = acc_rcol<NB16>(i, lane);
-          if (drow < d && rc < r) {
-            float* sp_ = S + (int64_t)drow * r + rc;
-            *sp_ = tab.overwrite ? v : *sp_ + v;
+        for (int w = 1; w < kLanes; ++w) v += red[((base + w) * CQ + jq) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // wave register c0 + 4 jq + e = (q NBW + nb) 4 + e -> tile register
+          const int lr = c0 + 4 * jq + e;
+          const int q = lr / (NBW * 4);
+          const int rem = lr % (NBW * 4);
+          const int i = (q * NB16 + rpart * NBW + (rem >> 2)) * 4 + (rem & 3);
+          if (my) {
+            my[i * 64 + lane] = v[e];
+          } else {
+            const int drow = acc_drow<Q, NB16>(dc0, i, lane);
+            const int rc = acc_rcol<NB16>(i, lane);
+            if (drow < d && rc < r) {
+              float* sp_ = S + (int64_t)drow * r + rc;
+              *sp_ = tab.overwrite ? v[e] : *sp_ + v[e];
+            }
           }
         }
       }
     }
-    __syncthreads();
+    if (c0 + CH < NREGW) __syncthreads();   // the next round overwrites the buffer
   }
 }
 
