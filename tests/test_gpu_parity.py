@@ -144,6 +144,36 @@ PROJECTION_CASES = [
 ]
 
 
+def _fuzz_shapes(n, seed, budget=1.5e8):
+    """Seeded random small shapes: any rank 1..256 (the padded-rank edges
+    and off-power-of-two values weighted up), ragged T, d and k, both bases,
+    one or two microbatches; the oracle's work T (k + d) r stays under
+    `budget` multiply-adds."""
+    rng = np.random.default_rng(seed)
+    ranks = [1, 2, 3, 5, 8, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 100, 127, 128, 129, 200,
+             255, 256]
+    out = []
+    while len(out) < n:
+        T = int(rng.integers(1, 3001))
+        d = int(rng.integers(1, 2200))
+        k = int(rng.integers(1, 1400))
+        r = int(rng.choice(ranks)) if rng.random() < 0.7 else int(rng.integers(1, 257))
+        if T * (k + d) * r > budget:
+            continue
+        out.append((T, d, k, r, int(rng.integers(0, 2)), int(rng.integers(1, 3))))
+    return out
+
+
+FUZZ_SKETCH = _fuzz_shapes(16, 2027)
+
+
+@pytest.mark.parametrize("T,d,k,r,kind,n_mb", FUZZ_SKETCH)
+def test_sketch_fuzz_small_shapes(lg, T, d, k, r, kind, n_mb):
+    say("sketch fuzz", T, d, k, r, kind, n_mb)
+    _, err, _ = _sketch_case(lg, T, d, k, r, kind, n_mb, seed=77 + T, stream=d % 3)
+    assert err < S_TOL, err
+
+
 @pytest.mark.parametrize("mode", ["0", "2"])
 @pytest.mark.parametrize("T,d,k,r,kind,n_mb", PROJECTION_CASES)
 def test_sketch_both_projection_kernels(lg, monkeypatch, mode, T, d, k, r, kind, n_mb):
@@ -428,6 +458,16 @@ def _merge_case(lg, d, k, r, kind, alpha, eta, seed=1234, stream=0, ld_pad=0):
 def test_merge_matches_oracle(lg, d, k, r, kind, alpha, eta):
     say("merge", d, k, r, kind, alpha, eta)
     _, err = _merge_case(lg, d, k, r, kind, alpha, eta)
+    assert err < W_TOL, err
+
+
+FUZZ_MERGE = [(d, k, r, kind) for (_, d, k, r, kind, _) in _fuzz_shapes(12, 2028, budget=1e12)]
+
+
+@pytest.mark.parametrize("d,k,r,kind", FUZZ_MERGE)
+def test_merge_fuzz_small_shapes(lg, d, k, r, kind):
+    say("merge fuzz", d, k, r, kind)
+    _, err = _merge_case(lg, d, k, r, kind, 1.0, 1e-3, seed=91 + d, stream=k % 3)
     assert err < W_TOL, err
 
 
