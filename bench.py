@@ -134,7 +134,7 @@ def run_layer(lg, synth, steps, warmup):
     step_ms = total_ms / steps
 
     # ---- average duration of each entry point: the same calls back to back
-    # (sketches cycling over the microbatches, merges of the same W), one
+    # (sketches cycling over the microbatches, merges over copies of W), one
     # event pair around each batch, outside the timed steps
     reps = max(steps, 20)
 
@@ -150,7 +150,14 @@ def run_layer(lg, synth, steps, warmup):
 
     sk_us = batch_us(lambda i: lg.sketch_accumulate(Xs[i % n_mb], dYs[i % n_mb], S, seed, stream,
                                                     kind, ws=ws), reps * n_mb)
-    mg_us = batch_us(lambda i: lg.merge(W, S, seed, stream, kind, alpha, eta), reps)
+    # merges cycle over copies of W that together exceed the 256 MB
+    # Infinity Cache, as inside a step (where W was last touched a step
+    # earlier): one W repeated would be served from that cache
+    n_w = max(2, -(-(320 << 20) // (2 * d * k)))
+    Wc = [W.clone() for _ in range(n_w)]
+    mg_us = batch_us(lambda i: lg.merge(Wc[i % n_w], S, seed, stream, kind, alpha, eta),
+                     max(reps, n_w))
+    del Wc
     sb = sketch_bytes(T, d, k, r)
     mb_ = merge_bytes(d, k, r)
     res = dict(
