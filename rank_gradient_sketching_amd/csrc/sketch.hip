@@ -31,8 +31,11 @@
 //              in a fixed order.  From r = 128 at T >= 16384 a work-group
 //              instead owns 2 or 4 such column groups and all of r, with dY
 //              and P staged once per step in LDS for all its waves
-//              (accumulate_wide_kernel).  With several work-groups along T
-//              each writes its partial tile, and
+//              (accumulate_wide_kernel).  Tasks (split, column group) are
+//              numbered split-major and dealt to the XCDs in contiguous runs,
+//              so each XCD's L2 fetches the P tiles of one or two splits.
+//              With several work-groups along T each writes its partial
+//              tile, and
 //   finalize   adds the partial tiles to S in split order.  S is therefore
 //              bit-reproducible.  With the overwrite flag the kernel that
 //              writes S stores the result instead of adding it.

@@ -30,20 +30,31 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
 
+def _code_only(text):
+    """C++ source text without comments and with whitespace runs collapsed,
+    so that edits to comments do not mark the counters stale (the sources
+    hold no string literal that contains a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
-    """sha256 over the HIP / C++ sources of the library, in name order."""
+    """sha256 over the code (comments stripped) of the library's HIP / C++
+    sources, in name order."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
         if path.endswith((".hip", ".hpp", ".cpp", ".h")):
             h.update(os.path.basename(path).encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+            with open(path, encoding="utf-8") as f:
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
