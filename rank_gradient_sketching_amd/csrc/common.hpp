@@ -232,6 +232,14 @@ __device__ __forceinline__ u32x4 load_bf16x8(const uint16_t* row, int col) {
   return *reinterpret_cast<const u32x4*>(row + col);
 }
 
+// 2^x from the hardware instruction alone (v_exp_f32).  It equals exp2f
+// wherever the result is a normal float; results below 2^-126 come out
+// flushed instead of passing through exp2f's subnormal range fix (six more
+// instructions per call).  Used for softmax weights 2^(a - max): a weight
+// below 2^-126 of the row's largest is far under the fp32 resolution of the
+// sums it joins.
+__device__ __forceinline__ float exp2_normal(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- grid order
 // Work-groups are dispatched round-robin over the 8 XCDs, so with a plain
 // index -> tile map XCD x only ever gets tiles whose index is x mod 8.  On

@@ -84,7 +84,7 @@ __device__ __forceinline__ void kl_group(KlState& st, const float* z,
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e < n) {
-      const float w = exp2f(a2[e] - st.m);
+      const float w = exp2_normal(a2[e] - st.m);
       st.s += w;
       st.u1 = fmaf(w, dd[e], st.u1);
       st.u3 = fmaf(w, excess_exp(dd[e]), st.u3);

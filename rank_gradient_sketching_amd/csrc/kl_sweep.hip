@@ -20,8 +20,12 @@
 //         e^t - 1 - t, t = alpha dl),
 //   R(alpha) = sum w (e^(alpha dl) - 1 - alpha dl) over the rare other
 //         elements, evaluated exactly for each multiplier.
-// So an element costs the same ~25 VALU operations whatever the number of
-// multipliers.  States merge by rescaling to the larger running max (shuffles
+// The kernel carries u1, the M_n and the multipliers in units of u = amax dl
+// (|u| <= 1 on the series path, so no power can overflow) and alpha / amax;
+// the products alpha^n M_n are the same.
+// So an element costs the same ~20 VALU operations whatever the number of
+// multipliers (dl is never formed: the moments are taken in units of delta
+// and 1/tau enters each row's finalisation).  States merge by rescaling to the larger running max (shuffles
 // inside a wave, LDS across the four waves of a row); rows are finalised in
 // fp64 and a one-work-group kernel forms the weighted means in a fixed order.
 #include <math.h>
@@ -90,28 +94,30 @@ struct Multipliers {
   float a[LOGRA_MAX_SWEEP];
 };
 
-// Adds n (<= 8) elements: z and dz are the logits and the direction.
+// Adds n (<= 8) elements: z and dz are the logits and the direction.  The
+// direction enters as u = dz su with su = max|alpha| / tau, so |u| <= 1 on
+// the series path (its powers cannot overflow) and the multipliers are
+// as = alpha / max|alpha| (alpha dz / tau = as u).  The weight exponent is
+// z l2t - m in one fma (the running max is taken over z: l2t > 0 and
+// rounding is monotonic, so max(z) l2t rounds to the max of the z l2t).
 template <int NA>
 __device__ __forceinline__ void sw_group(SwState<NA>& st, const float* z, const float* dz,
-                                         int n, float l2t, float inv_tau, float thr,
-                                         const Multipliers& al) {
-  float a2[8], dl[8];
-  float cmax = -INFINITY;
+                                         int n, float l2t, float su, float thr,
+                                         const Multipliers& as) {
+  float zmax = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a2[e] = e < n ? z[e] * l2t : -INFINITY;
-    dl[e] = e < n ? dz[e] * inv_tau : 0.0f;
-    cmax = fmaxf(cmax, a2[e]);
-  }
+  for (int e = 0; e < 8; ++e) zmax = fmaxf(zmax, e < n ? z[e] : -INFINITY);
+  const float cmax = zmax * l2t;
   if (cmax > st.m) {
     sw_scale(st, st.m == -INFINITY ? 0.0f : exp2f(st.m - cmax));
     st.m = cmax;
   }
+  const float nm = -st.m;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e < n) {
-      const float w = exp2f(a2[e] - st.m);
-      const float d = dl[e];
+      const float w = exp2_normal(fmaf(z[e], l2t, nm));
+      const float d = dz[e] * su;
       st.s += w;
       float y = w * d;
       st.u1 += y;
@@ -123,7 +129,7 @@ __device__ __forceinline__ void sw_group(SwState<NA>& st, const float* z, const 
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < NA; ++i) st.r[i] = fmaf(w, sw_excess(al.a[i] * d), st.r[i]);
+        for (int i = 0; i < NA; ++i) st.r[i] = fmaf(w, sw_excess(as.a[i] * d), st.r[i]);
       }
     }
   }
@@ -146,7 +152,7 @@ __device__ __forceinline__ SwState<NA> sw_shfl_xor(const SwState<NA>& st, int of
 template <int NA>
 __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
     const uint16_t* __restrict__ z, const uint16_t* __restrict__ dz, int V, int64_t ld,
-    int n_tok, int na, Multipliers al, float inv_tau, float thr,
+    int n_tok, int na, Multipliers al, float inv_tau, float su, float thr,
     float* __restrict__ kl_out) {
   __shared__ SwState<NA> wst[kSwThreads / 64];
   const int64_t row = blockIdx.x;
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
       dd[2 * p] = bf16_lo(vb[p]);
       dd[2 * p + 1] = bf16_hi(vb[p]);
     }
-    sw_group(st, zz, dd, 8, l2t, inv_tau, thr, al);
+    sw_group(st, zz, dd, 8, l2t, su, thr, al);
   }
   const int tail = V - 8 * nfull;
   if (tail > 0 && (int)threadIdx.x == nfull % kSwThreads) {
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
       zz[e] = e < tail ? bf16_to_f32(zr[8 * nfull + e]) : 0.0f;
       dd[e] = e < tail ? bf16_to_f32(dr[8 * nfull + e]) : 0.0f;
     }
-    sw_group(st, zz, dd, tail, l2t, inv_tau, thr, al);
+    sw_group(st, zz, dd, tail, l2t, su, thr, al);
   }
   // wave reduction (fixed butterfly), then the four waves in order
 #pragma unroll
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       if (i < na) {
-        const double a = al.a[i];
+        const double a = al.a[i];   // alpha / max|alpha|: the moments are in units of u
         double g = t.r[i];
         double an = a * a, fact = 2.0;
 #pragma unroll
@@ -255,10 +261,10 @@ __global__ __launch_bounds__(1024) void kl_sweep_mean_kernel(const float* __rest
 
 template <int NA>
 hipError_t launch_rows(const uint16_t* z, const uint16_t* dz, int n_tok, int vocab,
-                       int64_t ld, int na, const Multipliers& al, float inv_tau,
+                       int64_t ld, int na, const Multipliers& al, float inv_tau, float su,
                        float thr, float* kl_tok, hipStream_t s) {
   hipLaunchKernelGGL((kl_sweep_rows_kernel<NA>), dim3((unsigned)n_tok), dim3(kSwThreads), 0,
-                     s, z, dz, vocab, ld, n_tok, na, al, inv_tau, thr, kl_tok);
+                     s, z, dz, vocab, ld, n_tok, na, al, inv_tau, su, thr, kl_tok);
   return hipGetLastError();
 }
 
@@ -268,19 +274,24 @@ hipError_t launch_kl_sweep(const uint16_t* z, const uint16_t* dz, int n_tok, int
                            int64_t ld, const float* alphas, int n_alpha, float tau,
                            const float* weight, float* kl_mean, float* kl_tok,
                            hipStream_t s) {
-  Multipliers al{};
   float amax = 0.0f;
-  for (int i = 0; i < n_alpha; ++i) {
-    al.a[i] = alphas[i];
-    amax = fmaxf(amax, fabsf(alphas[i]));
-  }
+  for (int i = 0; i < n_alpha; ++i) amax = fmaxf(amax, fabsf(alphas[i]));
   const float inv_tau = 1.0f / tau;
-  const float thr = amax > 0.0f ? 1.0f / amax : INFINITY;   // series where amax |dl| <= 1
+  // u = delta su with su = amax / tau, multipliers alpha / amax: the series
+  // covers |u| <= 1 (amax |delta / tau| <= 1).  All multipliers zero: u =
+  // delta / tau, every element on the series, every KL zero.
+  Multipliers al{};
+  float su = inv_tau, thr = INFINITY;
+  if (amax > 0.0f) {
+    su = (float)((double)amax / (double)tau);
+    thr = 1.0f;
+    for (int i = 0; i < n_alpha; ++i) al.a[i] = (float)((double)alphas[i] / (double)amax);
+  }
   hipError_t e;
-  if (n_alpha <= 1) e = launch_rows<1>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, thr, kl_tok, s);
-  else if (n_alpha <= 2) e = launch_rows<2>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, thr, kl_tok, s);
-  else if (n_alpha <= 4) e = launch_rows<4>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, thr, kl_tok, s);
-  else e = launch_rows<8>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, thr, kl_tok, s);
+  if (n_alpha <= 1) e = launch_rows<1>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
+  else if (n_alpha <= 2) e = launch_rows<2>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
+  else if (n_alpha <= 4) e = launch_rows<4>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
+  else e = launch_rows<8>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kl_sweep_mean_kernel, dim3(1), dim3(1024), 0, s, kl_tok, weight, n_tok,
                      n_alpha, kl_mean);
