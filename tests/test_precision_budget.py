@@ -1,0 +1,104 @@
+"""Precision budget of the GPU path, checked on the CPU against the oracle.
+
+The kernels make three precision choices; each test below emulates the
+alternative in NumPy and shows that it would use up (or exceed) the parity
+tolerance, while the chosen form stays far inside it:
+
+- P = X A^T enters the matrix cores as a hi/lo pair of bf16 values, not as
+  one bf16 value ([LoGRA] Sketch: S += dY^T P accumulated in fp32);
+- the merge takes S as a hi/lo pair of bf16 values ([LoGRA] Sketch:
+  W <- W - alpha eta S A);
+- the predicted KL is formed from one online state (s, u1, u2) with
+  u2 = sum w expm1(d), not as a difference of two fp32 log-sum-exps
+  ([LoGRA] PKL: current vs proposed vocabulary distributions at one
+  temperature).
+
+Tolerances: 2e-3 relative Frobenius error on S and on the merged-W delta,
+1e-3 relative error on each token's KL.
+"""
+import numpy as np
+
+from oracle import bf16 as obf16
+from oracle import kl as okl
+from oracle import merge as omerge
+from oracle import projection as oproj
+from rank_gradient_sketching_amd import synth
+
+S_TOL = 2e-3
+W_TOL = 2e-3
+KL_TOL = 1e-3
+
+
+def rel_fro(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def test_projected_inputs_need_the_hi_lo_split():
+    T, d, k, r = 2048, 512, 1024, 64
+    X = synth.bf16_to_f64(synth.host_normal_bf16((T, k), synth.X_ID, salt=11))
+    dY = synth.bf16_to_f64(synth.host_normal_bf16((T, d), synth.DY_ID, salt=11))
+    A = oproj.projection(1234, 0, 0, r, k)
+    P = X @ A.T
+    hi = obf16.round_f64(P)
+    lo = obf16.round_f64(P - hi)
+    S = dY.T @ P
+    single = rel_fro(dY.T @ hi, S)
+    split = rel_fro(dY.T @ (hi + lo), S)
+    # one bf16: most of the tolerance gone before any accumulation error
+    assert single > 0.5 * S_TOL, single
+    # hi + lo: about 16 significant bits, three orders below the tolerance
+    assert split < 1e-5, split
+
+
+def test_merge_needs_the_hi_lo_split_of_S():
+    d, k, r = 512, 1024, 64
+    W = synth.host_normal_bf16((d, k), synth.W_ID, salt=11)
+    Wb = synth.bf16_bits(W)
+    # a sketch of realistic scale for one step
+    S = synth.host_normal_f32((d, r), synth.S_ID, salt=11, sigma=15.0).numpy().astype(np.float64)
+    A = oproj.projection(1234, 0, 0, r, k)
+    ref = omerge.merged_delta(Wb, S, A, 1.0, 1e-3)
+    hi = obf16.round_f64(S)
+    lo = obf16.round_f64(S - hi)
+    single = rel_fro(omerge.merged_delta(Wb, hi, A, 1.0, 1e-3), ref)
+    split = rel_fro(omerge.merged_delta(Wb, hi + lo, A, 1.0, 1e-3), ref)
+    assert single > W_TOL, single            # fails the tolerance
+    assert split < 0.25 * W_TOL, split       # what remains is W's own rounding
+
+
+def _lane_sums(x):
+    """Row sums as the KL kernels form them: 256 lanes each add their
+    elements in order in fp32, then the lanes' partials are combined."""
+    parts = np.cumsum(x.reshape(x.shape[0], 256, -1), axis=2, dtype=np.float32)[:, :, -1]
+    return np.sum(parts, axis=1, dtype=np.float32)
+
+
+def test_predicted_kl_needs_the_one_pass_form():
+    n, V, tau = 16, 152064, 1.0
+    z = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.Z_ID, salt=3, sigma=3.0))
+    dz = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.DIR_ID, salt=3, sigma=0.05))
+    zp = obf16.round_f64(z + dz)
+    ref = okl.kl_rows(z, zp, tau)
+    a = (z / tau).astype(np.float32)
+    b = (zp / tau).astype(np.float32)
+
+    def lse(x):
+        m = x.max(axis=1)
+        return (m + np.log(_lane_sums(np.exp(x - m[:, None])))).astype(np.float32)
+
+    # difference of two log-sum-exps, each about log V + max: the KL (~1e-3)
+    # is what is left after they cancel
+    la, lb = lse(a), lse(b)
+    p = np.exp(a - la[:, None]).astype(np.float32)
+    naive = _lane_sums(p * (a - b)) + (lb - la)
+    # one pass: w = e^(a - max), d = b - a, KL = log1p(u2/s) - u1/s
+    w = np.exp(a - a.max(axis=1, keepdims=True)).astype(np.float32)
+    d = (b - a).astype(np.float32)
+    s = _lane_sums(w)
+    u1 = _lane_sums(w * d)
+    u2 = _lane_sums(w * np.expm1(d))
+    one = (np.log1p(u2 / s) - u1 / s).astype(np.float32)
+    naive_err = float(np.max(np.abs(naive - ref) / np.abs(ref)))
+    one_err = float(np.max(np.abs(one - ref) / np.abs(ref)))
+    assert naive_err > 0.5 * KL_TOL, naive_err     # under a 2x margin per token
+    assert one_err < KL_TOL / 50, one_err          # over 50x
