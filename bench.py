@@ -148,25 +148,28 @@ def run_layer(lg, synth, steps, warmup):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n * 1e3
 
-    sk_us = batch_us(lambda i: lg.sketch_accumulate(Xs[i % n_mb], dYs[i % n_mb], S, seed, stream,
-                                                    kind, ws=ws), reps * n_mb)
-    # merges cycle over copies of W that together exceed the 256 MB
-    # Infinity Cache, as inside a step (where W was last touched a step
-    # earlier): one W repeated would be served from that cache
-    n_w = max(2, -(-(320 << 20) // (2 * d * k)))
+    # five batches each; the median batch mean is the figure, the minimum is
+    # reported beside it
+    sk_b = [batch_us(lambda i: lg.sketch_accumulate(Xs[i % n_mb], dYs[i % n_mb], S, seed, stream,
+                                                    kind, ws=ws), reps * n_mb) for _ in range(5)]
+    # merges cycle over at least 16 copies of W, 512 MiB in all: twice the
+    # 256 MB Infinity Cache, as inside a step (where W was last touched a
+    # step earlier); one W repeated would be served from that cache
+    n_w = max(16, -(-(512 << 20) // (2 * d * k)))
     Wc = [W.clone() for _ in range(n_w)]
-    mg_us = batch_us(lambda i: lg.merge(Wc[i % n_w], S, seed, stream, kind, alpha, eta),
-                     max(reps, n_w))
+    mg_b = [batch_us(lambda i: lg.merge(Wc[i % n_w], S, seed, stream, kind, alpha, eta),
+                     max(reps, n_w)) for _ in range(5)]
     del Wc
+    sk_us, mg_us = float(np.median(sk_b)), float(np.median(mg_b))
     sb = sketch_bytes(T, d, k, r)
     mb_ = merge_bytes(d, k, r)
     res = dict(
         cfg=cfg, total_ms=total_ms, step_ms=step_ms, wall_ms=wall_ms,
         tokens_per_step=T * n_mb,
-        sketch=dict(us_per_call=sk_us, bytes_per_call=sb,
+        sketch=dict(us_per_call=sk_us, us_min=min(sk_b), bytes_per_call=sb,
                     GBps=sb / (sk_us * 1e-6) / 1e9,
                     tokens_per_s=T / (sk_us * 1e-6)),
-        merge=dict(us_per_call=mg_us, bytes_per_call=mb_,
+        merge=dict(us_per_call=mg_us, us_min=min(mg_b), bytes_per_call=mb_,
                    GBps=mb_ / (mg_us * 1e-6) / 1e9),
         parity=parity)
     res["sketch"]["frac_hbm"] = res["sketch"]["GBps"] / HBM_PEAK_GBPS
@@ -614,8 +617,10 @@ def main():
                    "parallelism": "single-gpu"},
         "sketch": {"tokens_per_s": sk["tokens_per_s"], "GBps": sk["GBps"],
                    "frac_hbm": sk["frac_hbm"], "us_per_call": sk["us_per_call"],
+                   "us_per_call_min": sk["us_min"],
                    **sketch_mfma(cfg["T"], cfg["d"], cfg["k"], cfg["r"], sk["us_per_call"])},
-        "merge": {"GBps": mg["GBps"], "frac_hbm": mg["frac_hbm"], "us_per_call": mg["us_per_call"]},
+        "merge": {"GBps": mg["GBps"], "frac_hbm": mg["frac_hbm"], "us_per_call": mg["us_per_call"],
+                  "us_per_call_min": mg["us_min"]},
         "wall_ms_timed_steps": layer["wall_ms"],
         "roofline": roof,
         "cpu_baseline": cpu,
