@@ -8,8 +8,8 @@
 // proposed update; the mean predicted KL scales as alpha^2 q(D) and the
 // controller sets alpha = min(alpha_max, sqrt(delta / q(D))).
 //
-// One pass over both logit rows, no second read.  With a = z/tau, d = (z' - z)/tau
-// and p = softmax(a):
+// One pass over both logit rows, no second read.  With a = z/tau,
+// d = (z' - z - c)/tau and p = softmax(a):
 //   KL = log E_p[e^d] - E_p[d] = E_p[g] + (log1p(x) - x),
 //   g(d) = e^d - 1 - d >= 0,   x = E_p[e^d - 1] = E_p[d] + E_p[g].
 // Each thread keeps (m, s, u1, u3) = (running max of a in log2 units,
@@ -19,6 +19,13 @@
 // LDS across waves).  Per-row KL goes to kl_tok (or the workspace); a second
 // one-work-group kernel averages the rows in a fixed order in fp64 and
 // applies the controller.
+// c is a per-row reference, the mean of z' - z over the row's first
+// min(V, 64) elements (each wave forms the same value by a butterfly sum).
+// The KL does not change when a constant is added to every z' - z of a row,
+// so c changes nothing in exact arithmetic; it keeps a common offset of the
+// proposed logits (a shift of the whole row, e.g. a bias-like update) out of
+// g, whose fp32 sums would otherwise carry e^c - 1 - c and cancel against
+// log1p(x) - x (an offset of -3 had cost ~40 % of a row's KL).
 #include <math.h>
 
 #include "common.hpp"
@@ -62,16 +69,17 @@ __device__ __forceinline__ float excess_exp(float d) {
   return g;
 }
 
-// Adds n (<= 8) elements to the state; z and zq are bf16 pairs.
+// Adds n (<= 8) elements to the state; z and zq are bf16 pairs, dref the
+// row's reference difference.
 __device__ __forceinline__ void kl_group(KlState& st, const float* z,
                                          const float* zq, int n, float l2t,
-                                         float inv_tau) {
+                                         float inv_tau, float dref) {
   float a2[8], dd[8];
   float cmax = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     a2[e] = e < n ? z[e] * l2t : -INFINITY;
-    dd[e] = e < n ? (zq[e] - z[e]) * inv_tau : 0.0f;
+    dd[e] = e < n ? ((zq[e] - z[e]) - dref) * inv_tau : 0.0f;
     cmax = fmaxf(cmax, a2[e]);
   }
   if (cmax > st.m) {
@@ -92,6 +100,19 @@ __device__ __forceinline__ void kl_group(KlState& st, const float* z,
   }
 }
 
+// Mean of zq - z over the first min(V, 64) elements of a row: lane l takes
+// element l, then a butterfly sum.  Every lane (and every wave of the row)
+// ends with the same bits: each level adds the same two partial sums, and
+// fp32 addition is commutative.
+__device__ __forceinline__ float row_reference(const uint16_t* a, const uint16_t* b, int V) {
+  const int lane = threadIdx.x & 63;
+  const int nref = V < 64 ? V : 64;
+  float x = lane < nref ? bf16_to_f32(b[lane]) - bf16_to_f32(a[lane]) : 0.0f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x / (float)nref;
+}
+
 __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
     const uint16_t* __restrict__ zc, const uint16_t* __restrict__ zp, int V,
     int64_t ld, float inv_tau, float* __restrict__ kl_out) {
@@ -100,6 +121,7 @@ __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
   const uint16_t* a = zc + row * ld;
   const uint16_t* b = zp + row * ld;
   const float l2t = kLog2e * inv_tau;
+  const float dref = row_reference(a, b, V);
   KlState st{-INFINITY, 0.0f, 0.0f, 0.0f};
   const int nfull = V >> 3;
   for (int c = threadIdx.x; c < nfull; c += kKlThreads) {
@@ -113,7 +135,7 @@ __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
       zq[2 * p] = bf16_lo(vb[p]);
       zq[2 * p + 1] = bf16_hi(vb[p]);
     }
-    kl_group(st, z, zq, 8, l2t, inv_tau);
+    kl_group(st, z, zq, 8, l2t, inv_tau, dref);
   }
   const int tail = V - 8 * nfull;
   if (tail > 0 && (int)threadIdx.x == nfull % kKlThreads) {
@@ -123,7 +145,7 @@ __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
       z[e] = e < tail ? bf16_to_f32(a[8 * nfull + e]) : 0.0f;
       zq[e] = e < tail ? bf16_to_f32(b[8 * nfull + e]) : 0.0f;
     }
-    kl_group(st, z, zq, tail, l2t, inv_tau);
+    kl_group(st, z, zq, tail, l2t, inv_tau, dref);
   }
   // wave reduction (fixed butterfly), then the four waves in order
 #pragma unroll

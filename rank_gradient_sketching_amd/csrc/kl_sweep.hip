@@ -9,7 +9,7 @@
 // in fp32 registers for every multiplier, never rounded to bf16, so the
 // alpha^2 law holds on the inputs as given.
 //
-// With a = z/tau, dl = delta/tau, p = softmax(a) and w = e^(a - max):
+// With a = z/tau, dl = (delta - c)/tau, p = softmax(a) and w = e^(a - max):
 //   KL(alpha) = log E_p[e^(alpha dl)] - alpha E_p[dl]
 //             = g/s + log1p(x) - x,   x = (alpha u1 + g)/s,
 //   s = sum w,  u1 = sum w dl,  g = sum w (e^(alpha dl) - 1 - alpha dl).
@@ -23,6 +23,11 @@
 // The kernel carries u1, the M_n and the multipliers in units of u = amax dl
 // (|u| <= 1 on the series path, so no power can overflow) and alpha / amax;
 // the products alpha^n M_n are the same.
+// c is a per-row reference, the mean of delta over the row's first min(V, 64)
+// elements: adding alpha c to every proposed logit of a row leaves every
+// KL(alpha) unchanged, and taking it out keeps a common offset of the
+// direction out of the moments, where it would dominate them and cancel in
+// the finalisation (and push every element off the series path).
 // So an element costs the same ~20 VALU operations whatever the number of
 // multipliers (dl is never formed: the moments are taken in units of delta
 // and 1/tau enters each row's finalisation).  States merge by rescaling to the larger running max (shuffles
@@ -103,7 +108,7 @@ struct Multipliers {
 template <int NA>
 __device__ __forceinline__ void sw_group(SwState<NA>& st, const float* z, const float* dz,
                                          int n, float l2t, float su, float thr,
-                                         const Multipliers& as) {
+                                         const Multipliers& as, float dref) {
   float zmax = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 8; ++e) zmax = fmaxf(zmax, e < n ? z[e] : -INFINITY);
@@ -117,7 +122,7 @@ __device__ __forceinline__ void sw_group(SwState<NA>& st, const float* z, const 
   for (int e = 0; e < 8; ++e) {
     if (e < n) {
       const float w = exp2_normal(fmaf(z[e], l2t, nm));
-      const float d = dz[e] * su;
+      const float d = (dz[e] - dref) * su;
       st.s += w;
       float y = w * d;
       st.u1 += y;
@@ -148,6 +153,18 @@ __device__ __forceinline__ SwState<NA> sw_shfl_xor(const SwState<NA>& st, int of
   return o;
 }
 
+// Mean of delta over the first min(V, 64) elements of a row by a butterfly
+// sum; every lane and wave of the row ends with the same bits (each level
+// adds the same two partial sums, and fp32 addition is commutative).
+__device__ __forceinline__ float direction_reference(const uint16_t* dr, int V) {
+  const int lane = threadIdx.x & 63;
+  const int nref = V < 64 ? V : 64;
+  float x = lane < nref ? bf16_to_f32(dr[lane]) : 0.0f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x / (float)nref;
+}
+
 // One work-group per row: kl_out[i * n_tok + row] = KL_row(alpha_i).
 template <int NA>
 __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
@@ -159,6 +176,7 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
   const uint16_t* zr = z + row * ld;
   const uint16_t* dr = dz + row * ld;
   const float l2t = kSwLog2e * inv_tau;
+  const float dref = direction_reference(dr, V);
   SwState<NA> st;
   st.m = -INFINITY;
   st.s = 0.0f;
@@ -180,7 +198,7 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
       dd[2 * p] = bf16_lo(vb[p]);
       dd[2 * p + 1] = bf16_hi(vb[p]);
     }
-    sw_group(st, zz, dd, 8, l2t, su, thr, al);
+    sw_group(st, zz, dd, 8, l2t, su, thr, al, dref);
   }
   const int tail = V - 8 * nfull;
   if (tail > 0 && (int)threadIdx.x == nfull % kSwThreads) {
@@ -190,7 +208,7 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
       zz[e] = e < tail ? bf16_to_f32(zr[8 * nfull + e]) : 0.0f;
       dd[e] = e < tail ? bf16_to_f32(dr[8 * nfull + e]) : 0.0f;
     }
-    sw_group(st, zz, dd, tail, l2t, su, thr, al);
+    sw_group(st, zz, dd, tail, l2t, su, thr, al, dref);
   }
   // wave reduction (fixed butterfly), then the four waves in order
 #pragma unroll

@@ -8,10 +8,11 @@ tolerance, while the chosen form stays far inside it:
   one bf16 value ([LoGRA] Sketch: S += dY^T P accumulated in fp32);
 - the merge takes S as a hi/lo pair of bf16 values ([LoGRA] Sketch:
   W <- W - alpha eta S A);
-- the predicted KL is formed from one online state (s, u1, u2) with
-  u2 = sum w expm1(d), not as a difference of two fp32 log-sum-exps
-  ([LoGRA] PKL: current vs proposed vocabulary distributions at one
-  temperature).
+- the predicted KL is formed from one online state (s, u1, u3) with
+  u3 = sum w (e^d - 1 - d) (a Taylor polynomial for |d| <= 1/2) and d taken
+  relative to a per-row reference difference, not as a difference of two
+  fp32 log-sum-exps ([LoGRA] PKL: current vs proposed vocabulary
+  distributions at one temperature).
 
 Tolerances: 2e-3 relative Frobenius error on S and on the merged-W delta,
 1e-3 relative error on each token's KL.
@@ -73,6 +74,38 @@ def _lane_sums(x):
     return np.sum(parts, axis=1, dtype=np.float32)
 
 
+def _excess_f32(d):
+    """e^d - 1 - d in fp32 as the KL kernels form it: Taylor polynomial to d^7
+    (Horner, fp32) for |d| <= 1/2, exp otherwise."""
+    d = d.astype(np.float32)
+    p = np.full_like(d, np.float32(1.0 / 5040.0))
+    for c in (1.0 / 720.0, 1.0 / 120.0, 1.0 / 24.0, 1.0 / 6.0, 0.5):
+        p = (p * d + np.float32(c)).astype(np.float32)
+    g = (d * d * p).astype(np.float32)
+    big = np.abs(d) > 0.5
+    g[big] = (np.exp(d[big]) - np.float32(1.0) - d[big]).astype(np.float32)
+    return g
+
+
+def _one_pass_kl(z, zp, tau, reference):
+    """Per-row KL from the kernels' fp32 state (s, u1, u3), finalised in fp64:
+    KL = u3/s + log1p(x) - x with x = (u1 + u3)/s.  With `reference`, d is
+    taken relative to the mean of z' - z over the row's first 64 elements."""
+    a = (z / tau).astype(np.float32)
+    raw = (zp - z).astype(np.float32)
+    if reference:
+        n = min(64, z.shape[1])
+        dref = (raw[:, :n].sum(axis=1, dtype=np.float32) / np.float32(n)).astype(np.float32)
+        raw = (raw - dref[:, None]).astype(np.float32)
+    d = (raw * np.float32(1.0 / tau)).astype(np.float32)
+    w = np.exp(a - a.max(axis=1, keepdims=True)).astype(np.float32)
+    s = _lane_sums(w).astype(np.float64)
+    u1 = _lane_sums(w * d).astype(np.float64)
+    u3 = _lane_sums(w * _excess_f32(d)).astype(np.float64)
+    x = (u1 + u3) / s
+    return u3 / s + np.log1p(x) - x
+
+
 def test_predicted_kl_needs_the_one_pass_form():
     n, V, tau = 16, 152064, 1.0
     z = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.Z_ID, salt=3, sigma=3.0))
@@ -91,14 +124,25 @@ def test_predicted_kl_needs_the_one_pass_form():
     la, lb = lse(a), lse(b)
     p = np.exp(a - la[:, None]).astype(np.float32)
     naive = _lane_sums(p * (a - b)) + (lb - la)
-    # one pass: w = e^(a - max), d = b - a, KL = log1p(u2/s) - u1/s
-    w = np.exp(a - a.max(axis=1, keepdims=True)).astype(np.float32)
-    d = (b - a).astype(np.float32)
-    s = _lane_sums(w)
-    u1 = _lane_sums(w * d)
-    u2 = _lane_sums(w * np.expm1(d))
-    one = (np.log1p(u2 / s) - u1 / s).astype(np.float32)
+    # the kernels' one-pass state
+    one = _one_pass_kl(z, zp, tau, reference=True)
     naive_err = float(np.max(np.abs(naive - ref) / np.abs(ref)))
     one_err = float(np.max(np.abs(one - ref) / np.abs(ref)))
     assert naive_err > 0.5 * KL_TOL, naive_err     # under a 2x margin per token
     assert one_err < KL_TOL / 50, one_err          # over 50x
+
+
+def test_predicted_kl_needs_the_row_reference_under_a_logit_offset():
+    # proposed logits shifted by a per-row constant plus a small spread: the
+    # KL ignores the shift, but without the reference the fp32 sums carry
+    # e^c - 1 - c and cancel in the finalisation
+    n, V, tau = 8, 152064, 1.0
+    z = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.Z_ID, salt=5, sigma=3.0))
+    noise = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.DIR_ID, salt=5, sigma=0.01))
+    for off in (0.75, -3.0):
+        zp = obf16.round_f64(z + off + noise)
+        ref = okl.kl_rows(z, zp, tau)
+        plain = float(np.max(np.abs(_one_pass_kl(z, zp, tau, reference=False) - ref) / ref))
+        with_ref = float(np.max(np.abs(_one_pass_kl(z, zp, tau, reference=True) - ref) / ref))
+        assert plain > KL_TOL, (off, plain)            # fails the tolerance
+        assert with_ref < KL_TOL / 100, (off, with_ref)
