@@ -73,11 +73,13 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
     // registers (4 NT NKS u32x4 per lane: large ranks use NT = 2 to fit); with
     // NT = 4 and r > 64 they are rebuilt per pass (L2 hits).
     constexpr bool kHoistS = NKS <= 2 || NT <= 2;
-    // rows of this wave all inside d and r a multiple of 32: plain float4 loads.
-    // A rank that is not a multiple of 32 needs only these loads to clear its
-    // K tail; they run once, before the passes, so such ranks still take the
-    // unmasked kernel.
-    const bool s_fast = !M && (r % 32) == 0;
+    // rows of this wave all inside d, r a multiple of 32 and S 16-byte
+    // aligned (the ABI asks only for 4): plain float4 loads.  A rank that is
+    // not a multiple of 32 (or an S that is not 16-byte aligned) needs only
+    // the scalar loads below to clear its K tail; they run once, before the
+    // passes, so such calls still take the unmasked kernel.
+    const bool s_vec = (r % 32) == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+    const bool s_fast = !M && s_vec;
     auto s_raw = [&](int nt, int ks, float v[8]) {
       const int row = row0 + 16 * nt + m;
       if (s_fast) {
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
           v[e] = a[e];
           v[4 + e] = b[e];
         }
-      } else if ((r % 32) == 0) {   // only rows past d to clear
+      } else if (s_vec) {   // only rows past d to clear
         f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
         if (row < d) {
           const f32x4* sp = reinterpret_cast<const f32x4*>(S + (int64_t)row * r + 32 * ks + 8 * g);
