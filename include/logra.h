@@ -23,7 +23,8 @@
  *     elements; they must be >= the row length and a multiple of 8, and the
  *     base pointer of a bf16 matrix must be 16-byte aligned.
  *   - Buffers are device pointers owned by the caller.  The library never
- *     allocates or frees device memory and keeps no state between calls.
+ *     allocates or frees device memory and keeps no state between calls
+ *     (apart from the test-only kernel choice of logra_set_kernel_choice).
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream);
  *     scalar results are written to device memory, so no call synchronises.
  *   - Arguments are validated on the host before any HIP call; an invalid
@@ -32,13 +33,6 @@
  *   - Calls that share an output buffer (S, W) must be ordered by the caller
  *     (same stream or events).  Two concurrent calls must not share a
  *     workspace.
- *   - Two environment variables, read at every call, override the choice
- *     among equivalent kernels (results agree to fp32 rounding; meant for
- *     testing): LOGRA_PROJECT_TILE=0/2 never/always uses the 64-token
- *     projection tile, LOGRA_ACC_WIDE=0/2 never/always uses the
- *     work-group-wide accumulate kernel at r > 64.  The latter changes the
- *     workspace size, so it must not change between logra_sketch_ws_bytes
- *     (or logra_sketch_shared_ws_bytes) and the call the workspace serves.
  */
 #ifndef LOGRA_H
 #define LOGRA_H
@@ -98,6 +92,28 @@ const char* logra_status_str(int status);
  */
 int logra_regen_A(uint64_t seed, uint64_t stream, int kind, int32_t r,
                   int64_t k, float* A, hipStream_t s);
+
+/*
+ * logra_set_kernel_choice - force one of two equivalent kernels of the sketch
+ * entry points, for tests and measurements (not part of the method).  By
+ * default each call picks its kernels from the shapes; results of the
+ * alternatives agree to fp32 rounding.
+ *
+ * which: LOGRA_CHOICE_PROJECT_TILE - the 64-token projection tile (only
+ *            considered for r > 32);
+ *        LOGRA_CHOICE_ACC_WIDE - the work-group-wide accumulate kernel (only
+ *            considered for r > 64).  It changes the workspace size, so it
+ *            must not change between logra_sketch_ws_bytes (or
+ *            logra_sketch_shared_ws_bytes) and the call that workspace serves.
+ * mode:  LOGRA_CHOICE_AUTO (the default), 0 (never) or 1 (always).
+ * The setting is process-wide: it applies to every later sketch call on any
+ * thread until it is set again.  This is the library's only state.
+ * Returns LOGRA_OK, or LOGRA_EINVAL for an unknown `which` or `mode`.
+ */
+#define LOGRA_CHOICE_PROJECT_TILE 0
+#define LOGRA_CHOICE_ACC_WIDE 1
+#define LOGRA_CHOICE_AUTO (-1)
+int logra_set_kernel_choice(int which, int mode);
 
 /* Bytes of workspace logra_sketch_accumulate needs for these sizes (either
  * projection kind).  Returns 0 for invalid sizes. */

@@ -5,6 +5,8 @@ The work runs in liblogra.so (hand-written HIP for gfx950) behind a C ABI
 """
 from .api import (GAUSSIAN, MAX_SHARED, MAX_SWEEP, RADEMACHER, SKETCH_OVERWRITE,  # noqa: F401
                   UPDATE_ADAM, UPDATE_MOMENTUM, UPDATE_SGD,
+                  CHOICE_ACC_WIDE, CHOICE_AUTO, CHOICE_PROJECT_TILE, kernel_choice,
+                  set_kernel_choice,
                   kl_budget_schedule, kl_sweep_ws_bytes, kl_ws_bytes, merge, predicted_kl,
                   predicted_kl_sweep, regen_A, sketch_accumulate, sketch_accumulate_shared,
                   sketch_shared_ws_bytes, sketch_update, sketch_ws_bytes, sketch_workspace)

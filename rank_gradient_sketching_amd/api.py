@@ -53,6 +53,33 @@ def _rows(t, name):
     return rows, cols, ld
 
 
+CHOICE_PROJECT_TILE = 0   # LOGRA_CHOICE_PROJECT_TILE
+CHOICE_ACC_WIDE = 1       # LOGRA_CHOICE_ACC_WIDE
+CHOICE_AUTO = -1          # LOGRA_CHOICE_AUTO
+
+
+def set_kernel_choice(which, mode):
+    """Force (mode 0 never, 1 always) or release (CHOICE_AUTO) one of the
+    sketch's equivalent kernels, process-wide; for tests and measurements."""
+    _lib.check(_lib.lib().logra_set_kernel_choice(int(which), int(mode)),
+               "logra_set_kernel_choice")
+
+
+class kernel_choice:
+    """Context manager: set_kernel_choice(which, mode) inside, automatic after."""
+
+    def __init__(self, which, mode):
+        self.which, self.mode = which, mode
+
+    def __enter__(self):
+        set_kernel_choice(self.which, self.mode)
+        return self
+
+    def __exit__(self, *exc):
+        set_kernel_choice(self.which, CHOICE_AUTO)
+        return False
+
+
 def regen_A(seed, stream, kind, r, k, device="cuda", out=None):
     """A (r x k fp32) exactly as the sketch and merge kernels regenerate it."""
     if out is None:

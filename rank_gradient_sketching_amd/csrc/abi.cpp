@@ -63,6 +63,10 @@ int logra_regen_A(uint64_t seed, uint64_t stream, int kind, int32_t r,
   return hip_status(logra::launch_regen(seed, stream, kind, r, k, A, s));
 }
 
+int logra_set_kernel_choice(int which, int mode) {
+  return logra::set_kernel_choice(which, mode) ? LOGRA_OK : LOGRA_EINVAL;
+}
+
 size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r) {
   logra::SketchPlan p;
   if (!logra::make_sketch_plan(T, 1, &d, k, r, &p)) return 0;

@@ -50,6 +50,10 @@ struct SketchPlan {
 bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
                       SketchPlan* p);
 
+// Process-wide kernel-choice override (which: 0 projection tile, 1 wide
+// accumulate; mode: -1 automatic, 0 never, 1 always).  False on bad input.
+bool set_kernel_choice(int which, int mode);
+
 // c = 1/sqrt(r) computed in double and rounded once to float.
 float sign_scale(int r);
 

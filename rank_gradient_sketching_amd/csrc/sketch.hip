@@ -42,8 +42,7 @@
 // The Gaussian basis is first written once per call as a bf16 r x k matrix in
 // the workspace (Box-Muller per entry is too costly to repeat per token
 // block) and the project kernel reads its operand tiles from there.
-#include <stdlib.h>
-
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1080,18 +1079,21 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   }
 }
 
+// Kernel-choice overrides set through logra_set_kernel_choice (tests and
+// measurements): -1 automatic, 0 never, 1 always.
+std::atomic<int> g_choice_project_tile{-1};
+std::atomic<int> g_choice_acc_wide{-1};
+
 // Whether launch_project takes project_tile_kernel (only from two 32-row
 // blocks of A up).  It builds each basis operand for two token blocks, which
 // pays wherever operand building bounds project_kernel: always for the
 // Gaussian basis, and for the sign basis once its 64-token work-groups still
 // fill all 256 CUs (below that, project_kernel's twice as many work-groups
-// are worth more).  LOGRA_PROJECT_TILE in the environment overrides the
-// choice, read at every launch: 0 never, 2 always.
+// are worth more).
 bool use_tile_projection(const SketchPlan& p, int nb32, bool gauss) {
   if (nb32 < 2) return false;
-  const char* env = getenv("LOGRA_PROJECT_TILE");
-  if (env != nullptr && env[0] == '0') return false;
-  if (env != nullptr && env[0] == '2') return true;
+  const int mode = g_choice_project_tile.load(std::memory_order_relaxed);
+  if (mode >= 0) return mode == 1;
   return gauss || p.t_pad / kTileTokens >= 256;
 }
 
@@ -1193,13 +1195,6 @@ hipError_t launch_accumulate_wide(const SketchPlan& p, const OutTable& tab, int 
   return launch_finalize<kAccQ, NB16>(p, tab, r, part, s);
 }
 
-// LOGRA_ACC_WIDE in the environment overrides the choice of the accumulate
-// kernel for r >= 128: 0 never the wide kernel, 2 always (any T).
-int wide_accumulate_mode() {
-  const char* env = getenv("LOGRA_ACC_WIDE");
-  return env == nullptr ? 1 : env[0] - '0';
-}
-
 }  // namespace
 
 bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
@@ -1218,8 +1213,8 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
   q.n_out = n_out;
   // The wide kernel from r = 128 once T gives each work-group enough steps
   // (T >= 16384): at T = 8192 it left CUs idle and measured slower.
-  const int wide_mode = wide_accumulate_mode();
-  q.acc_wide = q.rp >= 128 && wide_mode != 0 && (q.steps >= 512 || wide_mode == 2);
+  const int wide_mode = g_choice_acc_wide.load(std::memory_order_relaxed);
+  q.acc_wide = q.rp >= 128 && (wide_mode >= 0 ? wide_mode == 1 : q.steps >= 512);
   q.wg_groups = q.acc_wide ? kAccWaves / (q.rp / 64) : 1;
   int64_t groups = 0, wgs_d = 0;
   for (int o = 0; o < n_out; ++o) {
@@ -1273,6 +1268,14 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
   q.off_gauss = take((size_t)q.p_rows * (size_t)q.k_pad * 2);
   q.total = off;
   *p = q;
+  return true;
+}
+
+bool set_kernel_choice(int which, int mode) {
+  if (mode < -1 || mode > 1) return false;
+  if (which == 0) g_choice_project_tile.store(mode, std::memory_order_relaxed);
+  else if (which == 1) g_choice_acc_wide.store(mode, std::memory_order_relaxed);
+  else return false;
   return true;
 }
 

@@ -9,7 +9,7 @@ import pytest
 
 from rank_gradient_sketching_amd import _lib
 
-EINVAL, EWS = _lib.EINVAL, _lib.EWORKSPACE
+OK, EINVAL, EWS = _lib.OK, _lib.EINVAL, _lib.EWORKSPACE
 P = 0x100000          # a 256-byte-aligned stand-in address; never dereferenced
 MIS = P + 2           # misaligned by 2 bytes
 
@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = _lib.header_symbols()
-    assert len(declared) == 13
+    assert len(declared) == 14
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -265,3 +265,24 @@ def test_sketch_update_ignores_unused_state_arguments(L):
     assert st != EINVAL
     st = _update(L, rule=1, v=None, b2=9.0, eps=float("nan"), step=0)
     assert st != EINVAL
+
+
+def test_kernel_choice_setter(L):
+    for which in (0, 1):
+        for mode in (-1, 0, 1):
+            assert L.logra_set_kernel_choice(which, mode) == OK
+        assert L.logra_set_kernel_choice(which, 2) == EINVAL
+        assert L.logra_set_kernel_choice(which, -2) == EINVAL
+    assert L.logra_set_kernel_choice(2, 0) == EINVAL
+    for which in (0, 1):
+        assert L.logra_set_kernel_choice(which, -1) == OK
+    # the wide accumulate choice changes the workspace plan at r > 64 only
+    base = L.logra_sketch_ws_bytes(8192, 4096, 4096, 256)
+    L.logra_set_kernel_choice(1, 1)
+    wide = L.logra_sketch_ws_bytes(8192, 4096, 4096, 256)
+    small_r = L.logra_sketch_ws_bytes(8192, 4096, 4096, 64)
+    L.logra_set_kernel_choice(1, -1)
+    assert L.logra_sketch_ws_bytes(8192, 4096, 4096, 256) == base
+    assert L.logra_sketch_ws_bytes(8192, 4096, 4096, 64) == small_r
+    assert wide != base
+
