@@ -178,6 +178,7 @@ def run_layer(lg, synth, steps, warmup):
 
 
 def check_layer_parity(synth, Xs, dYs, W0, W, S, cfg):
+    from oracle import bf16 as obf16
     from oracle import merge as omerge
     from oracle import projection as oproj
     d, k, r = cfg["d"], cfg["k"], cfg["r"]
@@ -188,11 +189,24 @@ def check_layer_parity(synth, Xs, dYs, W0, W, S, cfg):
         S_ref += synth.bf16_to_f64(dY).T @ P
     S_got = S.cpu().numpy().astype(np.float64)
     s_err = float(np.linalg.norm(S_got - S_ref) / np.linalg.norm(S_ref))
-    ref_delta = omerge.merged_delta(synth.bf16_bits(W0), S_got, A, cfg["alpha"], cfg["eta"])
+    s_elem = float(np.abs(S_got - S_ref).max() / np.abs(S_ref).max())
+    W0b = synth.bf16_bits(W0)
+    ref_delta = omerge.merged_delta(W0b, S_got, A, cfg["alpha"], cfg["eta"])
     got_delta = synth.bf16_to_f64(W) - synth.bf16_to_f64(W0)
     w_err = float(np.linalg.norm(got_delta - ref_delta) / np.linalg.norm(ref_delta))
-    return dict(S_rel_fro=s_err, W_delta_rel_fro=w_err, S_tol=2e-3, W_tol=2e-3,
-                ok=bool(s_err < 2e-3 and w_err < 2e-3))
+
+    # elementwise: each merged element within one bf16 spacing of the
+    # oracle's, plus 1e-4 of the largest delta (where W - alpha eta S A
+    # cancels to nearly zero, the fp32/fp64 difference of S A is what is left)
+    a = synth.bf16_to_f64(W)
+    b = obf16.bits_to_f64(omerge.merge_bits(W0b, S_got, A, cfg["alpha"], cfg["eta"]))
+    m = np.maximum(np.abs(a), np.abs(b))
+    spacing = np.where(m > 0, np.ldexp(1.0, np.frexp(m)[1] - 8), 0.0)
+    w_elem = float(np.maximum(np.abs(a - b) - spacing, 0.0).max() / np.abs(ref_delta).max())
+    return dict(S_rel_fro=s_err, S_max_entry_rel=s_elem, W_delta_rel_fro=w_err,
+                W_entry_excess=w_elem, S_tol=2e-3, S_entry_tol=1e-4, W_tol=2e-3,
+                W_entry_tol=1e-4,
+                ok=bool(s_err < 2e-3 and s_elem < 1e-4 and w_err < 2e-3 and w_elem <= 1e-4))
 
 
 def run_kl(lg, synth, reps=5):
@@ -632,6 +646,20 @@ def main():
         "copy_calibration": calib,
     }
     print(json.dumps(out), flush=True)
+    # a parity failure anywhere fails the run (after the line is printed)
+    bad = []
+    if not layer["parity"]["ok"]:
+        bad.append("layer")
+    if kl is not None:
+        if not (kl["sampled_row_max_rel_err"] < 1e-3 and kl["q_vs_row_mean_rel"] < 1e-6):
+            bad.append("predicted KL")
+        if not kl["sweep"]["sampled_row_max_rel_err"] < 1e-3:
+            bad.append("predicted-KL sweep")
+    if layer_set is not None and not layer_set["shared_vs_separate_rel_fro"] < 1e-5:
+        bad.append("shared sketch")
+    if bad:
+        log(f"[bench] PARITY FAILED: {', '.join(bad)}")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -3,8 +3,10 @@
 Bars: A bit-exact for the sign basis (the Gaussian basis: >= 99.9 % of entries
 equal, the rest within one bf16 ulp, since fp64 and fp32 transcendentals may
 round differently); S and the merged-W delta within 2e-3 relative Frobenius
-error; q(D) within 1e-3 relative error.  Shapes span several tiles and ragged
-tails; every input is seeded.
+error; q(D) within 1e-3 relative error.  Beside each Frobenius bound an
+elementwise one (tests/parity_bars.py), so that a single wrong entry cannot
+hide in the norm.  Shapes span several tiles and ragged tails; every input is
+seeded.
 """
 import numpy as np
 import pytest
@@ -20,9 +22,8 @@ from rank_gradient_sketching_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-S_TOL = 2e-3
-W_TOL = 2e-3
-Q_TOL = 1e-3
+from parity_bars import (Q_TOL, S_TOL, W_ELEM, W_TOL, max_rel, rel_fro, s_elem_bar,  # noqa: E402
+                         w_elem_bar, w_excess)
 
 
 @pytest.fixture(scope="module")
@@ -37,11 +38,10 @@ def say(*a):
     print(*a, flush=True)
 
 
-def rel_fro(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    nb = np.linalg.norm(b)
-    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+
+
 
 
 def padded_bf16(t, ld):
@@ -118,6 +118,8 @@ def _sketch_case(lg, T, d, k, r, kind, n_mb, seed=1234, stream=0, ld_pad=0):
                              [(synth.bf16_to_f64(X), synth.bf16_to_f64(dY)) for X, dY in mbs], A)
     delta_ref = ref - S0.numpy().astype(np.float64)
     delta_gpu = S.cpu().numpy().astype(np.float64) - S0.numpy().astype(np.float64)
+    elem = max_rel(delta_gpu, delta_ref)
+    assert elem < s_elem_bar(kind), ("elementwise", elem)
     return S, rel_fro(delta_gpu, delta_ref), rel_fro(S.cpu().numpy(), ref)
 
 
@@ -129,8 +131,9 @@ def test_sketch_matches_oracle(lg, T, d, k, r, kind, n_mb):
     assert err_total < S_TOL, err_total
 
 
-# Both projection kernels on each case (LOGRA_PROJECT_TILE: 0 = the 32-token
-# kernel, 2 = the 64-token tile kernel), ragged and whole tiles alike.
+# Both projection kernels on each case (logra_set_kernel_choice with
+# LOGRA_CHOICE_PROJECT_TILE: 0 = the 32-token kernel, 1 = the 64-token tile
+# kernel), ragged and whole tiles alike.
 PROJECTION_CASES = [
     # T, d, k, r, kind, n_mb
     (77, 1030, 264, 64, 0, 1),      # 3 steps: the last tile's second block is empty
@@ -174,19 +177,19 @@ def test_sketch_fuzz_small_shapes(lg, T, d, k, r, kind, n_mb):
     assert err < S_TOL, err
 
 
-@pytest.mark.parametrize("mode", ["0", "2"])
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("T,d,k,r,kind,n_mb", PROJECTION_CASES)
-def test_sketch_both_projection_kernels(lg, monkeypatch, mode, T, d, k, r, kind, n_mb):
+def test_sketch_both_projection_kernels(lg, mode, T, d, k, r, kind, n_mb):
     say("sketch projection kernel", mode, T, d, k, r, kind, n_mb)
-    monkeypatch.setenv("LOGRA_PROJECT_TILE", mode)
-    _, err_delta, err_total = _sketch_case(lg, T, d, k, r, kind, n_mb)
+    with lg.kernel_choice(lg.CHOICE_PROJECT_TILE, mode):
+        _, err_delta, err_total = _sketch_case(lg, T, d, k, r, kind, n_mb)
     assert err_delta < S_TOL, err_delta
     assert err_total < S_TOL, err_total
 
 
-# Both accumulate kernels at r = 128 and 256 (LOGRA_ACC_WIDE: 0 = the kernel
-# whose waves split r and T, 2 = the work-group-wide tile of 2 or 4 d groups,
-# which by default serves only T >= 16384).
+# Both accumulate kernels at r = 128 and 256 (LOGRA_CHOICE_ACC_WIDE: 0 = the
+# kernel whose waves split r and T, 1 = the work-group-wide tile of 2 or 4 d
+# groups, which by default serves only T >= 16384).
 WIDE_CASES = [
     # T, d, k, r, kind, n_mb
     (77, 1030, 264, 256, 0, 1),     # ragged T and d, nine d groups (the last work-group half empty)
@@ -199,12 +202,12 @@ WIDE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["0", "2"])
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("T,d,k,r,kind,n_mb", WIDE_CASES)
-def test_sketch_both_accumulate_kernels(lg, monkeypatch, mode, T, d, k, r, kind, n_mb):
+def test_sketch_both_accumulate_kernels(lg, mode, T, d, k, r, kind, n_mb):
     say("sketch accumulate kernel", mode, T, d, k, r, kind, n_mb)
-    monkeypatch.setenv("LOGRA_ACC_WIDE", mode)
-    _, err_delta, err_total = _sketch_case(lg, T, d, k, r, kind, n_mb)
+    with lg.kernel_choice(lg.CHOICE_ACC_WIDE, mode):
+        _, err_delta, err_total = _sketch_case(lg, T, d, k, r, kind, n_mb)
     assert err_delta < S_TOL, err_delta
     assert err_total < S_TOL, err_total
 
@@ -229,9 +232,9 @@ SHARED_WIDE_CASES = [
 
 
 @pytest.mark.parametrize("T,k,ds,r,kind", SHARED_WIDE_CASES)
-def test_sketch_shared_wide_accumulate(lg, monkeypatch, T, k, ds, r, kind):
-    monkeypatch.setenv("LOGRA_ACC_WIDE", "2")
-    test_sketch_shared_matches_oracle_and_single_calls(lg, T, k, ds, r, kind)
+def test_sketch_shared_wide_accumulate(lg, T, k, ds, r, kind):
+    with lg.kernel_choice(lg.CHOICE_ACC_WIDE, 1):
+        test_sketch_shared_matches_oracle_and_single_calls(lg, T, k, ds, r, kind)
 
 
 @pytest.mark.parametrize("T,k,ds,r,kind", SHARED_CASES)
@@ -257,6 +260,7 @@ def test_sketch_shared_matches_oracle_and_single_calls(lg, T, k, ds, r, kind):
         base = S0[o].numpy().astype(np.float64)
         got = Ss[o].cpu().numpy().astype(np.float64)
         assert rel_fro(got - base, ref - base) < S_TOL, o
+        assert max_rel(got - base, ref - base) < s_elem_bar(kind), o
         one = singles[o].cpu().numpy().astype(np.float64)
         assert rel_fro(got - base, one - base) < 1e-5, o
 
@@ -451,6 +455,9 @@ def _merge_case(lg, d, k, r, kind, alpha, eta, seed=1234, stream=0, ld_pad=0):
     Wb = synth.bf16_bits(W0)
     ref_delta = omerge.merged_delta(Wb, S.numpy().astype(np.float64), A, alpha, eta)
     got = synth.bf16_to_f64(W) - synth.bf16_to_f64(W0)
+    ex = w_excess(synth.bf16_bits(W), omerge.merge_bits(Wb, S.numpy().astype(np.float64), A,
+                                                          alpha, eta), ref_delta)
+    assert ex <= w_elem_bar(kind), ("elementwise", ex)
     return W, rel_fro(got, ref_delta)
 
 
@@ -483,6 +490,34 @@ def test_merge_padded_stride_keeps_padding(lg):
     A = oproj.projection(9, 0, 0, r, k)
     ref = omerge.merged_delta(synth.bf16_bits(W0), S.cpu().numpy().astype(np.float64), A, 1.0, 1e-3)
     assert rel_fro(synth.bf16_to_f64(buf[:, :k]) - synth.bf16_to_f64(W0), ref) < W_TOL
+    ref_bits = omerge.merge_bits(synth.bf16_bits(W0), S.cpu().numpy().astype(np.float64), A, 1.0,
+                                 1e-3)
+    assert w_excess(synth.bf16_bits(buf[:, :k]), ref_bits, ref) <= W_ELEM
+
+
+@pytest.mark.parametrize("d,k,r,kind", [(512, 768, 64, 0), (300, 1000, 17, 0), (256, 512, 128, 1),
+                                        (4096, 4096, 64, 0)])
+def test_merge_S_four_bytes_off_alignment(lg, d, k, r, kind):
+    # The ABI asks S for 4-byte alignment only: an S that starts 4 bytes into a
+    # 256-byte-aligned buffer must give the same weights as an aligned copy.
+    say("merge misaligned S", d, k, r, kind)
+    W0 = synth.host_normal_bf16((d, k), synth.W_ID, salt=d + 1).cuda()
+    S_host = synth.host_normal_f32((d, r), synth.S_ID, salt=d + 1, sigma=15.0)
+    buf = torch.empty(d * r + 4, device="cuda")
+    S_off = buf[1:1 + d * r].view(d, r)
+    assert S_off.data_ptr() % 16 == 4
+    S_off.copy_(S_host.cuda())
+    S_al = S_host.cuda()
+    W_a = lg.merge(W0.clone(), S_al, 31, 1, kind, 1.0, 1e-3)
+    W_b = lg.merge(W0.clone(), S_off, 31, 1, kind, 1.0, 1e-3)
+    torch.cuda.synchronize()
+    assert torch.equal(W_a.view(torch.int16), W_b.view(torch.int16))
+    A = oproj.projection(31, 1, kind, r, k)
+    Sh = S_host.numpy().astype(np.float64)
+    ref_bits = omerge.merge_bits(synth.bf16_bits(W0), Sh, A, 1.0, 1e-3)
+    ref = omerge.merged_delta(synth.bf16_bits(W0), Sh, A, 1.0, 1e-3)
+    assert rel_fro(synth.bf16_to_f64(W_b) - synth.bf16_to_f64(W0), ref) < W_TOL
+    assert w_excess(synth.bf16_bits(W_b), ref_bits, ref) <= w_elem_bar(kind)
 
 
 def test_merge_zero_step_is_bitwise_noop(lg):
@@ -507,6 +542,14 @@ def test_rollout_apply_matches_trainer_merge(lg):
     diff = (W_train.float() - W_roll.float()).abs().max().item()
     ulp = (W0.float().abs().max() * 2 ** -7).item()
     assert diff <= ulp
+    # and the rollout's weights against the oracle's merge of the received factor
+    A = oproj.projection(77, 0, 0, r, k)
+    W0b = synth.bf16_bits(W0)
+    U = U_sent.cpu().numpy().astype(np.float64)
+    ref = omerge.merged_delta(W0b, U, A, 1.0, 1.0)
+    got = synth.bf16_to_f64(W_roll) - synth.bf16_to_f64(W0)
+    assert rel_fro(got, ref) < W_TOL
+    assert w_excess(synth.bf16_bits(W_roll), omerge.merge_bits(W0b, U, A, 1.0, 1.0), ref) <= W_ELEM
 
 
 # ------------------------------------------------------------------ predicted KL
@@ -541,6 +584,45 @@ def test_predicted_kl_matches_oracle(lg, n, V, tau, sig):
     np.testing.assert_allclose(kl_tok.cpu().numpy(), ref_rows, rtol=1e-3, atol=1e-9)
     assert abs(alpha - okl.step_size(q_ref, 2e-4, 4.0)) <= 1e-3 * okl.step_size(q_ref, 2e-4, 4.0)
     assert torch.equal(out, out_ws)
+
+
+@pytest.mark.parametrize("n,V,offset", [(6, 152064, 0.75), (6, 152064, -3.0), (16, 4099, 2.0),
+                                        (3, 40, -1.5)])
+def test_predicted_kl_with_a_row_offset(lg, n, V, offset):
+    # proposed logits = current + a per-row constant + a small spread: the KL
+    # ignores the constant; the kernels take each row relative to a reference
+    # difference so the constant does not cancel in fp32
+    say("kl offset", n, V, offset)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V + 7)
+    noise = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V + 7, sigma=0.01)
+    shift = torch.linspace(-0.5, 0.5, n).view(n, 1) + offset     # a different constant per row
+    zp = (z.float() + shift + noise.float()).to(torch.bfloat16)
+    ld = -(-V // 8) * 8
+    kl_tok = torch.empty(n, device="cuda")
+    out = lg.predicted_kl(padded_bf16(z, ld), padded_bf16(zp, ld), 1.0, 2e-4, 4.0, kl_tok=kl_tok)
+    torch.cuda.synchronize()
+    ref_rows = okl.kl_rows(synth.bf16_to_f64(z), synth.bf16_to_f64(zp), 1.0)
+    np.testing.assert_allclose(kl_tok.cpu().numpy(), ref_rows, rtol=1e-3, atol=1e-9)
+    assert abs(out[0].item() / ref_rows.mean() - 1) < Q_TOL
+
+
+@pytest.mark.parametrize("n,V,offset,alphas", [(6, 152064, 0.75, [0.25, 0.5, 1.0, 2.0]),
+                                               (8, 4099, -3.0, [1.0, -0.5, 4.0])])
+def test_predicted_kl_sweep_with_a_direction_offset(lg, n, V, offset, alphas):
+    say("kl sweep offset", n, V, offset, alphas)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V + 9)
+    base = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V + 9, sigma=0.01)
+    dirn = (base.float() + offset + torch.linspace(0, 1, n).view(n, 1)).to(torch.bfloat16)
+    m = len(alphas)
+    kl_tok = torch.empty(m, n, device="cuda")
+    ld = -(-V // 8) * 8
+    out = lg.predicted_kl_sweep(padded_bf16(z, ld), padded_bf16(dirn, ld), alphas, 1.0,
+                                kl_tok=kl_tok)
+    torch.cuda.synchronize()
+    ref_rows = okl.kl_sweep_rows(synth.bf16_to_f64(z), synth.bf16_to_f64(dirn), alphas, 1.0)
+    np.testing.assert_allclose(kl_tok.cpu().numpy(), ref_rows, rtol=1e-3, atol=1e-9)
+    got = out.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got, ref_rows.mean(axis=1), rtol=Q_TOL)
 
 
 def test_kl_controller_edges(lg):
@@ -644,3 +726,13 @@ def test_rollout_payload_apply_is_bitwise_the_trainer_merge(lg):
         payload = sync.pack_update(S, 4321, 3, kind, 0.75, 2e-4, k)
         W_roll = sync.apply_update(W0.clone(), payload)
         assert torch.equal(W_train, W_roll)
+        # the rollout rebuilds A from the seed in the payload: its weights
+        # against the oracle's merge with the oracle's A for that seed
+        A = oproj.projection(4321, 3, kind, r, k)
+        W0b = synth.bf16_bits(W0)
+        Sh = S.cpu().numpy().astype(np.float64)
+        ref = omerge.merged_delta(W0b, Sh, A, 0.75, 2e-4)
+        got = synth.bf16_to_f64(W_roll) - synth.bf16_to_f64(W0)
+        assert rel_fro(got, ref) < W_TOL, kind
+        assert w_excess(synth.bf16_bits(W_roll), omerge.merge_bits(W0b, Sh, A, 0.75, 2e-4),
+                        ref) <= w_elem_bar(kind)
