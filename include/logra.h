@@ -153,6 +153,36 @@ int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
                             int32_t flags, float* S, void* ws, size_t ws_bytes,
                             hipStream_t s);
 
+/* Bytes of library-owned scratch behind logra_sketch_accumulate_noalloc
+ * (one copy per GPU, held until the process ends). */
+#define LOGRA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * logra_sketch_accumulate_noalloc - logra_sketch_accumulate without a
+ * workspace argument and without any device allocation, for callers that
+ * cannot allocate: code under stream capture, tight loops that must not call
+ * the allocator, harnesses that forbid it.  The scratch the kernels need
+ * lives in a device array inside the library, LOGRA_NOALLOC_SCRATCH_BYTES per
+ * GPU, whose address is looked up once per device on the first call there.
+ * The call itself allocates and frees nothing.
+ *
+ * Arguments, result and ordering as in logra_sketch_accumulate (same kernels,
+ * so the same bits).  The stream's device (the current device for the null
+ * stream) selects which GPU's scratch is used.
+ * Limit: the call needs logra_sketch_ws_bytes(T, d, k, r) bytes of scratch;
+ *     beyond LOGRA_NOALLOC_SCRATCH_BYTES it returns LOGRA_EWORKSPACE and
+ *     enqueues nothing (d = k = 4096 at r = 64 needs 10.5 MiB for T = 8192;
+ *     the r = 256 layers need more and must use logra_sketch_accumulate).
+ * Concurrency: every call on one GPU shares that GPU's scratch, so calls
+ *     that may overlap on one GPU (different streams without ordering, or
+ *     different threads) race and give wrong results; order them.
+ * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
+ */
+int logra_sketch_accumulate_noalloc(const uint16_t* X, int64_t ldx, const uint16_t* dY,
+                                    int64_t ldd, int64_t T, int64_t d, int64_t k, int32_t r,
+                                    uint64_t seed, uint64_t stream, int kind, int32_t flags,
+                                    float* S, hipStream_t s);
+
 /* Largest number of outputs one logra_sketch_accumulate_shared call takes. */
 #define LOGRA_MAX_SHARED 4
 

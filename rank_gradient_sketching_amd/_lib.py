@@ -52,6 +52,11 @@ SIGNATURES = {
                                                       ctypes.POINTER(ctypes.c_int64),
                                                       ctypes.POINTER(c_vp), c_vp,
                                                       ctypes.c_size_t, c_vp]),
+    "logra_sketch_accumulate_noalloc": (ctypes.c_int, [c_vp, ctypes.c_int64, c_vp, ctypes.c_int64,
+                                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.c_int32, ctypes.c_uint64,
+                                                       ctypes.c_uint64, ctypes.c_int, ctypes.c_int32,
+                                                       c_vp, c_vp]),
     "logra_set_kernel_choice": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "logra_kl_sweep_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
     "logra_predicted_kl_sweep": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int64, ctypes.c_int64,

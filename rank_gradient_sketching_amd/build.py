@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblogra.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "regen.hip", "sketch.hip", "merge.hip", "kl.hip", "kl_sweep.hip", "optim.hip"]
+SOURCES = ["abi.cpp", "regen.hip", "sketch.hip", "merge.hip", "kl.hip", "kl_sweep.hip", "optim.hip",
+           "noalloc.hip"]
 
 
 def hipcc():

@@ -25,6 +25,7 @@ bool aligned(const void* p, uintptr_t a) {
 }
 
 static_assert(LOGRA_MAX_SHARED == logra::kMaxShared, "shared-output limit");
+static_assert(LOGRA_NOALLOC_SCRATCH_BYTES == logra::kNoallocScratchBytes, "no-alloc scratch size");
 
 constexpr int64_t kDimLimit = int64_t(1) << 31;
 constexpr int64_t kDyStrideLimit = int64_t(1) << 26;
@@ -48,7 +49,7 @@ const char* logra_status_str(int status) {
     case LOGRA_EINVAL:
       return "invalid argument";
     case LOGRA_EWORKSPACE:
-      return "workspace missing or too small";
+      return "workspace (or the no-alloc scratch) missing or too small";
     case LOGRA_EHIP:
       return g_hip_msg[0] ? g_hip_msg : "HIP error";
     default:
@@ -136,6 +137,29 @@ int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
   const int st = sketch_checks(X, ldx, T, k, r, kind, flags, 1, &out, ws, ws_bytes, &p, &run);
   if (st != LOGRA_OK || !run) return st;
   if (T == 0) return hip_status(logra::launch_zero_outputs(&out, 1, r, s));
+  return hip_status(logra::launch_sketch(p, X, ldx, &out, (int)T, (int)k, r, seed, stream,
+                                         kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
+                                         static_cast<char*>(ws), s));
+}
+
+int logra_sketch_accumulate_noalloc(const uint16_t* X, int64_t ldx, const uint16_t* dY,
+                                    int64_t ldd, int64_t T, int64_t d, int64_t k, int32_t r,
+                                    uint64_t seed, uint64_t stream, int kind, int32_t flags,
+                                    float* S, hipStream_t s) {
+  const logra::SketchOut out{dY, ldd, d, S};
+  // every argument and the scratch size are checked before the first HIP call
+  // (the scratch-address lookup); the checks see a stand-in workspace of the
+  // full scratch size at a 256-byte-aligned address
+  logra::SketchPlan p;
+  bool run = false;
+  const int st = sketch_checks(X, ldx, T, k, r, kind, flags, 1, &out,
+                               reinterpret_cast<void*>(uintptr_t(256)),
+                               LOGRA_NOALLOC_SCRATCH_BYTES, &p, &run);
+  if (st != LOGRA_OK || !run) return st;
+  if (T == 0) return hip_status(logra::launch_zero_outputs(&out, 1, r, s));
+  void* ws = nullptr;
+  const int sh = hip_status(logra::noalloc_scratch(s, &ws));
+  if (sh != LOGRA_OK) return sh;
   return hip_status(logra::launch_sketch(p, X, ldx, &out, (int)T, (int)k, r, seed, stream,
                                          kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
                                          static_cast<char*>(ws), s));

@@ -54,6 +54,13 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
 // accumulate; mode: -1 automatic, 0 never, 1 always).  False on bad input.
 bool set_kernel_choice(int which, int mode);
 
+// Size of the library-owned scratch of logra_sketch_accumulate_noalloc.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+
+// Device address of that scratch on the device of stream s (the current
+// device for the null stream); looked up once per device, then cached.
+hipError_t noalloc_scratch(hipStream_t s, void** ptr);
+
 // c = 1/sqrt(r) computed in double and rounded once to float.
 float sign_scale(int r);
 

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = _lib.header_symbols()
-    assert len(declared) == 14
+    assert len(declared) == 15
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -286,3 +286,26 @@ def test_kernel_choice_setter(L):
     assert L.logra_sketch_ws_bytes(8192, 4096, 4096, 64) == small_r
     assert wide != base
 
+
+def test_sketch_noalloc_rejects_before_any_hip_call(L):
+    f = L.logra_sketch_accumulate_noalloc
+    ok = dict(X=P, ldx=4096, dY=P, ldd=4096, T=8192, d=4096, k=4096, r=64, seed=1, stream=0,
+              kind=0, flags=0, S=P, s=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["X"], a["ldx"], a["dY"], a["ldd"], a["T"], a["d"], a["k"], a["r"], a["seed"],
+                 a["stream"], a["kind"], a["flags"], a["S"], a["s"])
+    assert call(X=0) == EINVAL
+    assert call(dY=MIS) == EINVAL
+    assert call(S=0) == EINVAL
+    assert call(r=0) == EINVAL
+    assert call(kind=2) == EINVAL
+    assert call(flags=4) == EINVAL
+    assert call(ldd=4095) == EINVAL
+    # the r = 256 layers need more than the 32 MiB of library scratch
+    assert L.logra_sketch_ws_bytes(32768, 3584, 18944, 256) > 32 << 20
+    assert call(T=32768, d=3584, k=18944, r=256, ldx=18944, ldd=3584) == EWS
+    assert call(T=16384, d=5120, k=25600, r=256, ldx=25600, ldd=5120) == EWS
+    # T = 0 without the overwrite flag: nothing to do
+    assert call(T=0, X=0, dY=0) == OK
