@@ -2,8 +2,10 @@
 
 A step is one pass of the path over one batch of the d = k = 4096, r = 64
 layer: four microbatches of T = 8192 tokens are sketched into S
-(logra_sketch_accumulate, which regenerates the sign basis in registers) and
-the rank-64 update is merged into the bf16 weights (logra_merge,
+(logra_sketch_accumulate, which regenerates the sign basis in registers, as
+one deferred chain: the first three calls keep their contributions in the
+workspace and the fourth writes S, so the split reduction runs once per step)
+and the rank-64 update is merged into the bf16 weights (logra_merge,
 alpha * eta = 2e-4).  Inputs are synthetic, seeded, generated on the GPU and
 resident in HBM before the timed region; the four microbatches (512 MiB) are
 streamed in turn, so nothing is re-read from the 256 MB Infinity Cache.
@@ -44,6 +46,12 @@ def log(*a):
 def sketch_bytes(T, d, k, r):
     """Algorithmic bytes of one sketch call: X and dY once, S read + write."""
     return 2 * T * (d + k) + 8 * d * r
+
+
+def chain_bytes(T, d, k, r, n_mb):
+    """Algorithmic bytes of a deferred chain of n_mb sketch calls that ends with
+    the overwrite flag: X and dY of every microbatch once, S written once."""
+    return n_mb * 2 * T * (d + k) + 4 * d * r
 
 
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix cores
@@ -102,8 +110,15 @@ def run_layer(lg, synth, steps, warmup):
     # NaN: the first microbatch overwrites it, as in the timed steps)
     log("[bench] parity step")
     S.fill_(float("nan"))
-    for mb, (X, dY) in enumerate(zip(Xs, dYs)):
-        lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws, overwrite=mb == 0)
+
+    def sketch_chain():
+        # one deferred chain over the step's microbatches: S written by the last call
+        for mb, (X, dY) in enumerate(zip(Xs, dYs)):
+            last = mb == n_mb - 1
+            lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws, defer=not last,
+                                 pending=mb > 0, overwrite=last)
+
+    sketch_chain()
     lg.merge(W, S, seed, stream, kind, alpha, eta)
     torch.cuda.synchronize()
     parity = check_layer_parity(synth, Xs, dYs, W0, W, S, cfg)
@@ -112,9 +127,8 @@ def run_layer(lg, synth, steps, warmup):
     # ---- timed steps: back to back, one event pair around all of them (an
     # event recorded between calls would sit inside the step)
     def one_step():
-        # the first microbatch starts S (overwrite): no separate zero fill
-        for mb, (X, dY) in enumerate(zip(Xs, dYs)):
-            lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws, overwrite=mb == 0)
+        # the chain's last call stores S (overwrite): no separate zero fill
+        sketch_chain()
         lg.merge(W, S, seed, stream, kind, alpha, eta)
 
     for _ in range(warmup):
@@ -152,6 +166,8 @@ def run_layer(lg, synth, steps, warmup):
     # reported beside it
     sk_b = [batch_us(lambda i: lg.sketch_accumulate(Xs[i % n_mb], dYs[i % n_mb], S, seed, stream,
                                                     kind, ws=ws), reps * n_mb) for _ in range(5)]
+    # whole deferred chains back to back (per call: the chain's time / n_mb)
+    ch_b = [batch_us(lambda i: sketch_chain(), reps) / n_mb for _ in range(5)]
     # merges cycle over at least 16 copies of W, 512 MiB in all: twice the
     # 256 MB Infinity Cache, as inside a step (where W was last touched a
     # step earlier); one W repeated would be served from that cache
@@ -161,7 +177,9 @@ def run_layer(lg, synth, steps, warmup):
                      max(reps, n_w)) for _ in range(5)]
     del Wc
     sk_us, mg_us = float(np.median(sk_b)), float(np.median(mg_b))
+    ch_us = float(np.median(ch_b))
     sb = sketch_bytes(T, d, k, r)
+    cb = chain_bytes(T, d, k, r, n_mb) / n_mb
     mb_ = merge_bytes(d, k, r)
     res = dict(
         cfg=cfg, total_ms=total_ms, step_ms=step_ms, wall_ms=wall_ms,
@@ -169,10 +187,13 @@ def run_layer(lg, synth, steps, warmup):
         sketch=dict(us_per_call=sk_us, us_min=min(sk_b), bytes_per_call=sb,
                     GBps=sb / (sk_us * 1e-6) / 1e9,
                     tokens_per_s=T / (sk_us * 1e-6)),
+        chain=dict(us_per_call=ch_us, us_min=min(ch_b), bytes_per_call=cb,
+                   GBps=cb / (ch_us * 1e-6) / 1e9, tokens_per_s=T / (ch_us * 1e-6)),
         merge=dict(us_per_call=mg_us, us_min=min(mg_b), bytes_per_call=mb_,
                    GBps=mb_ / (mg_us * 1e-6) / 1e9),
         parity=parity)
     res["sketch"]["frac_hbm"] = res["sketch"]["GBps"] / HBM_PEAK_GBPS
+    res["chain"]["frac_hbm"] = res["chain"]["GBps"] / HBM_PEAK_GBPS
     res["merge"]["frac_hbm"] = res["merge"]["GBps"] / HBM_PEAK_GBPS
     return res, (Xs, dYs, W0, cfg)
 
@@ -632,7 +653,11 @@ def main():
         "sketch": {"tokens_per_s": sk["tokens_per_s"], "GBps": sk["GBps"],
                    "frac_hbm": sk["frac_hbm"], "us_per_call": sk["us_per_call"],
                    "us_per_call_min": sk["us_min"],
-                   **sketch_mfma(cfg["T"], cfg["d"], cfg["k"], cfg["r"], sk["us_per_call"])},
+                   **sketch_mfma(cfg["T"], cfg["d"], cfg["k"], cfg["r"], sk["us_per_call"]),
+                   # inside the step's deferred chain (one split reduction per step)
+                   "in_chain": {k_: layer["chain"][k_] for k_ in
+                                ("us_per_call", "us_min", "GBps", "frac_hbm", "tokens_per_s",
+                                 "bytes_per_call")}},
         "merge": {"GBps": mg["GBps"], "frac_hbm": mg["frac_hbm"], "us_per_call": mg["us_per_call"],
                   "us_per_call_min": mg["us_min"]},
         "wall_ms_timed_steps": layer["wall_ms"],

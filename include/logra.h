@@ -121,6 +121,8 @@ size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r);
 
 /* Flags of the sketch entry points. */
 #define LOGRA_SKETCH_OVERWRITE 1 /* S = dY^T (X A^T): start the accumulation */
+#define LOGRA_SKETCH_DEFER 2     /* keep the contribution in the workspace, S untouched */
+#define LOGRA_SKETCH_PENDING 4   /* the workspace holds deferred contributions: add them */
 
 /*
  * logra_sketch_accumulate - S += dY^T (X A^T), one microbatch.
@@ -138,10 +140,24 @@ size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r);
  * flags: 0, or LOGRA_SKETCH_OVERWRITE for the first microbatch of an
  *     optimizer step: S = dY^T (X A^T), S's contents on entry are ignored
  *     (they need not be initialised), which spares the caller a zero fill of
- *     S and the kernels a read of it.  Other bits: LOGRA_EINVAL.
+ *     S and the kernels a read of it.
+ *   Deferred chains (the microbatches of one optimizer step): a call with
+ *     LOGRA_SKETCH_DEFER does not touch S; its contribution stays in the
+ *     workspace, in the per-split partial sums the kernels keep anyway.  A
+ *     later call with LOGRA_SKETCH_PENDING adds its own contribution to
+ *     those; the chain ends with a call that has PENDING but not DEFER, which
+ *     adds everything to S (or, with OVERWRITE, stores it) and runs the one
+ *     split reduction of the chain instead of one per call.  Typical step:
+ *     DEFER, DEFER|PENDING, ..., PENDING|OVERWRITE.  Rules: every call of a
+ *     chain uses the same ws, T, d, k, r, seed, stream and kind (and kernel
+ *     choice), and T >= 1; DEFER with OVERWRITE, or either flag with T == 0,
+ *     is LOGRA_EINVAL; a PENDING call after anything but a DEFER call with
+ *     the same workspace gives undefined values (never out-of-bounds
+ *     accesses).  Other bits: LOGRA_EINVAL.
  * ws: device scratch of at least logra_sketch_ws_bytes(T, d, k, r) bytes,
  *     256-B aligned, owned by the caller; its contents on entry do not
- *     matter.  The result is deterministic (fixed summation order).
+ *     matter (except with LOGRA_SKETCH_PENDING, above).  The result is
+ *     deterministic (fixed summation order).
  * T == 0 is a no-op (returns LOGRA_OK; X, dY and ws are not inspected);
  *     with LOGRA_SKETCH_OVERWRITE it sets S to zero.
  * Constraints: d, k >= 1, T >= 0, 1 <= r <= 256, d, k, T < 2^31.
@@ -167,7 +183,9 @@ int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
  * The call itself allocates and frees nothing.
  *
  * Arguments, result and ordering as in logra_sketch_accumulate (same kernels,
- * so the same bits).  The stream's device (the current device for the null
+ * so the same bits), except that the deferral flags (LOGRA_SKETCH_DEFER,
+ * LOGRA_SKETCH_PENDING) are refused with LOGRA_EINVAL: the scratch is shared
+ * by every call on the GPU, so nothing may be left pending in it.  The stream's device (the current device for the null
  * stream) selects which GPU's scratch is used.
  * Limit: the call needs logra_sketch_ws_bytes(T, d, k, r) bytes of scratch;
  *     beyond LOGRA_NOALLOC_SCRATCH_BYTES it returns LOGRA_EWORKSPACE and
@@ -203,7 +221,8 @@ size_t logra_sketch_shared_ws_bytes(int64_t T, int64_t k, int32_t r, int32_t n_o
  * calls up to fp32 summation order.
  *
  * X, ldx, T, k, r, seed, stream, kind, flags: as in logra_sketch_accumulate
- *     (LOGRA_SKETCH_OVERWRITE applies to every S[o]).
+ *     (every flag applies to every S[o]; a deferred chain keeps the same
+ *     outputs in the same order).
  * dY, ldd, d, S: host arrays of n_out entries (1 <= n_out <= LOGRA_MAX_SHARED);
  *     dY[o] device bf16[T x ldd[o]] (same rules as dY above), S[o] device
  *     float[d[o] x r], distinct.

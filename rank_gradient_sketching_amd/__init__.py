@@ -4,6 +4,7 @@ The work runs in liblogra.so (hand-written HIP for gfx950) behind a C ABI
 (include/logra.h); this package only marshals torch tensors into it.
 """
 from .api import (GAUSSIAN, MAX_SHARED, MAX_SWEEP, RADEMACHER, SKETCH_OVERWRITE,  # noqa: F401
+                  SKETCH_DEFER, SKETCH_PENDING,
                   UPDATE_ADAM, UPDATE_MOMENTUM, UPDATE_SGD,
                   CHOICE_ACC_WIDE, CHOICE_AUTO, CHOICE_PROJECT_TILE, kernel_choice,
                   set_kernel_choice,

@@ -17,6 +17,13 @@ from . import _lib
 RADEMACHER = 0
 GAUSSIAN = 1
 SKETCH_OVERWRITE = 1      # LOGRA_SKETCH_OVERWRITE: S = ... instead of S += ...
+SKETCH_DEFER = 2          # LOGRA_SKETCH_DEFER: keep the contribution in the workspace
+SKETCH_PENDING = 4        # LOGRA_SKETCH_PENDING: the workspace holds deferred contributions
+
+
+def _sketch_flags(overwrite, defer, pending):
+    return ((SKETCH_OVERWRITE if overwrite else 0) | (SKETCH_DEFER if defer else 0) |
+            (SKETCH_PENDING if pending else 0))
 
 
 # torch's raw current-stream lookup costs well under a microsecond per call; the
@@ -102,10 +109,14 @@ def sketch_workspace(T, d, k, r, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None, overwrite=False):
+def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None, overwrite=False,
+                      defer=False, pending=False):
     """S += dY^T (X A^T) in place for one microbatch; returns S.  With
     overwrite=True (the first microbatch of a step) S = dY^T (X A^T) and S's
-    previous contents are ignored."""
+    previous contents are ignored.  defer/pending build a deferred chain over
+    the microbatches of a step (same ws and sizes throughout): defer keeps the
+    contribution in ws and leaves S alone, pending adds the contributions ws
+    holds; the last call (pending, not defer) writes S."""
     _require(X, "X", torch.bfloat16, 2)
     _require(dY, "dY", torch.bfloat16, 2)
     _require(S, "S", torch.float32, 2)
@@ -120,7 +131,7 @@ def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None, overwr
         ws = sketch_workspace(T, d, k, r, X.device)
     st = _lib.lib().logra_sketch_accumulate(
         X.data_ptr(), ldx, dY.data_ptr(), ldd, T, d, k, r, seed, stream, kind,
-        SKETCH_OVERWRITE if overwrite else 0, S.data_ptr(), ws.data_ptr(),
+        _sketch_flags(overwrite, defer, pending), S.data_ptr(), ws.data_ptr(),
         ws.numel() * ws.element_size(), _stream(X))
     _lib.check(st, "logra_sketch_accumulate")
     return S
@@ -136,10 +147,10 @@ def sketch_shared_ws_bytes(T, k, r, ds):
 
 
 def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=None,
-                             overwrite=False):
+                             overwrite=False, defer=False, pending=False):
     """S_o += dY_o^T (X A^T) in place for outputs sharing the input X and A
-    (e.g. q/k/v or gate/up of one layer); returns the list of S.  overwrite
-    as in sketch_accumulate, for every S_o."""
+    (e.g. q/k/v or gate/up of one layer); returns the list of S.  overwrite,
+    defer and pending as in sketch_accumulate, for every S_o."""
     _require(X, "X", torch.bfloat16, 2)
     T, k, ldx = _rows(X, "X")
     if not 1 <= len(dYs) <= MAX_SHARED or len(dYs) != len(Ss):
@@ -166,7 +177,7 @@ def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=Non
         ws = torch.empty(max(sketch_shared_ws_bytes(T, k, r, ds), 256), dtype=torch.uint8,
                          device=X.device)
     st = _lib.lib().logra_sketch_accumulate_shared(
-        X.data_ptr(), ldx, T, k, r, seed, stream, kind, SKETCH_OVERWRITE if overwrite else 0, n,
+        X.data_ptr(), ldx, T, k, r, seed, stream, kind, _sketch_flags(overwrite, defer, pending), n,
         (ctypes.c_void_p * n)(*ptr_dy),
         (ctypes.c_int64 * n)(*ldds), (ctypes.c_int64 * n)(*ds), (ctypes.c_void_p * n)(*ptr_s),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(X))

@@ -86,13 +86,22 @@ namespace {
 
 // Checks shared by the single- and multi-output sketch entry points; fills
 // the plan.  T == 0 is reported as LOGRA_OK with *run = false.
+constexpr int32_t kDeferFlags = LOGRA_SKETCH_DEFER | LOGRA_SKETCH_PENDING;
+
 int sketch_checks(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t r,
                   int kind, int32_t flags, int32_t n_out, const logra::SketchOut* outs,
-                  void* ws, size_t ws_bytes, logra::SketchPlan* plan, bool* run) {
+                  void* ws, size_t ws_bytes, logra::SketchPlan* plan, bool* run,
+                  bool allow_defer = true) {
   *run = false;
   if (n_out < 1 || n_out > LOGRA_MAX_SHARED) return LOGRA_EINVAL;
   if (!dim_ok(k) || !rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
-  if ((flags & ~LOGRA_SKETCH_OVERWRITE) != 0) return LOGRA_EINVAL;
+  if ((flags & ~(LOGRA_SKETCH_OVERWRITE | kDeferFlags)) != 0) return LOGRA_EINVAL;
+  if ((flags & kDeferFlags) != 0) {
+    // a deferred chain: every call has tokens; a deferring call writes no S,
+    // so it takes no overwrite flag
+    if (!allow_defer || T < 1) return LOGRA_EINVAL;
+    if ((flags & LOGRA_SKETCH_DEFER) && (flags & LOGRA_SKETCH_OVERWRITE)) return LOGRA_EINVAL;
+  }
   int64_t d[LOGRA_MAX_SHARED];
   for (int o = 0; o < n_out; ++o) {
     if (!dim_ok(outs[o].d)) return LOGRA_EINVAL;
@@ -101,6 +110,8 @@ int sketch_checks(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t 
   if (T < 0 || T >= kDimLimit) return LOGRA_EINVAL;
   if (T == 0 && (flags & LOGRA_SKETCH_OVERWRITE) == 0) return LOGRA_OK;
   // S of every output: needed by the kernels, and by the zero fill at T == 0
+  // (a deferring call never touches S, but its S must still be a valid
+  // argument)
   for (int o = 0; o < n_out; ++o) {
     if (outs[o].S == nullptr || !aligned(outs[o].S, 4)) return LOGRA_EINVAL;
     for (int o2 = 0; o2 < o; ++o2)
@@ -139,6 +150,8 @@ int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
   if (T == 0) return hip_status(logra::launch_zero_outputs(&out, 1, r, s));
   return hip_status(logra::launch_sketch(p, X, ldx, &out, (int)T, (int)k, r, seed, stream,
                                          kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
+                                         (flags & LOGRA_SKETCH_DEFER) != 0,
+                                         (flags & LOGRA_SKETCH_PENDING) != 0,
                                          static_cast<char*>(ws), s));
 }
 
@@ -154,7 +167,7 @@ int logra_sketch_accumulate_noalloc(const uint16_t* X, int64_t ldx, const uint16
   bool run = false;
   const int st = sketch_checks(X, ldx, T, k, r, kind, flags, 1, &out,
                                reinterpret_cast<void*>(uintptr_t(256)),
-                               LOGRA_NOALLOC_SCRATCH_BYTES, &p, &run);
+                               LOGRA_NOALLOC_SCRATCH_BYTES, &p, &run, /*allow_defer=*/false);
   if (st != LOGRA_OK || !run) return st;
   if (T == 0) return hip_status(logra::launch_zero_outputs(&out, 1, r, s));
   void* ws = nullptr;
@@ -162,6 +175,8 @@ int logra_sketch_accumulate_noalloc(const uint16_t* X, int64_t ldx, const uint16
   if (sh != LOGRA_OK) return sh;
   return hip_status(logra::launch_sketch(p, X, ldx, &out, (int)T, (int)k, r, seed, stream,
                                          kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
+                                         (flags & LOGRA_SKETCH_DEFER) != 0,
+                                         (flags & LOGRA_SKETCH_PENDING) != 0,
                                          static_cast<char*>(ws), s));
 }
 
@@ -182,6 +197,8 @@ int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, in
   if (T == 0) return hip_status(logra::launch_zero_outputs(outs, n_out, r, s));
   return hip_status(logra::launch_sketch(p, X, ldx, outs, (int)T, (int)k, r, seed, stream,
                                          kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
+                                         (flags & LOGRA_SKETCH_DEFER) != 0,
+                                         (flags & LOGRA_SKETCH_PENDING) != 0,
                                          static_cast<char*>(ws), s));
 }
 

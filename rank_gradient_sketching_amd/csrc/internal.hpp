@@ -67,11 +67,14 @@ float sign_scale(int r);
 hipError_t launch_regen(uint64_t seed, uint64_t stream, int kind, int r,
                         int64_t k, float* A, hipStream_t s);
 
-// overwrite: S = dY^T (X A^T) instead of S += (S is not read).
+// overwrite: S = dY^T (X A^T) instead of S += (S is not read).  defer: the
+// result stays in the workspace's partial tiles and S is left alone;
+// pending: the partial tiles hold earlier deferred results (same plan), which
+// are added.
 hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
                          const SketchOut* outs, int T, int k, int r, uint64_t seed,
-                         uint64_t stream, int kind, bool overwrite, char* ws,
-                         hipStream_t s);
+                         uint64_t stream, int kind, bool overwrite, bool defer, bool pending,
+                         char* ws, hipStream_t s);
 
 // S = 0 for n_out outputs of d x r floats (a fill kernel, no memset node).
 hipError_t launch_zero_outputs(const SketchOut* outs, int n_out, int r, hipStream_t s);

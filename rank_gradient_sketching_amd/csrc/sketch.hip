@@ -39,6 +39,10 @@
 //   finalize   adds the partial tiles to S in split order.  S is therefore
 //              bit-reproducible.  With the overwrite flag the kernel that
 //              writes S stores the result instead of adding it.
+// Deferred calls (defer) leave S alone: their contribution stays in the
+// partial tiles, which a later call (pending) adds its own to, split by
+// split; only a call without defer runs the finalize.  A step of several
+// microbatches then pays for one split reduction instead of one per call.
 // The Gaussian basis is first written once per call as a bf16 r x k matrix in
 // the workspace (Box-Muller per entry is too costly to repeat per token
 // block) and the project kernel reads its operand tiles from there.
@@ -125,9 +129,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
       int col = colbase + 8 * j;
       if (t0 + 32 > T) t = t < T ? t : T - 1;                       // ragged block only
       if (MASKED && (cnk + 1) * 256 > k) col = col < k ? col : 0;   // ragged chunk only
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(X + (int64_t)t * ldx + col),
-          (lds_void*)(dst + i * 1024), 16, 0, 0);
+      lds_dma16((const void*)(X + (int64_t)t * ldx + col), lds_addr(dst + i * 1024));
     }
   };
 
@@ -187,7 +189,11 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
   };
 
   // Per wave: logical chunks wave, wave + W, ...; the two halves of the next
-  // chunk load while the current one is multiplied.  Each work-group starts
+  // chunk load while the current one is multiplied.  The copies are issued
+  // from inline assembly (lds_dma16), so the compiler's wait-count pass does
+  // not make the reads of one half wait for the copy just issued into the
+  // other; the kernel waits for each half itself: 8 copies per half, in
+  // issue order.  Each work-group starts
   // its walk along k at a different chunk (physical chunk = logical + step,
   // mod n_chunks): work-groups that run in lock step would otherwise all read
   // the same byte range of their rows at the same time, and HBM channels are
@@ -203,10 +209,20 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
     const int pc = phys(ch);
     if constexpr (!GAUSS) sign_words(pc);
     const bool more = ch + kProjWaves < n_chunks;
+    vm_wait<8>();          // half 0 landed; half 1's copies may be in flight
     compute(pc, 0, buf0);
-    if (more) issue(phys(ch + kProjWaves), 0, buf0);
+    if (more) {
+      lgkm_wait0();        // this wave's reads of buf0 are done
+      issue(phys(ch + kProjWaves), 0, buf0);
+      vm_wait<8>();        // half 1 landed; the next half 0 stays in flight
+    } else {
+      vm_wait<0>();
+    }
     compute(pc, 1, buf1);
-    if (more) issue(phys(ch + kProjWaves), 1, buf1);
+    if (more) {
+      lgkm_wait0();
+      issue(phys(ch + kProjWaves), 1, buf1);
+    }
   }
 
   // Sum the waves' partial P in a fixed order (w0 + w1 + ...) and store the
@@ -527,13 +543,16 @@ __device__ __forceinline__ int dy_lane_offset(int64_t ldd, int d, int col, int g
   return (int)(((uint32_t)(8 * g4) * (uint32_t)ldd + (uint32_t)c) * 2u);
 }
 
+// valid = false gives a resource of zero bytes: the loads are still issued
+// (so every path through a pipeline has the same loads outstanding for the
+// compiler's wait counts) but read nothing and return zeros.
 template <int Q>
 __device__ __forceinline__ void load_dy_stage(const uint16_t* __restrict__ dY,
                                               int64_t ldd, int T, int vo, int step,
-                                              DyStage<Q>& st) {
+                                              DyStage<Q>& st, bool valid = true) {
   const int64_t row0 = (int64_t)step * 32;
   const int64_t rows = T - row0 < 32 ? T - row0 : 32;
-  const uint32_t bytes = (uint32_t)rows * (uint32_t)ldd * 2u;
+  const uint32_t bytes = valid && rows > 0 ? (uint32_t)rows * (uint32_t)ldd * 2u : 0u;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(dY + row0 * ldd), (short)0, (int)bytes, kBufferDword3);
 #pragma unroll
@@ -588,6 +607,7 @@ constexpr int acc_lds_bytes() {
 struct OutTable {
   int n;
   int overwrite;   // S = result instead of S += result (S is not read)
+  int pending;     // the partial tiles hold earlier deferred contributions: add to them
   int dg_off[kMaxShared + 1];
   int wg_off[kMaxShared + 1];   // first accumulate_wide_kernel work-group of each output
   const uint16_t* dY[kMaxShared];
@@ -721,11 +741,17 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
 
   // Ping-pong pipeline over this wave's n steps: the loads of step j + 1 are
   // in flight while step j is multiplied, and step j + 2 is issued into the
-  // stage step j frees.  Nothing is loaded past the wave's last step, so
-  // before reading a P slot the kernel waits for every load older than the
-  // next step's (8 dY loads behind it, and the 2 NBW + 8 loads of step j + 1
-  // when that step exists).  sched_barrier keeps the scheduler from sinking
-  // loads back next to their consumers.
+  // stage step j frees.  The dY loads of a stage are issued on every pass,
+  // for steps past the wave's last as loads of zero bytes: every path into
+  // the loop header then has the same loads outstanding, and the compiler's
+  // own wait for a stage's dY registers leaves the other stage's loads in
+  // flight (with a conditional reload it had to assume the stage just read
+  // was the last one issued, and drained every load every two steps).  Only
+  // the P copies, which the compiler does not see, are skipped past the last
+  // step, so before reading a P slot the kernel waits for every load older
+  // than the next step's: 8 dY loads, the next step's 2 NBW P copies when it
+  // exists, and its 8 dY loads.  sched_barrier keeps the scheduler from
+  // sinking loads back next to their consumers.
   const int first = s_begin + wl;
   const int n = first < s_end ? (s_end - first + kLanes - 1) / kLanes : 0;
   auto step_of = [&](int jj) { return first + kLanes * jj; };
@@ -733,36 +759,31 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
     DyStage<Q> y0, y1;
     auto wait_slot = [&](int jj) {
       if (jj + 1 < n) vm_wait<kAfterP>();
-      else vm_wait<8>();
+      else vm_wait<16>();
     };
-    p_issue(step_of(0), 0);
-    load_dy_stage<Q>(dY, ldd, T, vo, step_of(0), y0);
-    if (n > 1) {
-      p_issue(step_of(1), 1);
-      load_dy_stage<Q>(dY, ldd, T, vo, step_of(1), y1);
-    }
+    auto stage = [&](int jj, int slot, DyStage<Q>& y) {
+      const bool valid = jj < n;
+      if (valid) p_issue(step_of(jj), slot);
+      load_dy_stage<Q>(dY, ldd, T, vo, valid ? step_of(jj) : first, y, valid);
+    };
+    stage(0, 0, y0);
+    stage(1, 1, y1);
     __builtin_amdgcn_sched_barrier(0);
     for (int jj = 0; jj < n; jj += 2) {
       wait_slot(jj);
       compute_lds(mc, y0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (jj + 2 < n) {
-        lgkm_wait0();
-        p_issue(step_of(jj + 2), 0);
-        load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 2), y0);
-      }
+      lgkm_wait0();
+      stage(jj + 2, 0, y0);
       __builtin_amdgcn_sched_barrier(0);
       if (jj + 1 < n) {
         wait_slot(jj + 1);
         compute_lds(mc, y1, 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (jj + 3 < n) {
-          lgkm_wait0();
-          p_issue(step_of(jj + 3), 1);
-          load_dy_stage<Q>(dY, ldd, T, vo, step_of(jj + 3), y1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      lgkm_wait0();
+      stage(jj + 3, 1, y1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     vm_wait<0>();   // the ring is reused below
   };
@@ -786,6 +807,24 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
   __syncthreads();
 #pragma unroll
   for (int c0 = 0; c0 < NREGW; c0 += CH) {
+    // wave register c0 + 4 jq + e = (q NBW + nb) 4 + e -> tile register
+    auto tile_reg = [&](int jq, int e) {
+      const int lr = c0 + 4 * jq + e;
+      const int q = lr / (NBW * 4);
+      const int rem = lr % (NBW * 4);
+      return (q * NB16 + rpart * NBW + (rem >> 2)) * 4 + (rem & 3);
+    };
+    // earlier deferred contributions of this split, loaded while the round
+    // goes through LDS
+    float old[kPerQ][4];
+    if (my && tab.pending) {
+#pragma unroll
+      for (int u = 0; u < kPerQ; ++u) {
+        const int jq = wl * kPerQ + u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) old[u][e] = jq < CQ ? my[tile_reg(jq, e) * 64 + lane] : 0.0f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < CQ; ++j)
       red[(wave * CQ + j) * 64 + lane] =
@@ -801,13 +840,9 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
         for (int w = 1; w < kLanes; ++w) v += red[((base + w) * CQ + jq) * 64 + lane];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // wave register c0 + 4 jq + e = (q NBW + nb) 4 + e -> tile register
-          const int lr = c0 + 4 * jq + e;
-          const int q = lr / (NBW * 4);
-          const int rem = lr % (NBW * 4);
-          const int i = (q * NB16 + rpart * NBW + (rem >> 2)) * 4 + (rem & 3);
+          const int i = tile_reg(jq, e);
           if (my) {
-            my[i * 64 + lane] = v[e];
+            my[i * 64 + lane] = tab.pending ? old[u][e] + v[e] : v[e];
           } else {
             const int drow = acc_drow<Q, NB16>(dc0, i, lane);
             const int rc = acc_rcol<NB16>(i, lane);
@@ -1013,7 +1048,7 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
     const int i = (q * NB16 + rpart * NBW + (rem >> 2)) * 4 + (rem & 3);
     const float v = acc[il];
     if (my) {
-      my[i * 64 + lane] = v;
+      my[i * 64 + lane] = tab.pending ? my[i * 64 + lane] + v : v;
     } else {
       const int drow = acc_drow<Q, NB16>(dc0, i, lane);
       const int rc = acc_rcol<NB16>(i, lane);
@@ -1150,11 +1185,13 @@ hipError_t launch_finalize(const SketchPlan& p, const OutTable& tab, int r, floa
   return hipGetLastError();
 }
 
+// Partial tiles are used with several splits, and for every call of a
+// deferred chain (defer: keep the result there; tab.pending: add to them).
 template <int Q, int NB16>
 hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, int r,
-                             const uint16_t* Pt, float* part, hipStream_t s) {
+                             const uint16_t* Pt, float* part, bool defer, hipStream_t s) {
   const dim3 grid((unsigned)p.n_dgroups, (unsigned)p.n_split);
-  float* pp = p.n_split > 1 ? part : nullptr;
+  float* pp = p.n_split > 1 || defer || tab.pending ? part : nullptr;
   // masked for a ragged d group only: rows past T read as zero through the
   // buffer loads whatever the template
   bool masked = false;
@@ -1167,16 +1204,16 @@ hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, in
                        tab, T, r, Pt, p.steps, p.steps_per_split, pp);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_split == 1) return e;
+  if (e != hipSuccess || pp == nullptr || defer) return e;
   return launch_finalize<Q, NB16>(p, tab, r, part, s);
 }
 
 template <int NB16>
 hipError_t launch_accumulate_wide(const SketchPlan& p, const OutTable& tab, int T, int r,
-                                  const uint16_t* Pt, float* part, hipStream_t s) {
+                                  const uint16_t* Pt, float* part, bool defer, hipStream_t s) {
   constexpr int DP = kAccWaves / (NB16 / 4);
   const dim3 grid((unsigned)p.n_wg, (unsigned)p.n_split);
-  float* pp = p.n_split > 1 ? part : nullptr;
+  float* pp = p.n_split > 1 || defer || tab.pending ? part : nullptr;
   // masked: a ragged step, a ragged d group, or a work-group whose last d
   // groups lie past its output (their columns must not be read)
   bool masked = (T % 32) != 0;
@@ -1191,7 +1228,7 @@ hipError_t launch_accumulate_wide(const SketchPlan& p, const OutTable& tab, int 
                        tab, T, r, Pt, p.steps, p.steps_per_split, p.n_dgroups, pp);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_split == 1) return e;
+  if (e != hipSuccess || pp == nullptr || defer) return e;
   return launch_finalize<kAccQ, NB16>(p, tab, r, part, s);
 }
 
@@ -1264,7 +1301,9 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
     return o;
   };
   q.off_pt = take((size_t)2 * q.rp * (size_t)q.t_pad * 2);
-  q.off_part = take(q.n_split > 1 ? (size_t)q.n_split * q.d_pad * q.rp * 4 : 0);
+  // (one split's worth even when a single split writes S directly: a
+  // deferred call keeps its result there)
+  q.off_part = take((size_t)q.n_split * q.d_pad * q.rp * 4);
   q.off_gauss = take((size_t)q.p_rows * (size_t)q.k_pad * 2);
   q.total = off;
   *p = q;
@@ -1281,8 +1320,8 @@ bool set_kernel_choice(int which, int mode) {
 
 hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
                          const SketchOut* outs, int T, int k, int r, uint64_t seed,
-                         uint64_t stream, int kind, bool overwrite, char* ws,
-                         hipStream_t s) {
+                         uint64_t stream, int kind, bool overwrite, bool defer, bool pending,
+                         char* ws, hipStream_t s) {
   uint16_t* Pt = reinterpret_cast<uint16_t*>(ws + p.off_pt);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   uint16_t* Ab = reinterpret_cast<uint16_t*>(ws + p.off_gauss);
@@ -1306,6 +1345,7 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
   OutTable tab{};
   tab.n = p.n_out;
   tab.overwrite = overwrite ? 1 : 0;
+  tab.pending = pending ? 1 : 0;
   for (int o = 0; o <= p.n_out; ++o) {
     tab.dg_off[o] = p.dg_off[o];
     tab.wg_off[o] = p.wg_off[o];
@@ -1317,15 +1357,15 @@ hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
     tab.S[o] = outs[o].S;
   }
   if (p.acc_wide) {
-    if (p.rp == 128) return launch_accumulate_wide<8>(p, tab, T, r, Pt, part, s);
-    return launch_accumulate_wide<16>(p, tab, T, r, Pt, part, s);
+    if (p.rp == 128) return launch_accumulate_wide<8>(p, tab, T, r, Pt, part, defer, s);
+    return launch_accumulate_wide<16>(p, tab, T, r, Pt, part, defer, s);
   }
   switch (p.rp) {
-    case 16: return launch_accumulate<kAccQ, 1>(p, tab, T, r, Pt, part, s);
-    case 32: return launch_accumulate<kAccQ, 2>(p, tab, T, r, Pt, part, s);
-    case 64: return launch_accumulate<kAccQ, 4>(p, tab, T, r, Pt, part, s);
-    case 128: return launch_accumulate<kAccQ, 8>(p, tab, T, r, Pt, part, s);
-    default: return launch_accumulate<kAccQ, 16>(p, tab, T, r, Pt, part, s);
+    case 16: return launch_accumulate<kAccQ, 1>(p, tab, T, r, Pt, part, defer, s);
+    case 32: return launch_accumulate<kAccQ, 2>(p, tab, T, r, Pt, part, defer, s);
+    case 64: return launch_accumulate<kAccQ, 4>(p, tab, T, r, Pt, part, defer, s);
+    case 128: return launch_accumulate<kAccQ, 8>(p, tab, T, r, Pt, part, defer, s);
+    default: return launch_accumulate<kAccQ, 16>(p, tab, T, r, Pt, part, defer, s);
   }
 }
 

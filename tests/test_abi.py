@@ -66,7 +66,11 @@ def _sketch(L, **kw):
     (dict(X=MIS), EINVAL), (dict(dY=MIS), EINVAL), (dict(S=P + 1), EINVAL),
     (dict(d=1 << 31), EINVAL), (dict(T=1 << 31), EINVAL), (dict(ldd=1 << 26), EINVAL),
     (dict(ws=None), EWS), (dict(ws_bytes=16), EWS), (dict(ws=P + 16), EWS),
-    (dict(flags=2), EINVAL), (dict(flags=-1), EINVAL), (dict(flags=3), EINVAL),
+    (dict(flags=8), EINVAL), (dict(flags=-1), EINVAL),
+    # deferred chains: a deferring call takes no overwrite flag, and every
+    # call of a chain has tokens
+    (dict(flags=3), EINVAL), (dict(flags=7), EINVAL), (dict(flags=4, T=0), EINVAL),
+    (dict(flags=6, T=0), EINVAL), (dict(flags=5, T=0), EINVAL),
     (dict(flags=1, S=None), EINVAL),
     # the zero fill of an empty first microbatch still needs a valid S
     (dict(flags=1, T=0, S=None), EINVAL), (dict(flags=1, T=0, S=P + 2), EINVAL),
@@ -206,7 +210,8 @@ def _shared(L, n_out=2, **kw):
     (dict(dY=[P, MIS]), EINVAL), (dict(S=[P, P + 2]), EINVAL), (dict(ldx=255), EINVAL),
     (dict(r=0), EINVAL), (dict(kind=5), EINVAL),
     (dict(ws=None), EWS), (dict(ws_bytes=16), EWS),
-    (dict(flags=4), EINVAL), (dict(flags=1, T=0, S=[P, None]), EINVAL),
+    (dict(flags=8), EINVAL), (dict(flags=3), EINVAL), (dict(flags=4, T=0), EINVAL),
+    (dict(flags=1, T=0, S=[P, None]), EINVAL),
     (dict(flags=1, T=0, S=[P, P]), EINVAL),
 ])
 def test_sketch_shared_rejects(L, kw, status):
@@ -301,8 +306,11 @@ def test_sketch_noalloc_rejects_before_any_hip_call(L):
     assert call(S=0) == EINVAL
     assert call(r=0) == EINVAL
     assert call(kind=2) == EINVAL
-    assert call(flags=4) == EINVAL
+    assert call(flags=8) == EINVAL
     assert call(ldd=4095) == EINVAL
+    # no deferred chains in the shared scratch
+    for fl in (2, 4, 6, 5):
+        assert call(flags=fl) == EINVAL
     # the r = 256 layers need more than the 32 MiB of library scratch
     assert L.logra_sketch_ws_bytes(32768, 3584, 18944, 256) > 32 << 20
     assert call(T=32768, d=3584, k=18944, r=256, ldx=18944, ldd=3584) == EWS

@@ -345,6 +345,86 @@ def test_sketch_shared_overwrite(lg):
         assert torch.count_nonzero(e).item() == 0 and not torch.isnan(e).any()
 
 
+DEFER_CASES = [
+    # T, d, k, r, kind, n_mb, accumulate kernel at r > 64 (None: automatic)
+    (2048, 512, 1024, 64, 0, 4, None),    # several splits
+    (128, 256, 256, 4, 0, 3, None),       # a single split (deferred through the partial tile)
+    (1000, 300, 520, 16, 1, 2, None),     # Gaussian basis, ragged
+    (8192, 4096, 512, 64, 0, 4, None),    # the headline's split plan (8 x 32) on a narrow k
+    (512, 384, 256, 256, 0, 3, 1),        # work-group-wide accumulate kernel
+    (512, 384, 256, 256, 0, 2, 0),        # the other kernel at r = 256
+]
+
+
+@pytest.mark.parametrize("T,d,k,r,kind,n_mb,wide", DEFER_CASES)
+def test_sketch_deferred_chain(lg, T, d, k, r, kind, n_mb, wide):
+    # DEFER, DEFER|PENDING, ..., PENDING (+ OVERWRITE): S written once, at the end
+    say("sketch deferred chain", T, d, k, r, kind, n_mb, wide)
+    mbs = [(padded_bf16(synth.host_normal_bf16((T, k), synth.X_ID, mb=mb, salt=d + 3), -(-k // 8) * 8),
+            padded_bf16(synth.host_normal_bf16((T, d), synth.DY_ID, mb=mb, salt=d + 3), -(-d // 8) * 8))
+           for mb in range(n_mb)]
+    S0 = synth.host_normal_f32((d, r), synth.S_ID, salt=T + 3)
+    ctx = lg.kernel_choice(lg.CHOICE_ACC_WIDE, wide) if wide is not None else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        ws = lg.sketch_workspace(T, d, k, r)
+        for overwrite in (False, True):
+            S = S0.clone().cuda()
+            plain = S0.clone().cuda()
+            for mb, (X, dY) in enumerate(mbs):
+                last = mb == n_mb - 1
+                lg.sketch_accumulate(X, dY, S, 1234, 1, kind, ws=ws, defer=not last, pending=mb > 0,
+                                     overwrite=overwrite and last)
+                if not last:
+                    torch.cuda.synchronize()
+                    assert torch.equal(S.cpu(), S0), "a deferring call touched S"
+                lg.sketch_accumulate(X, dY, plain, 1234, 1, kind, overwrite=overwrite and mb == 0)
+            torch.cuda.synchronize()
+            A = oproj.projection(1234, 1, kind, r, k)
+            base = np.zeros((d, r)) if overwrite else S0.numpy().astype(np.float64)
+            ref = osketch.accumulate(base, [(synth.bf16_to_f64(X), synth.bf16_to_f64(dY))
+                                            for X, dY in mbs], A)
+            got = S.cpu().numpy().astype(np.float64)
+            assert rel_fro(got - base, ref - base) < S_TOL
+            assert max_rel(got - base, ref - base) < s_elem_bar(kind)
+            # the same sums as the call-by-call chain, up to fp32 summation order
+            assert rel_fro(got, plain.cpu().numpy()) < 1e-5
+        # deterministic: the same chain again gives the same bits
+        again = S0.clone().cuda()
+        for mb, (X, dY) in enumerate(mbs):
+            last = mb == n_mb - 1
+            lg.sketch_accumulate(X, dY, again, 1234, 1, kind, ws=ws, defer=not last, pending=mb > 0,
+                                 overwrite=last)
+        torch.cuda.synchronize()
+        assert torch.equal(again, S)
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+
+
+def test_sketch_shared_deferred_chain(lg):
+    say("sketch shared deferred chain")
+    T, k, ds, r = 1024, 512, (512, 128, 136), 64
+    X = [synth.host_normal_bf16((T, k), synth.X_ID, mb=mb, salt=9).cuda() for mb in range(3)]
+    dYs = [[synth.host_normal_bf16((T, dd), synth.DY_ID, mb=mb * 10 + o, salt=9).cuda()
+            for o, dd in enumerate(ds)] for mb in range(3)]
+    S = [torch.full((dd, r), float("nan"), device="cuda") for dd in ds]
+    ws = torch.empty(lg.sketch_shared_ws_bytes(T, k, r, ds), dtype=torch.uint8, device="cuda")
+    for mb in range(3):
+        last = mb == 2
+        lg.sketch_accumulate_shared(X[mb], dYs[mb], S, 77, 0, 0, ws=ws, defer=not last,
+                                    pending=mb > 0, overwrite=last)
+    torch.cuda.synchronize()
+    A = oproj.projection(77, 0, 0, r, k)
+    for o, dd in enumerate(ds):
+        ref = osketch.accumulate(np.zeros((dd, r)), [(synth.bf16_to_f64(X[mb]),
+                                                       synth.bf16_to_f64(dYs[mb][o])) for mb in range(3)], A)
+        got = S[o].cpu().numpy().astype(np.float64)
+        assert rel_fro(got, ref) < S_TOL, o
+        assert max_rel(got, ref) < s_elem_bar(0), o
+
+
 @pytest.mark.parametrize("T,d,k,r", [(2048, 1536, 256, 64), (3000, 4096, 512, 16), (4096, 1536, 256, 64),
                                      (1000, 4000, 256, 64)])
 def test_sketch_overflow_stays_infinite(lg, T, d, k, r):
