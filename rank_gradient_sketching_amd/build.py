@@ -16,6 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblogra.so")
+CALIB_LIB = os.path.join(PKG, "liblogra_calib.so")   # measurement helper (a plain device copy)
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "regen.hip", "sketch.hip", "merge.hip", "kl.hip", "kl_sweep.hip", "optim.hip",
@@ -57,8 +58,15 @@ def build(verbose=True):
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    calib_obj = _compile("calib.hip")
+    tmp = CALIB_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, calib_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

@@ -16,11 +16,19 @@
 //   2. 16x16x32 bf16 MFMA with M = W columns, N = W rows, K = r computes the
 //      slice of S A; S enters as a hi/lo bf16 pair, so the product keeps about
 //      16 bits of S;
-//   3. the lane owning 16 contiguous columns of one row loads them (two
-//      16-byte loads issued before the MFMAs), subtracts the scaled product in
-//      fp32 and rounds once to bf16 (v_cvt_pk_bf16_f32, ties to even).
+//   3. the scaled product is subtracted from W in fp32 and rounded once to
+//      bf16 (v_cvt_pk_bf16_f32, ties to even).
 // The M -> column map (m / 4) * 16 + 4 t + m % 4 makes each lane's 16
 // accumulator values land on 16 consecutive columns of one row.
+// Interior tiles of 16-row waves with the sign basis (r <= 64) move W in
+// whole 128-byte lines:
+// each load and store instruction covers 8 rows x 128 B (8 lanes per row),
+// non-temporal both ways, and the products reach that layout through a
+// per-wave fp32 stage in LDS.  In the MFMA layout each instruction touched 16
+// rows x 64 B (half lines); W's read-modify-write alone measured 17.9 us that
+// way and 12.7 us coalesced and non-temporal (d = k = 4096, the rate of a
+// device copy).  Other tiles load W in the MFMA layout and store whole lines
+// through a bf16 stage.
 #include <type_traits>
 
 #include "common.hpp"
@@ -44,10 +52,17 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   constexpr bool kDouble = NKS <= 4 || NT <= 2;
   __shared__ __attribute__((aligned(16))) uint16_t At[(kDouble ? 2 : 1) * kPassCols * LDA];
   __shared__ __attribute__((aligned(16))) uint64_t sgn[GAUSS ? 1 : 4 * RP];
-  // Per-wave staging of one pass's results (WR rows x 64 columns, row stride
-  // kStRow bf16) for row-contiguous stores (interior tiles only).
+  // Per-wave staging of one pass's results (WR rows x 64 columns) for
+  // row-contiguous stores (interior tiles only): fp32 products (row stride
+  // kStRowF floats) where W moves in whole lines (NT = 1), else bf16 results
+  // (row stride kStRow).
+  constexpr bool kLines = NT == 1 && !GAUSS;
   constexpr int kStRow = kPassCols + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t stage[kWaves * WR * kStRow];
+  constexpr int kStRowF = kPassCols + 4;
+  constexpr int kStageBytes = kLines ? WR * kStRowF * 4 : WR * kStRow * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char stage_raw[kWaves * kStageBytes];
+  uint16_t* const stage = reinterpret_cast<uint16_t*>(stage_raw);
+  float* const stagef = reinterpret_cast<float*>(stage_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -56,8 +71,18 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   const int g = lane >> 4;   // K group for operands, row group for D
   // flat grid: column block fastest, so neighbouring work-groups share rows
   const int n_cb = (k + kMergeCols - 1) / kMergeCols;
-  const int rblk = (int)(blockIdx.x / (unsigned)n_cb);
-  const int cb = xcd_spread((int)(blockIdx.x % (unsigned)n_cb), rblk, n_cb);
+  // Whole-line tiles: each XCD takes one contiguous run of row-major tiles
+  // (whole row blocks, so its L2 fetches those S rows once).  Others:
+  // column blocks rotated over the XCDs.
+  int rblk, cb;
+  if constexpr (kLines) {
+    const int task = xcd_runs((int)blockIdx.x, (int)gridDim.x);
+    rblk = task / n_cb;
+    cb = task % n_cb;
+  } else {
+    rblk = (int)(blockIdx.x / (unsigned)n_cb);
+    cb = xcd_spread((int)(blockIdx.x % (unsigned)n_cb), rblk, n_cb);
+  }
   const int col0 = cb * kMergeCols;
   const int row0 = rblk * (WR * kWaves) + wave * WR;
   const int n_pass = min(kMergeCols / kPassCols, (k - col0 + kPassCols - 1) / kPassCols);
@@ -67,6 +92,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   // every work-group).
   auto body = [&](auto masked_c) {
     constexpr bool M = decltype(masked_c)::value;
+    constexpr bool kPreW = kLines && !M;
 
     // S operands: rows row0 + 16 nt + m, K = r columns 32 ks + 8 g + (0..7),
     // as hi/lo bf16.  They do not depend on the column pass and stay in
@@ -196,7 +222,13 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
     auto load_W = [&](int pass, u32x4 wv[NT][2]) {
       const int c0 = col0 + pass * kPassCols;
       const int wc = c0 + 16 * g;
-      if (!M) {
+      if (!M && kLines) {
+        // whole lines: rows row0 + 8 h + lane / 8, columns c0 + 8 (lane % 8) .. + 7
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          wv[0][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              W + (int64_t)(row0 + 8 * h + (lane >> 3)) * ldw + c0 + 8 * (lane & 7)));
+      } else if (!M) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const uint16_t* wr = W + (int64_t)(row0 + 16 * nt + m) * ldw;
@@ -227,8 +259,10 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
       }
       __syncthreads();            // slice `pass` is complete
       if (pass + 1 < n_pass) {
-        load_W(pass + 1, wnxt);
-        __builtin_amdgcn_sched_barrier(0);
+        if (!kPreW) {
+          load_W(pass + 1, wnxt);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (kDouble) build_A(pass + 1, (pass & 1) ? buf0 : buf1);
       }
       const uint16_t* cur_buf = (kDouble && (pass & 1)) ? buf1 : buf0;
@@ -266,6 +300,33 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
 
       // Update and store.
       const int wc = col0 + pass * kPassCols + 16 * g;
+      if constexpr (!M && kLines) {
+        // products to the wave's fp32 stage (row m, columns 16 g + 4 t + v),
+        // back in whole-line order (row 8 h + lane / 8, columns 8 (lane % 8)
+        // .. + 7), subtracted from W there, rounded once and stored.  A wave
+        // only touches its own stage and its LDS operations complete in
+        // order, so no barrier is needed.
+        float* st = stagef + wave * (WR * kStRowF);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          *reinterpret_cast<f32x4*>(st + m * kStRowF + 16 * g + 4 * t) = acc[t][0];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rr = 8 * h + (lane >> 3);
+          const float* src = st + rr * kStRowF + 8 * (lane & 7);
+          const f32x4 p0 = *reinterpret_cast<const f32x4*>(src);
+          const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + 4);
+          const float pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+          u32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            o[q] = pack_bf16x2(bf16_lo(wcur[0][h][q]) - scale * pr[2 * q],
+                               bf16_hi(wcur[0][h][q]) - scale * pr[2 * q + 1]);
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(
+              W + (int64_t)(row0 + rr) * ldw + col0 + pass * kPassCols + 8 * (lane & 7)));
+        }
+        return;
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int row = row0 + 16 * nt + m;
@@ -334,7 +395,16 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) s_raw(nt, ks, sraw[nt][ks]);
     }
-    load_W(0, wa);
+    // Whole-line interior tiles load the W of all four passes up front (8
+    // registers per pass; the loads of a short last column block re-read its
+    // last pass), others one pass ahead.
+    u32x4 wall[kPreW ? 4 : 1][NT][2];
+    if constexpr (kPreW) {
+#pragma unroll
+      for (int ps = 0; ps < 4; ++ps) load_W(ps < n_pass ? ps : n_pass - 1, wall[ps]);
+    } else {
+      load_W(0, wa);
+    }
     __builtin_amdgcn_sched_barrier(0);
     sign_words();
     __syncthreads();
@@ -345,10 +415,17 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) s_split(sraw[nt][ks], sh[nt][ks], sl[nt][ks]);
     }
-    do_pass(0, wa, wb);
-    if (n_pass > 1) do_pass(1, wb, wa);
-    if (n_pass > 2) do_pass(2, wa, wb);
-    if (n_pass > 3) do_pass(3, wb, wa);
+    if constexpr (kPreW) {
+      do_pass(0, wall[0], wb);
+      if (n_pass > 1) do_pass(1, wall[1], wa);
+      if (n_pass > 2) do_pass(2, wall[2], wb);
+      if (n_pass > 3) do_pass(3, wall[3], wa);
+    } else {
+      do_pass(0, wa, wb);
+      if (n_pass > 1) do_pass(1, wb, wa);
+      if (n_pass > 2) do_pass(2, wa, wb);
+      if (n_pass > 3) do_pass(3, wb, wa);
+    }
   };
   const bool edge = MASKED && ((rblk + 1) * (WR * kWaves) > d ||
                                col0 + n_pass * kPassCols > k);

@@ -8,7 +8,8 @@ Two commands, both reading the CSV files rocprofv3 writes with
   traffic  two counter runs (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`,
            `*_counter_collection.csv`) -> HBM bytes per dispatch of each
            kernel, scaled by what the same counters read for a plain device
-           copy of known size (the largest `copyBuffer` dispatch of the run).
+           copy of known size (the largest dispatch of the hand-written
+           `copy_chunks` kernel of liblogra_calib.so in the run).
   mfma     one counter run (`--pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES
            SQ_BUSY_CU_CYCLES SQ_INSTS_VALU`) -> per kernel and grid size: MFMA
            and VALU instructions per dispatch and the matrix-core busy share,
@@ -81,7 +82,7 @@ def stats_table(stats_csv):
     rows = []
     for r in csv.DictReader(open(stats_csv)):
         name = r["Name"]
-        if "logra" not in name and "copyBuffer" not in name:
+        if "logra" not in name and "copyBuffer" not in name and "copy_chunks" not in name:
             continue
         rows.append(dict(kernel=short_name(name), calls=int(r["Calls"]),
                          avg_us=float(r["AverageNs"]) / 1e3, min_us=float(r["MinNs"]) / 1e3,
@@ -102,10 +103,12 @@ def counter_per_kernel(run_dir, counter):
 def traffic(fetch_dir, write_dir, copy_bytes):
     fetch = counter_per_kernel(fetch_dir, "FETCH_SIZE")
     write = counter_per_kernel(write_dir, "WRITE_SIZE")
-    cp_f = max((v for k, vs in fetch.items() if "copyBuffer" in k for v in vs), default=None)
-    cp_w = max((v for k, vs in write.items() if "copyBuffer" in k for v in vs), default=None)
+    def is_copy(k):
+        return "copyBuffer" in k or "copy_chunks" in k
+    cp_f = max((v for k, vs in fetch.items() if is_copy(k) for v in vs), default=None)
+    cp_w = max((v for k, vs in write.items() if is_copy(k) for v in vs), default=None)
     if not cp_f or not cp_w:
-        raise SystemExit("no copyBuffer dispatch found for calibration")
+        raise SystemExit("no copy dispatch (copy_chunks or copyBuffer) found for calibration")
     f_scale = copy_bytes / (cp_f * 1024.0)
     w_scale = copy_bytes / (cp_w * 1024.0)
     kernels = {}
