@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
       int col = colbase + 8 * j;
       if (t0 + 32 > T) t = t < T ? t : T - 1;                       // ragged block only
       if (MASKED && (cnk + 1) * 256 > k) col = col < k ? col : 0;   // ragged chunk only
-      lds_dma16((const void*)(X + (int64_t)t * ldx + col), lds_addr(dst + i * 1024));
+      lds_dma16_nt((const void*)(X + (int64_t)t * ldx + col), lds_addr(dst + i * 1024));
     }
   };
 
@@ -327,8 +327,8 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
       int col = colbase + 8 * j;
       if (t0 + kTileTokens > T) t = t < T ? t : T - 1;              // ragged tile only
       if (MASKED && (cnk + 1) * 256 > k) col = col < k ? col : 0;  // ragged chunk only
-      lds_dma16((const void*)(X + (int64_t)t * ldx + col),
-                lds_addr(dst + (32 * rpart + 4 * i) * (kHalfCols * 2)));
+      lds_dma16_nt((const void*)(X + (int64_t)t * ldx + col),
+                   lds_addr(dst + (32 * rpart + 4 * i) * (kHalfCols * 2)));
     }
   };
 
