@@ -149,20 +149,31 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 // Eight sign bits (bit e set = negative) -> eight bf16 +-1.0 values packed as
 // an MFMA operand (element 2p in the low half of dword p).  With
 // x = b | (b << 15), bit 2p of b sits at 2p and bit 2p+1 at 2p+16; shifting
-// left by 15 - 2p moves them to bits 15 and 31, the two bf16 sign positions.
-// x passes through an empty asm statement so the compiler no longer knows
-// that b < 256: with that knowledge it rewrites each shift of x as a
-// multiply of b by 2^n + 2^(n + 15), a quarter-rate v_mul_lo_u32 in place of
-// a full-rate shift (measured neutral in the kernels, which are not bound by
-// VALU issue, but never slower).
-__device__ __forceinline__ u32x4 signs_to_bf16x8(uint32_t byte) {
+// left by 15 - 2p moves them to bits 15 and 31, the two bf16 sign positions,
+// and v_and_or_b32 keeps those and adds the +1.0 pattern.  x passes through an
+// empty asm statement so the compiler no longer knows that b < 256 (with that
+// knowledge it rewrites each shift as a quarter-rate multiply).  The two masks
+// (k.m = 0x80008000, k.one = 0x3F803F80) come from sign_masks(), made opaque
+// VGPR values once per kernel: one instruction may take only one scalar
+// constant on this target, so with literal masks the compiler emitted a
+// separate and and or per dword (r = 256 projection loop: 970 -> 842 VALU
+// instructions per 64 MFMAs; wide-layer sketch 339 -> 318 us).
+struct SignMasks {
+  uint32_t m, one;
+};
+__device__ __forceinline__ SignMasks sign_masks() {
+  SignMasks k{0x80008000u, 0x3F803F80u};
+  asm volatile("" : "+v"(k.m), "+v"(k.one));
+  return k;
+}
+__device__ __forceinline__ u32x4 signs_to_bf16x8(uint32_t byte, const SignMasks& k) {
   uint32_t x = byte | (byte << 15);
   asm("" : "+v"(x));
   u32x4 v;
-  v[0] = ((x << 15) & 0x80008000u) | 0x3F803F80u;
-  v[1] = ((x << 13) & 0x80008000u) | 0x3F803F80u;
-  v[2] = ((x << 11) & 0x80008000u) | 0x3F803F80u;
-  v[3] = ((x << 9) & 0x80008000u) | 0x3F803F80u;
+  v[0] = ((x << 15) & k.m) | k.one;
+  v[1] = ((x << 13) & k.m) | k.one;
+  v[2] = ((x << 11) & k.m) | k.one;
+  v[3] = ((x << 9) & k.m) | k.one;
   return v;
 }
 

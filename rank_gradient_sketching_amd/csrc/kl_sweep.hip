@@ -186,10 +186,11 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
 #pragma unroll
   for (int i = 0; i < NA; ++i) st.r[i] = 0.0f;
 
+  // logits and direction are read once: non-temporal loads
   const int nfull = V >> 3;
   for (int c = threadIdx.x; c < nfull; c += kSwThreads) {
-    const u32x4 va = *reinterpret_cast<const u32x4*>(zr + 8 * c);
-    const u32x4 vb = *reinterpret_cast<const u32x4*>(dr + 8 * c);
+    const u32x4 va = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(zr + 8 * c));
+    const u32x4 vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dr + 8 * c));
     float zz[8], dd[8];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {

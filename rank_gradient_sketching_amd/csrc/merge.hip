@@ -68,6 +68,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int m = lane & 15;   // A-operand row (column slot) and B/D column (row)
+  const SignMasks smk = sign_masks();
   const int g = lane >> 4;   // K group for operands, row group for D
   // flat grid: column block fastest, so neighbouring work-groups share rows
   const int n_cb = (k + kMergeCols - 1) / kMergeCols;
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
           uint32_t byte = 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) byte |= ((wp[2 * e + half] >> bit) & 1u) << e;
-          u32x4 v = signs_to_bf16x8(byte);
+          u32x4 v = signs_to_bf16x8(byte, smk);
           const int valid = r - 8 * grp;     // rows of this group below r
           if (valid < 8) {
 #pragma unroll

@@ -104,6 +104,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
   const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
   const int step = xcd_spread((int)blockIdx.x, (int)blockIdx.x >> 3, (int)gridDim.x);
   const int t0 = step * 32;
+  const SignMasks smk = sign_masks();
   const int n_chunks = (k + 255) >> 8;
   unsigned char* buf0 = stage0[wave];
   unsigned char* buf1 = stage1[wave];
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const uint32_t byte = (uint32_t)(sw[nb][hc] >> (8 * s)) & 0xFFu;
-          acc[nb] = mfma32(a, signs_to_bf16x8(byte), acc[nb]);
+          acc[nb] = mfma32(a, signs_to_bf16x8(byte, smk), acc[nb]);
         }
       }
     }
@@ -302,6 +303,7 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
   const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
   const int blk = xcd_spread((int)blockIdx.x, (int)blockIdx.x >> 3, (int)gridDim.x);
   const int t0 = blk * kTileTokens;
+  const SignMasks smk = sign_masks();
   const int n_chunks = (k + 255) >> 8;
   const int row_base = rpart * NBW * 32;   // first A row of this wave
 
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
           b = *reinterpret_cast<const u32x4*>(Ab + (int64_t)(row_base + nb * 32 + m) * lda +
                                               colq + 8 * s);
         } else {
-          b = signs_to_bf16x8((uint32_t)(sw[nb][hc] >> (8 * s)) & 0xFFu);
+          b = signs_to_bf16x8((uint32_t)(sw[nb][hc] >> (8 * s)) & 0xFFu, smk);
         }
         acc[0][nb] = mfma32(a0, b, acc[0][nb]);
         acc[1][nb] = mfma32(a1, b, acc[1][nb]);
