@@ -388,47 +388,74 @@ def _time_ms(fn, reps, batches=5):
     return float(np.median(per))
 
 
-def _layer_set_step(lg, synth, wl, cfg, r, kind, stream, n_mb, salt=0):
-    """One decoder layer of a layer-set workload: every projection sketched over
-    n_mb microbatches (q/k/v and gate/up sharing their input) and merged.
-    Returns (fn, algorithmic bytes, tokens) for one optimizer step of the layer."""
+def _layer_set_step(lg, synth, wl, cfg, r, kind, stream, n_mb, n_layers=2):
+    """n_layers distinct decoder layers of a layer-set workload (own buffers; A
+    from seed 1234 + layer, as the workload states), one optimizer step each:
+    every projection sketched over n_mb microbatches as one deferred chain per
+    input group (q/k/v and gate/up share their input), then merged.  The
+    microbatches reuse one set of tensors per layer (each is either far above
+    the Infinity Cache or evicted by the layer's other tensors before its next
+    use).  Returns (fn, algorithmic bytes, algorithmic FLOPs, tokens) for the
+    n_layers layers."""
     T = cfg["T"]
     proj = {n: (d, k) for n, d, k in cfg["projections"]}
     groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
-    seed = 1234 + salt
-    X = [synth.device_normal_bf16((T, proj[g[0]][1]), synth.X_ID, wl, salt=gi)
-         for gi, g in enumerate(groups)]
-    dY = {n: synth.device_normal_bf16((T, proj[n][0]), synth.DY_ID, wl, salt=i)
-          for i, n in enumerate(proj)}
-    W = {n: synth.device_normal_bf16(proj[n], synth.W_ID, wl, salt=i) for i, n in enumerate(proj)}
-    S = {n: torch.zeros(proj[n][0], r, device="cuda") for n in proj}
-    ws = []
-    for g in groups:
-        nb = lg.sketch_shared_ws_bytes(T, proj[g[0]][1], r, [proj[n][0] for n in g])
-        ws.append(torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"))
+    layers = []
+    for layer in range(n_layers):
+        X = [synth.device_normal_bf16((T, proj[g[0]][1]), synth.X_ID, wl, salt=16 * layer + gi)
+             for gi, g in enumerate(groups)]
+        dY = {n: synth.device_normal_bf16((T, proj[n][0]), synth.DY_ID, wl, salt=16 * layer + i)
+              for i, n in enumerate(proj)}
+        W = {n: synth.device_normal_bf16(proj[n], synth.W_ID, wl, salt=16 * layer + i)
+             for i, n in enumerate(proj)}
+        S = {n: torch.zeros(proj[n][0], r, device="cuda") for n in proj}
+        ws = []
+        for g in groups:
+            nb = lg.sketch_shared_ws_bytes(T, proj[g[0]][1], r, [proj[n][0] for n in g])
+            ws.append(torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"))
+        layers.append((1234 + layer, X, dY, W, S, ws))
 
     def step():
-        # the first microbatch starts each S (overwrite); the others add.  The
-        # microbatches' tensors are reused: each is far above the MALL.
-        for mb in range(n_mb):
-            for gi, g in enumerate(groups):
-                lg.sketch_accumulate_shared(X[gi], [dY[n] for n in g], [S[n] for n in g], seed,
-                                            stream, kind, ws=ws[gi], overwrite=mb == 0)
-        for n in proj:
-            lg.merge(W[n], S[n], seed, stream, kind, 1.0, 2e-4)
+        for seed, X, dY, W, S, ws in layers:
+            # one deferred chain per input group: the last microbatch stores S
+            for mb in range(n_mb):
+                last = mb == n_mb - 1
+                for gi, g in enumerate(groups):
+                    lg.sketch_accumulate_shared(X[gi], [dY[n] for n in g], [S[n] for n in g], seed,
+                                                stream, kind, ws=ws[gi], defer=not last,
+                                                pending=mb > 0, overwrite=last)
+            for n in proj:
+                lg.merge(W[n], S[n], seed, stream, kind, 1.0, 2e-4)
 
-    nbytes = n_mb * (sum(2 * T * proj[g[0]][1] for g in groups) +
-                     sum(2 * T * proj[n][0] + 8 * proj[n][0] * r for n in proj)) + \
-        sum(merge_bytes(proj[n][0], proj[n][1], r) for n in proj)
-    return step, nbytes, n_mb * T
+    per_layer_bytes = n_mb * (sum(2 * T * proj[g[0]][1] for g in groups) +
+                              sum(2 * T * proj[n][0] for n in proj)) + \
+        sum(4 * proj[n][0] * r for n in proj) + sum(merge_bytes(proj[n][0], proj[n][1], r) for n in proj)
+    # algorithmic FLOPs: projection 2 T k r per input group, contraction 2 T d r
+    # per projection, merge 2 d k r per weight
+    per_layer_flop = n_mb * 2.0 * T * r * (sum(proj[g[0]][1] for g in groups) +
+                                           sum(proj[n][0] for n in proj)) + \
+        sum(2.0 * proj[n][0] * proj[n][1] * r for n in proj)
+    return step, n_layers * per_layer_bytes, n_layers * per_layer_flop, n_layers * n_mb * T
+
+
+def _mfma_roofline(flop, ms):
+    """Roofline object of an MFMA-bound workload: algorithmic FLOPs over time,
+    against the dense bf16 matrix-core peak."""
+    tf = flop / (ms * 1e-3) / 1e12
+    return dict(bound="mfma", achieved=tf, peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=tf / BF16_MFMA_PEAK_TFLOPS, flop_per_step=flop,
+                note="algorithmic FLOPs (projection 2Tkr per input, contraction 2Tdr, merge 2dkr); "
+                     "the kernels execute more (P and S enter the matrix cores as hi/lo pairs)")
 
 
 def run_other_configs(lg, synth):
-    """Throughput of the other workloads at one GPU: the d = k = 256 layer, one
-    layer of the 1.5B-shaped set at each rank and basis, one layer of the
+    """Throughput of the other workloads at one GPU: the d = k = 256 layer,
+    decoder layers of the 1.5B-shaped set at each rank and basis, of the
     7B-shaped set at r = 256, and the wide layer (d = 5120, k = 25600,
     r = 256, T = 16384).  Each: one optimizer step (every microbatch sketched,
-    then merged), algorithmic bytes / time."""
+    then merged), algorithmic bytes / time; layer sets also as the time of a
+    28-layer pass, extrapolated from two distinct layers; r = 256 also against
+    the matrix-core peak."""
     out = {}
 
     def report(name, ms, nbytes, tokens, **extra):
@@ -453,20 +480,26 @@ def run_other_configs(lg, synth):
     report("layer_d256_r4", _time_ms(small, 50), 2 * sketch_bytes(T, d, k, r) + merge_bytes(d, k, r),
            2 * T)
 
-    for r, kind, stream, label in ((4, 0, 0, "r4"), (16, 0, 0, "r16"), (64, 0, 0, "r64"),
-                                   (64, 0, 1, "r64_refreshed"), (64, 1, 0, "r64_gaussian"),
-                                   (256, 0, 0, "r256")):
-        fn, nbytes, tokens = _layer_set_step(lg, synth, "qwen1p5b_layers", synth.QWEN1P5B, r, kind,
-                                             stream, synth.QWEN1P5B["n_mb"])
-        report(f"qwen1p5b_layer_{label}", _time_ms(fn, 3), nbytes, tokens)
+    n_layers = 2
+    for wl, cfg, r, kind, stream, label, reps in (
+            ("qwen1p5b_layers", synth.QWEN1P5B, 4, 0, 0, "qwen1p5b_layer_r4", 3),
+            ("qwen1p5b_layers", synth.QWEN1P5B, 16, 0, 0, "qwen1p5b_layer_r16", 3),
+            ("qwen1p5b_layers", synth.QWEN1P5B, 64, 0, 0, "qwen1p5b_layer_r64", 3),
+            ("qwen1p5b_layers", synth.QWEN1P5B, 64, 0, 1, "qwen1p5b_layer_r64_refreshed", 3),
+            ("qwen1p5b_layers", synth.QWEN1P5B, 64, 1, 0, "qwen1p5b_layer_r64_gaussian", 3),
+            ("qwen1p5b_layers", synth.QWEN1P5B, 256, 0, 0, "qwen1p5b_layer_r256", 3),
+            ("qwen7b_layers", synth.QWEN7B, 256, 0, 0, "qwen7b_layer_r256", 2)):
+        fn, nbytes, flop, tokens = _layer_set_step(lg, synth, wl, cfg, r, kind, stream, cfg["n_mb"],
+                                                   n_layers)
+        ms = _time_ms(fn, reps) / n_layers
+        extra = dict(pass_28_layers_ms=28 * ms,
+                     pass_note=f"28 x the per-layer time of {n_layers} distinct layers stepped in turn",
+                     layers_measured=n_layers)
+        if r == 256:
+            extra["roofline_mfma"] = _mfma_roofline(flop / n_layers, ms)
+        report(label, ms, nbytes / n_layers, tokens / n_layers, **extra)
         del fn
         torch.cuda.empty_cache()
-
-    fn, nbytes, tokens = _layer_set_step(lg, synth, "qwen7b_layers", synth.QWEN7B, 256, 0, 0,
-                                         synth.QWEN7B["n_mb"])
-    report("qwen7b_layer_r256", _time_ms(fn, 2), nbytes, tokens)
-    del fn
-    torch.cuda.empty_cache()
 
     wide = synth.WORKLOADS["kl_vocab152064"]["wide"]
     d, k, r, T = wide["d"], wide["k"], wide["r"], wide["T"]
@@ -477,11 +510,14 @@ def run_other_configs(lg, synth):
     ws = lg.sketch_workspace(T, d, k, r)
     sk_ms = _time_ms(lambda: lg.sketch_accumulate(X, dY, S, 1234, ws=ws), 5)
     mg_ms = _time_ms(lambda: lg.merge(W, S, 1234, 0, 0, 1.0, 2e-4), 5)
+    flop = 2.0 * T * r * (k + d) + 2.0 * d * k * r
     report("wide_layer_d5120_k25600_r256", sk_ms + mg_ms, sketch_bytes(T, d, k, r) + merge_bytes(d, k, r),
            T, sketch_us=sk_ms * 1e3, sketch_GBps=sketch_bytes(T, d, k, r) / (sk_ms * 1e-3) / 1e9,
            merge_us=mg_ms * 1e3, merge_GBps=merge_bytes(d, k, r) / (mg_ms * 1e-3) / 1e9,
            sketch_mfma=sketch_mfma(T, d, k, r, sk_ms * 1e3),
-           merge_TFLOPs_executed=4.0 * d * k * r / (mg_ms * 1e-3) / 1e12)
+           merge_TFLOPs_executed=4.0 * d * k * r / (mg_ms * 1e-3) / 1e12,
+           roofline_mfma=_mfma_roofline(flop, sk_ms + mg_ms),
+           roofline_mfma_sketch=_mfma_roofline(2.0 * T * r * (k + d), sk_ms))
     del X, dY, W
     torch.cuda.empty_cache()
     return out
@@ -617,6 +653,86 @@ def cpu_baseline(synth, data, budget_s=12.0):
                 host_cores_available=len(os.sched_getaffinity(0)))
 
 
+def cpu_baseline_others(synth):
+    """The oracle, as it stands, on bounded samples of the other workloads
+    (each figure extrapolated linearly and said so): the d = k = 256 layer in
+    full; one layer x one microbatch of the 1.5B-shaped set at r = 64 and of
+    the 7B-shaped set at r = 256 (its first 4096 of 32768 tokens), scaled to
+    a 28-layer pass; 1024 of the 65536 predicted-KL rows, scaled x 64."""
+    from oracle import kl as okl
+    from oracle import merge as omerge
+    from oracle import projection as oproj
+    from oracle import sketch as osketch
+    out = {}
+    # d = k = 256, r = 4: whole steps for about a second
+    c = synth.WORKLOADS["layer_d256_r4"]
+    d, k, r, T = c["d"], c["k"], c["r"], c["T"]
+    mbs = [(synth.bf16_to_f64(synth.host_normal_bf16((T, k), synth.X_ID, "layer_d256_r4", mb)),
+            synth.bf16_to_f64(synth.host_normal_bf16((T, d), synth.DY_ID, "layer_d256_r4", mb)))
+           for mb in range(c["n_mb"])]
+    Wb = synth.bf16_bits(synth.host_normal_bf16((d, k), synth.W_ID, "layer_d256_r4"))
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        A = oproj.projection(c["seed"], c["stream"], c["kind"], r, k)
+        S = osketch.accumulate(np.zeros((d, r)), mbs, A)
+        omerge.merge_bits(Wb, S, A, c["alpha"], c["eta"])
+        n += 1
+    el = time.perf_counter() - t0
+    out["layer_d256_r4"] = dict(value=n * T * c["n_mb"] / el, unit="tokens/s",
+                                sample=f"{n} whole steps (2 x T={T} + merge), {el:.1f} s")
+    # one decoder layer: the sketch of one microbatch on sub-sampled tokens,
+    # scaled by tokens and microbatches; the merge on 256 rows of every W (each
+    # row of W depends only on its row of S), scaled by the rows
+    for name, cfg, r, t_used in (("qwen1p5b_layers_r64", synth.QWEN1P5B, 64, 8192),
+                                 ("qwen7b_layers_r256", synth.QWEN7B, 256, 4096)):
+        T = cfg["T"]
+        proj = {nm: (dd, kk) for nm, dd, kk in cfg["projections"]}
+        groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+        rng = np.random.default_rng(7)
+        t_sk = t_mg = 0.0
+        for g in groups:
+            kk = proj[g[0]][1]
+            A = oproj.projection(1234, 0, 0, r, kk)
+            X = rng.standard_normal((t_used, kk))
+            for nm in g:
+                dd = proj[nm][0]
+                dY = rng.standard_normal((t_used, dd)) * 1e-2
+                t0 = time.perf_counter()
+                S = osketch.sketch_input_first(X, dY, A)
+                t_sk += time.perf_counter() - t0
+                rows = min(dd, 256)
+                Wb = synth.bf16_bits(synth.host_normal_bf16((rows, kk), synth.W_ID, salt=1))
+                t0 = time.perf_counter()
+                omerge.merge_bits(Wb, S[:rows], A, 1.0, 2e-4)
+                t_mg += (time.perf_counter() - t0) * dd / rows
+        per_layer_step = t_sk * (T / t_used) * cfg["n_mb"] + t_mg
+        tokens = T * cfg["n_mb"]
+        out[name] = dict(value=tokens / per_layer_step, unit="tokens/s (per layer step)",
+                         pass_28_layers_s=28 * per_layer_step,
+                         sample=f"one decoder layer (7 projections, each sketched input-first on "
+                                f"its own): sketch of {t_used} of {T} tokens in {t_sk:.2f} s, "
+                                f"scaled x {T // t_used} tokens x {cfg['n_mb']} microbatches; "
+                                f"merge of 256 rows per W, scaled to all rows ({t_mg:.1f} s); "
+                                "the pass is 28 x that")
+    # predicted KL: 512 of 65536 rows
+    kc = synth.WORKLOADS["kl_vocab152064"]
+    V = kc["vocab"]
+    rows = 512
+    z = synth.bf16_to_f64(synth.host_normal_bf16((rows, V), synth.Z_ID, "kl_vocab152064"))
+    dz = synth.host_normal_bf16((rows, V), synth.DIR_ID, "kl_vocab152064")
+    zp = synth.bf16_to_f64(synth.proposal_logits(synth.host_normal_bf16((rows, V), synth.Z_ID,
+                                                                        "kl_vocab152064"), dz, 1.0))
+    t0 = time.perf_counter()
+    for r0 in range(0, rows, 128):
+        okl.kl_rows(z[r0:r0 + 128], zp[r0:r0 + 128], kc["tau"])
+    el = time.perf_counter() - t0
+    n_all = kc["n_resp"] * kc["resp_len"]
+    out["kl_vocab152064"] = dict(value=rows * V * 4 / el / 1e9, unit="GB/s",
+                                 call_s=el * n_all / rows,
+                                 sample=f"{rows} of {n_all} rows x {V} in {el:.1f} s, scaled x {n_all // rows}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -650,6 +766,8 @@ def main():
     others = None if args.no_configs else run_other_configs(lg, synth)
     calib = None if args.no_calib else run_copy_calibration()
     cpu = None if args.no_cpu else cpu_baseline(synth, data, args.cpu_budget)
+    if cpu is not None:
+        cpu["other_configs"] = cpu_baseline_others(synth)
 
     cfg = layer["cfg"]
     sk, mg = layer["sketch"], layer["merge"]
