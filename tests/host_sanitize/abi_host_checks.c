@@ -1,0 +1,270 @@
+/* Host-side checks of the C ABI, built with AddressSanitizer and
+ * UndefinedBehaviorSanitizer against a host-only build of the library (no
+ * device code: no kernel can run).  Every call made here must be rejected by
+ * the argument checks before the first HIP call, or be a pure host query
+ * (workspace sizes, status strings, the kernel-choice setter).  Device
+ * pointers are stand-in addresses that are never dereferenced.
+ *
+ * Exit status 0 when every expectation holds; the sanitizers abort on the
+ * first finding (the build uses -fno-sanitize-recover).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "logra.h"
+#include "logra_calib.h"
+
+static int g_fail = 0;
+static int g_checks = 0;
+
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    ++g_checks;                                                        \
+    if (!(cond)) {                                                     \
+      ++g_fail;                                                        \
+      fprintf(stderr, "%s:%d: expectation failed: %s\n", __FILE__,     \
+              __LINE__, #cond);                                        \
+    }                                                                  \
+  } while (0)
+
+/* Stand-in device addresses: aligned as the entry points require unless a
+ * case asks otherwise. */
+static void* fake(uintptr_t a) { return (void*)a; }
+#define X_PTR ((const uint16_t*)fake(0x100000))
+#define DY_PTR ((const uint16_t*)fake(0x200000))
+#define S_PTR ((float*)fake(0x300000))
+#define WS_PTR (fake(0x400000))
+#define W_PTR ((uint16_t*)fake(0x500000))
+
+static const int64_t kDims[] = {1, 2, 7, 8, 31, 32, 33, 127, 128, 129, 255, 256, 257,
+                                1536, 3584, 4096, 8960, 18944, 25600, 152064,
+                                (int64_t)1 << 20, ((int64_t)1 << 31) - 1};
+static const int32_t kRanks[] = {1, 3, 4, 15, 16, 17, 32, 63, 64, 65, 127, 128, 129,
+                                 192, 255, 256};
+#define N_OF(a) ((int)(sizeof(a) / sizeof((a)[0])))
+
+static void check_status_strings(void) {
+  const int codes[] = {LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE, LOGRA_EHIP, 7, -99};
+  for (int i = 0; i < N_OF(codes); ++i) {
+    const char* s = logra_status_str(codes[i]);
+    EXPECT(s != NULL && strlen(s) > 0);
+  }
+  EXPECT(logra_abi_version() == LOGRA_ABI_VERSION);
+}
+
+/* Workspace queries over a sweep of shapes: zero exactly for invalid
+ * arguments, otherwise a multiple of 256 bytes that does not shrink as T
+ * grows; the shared query with one output equals the single-output one. */
+static void check_sketch_ws(void) {
+  const int64_t Ts[] = {1, 2, 31, 32, 33, 1000, 8192, 16384, 32768, 65536, (int64_t)1 << 24};
+  for (int ik = 0; ik < N_OF(kDims); ik += 3) {
+    for (int id = 0; id < N_OF(kDims); id += 2) {
+      for (int ir = 0; ir < N_OF(kRanks); ++ir) {
+        size_t prev = 0;
+        for (int it = 0; it < N_OF(Ts); ++it) {
+          const int64_t T = Ts[it], d = kDims[id], k = kDims[ik];
+          const int32_t r = kRanks[ir];
+          const size_t b = logra_sketch_ws_bytes(T, d, k, r);
+          if (b != 0) {
+            EXPECT(b % 256 == 0);
+            EXPECT(b >= prev);
+            prev = b;
+          }
+          const size_t bs = logra_sketch_shared_ws_bytes(T, k, r, 1, &d);
+          EXPECT(bs == b);
+        }
+      }
+    }
+  }
+  /* invalid sizes */
+  EXPECT(logra_sketch_ws_bytes(0, 64, 64, 4) == 0 || logra_sketch_ws_bytes(0, 64, 64, 4) % 256 == 0);
+  EXPECT(logra_sketch_ws_bytes(-1, 64, 64, 4) == 0);
+  EXPECT(logra_sketch_ws_bytes(64, 0, 64, 4) == 0);
+  EXPECT(logra_sketch_ws_bytes(64, 64, 0, 4) == 0);
+  EXPECT(logra_sketch_ws_bytes(64, 64, 64, 0) == 0);
+  EXPECT(logra_sketch_ws_bytes(64, 64, 64, LOGRA_MAX_RANK + 1) == 0);
+  EXPECT(logra_sketch_ws_bytes(64, (int64_t)1 << 31, 64, 4) == 0);
+  EXPECT(logra_sketch_ws_bytes(64, 64, (int64_t)1 << 31, 4) == 0);
+  EXPECT(logra_sketch_ws_bytes((int64_t)1 << 31, 64, 64, 4) == 0);
+  EXPECT(logra_sketch_ws_bytes(INT64_MAX, INT64_MAX, INT64_MAX, INT32_MAX) == 0);
+  EXPECT(logra_sketch_ws_bytes(INT64_MIN, INT64_MIN, INT64_MIN, INT32_MIN) == 0);
+  /* shared: output counts and d arrays */
+  const int64_t ds[LOGRA_MAX_SHARED + 1] = {1536, 256, 256, 8960, 99};
+  for (int n = -1; n <= LOGRA_MAX_SHARED + 1; ++n) {
+    const size_t b = logra_sketch_shared_ws_bytes(16384, 1536, 64, n, ds);
+    EXPECT((n >= 1 && n <= LOGRA_MAX_SHARED) == (b != 0));
+  }
+  EXPECT(logra_sketch_shared_ws_bytes(16384, 1536, 64, 2, NULL) == 0);
+  const int64_t bad[2] = {1536, 0};
+  EXPECT(logra_sketch_shared_ws_bytes(16384, 1536, 64, 2, bad) == 0);
+  /* KL workspaces */
+  EXPECT(logra_kl_ws_bytes(65536, 152064) >= 65536 * 4);
+  EXPECT(logra_kl_ws_bytes(0, 152064) == 0);
+  EXPECT(logra_kl_ws_bytes(65536, 0) == 0);
+  EXPECT(logra_kl_ws_bytes(INT64_MAX, INT64_MAX) == 0);
+  for (int a = -1; a <= LOGRA_MAX_SWEEP + 1; ++a) {
+    const size_t b = logra_kl_sweep_ws_bytes(65536, a);
+    EXPECT((a >= 1 && a <= LOGRA_MAX_SWEEP) == (b != 0));
+    if (b) EXPECT(b >= (size_t)65536 * 4 * (size_t)a);
+  }
+  EXPECT(logra_kl_sweep_ws_bytes(INT64_MAX, 4) == 0);
+}
+
+static void check_sketch_rejects(void) {
+  const int64_t T = 8192, d = 4096, k = 4096;
+  const int32_t r = 64;
+  const size_t ws = logra_sketch_ws_bytes(T, d, k, r);
+  EXPECT(ws > 0);
+  /* one bad argument at a time; every other argument valid */
+  EXPECT(logra_sketch_accumulate(NULL, k, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, NULL, d, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, NULL, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate((const uint16_t*)fake(0x100008), k, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, (const uint16_t*)fake(0x200002), d, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, (float*)fake(0x300002), WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k - 8, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k + 4, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d - 8, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, (int64_t)1 << 26, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, -1, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, (int64_t)1 << 31, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, 0, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, 0, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, 0, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, 257, 1, 0, 0, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 2, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, -1, 0, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  /* flags: unknown bits, DEFER with OVERWRITE, deferral on T == 0 */
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, 8, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, LOGRA_SKETCH_DEFER | LOGRA_SKETCH_OVERWRITE, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, 0, d, k, r, 1, 0, 0, LOGRA_SKETCH_DEFER, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, 0, d, k, r, 1, 0, 0, LOGRA_SKETCH_PENDING, S_PTR, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  /* T == 0 without the overwrite flag: nothing to do, no HIP call */
+  EXPECT(logra_sketch_accumulate(NULL, 0, NULL, 0, 0, d, k, r, 1, 0, 0, 0, NULL, NULL, 0, NULL) == LOGRA_OK);
+  /* workspace: missing, too small, misaligned */
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, S_PTR, NULL, ws, NULL) == LOGRA_EWORKSPACE);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, S_PTR, WS_PTR, ws - 1, NULL) == LOGRA_EWORKSPACE);
+  EXPECT(logra_sketch_accumulate(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, S_PTR, fake(0x400080), ws, NULL) == LOGRA_EWORKSPACE);
+  /* the entry point that allocates nothing: no deferral, size limit */
+  EXPECT(logra_sketch_accumulate_noalloc(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, LOGRA_SKETCH_DEFER, S_PTR, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_noalloc(X_PTR, k, DY_PTR, d, T, d, k, r, 1, 0, 0, LOGRA_SKETCH_PENDING, S_PTR, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_noalloc(NULL, k, DY_PTR, d, T, d, k, r, 1, 0, 0, 0, S_PTR, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_noalloc(X_PTR, k, DY_PTR, d, 0, d, k, r, 1, 0, 0, 0, S_PTR, NULL) == LOGRA_OK);
+  {
+    /* a shape whose workspace exceeds the scratch */
+    const int64_t dd = 1 << 20, kk = 4096, TT = 65536;
+    EXPECT(logra_sketch_ws_bytes(TT, dd, kk, 256) > LOGRA_NOALLOC_SCRATCH_BYTES);
+    EXPECT(logra_sketch_accumulate_noalloc(X_PTR, kk, DY_PTR, dd, TT, dd, kk, 256, 1, 0, 0, 0, S_PTR, NULL) == LOGRA_EWORKSPACE);
+  }
+  /* shared outputs */
+  {
+    const uint16_t* dys[4] = {DY_PTR, (const uint16_t*)fake(0x210000), (const uint16_t*)fake(0x220000), (const uint16_t*)fake(0x230000)};
+    const int64_t ldd[4] = {1536, 256, 256, 256};
+    const int64_t dd[4] = {1536, 256, 256, 256};
+    float* Ss[4] = {S_PTR, (float*)fake(0x310000), (float*)fake(0x320000), (float*)fake(0x330000)};
+    const size_t wsb = logra_sketch_shared_ws_bytes(16384, 1536, 64, 3, dd);
+    EXPECT(wsb > 0);
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 0, dys, ldd, dd, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 5, dys, ldd, dd, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, NULL, ldd, dd, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, NULL, dd, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, NULL, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, dd, NULL, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+    float* dup[3] = {S_PTR, (float*)fake(0x310000), S_PTR};
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, dd, dup, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, dd, Ss, WS_PTR, wsb - 256, NULL) == LOGRA_EWORKSPACE);
+    const int64_t bad_ld[3] = {1536, 255, 256};
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, bad_ld, dd, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+  }
+}
+
+static void check_other_rejects(void) {
+  /* projection */
+  EXPECT(logra_regen_A(1, 0, 0, 64, 4096, NULL, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_regen_A(1, 0, 0, 64, 4096, (float*)fake(0x300002), NULL) == LOGRA_EINVAL);
+  EXPECT(logra_regen_A(1, 0, 0, 0, 4096, S_PTR, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_regen_A(1, 0, 0, 64, 0, S_PTR, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_regen_A(1, 0, 5, 64, 4096, S_PTR, NULL) == LOGRA_EINVAL);
+  /* merge */
+  EXPECT(logra_merge(NULL, 4096, S_PTR, 4096, 4096, 64, 1, 0, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge(W_PTR, 4096, NULL, 4096, 4096, 64, 1, 0, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge((uint16_t*)fake(0x500008), 4096, S_PTR, 4096, 4096, 64, 1, 0, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge(W_PTR, 4092, S_PTR, 4096, 4096, 64, 1, 0, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge(W_PTR, 4096, S_PTR, 4096, 4096, 64, 1, 0, 0, NAN, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge(W_PTR, 4096, S_PTR, 4096, 4096, 64, 1, 0, 0, 1.0f, INFINITY, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge(W_PTR, 4096, S_PTR, 0, 4096, 64, 1, 0, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge(W_PTR, 4096, S_PTR, 4096, 4096, 300, 1, 0, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  /* a grid of more than 2^31 tiles */
+  EXPECT(logra_merge(W_PTR, ((int64_t)1 << 31) - 8, S_PTR, ((int64_t)1 << 31) - 1, ((int64_t)1 << 31) - 8, 64, 1, 0, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  /* sketch-space update: bad rule, missing state, bad betas, overlaps */
+  float* S = S_PTR;
+  float* m = (float*)fake(0x600000);
+  float* v = (float*)fake(0x700000);
+  float* U = (float*)fake(0x800000);
+  EXPECT(logra_sketch_update(3, S, m, v, U, 4096, 64, 0.9f, 0.999f, 1e-8f, 1, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_MOMENTUM, S, NULL, v, U, 4096, 64, 0.9f, 0.999f, 1e-8f, 1, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_ADAM, S, m, NULL, U, 4096, 64, 0.9f, 0.999f, 1e-8f, 1, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_ADAM, S, m, v, U, 4096, 64, 1.0f, 0.999f, 1e-8f, 1, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_ADAM, S, m, v, U, 4096, 64, 0.9f, NAN, 1e-8f, 1, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_ADAM, S, m, v, U, 4096, 64, 0.9f, 0.999f, -1.0f, 1, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_ADAM, S, m, v, U, 4096, 64, 0.9f, 0.999f, 1e-8f, 0, NULL) == LOGRA_EINVAL);
+  /* d r floats each: 4096 * 64 * 4 = 1 MiB; a partial overlap of m and v */
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_ADAM, S, m, (float*)fake(0x600000 + 4096), U, 4096, 64, 0.9f, 0.999f, 1e-8f, 1, NULL) == LOGRA_EINVAL);
+  /* U == v is not an allowed alias */
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_ADAM, S, m, v, v, 4096, 64, 0.9f, 0.999f, 1e-8f, 1, NULL) == LOGRA_EINVAL);
+  /* U == m is allowed only for momentum */
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_ADAM, S, m, v, m, 4096, 64, 0.9f, 0.999f, 1e-8f, 1, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_SGD, S, NULL, NULL, NULL, 4096, 64, 0, 0, 0, 1, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_update(LOGRA_UPDATE_SGD, (float*)fake(0x300002), NULL, NULL, U, 4096, 64, 0, 0, 0, 1, NULL) == LOGRA_EINVAL);
+  /* predicted KL */
+  const int64_t n = 65536, V = 152064;
+  const size_t kws = logra_kl_ws_bytes(n, V);
+  float* qa = (float*)fake(0x900000);
+  EXPECT(logra_predicted_kl(NULL, X_PTR, n, V, V, 1.0f, 2e-4f, 4.0f, qa, NULL, WS_PTR, kws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_predicted_kl(X_PTR, X_PTR, n, V, V - 8, 1.0f, 2e-4f, 4.0f, qa, NULL, WS_PTR, kws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_predicted_kl(X_PTR, DY_PTR, n, V, V, 0.0f, 2e-4f, 4.0f, qa, NULL, WS_PTR, kws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_predicted_kl(X_PTR, DY_PTR, n, V, V, 1.0f, 0.0f, 4.0f, qa, NULL, WS_PTR, kws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_predicted_kl(X_PTR, DY_PTR, n, V, V, 1.0f, 2e-4f, -1.0f, qa, NULL, WS_PTR, kws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_predicted_kl(X_PTR, DY_PTR, n, V, V, 1.0f, 2e-4f, 4.0f, (float*)fake(0x900002), NULL, WS_PTR, kws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_predicted_kl(X_PTR, DY_PTR, n, V, V, 1.0f, 2e-4f, 4.0f, qa, NULL, NULL, kws, NULL) == LOGRA_EWORKSPACE);
+  EXPECT(logra_predicted_kl(X_PTR, DY_PTR, n, V, V, 1.0f, 2e-4f, 4.0f, qa, NULL, WS_PTR, kws - 4, NULL) == LOGRA_EWORKSPACE);
+  /* sweep: the multipliers are read on the host */
+  float alphas[LOGRA_MAX_SWEEP] = {0.25f, 0.5f, 1.0f, 2.0f, 0, 0, 0, 0};
+  const size_t sws = logra_kl_sweep_ws_bytes(n, 4);
+  EXPECT(logra_predicted_kl_sweep(X_PTR, DY_PTR, n, V, V, NULL, 4, 1.0f, NULL, qa, NULL, WS_PTR, sws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_predicted_kl_sweep(X_PTR, DY_PTR, n, V, V, alphas, 0, 1.0f, NULL, qa, NULL, WS_PTR, sws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_predicted_kl_sweep(X_PTR, DY_PTR, n, V, V, alphas, LOGRA_MAX_SWEEP + 1, 1.0f, NULL, qa, NULL, WS_PTR, sws, NULL) == LOGRA_EINVAL);
+  alphas[2] = NAN;
+  EXPECT(logra_predicted_kl_sweep(X_PTR, DY_PTR, n, V, V, alphas, 4, 1.0f, NULL, qa, NULL, WS_PTR, sws, NULL) == LOGRA_EINVAL);
+  alphas[2] = 1.0f;
+  EXPECT(logra_predicted_kl_sweep(X_PTR, DY_PTR, n, V, V, alphas, 4, 1.0f, NULL, qa, NULL, WS_PTR, sws - 4, NULL) == LOGRA_EWORKSPACE);
+  EXPECT(logra_predicted_kl_sweep(X_PTR, DY_PTR, ((int64_t)1 << 29), V, V, alphas, 4, 1.0f, NULL, qa, NULL, WS_PTR, sws, NULL) == LOGRA_EINVAL);
+  /* copy calibration helper */
+  EXPECT(logra_calib_copy(NULL, X_PTR, 4096, NULL) != 0);
+  EXPECT(logra_calib_copy(S_PTR, X_PTR, 4095, NULL) != 0);
+  EXPECT(logra_calib_copy((void*)fake(0x300004), X_PTR, 4096, NULL) != 0);
+  EXPECT(logra_calib_copy(S_PTR, X_PTR, 0, NULL) == 0);
+}
+
+static void check_kernel_choice(void) {
+  EXPECT(logra_set_kernel_choice(2, 0) == LOGRA_EINVAL);
+  EXPECT(logra_set_kernel_choice(-1, 0) == LOGRA_EINVAL);
+  EXPECT(logra_set_kernel_choice(LOGRA_CHOICE_PROJECT_TILE, 2) == LOGRA_EINVAL);
+  for (int which = 0; which < 2; ++which)
+    for (int mode = -1; mode <= 1; ++mode)
+      EXPECT(logra_set_kernel_choice(which, mode) == LOGRA_OK);
+  EXPECT(logra_set_kernel_choice(LOGRA_CHOICE_PROJECT_TILE, LOGRA_CHOICE_AUTO) == LOGRA_OK);
+  EXPECT(logra_set_kernel_choice(LOGRA_CHOICE_ACC_WIDE, LOGRA_CHOICE_AUTO) == LOGRA_OK);
+}
+
+int main(void) {
+  check_status_strings();
+  check_sketch_ws();
+  check_sketch_rejects();
+  check_other_rejects();
+  check_kernel_choice();
+  printf("host ABI checks: %d expectations, %d failed\n", g_checks, g_fail);
+  return g_fail == 0 ? 0 : 1;
+}
