@@ -333,16 +333,26 @@ def run_layer_set(lg, synth, reps=10, r=64):
             lg.sketch_accumulate_shared(X[g], [dY[n] for n in names], [S_sh[n] for n in names],
                                         seed, ws=ws_sh[g])
 
+    S_ly = {n: torch.zeros(proj[n][0], r, device="cuda") for n in proj}
+    ws_ly = lg.sketch_layer_workspace(T, r, [(proj[names[0]][1], [proj[n][0] for n in names])
+                                             for _, names in groups])
+
+    def layer():
+        lg.sketch_accumulate_layer([(X[g], [dY[n] for n in names], [S_ly[n] for n in names], seed, 0)
+                                    for g, names in groups], ws=ws_ly)
+
     separate()
     shared()
+    layer()
     torch.cuda.synchronize()
     def rel_fro(a, b):
         a, b = a.astype(np.float64), b.astype(np.float64)
         return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
     err = max(rel_fro(S_sh[n].cpu().numpy(), S_sep[n].cpu().numpy()) for n in proj)
+    err_ly = max(rel_fro(S_ly[n].cpu().numpy(), S_sep[n].cpu().numpy()) for n in proj)
     times = {}
-    for name, fn in (("separate", separate), ("shared", shared)):
+    for name, fn in (("separate", separate), ("shared", shared), ("layer", layer)):
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
@@ -364,8 +374,12 @@ def run_layer_set(lg, synth, reps=10, r=64):
                GBps_separate=b_sep / (times["separate"] * 1e-3) / 1e9,
                GBps_shared=b_sh / (times["shared"] * 1e-3) / 1e9,
                speedup=times["separate"] / times["shared"],
-               shared_vs_separate_rel_fro=err)
-    del X, dY, ws_sep, ws_sh
+               shared_vs_separate_rel_fro=err,
+               us_layer_call=times["layer"] * 1e3,
+               GBps_layer_call=b_sh / (times["layer"] * 1e-3) / 1e9,
+               speedup_layer_call=times["separate"] / times["layer"],
+               layer_vs_separate_rel_fro=err_ly)
+    del X, dY, ws_sep, ws_sh, ws_ly
     torch.cuda.empty_cache()
     return res
 
@@ -388,15 +402,17 @@ def _time_ms(fn, reps, batches=5):
     return float(np.median(per))
 
 
-def _layer_set_step(lg, synth, wl, cfg, r, kind, stream, n_mb, n_layers=2):
+def _layer_set_step(lg, synth, wl, cfg, r, kind, stream, n_mb, n_layers=2, fused=True):
     """n_layers distinct decoder layers of a layer-set workload (own buffers; A
     from seed 1234 + layer, as the workload states), one optimizer step each:
-    every projection sketched over n_mb microbatches as one deferred chain per
-    input group (q/k/v and gate/up share their input), then merged.  The
-    microbatches reuse one set of tensors per layer (each is either far above
-    the Infinity Cache or evicted by the layer's other tensors before its next
-    use).  Returns (fn, algorithmic bytes, algorithmic FLOPs, tokens) for the
-    n_layers layers."""
+    every projection sketched over n_mb microbatches as one deferred chain
+    (q/k/v and gate/up share their input), then merged.  fused: one layer call
+    per microbatch (all four input groups in one projection and one accumulate
+    launch) and one merge call for the seven weights; else one shared call per
+    input group and one merge per weight.  The microbatches reuse one set of
+    tensors per layer (each is either far above the Infinity Cache or evicted
+    by the layer's other tensors before its next use).  Returns (fn,
+    algorithmic bytes, algorithmic FLOPs, tokens) for the n_layers layers."""
     T = cfg["T"]
     proj = {n: (d, k) for n, d, k in cfg["projections"]}
     groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
@@ -409,23 +425,36 @@ def _layer_set_step(lg, synth, wl, cfg, r, kind, stream, n_mb, n_layers=2):
         W = {n: synth.device_normal_bf16(proj[n], synth.W_ID, wl, salt=16 * layer + i)
              for i, n in enumerate(proj)}
         S = {n: torch.zeros(proj[n][0], r, device="cuda") for n in proj}
-        ws = []
-        for g in groups:
-            nb = lg.sketch_shared_ws_bytes(T, proj[g[0]][1], r, [proj[n][0] for n in g])
-            ws.append(torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"))
+        if fused:
+            ws = lg.sketch_layer_workspace(T, r, [(proj[g[0]][1], [proj[n][0] for n in g])
+                                                  for g in groups])
+        else:
+            ws = []
+            for g in groups:
+                nb = lg.sketch_shared_ws_bytes(T, proj[g[0]][1], r, [proj[n][0] for n in g])
+                ws.append(torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"))
         layers.append((1234 + layer, X, dY, W, S, ws))
 
     def step():
         for seed, X, dY, W, S, ws in layers:
-            # one deferred chain per input group: the last microbatch stores S
+            # one deferred chain per layer (or per input group): the last
+            # microbatch stores S
             for mb in range(n_mb):
                 last = mb == n_mb - 1
-                for gi, g in enumerate(groups):
-                    lg.sketch_accumulate_shared(X[gi], [dY[n] for n in g], [S[n] for n in g], seed,
-                                                stream, kind, ws=ws[gi], defer=not last,
-                                                pending=mb > 0, overwrite=last)
-            for n in proj:
-                lg.merge(W[n], S[n], seed, stream, kind, 1.0, 2e-4)
+                flags = dict(defer=not last, pending=mb > 0, overwrite=last)
+                if fused:
+                    lg.sketch_accumulate_layer(
+                        [(X[gi], [dY[n] for n in g], [S[n] for n in g], seed, stream)
+                         for gi, g in enumerate(groups)], kind, ws=ws, **flags)
+                else:
+                    for gi, g in enumerate(groups):
+                        lg.sketch_accumulate_shared(X[gi], [dY[n] for n in g], [S[n] for n in g],
+                                                    seed, stream, kind, ws=ws[gi], **flags)
+            if fused:
+                lg.merge_many([(W[n], S[n], seed, stream) for n in proj], kind, 1.0, 2e-4)
+            else:
+                for n in proj:
+                    lg.merge(W[n], S[n], seed, stream, kind, 1.0, 2e-4)
 
     per_layer_bytes = n_mb * (sum(2 * T * proj[g[0]][1] for g in groups) +
                               sum(2 * T * proj[n][0] for n in proj)) + \
@@ -494,7 +523,17 @@ def run_other_configs(lg, synth):
         ms = _time_ms(fn, reps) / n_layers
         extra = dict(pass_28_layers_ms=28 * ms,
                      pass_note=f"28 x the per-layer time of {n_layers} distinct layers stepped in turn",
-                     layers_measured=n_layers)
+                     layers_measured=n_layers,
+                     launches="one layer sketch call per microbatch, one merge call for the 7 weights")
+        if label == "qwen1p5b_layer_r64":
+            del fn
+            torch.cuda.empty_cache()
+            fn_g = _layer_set_step(lg, synth, wl, cfg, r, kind, stream, cfg["n_mb"], n_layers,
+                                   fused=False)[0]
+            extra["us_per_step_per_group_calls"] = _time_ms(fn_g, reps) / n_layers * 1e3
+            del fn_g
+            torch.cuda.empty_cache()
+            fn = None
         if r == 256:
             extra["roofline_mfma"] = _mfma_roofline(flop / n_layers, ms)
         report(label, ms, nbytes / n_layers, tokens / n_layers, **extra)

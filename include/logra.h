@@ -225,7 +225,7 @@ size_t logra_sketch_shared_ws_bytes(int64_t T, int64_t k, int32_t r, int32_t n_o
  *     outputs in the same order).
  * dY, ldd, d, S: host arrays of n_out entries (1 <= n_out <= LOGRA_MAX_SHARED);
  *     dY[o] device bf16[T x ldd[o]] (same rules as dY above), S[o] device
- *     float[d[o] x r], distinct.
+ *     float[d[o] x r]; no two S ranges overlap.
  * ws: device scratch of logra_sketch_shared_ws_bytes(T, k, r, n_out, d)
  *     bytes, 256-B aligned.
  * T == 0 is a no-op (X, dY and ws are not inspected); with
@@ -237,6 +237,63 @@ int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, in
                                    int32_t flags, int32_t n_out, const uint16_t* const* dY,
                                    const int64_t* ldd, const int64_t* d, float* const* S,
                                    void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Limits of logra_sketch_accumulate_layer: input groups per call, and
+ * outputs per call over all groups. */
+#define LOGRA_MAX_GROUPS 4
+#define LOGRA_MAX_LAYER_OUT 8
+
+/* One input group of logra_sketch_accumulate_layer: X (device bf16[T x ldx],
+ * rules as in logra_sketch_accumulate) with k columns and A from (seed,
+ * stream), feeding n_out (1..LOGRA_MAX_SHARED) outputs: dY[o] (device
+ * bf16[T x ldd[o]]) with d[o] columns into S[o] (device float[d[o] x r]).
+ * Entries past n_out are ignored.  A plain C struct, passed in host memory. */
+typedef struct logra_sketch_group {
+  const uint16_t* X;
+  int64_t ldx;
+  int64_t k;
+  uint64_t seed;
+  uint64_t stream;
+  int32_t n_out;
+  const uint16_t* dY[LOGRA_MAX_SHARED];
+  int64_t ldd[LOGRA_MAX_SHARED];
+  int64_t d[LOGRA_MAX_SHARED];
+  float* S[LOGRA_MAX_SHARED];
+} logra_sketch_group;
+
+/* Bytes of workspace logra_sketch_accumulate_layer needs (only k, n_out and
+ * d of the groups are read).  Returns 0 for invalid sizes. */
+size_t logra_sketch_layer_ws_bytes(int64_t T, int32_t r, int32_t n_groups,
+                                   const logra_sketch_group* groups);
+
+/*
+ * logra_sketch_accumulate_layer - the sketches of a whole layer set for one
+ * microbatch: S_o += dY_o^T (X_g A_g^T) for every output o of every input
+ * group g, in one projection launch (every group's token blocks, largest k
+ * first) and one accumulate launch (every output's column groups), plus one
+ * split reduction at the end of a call or chain.
+ * [LoGRA] Sketch (wispaper.ai summary): each weight's sketch is accumulated
+ * input-first per microbatch; the cloud.baidu.com evaluation guide, section
+ * on the evaluated objects (first bullet), sketches selected attention and
+ * MLP projections of each decoder layer: q/k/v (one input), o, gate/up (one
+ * input) and down are four input groups with seven outputs.  Equal, output by
+ * output, to logra_sketch_accumulate_shared per group up to fp32 summation
+ * order.
+ *
+ * T, r, kind, flags: as in logra_sketch_accumulate; T is every group's token
+ *     count, and every flag applies to every output (a deferred chain keeps
+ *     the same groups and outputs in the same order).
+ * groups: host array of n_groups (1..LOGRA_MAX_GROUPS) entries with
+ *     LOGRA_MAX_LAYER_OUT outputs at most in all; no two S ranges overlap.
+ * ws: device scratch of logra_sketch_layer_ws_bytes(T, r, n_groups, groups)
+ *     bytes, 256-B aligned (each group's projected input, the partial sums).
+ * T == 0 is a no-op (no X, dY or ws inspected); with LOGRA_SKETCH_OVERWRITE
+ *     it sets every S to zero.
+ * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
+ */
+int logra_sketch_accumulate_layer(int64_t T, int32_t r, int kind, int32_t flags,
+                                  int32_t n_groups, const logra_sketch_group* groups, void* ws,
+                                  size_t ws_bytes, hipStream_t s);
 
 /*
  * logra_merge - W <- RNE_bf16(W - alpha * eta * S A), in place.
@@ -258,6 +315,36 @@ int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, in
 int logra_merge(uint16_t* W, int64_t ldw, const float* S, int64_t d, int64_t k,
                 int32_t r, uint64_t seed, uint64_t stream, int kind,
                 float alpha, float eta, hipStream_t s);
+
+/* Largest number of weights one logra_merge_many call takes. */
+#define LOGRA_MAX_MERGE 8
+
+/* One weight of logra_merge_many: W (device bf16[d x ldw]) and its sketch S
+ * (device float[d x r]), A from (seed, stream); rules as in logra_merge. */
+typedef struct logra_merge_item {
+  uint16_t* W;
+  int64_t ldw;
+  const float* S;
+  int64_t d;
+  int64_t k;
+  uint64_t seed;
+  uint64_t stream;
+} logra_merge_item;
+
+/*
+ * logra_merge_many - logra_merge for n (1..LOGRA_MAX_MERGE) weights that
+ * share r, kind, alpha and eta (the weights of one layer set), in one launch.
+ * [LoGRA] Sketch: every sketched weight takes W <- W - alpha eta U A after the
+ * step; the step size alpha comes from the one predicted-KL controller.
+ * Bit-identical, weight by weight, to n logra_merge calls (the same tiles
+ * and arithmetic; only the launch is shared).
+ *
+ * items: host array of n entries.  No W's rows may overlap another W's or
+ *     any S (W is written in place while every S is read).
+ * Returns LOGRA_OK, LOGRA_EINVAL or LOGRA_EHIP.
+ */
+int logra_merge_many(int32_t n, const logra_merge_item* items, int32_t r, int kind,
+                     float alpha, float eta, hipStream_t s);
 
 /* Sketch-space update rules for logra_sketch_update. */
 #define LOGRA_UPDATE_SGD 0      /* U = S */

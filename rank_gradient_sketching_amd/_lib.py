@@ -65,6 +65,35 @@ SIGNATURES = {
                                                 c_vp, ctypes.c_size_t, c_vp]),
 }
 
+MAX_SHARED, MAX_GROUPS, MAX_LAYER_OUT, MAX_MERGE = 4, 4, 8, 8
+
+
+class SketchGroup(ctypes.Structure):
+    """logra_sketch_group of include/logra.h (field for field)."""
+    _fields_ = [("X", c_vp), ("ldx", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("seed", ctypes.c_uint64), ("stream", ctypes.c_uint64), ("n_out", ctypes.c_int32),
+                ("dY", c_vp * MAX_SHARED), ("ldd", ctypes.c_int64 * MAX_SHARED),
+                ("d", ctypes.c_int64 * MAX_SHARED), ("S", c_vp * MAX_SHARED)]
+
+
+class MergeItem(ctypes.Structure):
+    """logra_merge_item of include/logra.h (field for field)."""
+    _fields_ = [("W", c_vp), ("ldw", ctypes.c_int64), ("S", c_vp), ("d", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("seed", ctypes.c_uint64), ("stream", ctypes.c_uint64)]
+
+
+SIGNATURES.update({
+    "logra_sketch_layer_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32,
+                                                      ctypes.c_int32,
+                                                      ctypes.POINTER(SketchGroup)]),
+    "logra_sketch_accumulate_layer": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int,
+                                                     ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.POINTER(SketchGroup), c_vp,
+                                                     ctypes.c_size_t, c_vp]),
+    "logra_merge_many": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(MergeItem), ctypes.c_int32,
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_float, c_vp]),
+})
+
 OK, EINVAL, EWORKSPACE, EHIP = 0, -1, -2, -3
 
 

@@ -137,7 +137,7 @@ def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None, overwr
     return S
 
 
-MAX_SHARED = 4
+MAX_SHARED = _lib.MAX_SHARED
 
 
 def sketch_shared_ws_bytes(T, k, r, ds):
@@ -183,6 +183,106 @@ def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=Non
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(X))
     _lib.check(st, "logra_sketch_accumulate_shared")
     return list(Ss)
+
+
+MAX_GROUPS = _lib.MAX_GROUPS
+MAX_LAYER_OUT = _lib.MAX_LAYER_OUT
+
+
+def _group_array(groups):
+    """ctypes array of logra_sketch_group from [(X, dYs, Ss, seed, stream)];
+    also returns T and r (checked equal across groups)."""
+    if not 1 <= len(groups) <= MAX_GROUPS:
+        raise ValueError(f"between 1 and {MAX_GROUPS} input groups")
+    arr = (_lib.SketchGroup * len(groups))()
+    T = r = None
+    n_out = 0
+    for g, (X, dYs, Ss, seed, stream) in enumerate(groups):
+        _require(X, "X", torch.bfloat16, 2)
+        Tg, k, ldx = _rows(X, "X")
+        if T is not None and Tg != T:
+            raise ValueError("every group's X must have the same number of rows")
+        T = Tg
+        if not 1 <= len(dYs) <= MAX_SHARED or len(dYs) != len(Ss):
+            raise ValueError(f"between 1 and {MAX_SHARED} (dY, S) pairs per group")
+        n_out += len(dYs)
+        q = arr[g]
+        q.X, q.ldx, q.k, q.seed, q.stream, q.n_out = X.data_ptr(), ldx, k, seed, stream, len(dYs)
+        for o, (dY, S) in enumerate(zip(dYs, Ss)):
+            _require(dY, "dY", torch.bfloat16, 2)
+            _require(S, "S", torch.float32, 2)
+            T2, d, ldd = _rows(dY, "dY")
+            if T2 != T:
+                raise ValueError(f"X has {T} rows but a dY has {T2}")
+            if S.shape[0] != d or not S.is_contiguous():
+                raise ValueError("each S must be a contiguous (d, r) float32 tensor")
+            if r is not None and S.shape[1] != r:
+                raise ValueError("every S must have the same rank r")
+            r = S.shape[1]
+            q.dY[o], q.ldd[o], q.d[o], q.S[o] = dY.data_ptr(), ldd, d, S.data_ptr()
+    if n_out > MAX_LAYER_OUT:
+        raise ValueError(f"at most {MAX_LAYER_OUT} outputs in all")
+    return arr, T, r
+
+
+def sketch_layer_ws_bytes(T, r, groups):
+    """Workspace bytes of sketch_accumulate_layer; groups: [(k, [d, ...])]."""
+    arr = (_lib.SketchGroup * max(1, len(groups)))()
+    for g, (k, ds) in enumerate(groups):
+        arr[g].k, arr[g].n_out = int(k), len(ds)
+        for o, d in enumerate(ds):
+            arr[g].d[o] = int(d)
+    return int(_lib.lib().logra_sketch_layer_ws_bytes(T, r, len(groups), arr))
+
+
+def sketch_layer_workspace(T, r, groups, device="cuda"):
+    """A workspace tensor for sketch_accumulate_layer; groups: [(k, [d, ...])]."""
+    return torch.empty(max(sketch_layer_ws_bytes(T, r, groups), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def sketch_accumulate_layer(groups, kind=RADEMACHER, ws=None, overwrite=False, defer=False,
+                            pending=False):
+    """The sketches of a layer set for one microbatch in one projection and one
+    accumulate launch.  groups: up to 4 entries (X, dYs, Ss, seed, stream), each
+    an input X shared by its outputs (dY_o, S_o), up to 8 outputs in all:
+    S_o += dY_o^T (X A^T).  overwrite, defer and pending as in
+    sketch_accumulate, for every S_o; returns None."""
+    arr, T, r = _group_array(groups)
+    X0 = groups[0][0]
+    if ws is None:
+        ws = sketch_layer_workspace(T, r, [(g[0].shape[1], [dy.shape[1] for dy in g[1]])
+                                           for g in groups], X0.device)
+    st = _lib.lib().logra_sketch_accumulate_layer(
+        T, r, kind, _sketch_flags(overwrite, defer, pending), len(groups), arr, ws.data_ptr(),
+        ws.numel() * ws.element_size(), _stream(X0))
+    _lib.check(st, "logra_sketch_accumulate_layer")
+
+
+MAX_MERGE = _lib.MAX_MERGE
+
+
+def merge_many(items, kind=RADEMACHER, alpha=1.0, eta=1.0):
+    """merge for up to 8 weights in one launch; items: [(W, S, seed, stream)],
+    every S of the same rank.  Bit-identical to one merge call per item."""
+    if not 1 <= len(items) <= MAX_MERGE:
+        raise ValueError(f"between 1 and {MAX_MERGE} weights")
+    arr = (_lib.MergeItem * len(items))()
+    r = None
+    for i, (W, S, seed, stream) in enumerate(items):
+        _require(W, "W", torch.bfloat16, 2)
+        _require(S, "S", torch.float32, 2)
+        d, k, ldw = _rows(W, "W")
+        if S.shape[0] != d or not S.is_contiguous():
+            raise ValueError("each S must be a contiguous (d, r) float32 tensor")
+        if r is not None and S.shape[1] != r:
+            raise ValueError("every S must have the same rank r")
+        r = S.shape[1]
+        arr[i].W, arr[i].ldw, arr[i].S, arr[i].d, arr[i].k = W.data_ptr(), ldw, S.data_ptr(), d, k
+        arr[i].seed, arr[i].stream = seed, stream
+    st = _lib.lib().logra_merge_many(len(items), arr, r, kind, float(alpha), float(eta),
+                                     _stream(items[0][0]))
+    _lib.check(st, "logra_merge_many")
 
 
 def merge(W, S, seed, stream=0, kind=RADEMACHER, alpha=1.0, eta=1.0):

@@ -25,6 +25,9 @@ bool aligned(const void* p, uintptr_t a) {
 }
 
 static_assert(LOGRA_MAX_SHARED == logra::kMaxShared, "shared-output limit");
+static_assert(LOGRA_MAX_GROUPS == logra::kMaxGroups, "input-group limit");
+static_assert(LOGRA_MAX_LAYER_OUT == logra::kMaxOut, "outputs per call");
+static_assert(LOGRA_MAX_MERGE == logra::kMaxMerge, "weights per merge call");
 static_assert(LOGRA_NOALLOC_SCRATCH_BYTES == logra::kNoallocScratchBytes, "no-alloc scratch size");
 
 constexpr int64_t kDimLimit = int64_t(1) << 31;
@@ -69,7 +72,7 @@ int logra_set_kernel_choice(int which, int mode) {
 }
 
 size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r) {
-  logra::SketchPlan p;
+  logra::SketchPlan p{};
   if (!logra::make_sketch_plan(T, 1, &d, k, r, &p)) return 0;
   return p.total;
 }
@@ -77,24 +80,43 @@ size_t logra_sketch_ws_bytes(int64_t T, int64_t d, int64_t k, int32_t r) {
 size_t logra_sketch_shared_ws_bytes(int64_t T, int64_t k, int32_t r, int32_t n_out,
                                     const int64_t* d) {
   if (d == nullptr || n_out < 1 || n_out > LOGRA_MAX_SHARED) return 0;
-  logra::SketchPlan p;
+  logra::SketchPlan p{};
   if (!logra::make_sketch_plan(T, n_out, d, k, r, &p)) return 0;
+  return p.total;
+}
+
+size_t logra_sketch_layer_ws_bytes(int64_t T, int32_t r, int32_t n_groups,
+                                   const logra_sketch_group* groups) {
+  if (groups == nullptr || n_groups < 1 || n_groups > LOGRA_MAX_GROUPS) return 0;
+  int64_t k[LOGRA_MAX_GROUPS];
+  int n_out[LOGRA_MAX_GROUPS];
+  int64_t d[LOGRA_MAX_LAYER_OUT];
+  int o = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    k[g] = groups[g].k;
+    n_out[g] = groups[g].n_out;
+    if (n_out[g] < 1 || n_out[g] > LOGRA_MAX_SHARED || o + n_out[g] > LOGRA_MAX_LAYER_OUT)
+      return 0;
+    for (int i = 0; i < n_out[g]; ++i) d[o++] = groups[g].d[i];
+  }
+  logra::SketchPlan p{};
+  if (!logra::make_sketch_plan_groups(T, n_groups, k, n_out, d, r, &p)) return 0;
   return p.total;
 }
 
 namespace {
 
-// Checks shared by the single- and multi-output sketch entry points; fills
-// the plan.  T == 0 is reported as LOGRA_OK with *run = false.
+// Checks shared by every sketch entry point; fills the plan.  T == 0 is
+// reported as LOGRA_OK with *run = false.
 constexpr int32_t kDeferFlags = LOGRA_SKETCH_DEFER | LOGRA_SKETCH_PENDING;
 
-int sketch_checks(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t r,
-                  int kind, int32_t flags, int32_t n_out, const logra::SketchOut* outs,
-                  void* ws, size_t ws_bytes, logra::SketchPlan* plan, bool* run,
+int sketch_checks(const logra::SketchGroup* groups, int n_groups, int64_t T, int32_t r,
+                  int kind, int32_t flags, const logra::SketchOut* outs, void* ws,
+                  size_t ws_bytes, logra::SketchPlan* plan, bool* run,
                   bool allow_defer = true) {
   *run = false;
-  if (n_out < 1 || n_out > LOGRA_MAX_SHARED) return LOGRA_EINVAL;
-  if (!dim_ok(k) || !rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
+  if (n_groups < 1 || n_groups > LOGRA_MAX_GROUPS) return LOGRA_EINVAL;
+  if (!rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
   if ((flags & ~(LOGRA_SKETCH_OVERWRITE | kDeferFlags)) != 0) return LOGRA_EINVAL;
   if ((flags & kDeferFlags) != 0) {
     // a deferred chain: every call has tokens; a deferring call writes no S,
@@ -102,7 +124,18 @@ int sketch_checks(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t 
     if (!allow_defer || T < 1) return LOGRA_EINVAL;
     if ((flags & LOGRA_SKETCH_DEFER) && (flags & LOGRA_SKETCH_OVERWRITE)) return LOGRA_EINVAL;
   }
-  int64_t d[LOGRA_MAX_SHARED];
+  int64_t k[LOGRA_MAX_GROUPS];
+  int n_out_g[LOGRA_MAX_GROUPS];
+  int64_t d[LOGRA_MAX_LAYER_OUT];
+  int n_out = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    if (!dim_ok(groups[g].k)) return LOGRA_EINVAL;
+    if (groups[g].n_out < 1 || groups[g].n_out > LOGRA_MAX_SHARED) return LOGRA_EINVAL;
+    if (n_out + groups[g].n_out > LOGRA_MAX_LAYER_OUT) return LOGRA_EINVAL;
+    k[g] = groups[g].k;
+    n_out_g[g] = groups[g].n_out;
+    n_out += groups[g].n_out;
+  }
   for (int o = 0; o < n_out; ++o) {
     if (!dim_ok(outs[o].d)) return LOGRA_EINVAL;
     d[o] = outs[o].d;
@@ -111,17 +144,26 @@ int sketch_checks(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t 
   if (T == 0 && (flags & LOGRA_SKETCH_OVERWRITE) == 0) return LOGRA_OK;
   // S of every output: needed by the kernels, and by the zero fill at T == 0
   // (a deferring call never touches S, but its S must still be a valid
-  // argument)
+  // argument).  One accumulator per output: no two S ranges (d x r floats)
+  // overlap.
   for (int o = 0; o < n_out; ++o) {
     if (outs[o].S == nullptr || !aligned(outs[o].S, 4)) return LOGRA_EINVAL;
-    for (int o2 = 0; o2 < o; ++o2)
-      if (outs[o2].S == outs[o].S) return LOGRA_EINVAL;   // one accumulator per output
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(outs[o].S);
+    const uintptr_t hi = lo + 4 * (uintptr_t)outs[o].d * (uintptr_t)r;
+    for (int o2 = 0; o2 < o; ++o2) {
+      const uintptr_t lo2 = reinterpret_cast<uintptr_t>(outs[o2].S);
+      const uintptr_t hi2 = lo2 + 4 * (uintptr_t)outs[o2].d * (uintptr_t)r;
+      if (lo < hi2 && lo2 < hi) return LOGRA_EINVAL;
+    }
   }
   if (T == 0) {
     *run = true;
     return LOGRA_OK;
   }
-  if (X == nullptr || !aligned(X, 16) || !ld_ok(ldx, k)) return LOGRA_EINVAL;
+  for (int g = 0; g < n_groups; ++g) {
+    const logra::SketchGroup& q = groups[g];
+    if (q.X == nullptr || !aligned(q.X, 16) || !ld_ok(q.ldx, q.k)) return LOGRA_EINVAL;
+  }
   for (int o = 0; o < n_out; ++o) {
     const logra::SketchOut& q = outs[o];
     if (q.dY == nullptr) return LOGRA_EINVAL;
@@ -129,10 +171,24 @@ int sketch_checks(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t 
     // dY is read through 32-bit buffer offsets spanning 32 rows of 2 * ldd bytes
     if (q.ldd >= kDyStrideLimit) return LOGRA_EINVAL;
   }
-  if (!logra::make_sketch_plan(T, n_out, d, k, r, plan)) return LOGRA_EINVAL;
+  if (!logra::make_sketch_plan_groups(T, n_groups, k, n_out_g, d, r, plan)) return LOGRA_EINVAL;
   if (ws == nullptr || ws_bytes < plan->total || !aligned(ws, 256)) return LOGRA_EWORKSPACE;
   *run = true;
   return LOGRA_OK;
+}
+
+// After sketch_checks set *run: the zero fill of every output at T == 0 (the
+// plan is not built then; n_out is the call's own output count), else the
+// kernels.
+int run_sketch(const logra::SketchPlan& p, const logra::SketchGroup* groups,
+               const logra::SketchOut* outs, int n_out, int64_t T, int32_t r, int kind,
+               int32_t flags, void* ws, hipStream_t s) {
+  if (T == 0) return hip_status(logra::launch_zero_outputs(outs, n_out, r, s));
+  return hip_status(logra::launch_sketch(p, groups, outs, (int)T, r, kind,
+                                         (flags & LOGRA_SKETCH_OVERWRITE) != 0,
+                                         (flags & LOGRA_SKETCH_DEFER) != 0,
+                                         (flags & LOGRA_SKETCH_PENDING) != 0,
+                                         static_cast<char*>(ws), s));
 }
 
 }  // namespace
@@ -142,30 +198,27 @@ int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
                             int32_t r, uint64_t seed, uint64_t stream, int kind,
                             int32_t flags, float* S, void* ws, size_t ws_bytes,
                             hipStream_t s) {
+  const logra::SketchGroup grp{X, ldx, k, seed, stream, 1};
   const logra::SketchOut out{dY, ldd, d, S};
-  logra::SketchPlan p;
+  logra::SketchPlan p{};
   bool run = false;
-  const int st = sketch_checks(X, ldx, T, k, r, kind, flags, 1, &out, ws, ws_bytes, &p, &run);
+  const int st = sketch_checks(&grp, 1, T, r, kind, flags, &out, ws, ws_bytes, &p, &run);
   if (st != LOGRA_OK || !run) return st;
-  if (T == 0) return hip_status(logra::launch_zero_outputs(&out, 1, r, s));
-  return hip_status(logra::launch_sketch(p, X, ldx, &out, (int)T, (int)k, r, seed, stream,
-                                         kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
-                                         (flags & LOGRA_SKETCH_DEFER) != 0,
-                                         (flags & LOGRA_SKETCH_PENDING) != 0,
-                                         static_cast<char*>(ws), s));
+  return run_sketch(p, &grp, &out, 1, T, r, kind, flags, ws, s);
 }
 
 int logra_sketch_accumulate_noalloc(const uint16_t* X, int64_t ldx, const uint16_t* dY,
                                     int64_t ldd, int64_t T, int64_t d, int64_t k, int32_t r,
                                     uint64_t seed, uint64_t stream, int kind, int32_t flags,
                                     float* S, hipStream_t s) {
+  const logra::SketchGroup grp{X, ldx, k, seed, stream, 1};
   const logra::SketchOut out{dY, ldd, d, S};
   // every argument and the scratch size are checked before the first HIP call
   // (the scratch-address lookup); the checks see a stand-in workspace of the
   // full scratch size at a 256-byte-aligned address
-  logra::SketchPlan p;
+  logra::SketchPlan p{};
   bool run = false;
-  const int st = sketch_checks(X, ldx, T, k, r, kind, flags, 1, &out,
+  const int st = sketch_checks(&grp, 1, T, r, kind, flags, &out,
                                reinterpret_cast<void*>(uintptr_t(256)),
                                LOGRA_NOALLOC_SCRATCH_BYTES, &p, &run, /*allow_defer=*/false);
   if (st != LOGRA_OK || !run) return st;
@@ -173,11 +226,7 @@ int logra_sketch_accumulate_noalloc(const uint16_t* X, int64_t ldx, const uint16
   void* ws = nullptr;
   const int sh = hip_status(logra::noalloc_scratch(s, &ws));
   if (sh != LOGRA_OK) return sh;
-  return hip_status(logra::launch_sketch(p, X, ldx, &out, (int)T, (int)k, r, seed, stream,
-                                         kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
-                                         (flags & LOGRA_SKETCH_DEFER) != 0,
-                                         (flags & LOGRA_SKETCH_PENDING) != 0,
-                                         static_cast<char*>(ws), s));
+  return run_sketch(p, &grp, &out, 1, T, r, kind, flags, ws, s);
 }
 
 int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, int64_t k,
@@ -187,32 +236,90 @@ int logra_sketch_accumulate_shared(const uint16_t* X, int64_t ldx, int64_t T, in
                                    void* ws, size_t ws_bytes, hipStream_t s) {
   if (n_out < 1 || n_out > LOGRA_MAX_SHARED) return LOGRA_EINVAL;
   if (dY == nullptr || ldd == nullptr || d == nullptr || S == nullptr) return LOGRA_EINVAL;
+  const logra::SketchGroup grp{X, ldx, k, seed, stream, n_out};
   logra::SketchOut outs[LOGRA_MAX_SHARED];
   for (int o = 0; o < n_out; ++o) outs[o] = logra::SketchOut{dY[o], ldd[o], d[o], S[o]};
-  logra::SketchPlan p;
+  logra::SketchPlan p{};
   bool run = false;
-  const int st = sketch_checks(X, ldx, T, k, r, kind, flags, n_out, outs, ws, ws_bytes, &p,
-                               &run);
+  const int st = sketch_checks(&grp, 1, T, r, kind, flags, outs, ws, ws_bytes, &p, &run);
   if (st != LOGRA_OK || !run) return st;
-  if (T == 0) return hip_status(logra::launch_zero_outputs(outs, n_out, r, s));
-  return hip_status(logra::launch_sketch(p, X, ldx, outs, (int)T, (int)k, r, seed, stream,
-                                         kind, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
-                                         (flags & LOGRA_SKETCH_DEFER) != 0,
-                                         (flags & LOGRA_SKETCH_PENDING) != 0,
-                                         static_cast<char*>(ws), s));
+  return run_sketch(p, &grp, outs, n_out, T, r, kind, flags, ws, s);
 }
+
+int logra_sketch_accumulate_layer(int64_t T, int32_t r, int kind, int32_t flags,
+                                  int32_t n_groups, const logra_sketch_group* groups, void* ws,
+                                  size_t ws_bytes, hipStream_t s) {
+  if (groups == nullptr || n_groups < 1 || n_groups > LOGRA_MAX_GROUPS) return LOGRA_EINVAL;
+  logra::SketchGroup grp[LOGRA_MAX_GROUPS];
+  logra::SketchOut outs[LOGRA_MAX_LAYER_OUT];
+  int n_out = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    const logra_sketch_group& q = groups[g];
+    if (q.n_out < 1 || q.n_out > LOGRA_MAX_SHARED || n_out + q.n_out > LOGRA_MAX_LAYER_OUT)
+      return LOGRA_EINVAL;
+    grp[g] = logra::SketchGroup{q.X, q.ldx, q.k, q.seed, q.stream, q.n_out};
+    for (int i = 0; i < q.n_out; ++i) outs[n_out++] = logra::SketchOut{q.dY[i], q.ldd[i], q.d[i], q.S[i]};
+  }
+  logra::SketchPlan p{};
+  bool run = false;
+  const int st = sketch_checks(grp, n_groups, T, r, kind, flags, outs, ws, ws_bytes, &p, &run);
+  if (st != LOGRA_OK || !run) return st;
+  return run_sketch(p, grp, outs, n_out, T, r, kind, flags, ws, s);
+}
+
+namespace {
+
+// Checks of one merge weight (shared by both merge entry points).
+bool merge_item_ok(const logra::MergeItem& m, int32_t r) {
+  if (m.W == nullptr || m.S == nullptr) return false;
+  if (!dim_ok(m.d) || !dim_ok(m.k) || !rank_ok(r)) return false;
+  if (!aligned(m.W, 16) || !aligned(m.S, 4) || !ld_ok(m.ldw, m.k)) return false;
+  // one work-group per tile of at least 128 rows x 256 columns, flat grid
+  return ((m.d + 127) / 128) * ((m.k + 255) / 256) < (int64_t(1) << 31);
+}
+
+}  // namespace
 
 int logra_merge(uint16_t* W, int64_t ldw, const float* S, int64_t d, int64_t k,
                 int32_t r, uint64_t seed, uint64_t stream, int kind, float alpha,
                 float eta, hipStream_t s) {
-  if (W == nullptr || S == nullptr) return LOGRA_EINVAL;
-  if (!dim_ok(d) || !dim_ok(k) || !rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
-  if (!aligned(W, 16) || !aligned(S, 4) || !ld_ok(ldw, k)) return LOGRA_EINVAL;
+  const logra::MergeItem m{W, ldw, S, d, k, seed, stream};
+  if (!merge_item_ok(m, r) || !kind_ok(kind)) return LOGRA_EINVAL;
   if (!isfinite(alpha) || !isfinite(eta)) return LOGRA_EINVAL;
-  // one work-group per tile of at least 128 rows x 256 columns, flat grid
-  if (((d + 127) / 128) * ((k + 255) / 256) >= (int64_t(1) << 31)) return LOGRA_EINVAL;
-  return hip_status(logra::launch_merge(W, ldw, S, (int)d, (int)k, r, seed, stream,
-                                        kind, alpha, eta, s));
+  return hip_status(logra::launch_merge(&m, 1, r, kind, alpha, eta, s));
+}
+
+int logra_merge_many(int32_t n, const logra_merge_item* items, int32_t r, int kind,
+                     float alpha, float eta, hipStream_t s) {
+  if (items == nullptr || n < 1 || n > LOGRA_MAX_MERGE) return LOGRA_EINVAL;
+  if (!rank_ok(r) || !kind_ok(kind) || !isfinite(alpha) || !isfinite(eta)) return LOGRA_EINVAL;
+  logra::MergeItem m[LOGRA_MAX_MERGE];
+  int64_t tasks = 0;
+  for (int i = 0; i < n; ++i) {
+    const logra_merge_item& q = items[i];
+    m[i] = logra::MergeItem{q.W, q.ldw, q.S, q.d, q.k, q.seed, q.stream};
+    if (!merge_item_ok(m[i], r)) return LOGRA_EINVAL;
+    tasks += ((q.d + 127) / 128) * ((q.k + 255) / 256);
+  }
+  if (tasks >= (int64_t(1) << 31)) return LOGRA_EINVAL;
+  // W is written in place: no weight's rows may overlap another's, nor any S
+  // (read while every W is written)
+  for (int i = 0; i < n; ++i) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(m[i].W);
+    const uintptr_t hi = lo + 2 * ((uintptr_t)(m[i].d - 1) * (uintptr_t)m[i].ldw + (uintptr_t)m[i].k);
+    for (int j = 0; j < n; ++j) {
+      const uintptr_t slo = reinterpret_cast<uintptr_t>(m[j].S);
+      const uintptr_t shi = slo + 4 * (uintptr_t)m[j].d * (uintptr_t)r;
+      if (slo < hi && lo < shi) return LOGRA_EINVAL;
+      if (j < i) {
+        const uintptr_t lo2 = reinterpret_cast<uintptr_t>(m[j].W);
+        const uintptr_t hi2 =
+            lo2 + 2 * ((uintptr_t)(m[j].d - 1) * (uintptr_t)m[j].ldw + (uintptr_t)m[j].k);
+        if (lo < hi2 && lo2 < hi) return LOGRA_EINVAL;
+      }
+    }
+  }
+  return hip_status(logra::launch_merge(m, n, r, kind, alpha, eta, s));
 }
 
 int logra_sketch_update(int rule, const float* S, float* m, float* v, float* U,

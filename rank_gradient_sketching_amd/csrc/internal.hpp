@@ -12,8 +12,13 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Projections that share the layer input X (and so, with the same seed, the
 // same A) can be sketched together: one projection pass, one accumulate
-// launch over all of their d groups.
+// launch over all of their d groups.  A call takes up to kMaxGroups such input
+// groups (a decoder layer's q/k/v, o, gate/up and down) with up to kMaxOut
+// outputs in all: one projection launch over every group's token blocks, one
+// accumulate launch over every output's d groups.
 constexpr int kMaxShared = 4;
+constexpr int kMaxGroups = 4;
+constexpr int kMaxOut = 8;
 
 // One output of a sketch call: S (d x r, fp32) += dY^T P.
 struct SketchOut {
@@ -21,6 +26,17 @@ struct SketchOut {
   int64_t ldd;
   int64_t d;
   float* S;
+};
+
+// One input group of a sketch call: P = X A^T with A from (seed, stream),
+// feeding the group's n_out outputs (consecutive in the call's output list).
+struct SketchGroup {
+  const uint16_t* X;
+  int64_t ldx;
+  int64_t k;
+  uint64_t seed;
+  uint64_t stream;
+  int n_out;
 };
 
 // Tiling of one sketch call (one or several outputs sharing X).  Both the
@@ -32,23 +48,34 @@ struct SketchPlan {
   int nb32;         // 32-row blocks of A handled by the projection kernel
   int q_cols;       // d columns per lane in the accumulate kernel
   int64_t t_pad;    // T rounded up to 32 (one MFMA K step of tokens)
-  int64_t k_pad;    // k rounded up to 256 (one sign block)
   int steps;        // t_pad / 32
-  int n_out;        // outputs sharing X
-  int dg_off[kMaxShared + 1];  // first d group of each output (prefix sums)
+  int n_groups;     // input groups
+  int64_t k_pad[kMaxGroups];   // each group's k rounded up to 256 (one sign block)
+  int out_off[kMaxGroups + 1]; // first output of each group
+  int n_out;        // outputs, all groups together
+  int dg_off[kMaxOut + 1];     // first d group of each output (prefix sums)
   int n_dgroups;    // 128-column d groups, all outputs together
   bool acc_wide;    // accumulate_wide_kernel (r >= 128) instead of accumulate_kernel
   int wg_groups;    // d groups per accumulate work-group (1, or 8 / (rp / 64) when wide)
-  int wg_off[kMaxShared + 1];  // first accumulate work-group along d of each output
+  int wg_off[kMaxOut + 1];     // first accumulate work-group along d of each output
   int n_wg;         // accumulate work-groups along d, all outputs together
   int n_split;      // accumulate work-groups along T
   int steps_per_split;
   int64_t d_pad;    // n_dgroups * 16 * q_cols
-  size_t off_pt, off_part, off_gauss, total;
+  // workspace: each group's P (and Gaussian basis), the partial tiles
+  size_t off_pt[kMaxGroups], off_gauss[kMaxGroups], off_part, total;
 };
 
-bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
-                      SketchPlan* p);
+// n_groups input groups with k[g] columns and n_out[g] outputs each; d lists
+// the outputs' row counts, group by group.
+bool make_sketch_plan_groups(int64_t T, int n_groups, const int64_t* k, const int* n_out,
+                             const int64_t* d, int r, SketchPlan* p);
+
+// One input group with n_out outputs.
+inline bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
+                             SketchPlan* p) {
+  return make_sketch_plan_groups(T, 1, &k, &n_out, d, r, p);
+}
 
 // Process-wide kernel-choice override (which: 0 projection tile, 1 wide
 // accumulate; mode: -1 automatic, 0 never, 1 always).  False on bad input.
@@ -70,18 +97,31 @@ hipError_t launch_regen(uint64_t seed, uint64_t stream, int kind, int r,
 // overwrite: S = dY^T (X A^T) instead of S += (S is not read).  defer: the
 // result stays in the workspace's partial tiles and S is left alone;
 // pending: the partial tiles hold earlier deferred results (same plan), which
-// are added.
-hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
-                         const SketchOut* outs, int T, int k, int r, uint64_t seed,
-                         uint64_t stream, int kind, bool overwrite, bool defer, bool pending,
+// are added.  groups: p.n_groups entries; outs: p.n_out entries, group by
+// group.
+hipError_t launch_sketch(const SketchPlan& p, const SketchGroup* groups, const SketchOut* outs,
+                         int T, int r, int kind, bool overwrite, bool defer, bool pending,
                          char* ws, hipStream_t s);
 
 // S = 0 for n_out outputs of d x r floats (a fill kernel, no memset node).
 hipError_t launch_zero_outputs(const SketchOut* outs, int n_out, int r, hipStream_t s);
 
-hipError_t launch_merge(uint16_t* W, int64_t ldw, const float* S, int d, int k,
-                        int r, uint64_t seed, uint64_t stream, int kind,
-                        float alpha, float eta, hipStream_t s);
+// One weight of a merge call: W (d x k bf16, row stride ldw) -= alpha eta S A
+// with A from (seed, stream).
+struct MergeItem {
+  uint16_t* W;
+  int64_t ldw;
+  const float* S;
+  int64_t d;
+  int64_t k;
+  uint64_t seed;
+  uint64_t stream;
+};
+constexpr int kMaxMerge = 8;
+
+// n items (1..kMaxMerge) with one rank and basis kind, in one launch.
+hipError_t launch_merge(const MergeItem* items, int n, int r, int kind, float alpha,
+                        float eta, hipStream_t s);
 
 hipError_t launch_kl(const uint16_t* zc, const uint16_t* zp, int n_tok,
                      int vocab, int64_t ld, float tau, float kl_budget,

@@ -41,10 +41,59 @@ namespace {
 constexpr int kMergeCols = 256;
 constexpr int kPassCols = 64;
 
-template <int NKS, bool GAUSS, bool MASKED, int kWaves, int NT>
-__global__ __launch_bounds__(64 * kWaves) void merge_kernel(
-    uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ S, int d,
-    int k, int r, uint64_t seed, uint64_t stream, float scale, float cr) {
+// The weights of a launch as its first kernel argument.  MergeOne: the one
+// weight of logra_merge (the launch arguments stay as small as separate
+// parameters; a launch's cost was measured to grow with its argument bytes).
+// MergeTable: the weights of logra_merge_many; weight i owns the tasks
+// t_off[i] .. t_off[i + 1] - 1, its row blocks x column blocks (column block
+// fastest).  All share the rank, the basis kind and the step size.
+struct MergeOne {
+  uint16_t* W;
+  int64_t ldw;
+  const float* S;
+  int d;
+  int k;
+  uint64_t seed;
+  uint64_t stream;
+};
+struct MergeTable {
+  int n;
+  int t_off[kMaxMerge + 1];
+  uint16_t* W[kMaxMerge];
+  int64_t ldw[kMaxMerge];
+  const float* S[kMaxMerge];
+  int d[kMaxMerge];
+  int k[kMaxMerge];
+  uint64_t seed[kMaxMerge];
+  uint64_t stream[kMaxMerge];
+};
+
+// The weight of task `task` and the task's index within the weight (table
+// entries by compares and selects on constant indices).
+struct MergeSel {
+  MergeOne w;
+  int local;
+};
+__device__ __forceinline__ MergeSel select_weight(const MergeOne& t, int task) {
+  return MergeSel{t, task};
+}
+// (Each later weight that the task reaches overrides the fields: compares,
+// not a variable index, which would copy the table to scratch memory.)
+__device__ __forceinline__ MergeSel select_weight(const MergeTable& t, int task) {
+  MergeSel q{MergeOne{t.W[0], t.ldw[0], t.S[0], t.d[0], t.k[0], t.seed[0], t.stream[0]},
+             task - t.t_off[0]};
+#pragma unroll
+  for (int i = 1; i < kMaxMerge; ++i) {
+    if (i < t.n && task >= t.t_off[i]) {
+      q.w = MergeOne{t.W[i], t.ldw[i], t.S[i], t.d[i], t.k[i], t.seed[i], t.stream[i]};
+      q.local = task - t.t_off[i];
+    }
+  }
+  return q;
+}
+
+template <int NKS, bool GAUSS, bool MASKED, int kWaves, int NT, class MT>
+__global__ __launch_bounds__(64 * kWaves) void merge_kernel(MT tab, int r, float scale, float cr) {
   constexpr int RP = 32 * NKS;    // r padded to whole K steps
   constexpr int LDA = RP + 8;     // bf16 per LDS column (+16 B against conflicts)
   constexpr int WR = 16 * NT;     // W rows per wave
@@ -70,20 +119,23 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(
   const int m = lane & 15;   // A-operand row (column slot) and B/D column (row)
   const SignMasks smk = sign_masks();
   const int g = lane >> 4;   // K group for operands, row group for D
-  // flat grid: column block fastest, so neighbouring work-groups share rows
+  // Flat grid over every weight's tiles, column block fastest, so
+  // neighbouring work-groups share rows.  Whole-line tiles: each XCD takes one
+  // contiguous run of tasks (whole row blocks, so its L2 fetches those S rows
+  // once).  Others: column blocks rotated over the XCDs.
+  const int task = kLines ? xcd_runs((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+  const MergeSel sel = select_weight(tab, task);
+  uint16_t* __restrict__ W = sel.w.W;
+  const int64_t ldw = sel.w.ldw;
+  const float* __restrict__ S = sel.w.S;
+  const int d = sel.w.d;
+  const int k = sel.w.k;
+  const uint64_t seed = sel.w.seed;
+  const uint64_t stream = sel.w.stream;
+  const int local = sel.local;
   const int n_cb = (k + kMergeCols - 1) / kMergeCols;
-  // Whole-line tiles: each XCD takes one contiguous run of row-major tiles
-  // (whole row blocks, so its L2 fetches those S rows once).  Others:
-  // column blocks rotated over the XCDs.
-  int rblk, cb;
-  if constexpr (kLines) {
-    const int task = xcd_runs((int)blockIdx.x, (int)gridDim.x);
-    rblk = task / n_cb;
-    cb = task % n_cb;
-  } else {
-    rblk = (int)(blockIdx.x / (unsigned)n_cb);
-    cb = xcd_spread((int)(blockIdx.x % (unsigned)n_cb), rblk, n_cb);
-  }
+  const int rblk = local / n_cb;
+  const int cb = kLines ? local % n_cb : xcd_spread(local % n_cb, rblk, n_cb);
   const int col0 = cb * kMergeCols;
   const int row0 = rblk * (WR * kWaves) + wave * WR;
   const int n_pass = min(kMergeCols / kPassCols, (k - col0 + kPassCols - 1) / kPassCols);
@@ -451,52 +503,80 @@ constexpr int merge_rows(int nks, bool gauss) { return nks <= 2 && !gauss ? 128 
 constexpr int merge_nt(int nks) { return nks <= 2 ? 1 : 2; }
 constexpr int merge_waves(int nks, bool gauss) { return merge_rows(nks, gauss) / (16 * merge_nt(nks)); }
 
-template <int NKS, bool MASKED>
-void launch_merge_m(uint16_t* W, int64_t ldw, const float* S, int d, int k, int r,
-                    uint64_t seed, uint64_t stream, bool gauss, float scale,
-                    float cr, hipStream_t s, dim3 grid) {
+template <int NKS, bool MASKED, class MT>
+void launch_merge_m(const MT& tab, int r, bool gauss, float scale, float cr, hipStream_t s,
+                    dim3 grid) {
   constexpr int kNT = merge_nt(NKS);
   if (gauss) {
     constexpr int kW = merge_waves(NKS, true);
-    hipLaunchKernelGGL((merge_kernel<NKS, true, MASKED, kW, kNT>), grid,
-                       dim3(64 * kW), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
+    hipLaunchKernelGGL((merge_kernel<NKS, true, MASKED, kW, kNT, MT>), grid, dim3(64 * kW), 0, s,
+                       tab, r, scale, cr);
   } else {
     constexpr int kW = merge_waves(NKS, false);
-    hipLaunchKernelGGL((merge_kernel<NKS, false, MASKED, kW, kNT>), grid,
-                       dim3(64 * kW), 0, s, W, ldw, S, d, k, r, seed, stream, scale, cr);
+    hipLaunchKernelGGL((merge_kernel<NKS, false, MASKED, kW, kNT, MT>), grid, dim3(64 * kW), 0, s,
+                       tab, r, scale, cr);
   }
 }
 
 template <int NKS>
-hipError_t launch_merge_t(uint16_t* W, int64_t ldw, const float* S, int d, int k,
-                          int r, uint64_t seed, uint64_t stream, bool gauss,
-                          float scale, float cr, hipStream_t s) {
+hipError_t launch_merge_t(const MergeItem* items, int n, int r, bool gauss, float scale,
+                          float cr, hipStream_t s) {
   const int rows = merge_rows(NKS, gauss);
-  const int64_t blocks = (int64_t)((k + kMergeCols - 1) / kMergeCols) * ((d + rows - 1) / rows);
-  const dim3 grid((unsigned)blocks);
+  int64_t tasks = 0;
   // unmasked when every row block is whole and every 64-column pass is whole
-  // (a short last column block just runs fewer passes)
-  const bool masked = (d % rows) != 0 || (k % kPassCols) != 0;
-  if (masked) launch_merge_m<NKS, true>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
-  else launch_merge_m<NKS, false>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s, grid);
+  // (a short last column block just runs fewer passes); one ragged weight
+  // makes the launch masked, and only its edge work-groups take the masked
+  // body
+  bool masked = false;
+  for (int i = 0; i < n; ++i) {
+    tasks += ((items[i].k + kMergeCols - 1) / kMergeCols) * ((items[i].d + rows - 1) / rows);
+    masked = masked || (items[i].d % rows) != 0 || (items[i].k % kPassCols) != 0;
+  }
+  if (tasks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tasks);
+  if (n == 1) {
+    const MergeItem& m = items[0];
+    const MergeOne one{m.W, m.ldw, m.S, (int)m.d, (int)m.k, m.seed, m.stream};
+    if (masked) launch_merge_m<NKS, true>(one, r, gauss, scale, cr, s, grid);
+    else launch_merge_m<NKS, false>(one, r, gauss, scale, cr, s, grid);
+    return hipGetLastError();
+  }
+  MergeTable tab{};
+  tab.n = n;
+  int64_t t = 0;
+  for (int i = 0; i < n; ++i) {
+    const MergeItem& m = items[i];
+    tab.t_off[i] = (int)t;
+    t += ((m.k + kMergeCols - 1) / kMergeCols) * ((m.d + rows - 1) / rows);
+    tab.W[i] = m.W;
+    tab.ldw[i] = m.ldw;
+    tab.S[i] = m.S;
+    tab.d[i] = (int)m.d;
+    tab.k[i] = (int)m.k;
+    tab.seed[i] = m.seed;
+    tab.stream[i] = m.stream;
+  }
+  tab.t_off[n] = (int)t;
+  if (masked) launch_merge_m<NKS, true>(tab, r, gauss, scale, cr, s, grid);
+  else launch_merge_m<NKS, false>(tab, r, gauss, scale, cr, s, grid);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_merge(uint16_t* W, int64_t ldw, const float* S, int d, int k,
-                        int r, uint64_t seed, uint64_t stream, int kind,
-                        float alpha, float eta, hipStream_t s) {
+hipError_t launch_merge(const MergeItem* items, int n, int r, int kind, float alpha, float eta,
+                        hipStream_t s) {
+  if (n < 1 || n > kMaxMerge) return hipErrorInvalidValue;
   const bool gauss = kind == 1;
   const float cr = sign_scale(r);
   const float step = alpha * eta;             // fp32 product, as documented
   const float scale = gauss ? step : step * cr;
   const int nks = (r + 31) / 32;
   switch (nks <= 1 ? 1 : nks <= 2 ? 2 : nks <= 4 ? 4 : 8) {
-    case 1: return launch_merge_t<1>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s);
-    case 2: return launch_merge_t<2>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s);
-    case 4: return launch_merge_t<4>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s);
-    default: return launch_merge_t<8>(W, ldw, S, d, k, r, seed, stream, gauss, scale, cr, s);
+    case 1: return launch_merge_t<1>(items, n, r, gauss, scale, cr, s);
+    case 2: return launch_merge_t<2>(items, n, r, gauss, scale, cr, s);
+    case 4: return launch_merge_t<4>(items, n, r, gauss, scale, cr, s);
+    default: return launch_merge_t<8>(items, n, r, gauss, scale, cr, s);
   }
 }
 

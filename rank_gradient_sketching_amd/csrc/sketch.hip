@@ -90,11 +90,89 @@ __device__ __forceinline__ int64_t p_block(int step, int nb, int hl, int nb16) {
   return ((int64_t)(step * nb16 + nb) * 2 + hl) * 512;
 }
 
-template <int NB, bool GAUSS, bool MASKED, int kProjWaves>
-__global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
-    const uint16_t* __restrict__ X, int64_t ldx, int T, int k, int rp,
-    uint64_t seed, uint64_t stream, float c, const uint16_t* __restrict__ Ab,
-    int64_t lda, uint16_t* __restrict__ Pt) {
+// The input groups of a projection launch as its first kernel argument.
+// ProjOne: the one group of a single or shared call (the launch arguments
+// stay as small as separate parameters; a launch's cost was measured to grow
+// with its argument bytes).  ProjTable: the groups of a layer call; group g
+// owns work-groups g n_blk .. (g + 1) n_blk - 1, each group with its own X,
+// k, A (seed, stream; or the Gaussian basis Ab with row stride lda) and P.
+struct ProjOne {
+  const uint16_t* X;
+  int64_t ldx;
+  int k;
+  uint64_t seed;
+  uint64_t stream;
+  const uint16_t* Ab;
+  int64_t lda;
+  uint16_t* Pt;
+};
+struct ProjTable {
+  int n;
+  int n_blk;
+  const uint16_t* X[kMaxGroups];
+  int64_t ldx[kMaxGroups];
+  int k[kMaxGroups];
+  uint64_t seed[kMaxGroups];
+  uint64_t stream[kMaxGroups];
+  const uint16_t* Ab[kMaxGroups];
+  int64_t lda[kMaxGroups];
+  uint16_t* Pt[kMaxGroups];
+};
+
+// The group of work-group bx, its block index within the group (bl) and the
+// group's block count.  Table entries are chosen with compares and selects
+// on constant indices (a variable index into the by-value argument would copy
+// it to scratch memory).
+struct ProjSel {
+  const uint16_t* X;
+  int64_t ldx;
+  int k;
+  uint64_t seed;
+  uint64_t stream;
+  const uint16_t* Ab;
+  int64_t lda;
+  uint16_t* Pt;
+  int bl;
+  int n_blk;
+};
+__device__ __forceinline__ ProjSel select_group(const ProjOne& t, int bx) {
+  return ProjSel{t.X, t.ldx, t.k, t.seed, t.stream, t.Ab, t.lda, t.Pt, bx, (int)gridDim.x};
+}
+// (Each later group that the block index reaches overrides the fields: the
+// compares stay compares.  Written as "entry i == chosen index" the compiler
+// turns the selects back into a variable index and copies the table to
+// scratch memory.)
+__device__ __forceinline__ ProjSel select_group(const ProjTable& t, int bx) {
+  ProjSel q{t.X[0], t.ldx[0], t.k[0], t.seed[0], t.stream[0], t.Ab[0], t.lda[0], t.Pt[0], bx,
+            t.n_blk};
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) {
+    if (i < t.n && bx >= i * t.n_blk) {
+      q.X = t.X[i];
+      q.ldx = t.ldx[i];
+      q.k = t.k[i];
+      q.seed = t.seed[i];
+      q.stream = t.stream[i];
+      q.Ab = t.Ab[i];
+      q.lda = t.lda[i];
+      q.Pt = t.Pt[i];
+      q.bl = bx - i * t.n_blk;
+    }
+  }
+  return q;
+}
+#define LOGRA_GROUP_FIELDS(gs)                       \
+  const uint16_t* __restrict__ X = (gs).X;           \
+  const int64_t ldx = (gs).ldx;                      \
+  const int k = (gs).k;                              \
+  const uint64_t seed = (gs).seed;                   \
+  const uint64_t stream = (gs).stream;               \
+  const uint16_t* __restrict__ Ab = (gs).Ab;         \
+  const int64_t lda = (gs).lda;                      \
+  uint16_t* __restrict__ Pt = (gs).Pt
+
+template <int NB, bool GAUSS, bool MASKED, int kProjWaves, class PT>
+__global__ __launch_bounds__(64 * kProjWaves) void project_kernel(PT tab, int T, int rp, float c) {
   __shared__ __attribute__((aligned(16))) unsigned char stage0[kProjWaves][kHalfBytes];
   __shared__ __attribute__((aligned(16))) unsigned char stage1[kProjWaves][kHalfBytes];
   const int tid = threadIdx.x;
@@ -102,7 +180,9 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
   const int wave = tid >> 6;
   const int m = lane & 31;  // A-operand row (token) and B-operand column (A row)
   const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
-  const int step = xcd_spread((int)blockIdx.x, (int)blockIdx.x >> 3, (int)gridDim.x);
+  const ProjSel gs = select_group(tab, (int)blockIdx.x);
+  LOGRA_GROUP_FIELDS(gs);
+  const int step = xcd_spread(gs.bl, gs.bl >> 3, gs.n_blk);
   const int t0 = step * 32;
   const SignMasks smk = sign_masks();
   const int n_chunks = (k + 255) >> 8;
@@ -286,11 +366,9 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(
 constexpr int kTileTokens = 64;
 constexpr int kTileLanes = 4;
 
-template <int NBW, bool GAUSS, bool MASKED>
-__global__ __launch_bounds__(512) void project_tile_kernel(
-    const uint16_t* __restrict__ X, int64_t ldx, int T, int k, int rp, int steps_total,
-    uint64_t seed, uint64_t stream, float c, const uint16_t* __restrict__ Ab,
-    int64_t lda, uint16_t* __restrict__ Pt) {
+template <int NBW, bool GAUSS, bool MASKED, class PT>
+__global__ __launch_bounds__(512) void project_tile_kernel(PT tab, int T, int rp, int steps_total,
+                                                           float c) {
   static_assert(NBW % 2 == 0 || NBW == 1, "sign words pair 32-row blocks");
   // [chunk lane][half][64 rows x 128 columns bf16], 16-byte pieces swizzled by row
   __shared__ __attribute__((aligned(16))) unsigned char stage[kTileLanes][2][2 * kHalfBytes];
@@ -301,7 +379,9 @@ __global__ __launch_bounds__(512) void project_tile_kernel(
   const int cl = wave % kTileLanes;      // chunk lane
   const int m = lane & 31;  // A-operand row (token) and B-operand column (A row)
   const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
-  const int blk = xcd_spread((int)blockIdx.x, (int)blockIdx.x >> 3, (int)gridDim.x);
+  const ProjSel gs = select_group(tab, (int)blockIdx.x);
+  LOGRA_GROUP_FIELDS(gs);
+  const int blk = xcd_spread(gs.bl, gs.bl >> 3, gs.n_blk);
   const int t0 = blk * kTileTokens;
   const SignMasks smk = sign_masks();
   const int n_chunks = (k + 255) >> 8;
@@ -606,39 +686,84 @@ constexpr int acc_lds_bytes() {
 
 // The outputs of one call as a kernel argument.  Work-group d groups are
 // numbered across all outputs; output o owns groups dg_off[o] .. dg_off[o+1].
+// OutTable: the outputs of one input group (single and shared calls; their P
+// is a separate argument, so the launch arguments stay as small as before).
+// LayerOutTable: the outputs of a layer call, each with its group's P.
 struct OutTable {
+  static constexpr int kN = kMaxShared;
   int n;
   int overwrite;   // S = result instead of S += result (S is not read)
   int pending;     // the partial tiles hold earlier deferred contributions: add to them
-  int dg_off[kMaxShared + 1];
-  int wg_off[kMaxShared + 1];   // first accumulate_wide_kernel work-group of each output
-  const uint16_t* dY[kMaxShared];
-  int64_t ldd[kMaxShared];
-  int d[kMaxShared];
-  float* S[kMaxShared];
+  int dg_off[kN + 1];
+  int wg_off[kN + 1];   // first accumulate_wide_kernel work-group of each output
+  const uint16_t* dY[kN];
+  int64_t ldd[kN];
+  int d[kN];
+  float* S[kN];
+};
+struct LayerOutTable {
+  static constexpr int kN = kMaxOut;
+  int n;
+  int overwrite;
+  int pending;
+  int dg_off[kN + 1];
+  int wg_off[kN + 1];
+  const uint16_t* dY[kN];
+  int64_t ldd[kN];
+  int d[kN];
+  float* S[kN];
+  const uint16_t* Pt[kN];   // the P of the output's input group
 };
 
-// Output of a (wave-uniform) global d group, chosen with compares and selects
-// on the kernel argument's fields (constant indices only: taking the
-// argument's address would copy the table to scratch memory).
+// P of output i: the call's one P, or the output's own.
+__device__ __forceinline__ const uint16_t* out_p(const OutTable&, int, const uint16_t* p) {
+  return p;
+}
+__device__ __forceinline__ const uint16_t* out_p(const LayerOutTable& t, int i, const uint16_t*) {
+  return t.Pt[i];
+}
+
+// The fields of one output, chosen from a table (below).
 struct OutSel {
-  int dg;
   const uint16_t* dY;
   int64_t ldd;
   int d;
   float* S;
+  const uint16_t* Pt;
+  int dg_first;
+  int dg_end;
+  int wg_first;
 };
-#define LOGRA_SELECT_OUT(tab, dgg, out)                                    \
-  OutSel out{(dgg), (tab).dY[0], (tab).ldd[0], (tab).d[0], (tab).S[0]};   \
-  _Pragma("unroll") for (int i_ = 1; i_ < kMaxShared; ++i_) {              \
-    if (i_ < (tab).n && (dgg) >= (tab).dg_off[i_]) {                       \
-      out.dg = (dgg) - (tab).dg_off[i_];                                   \
-      out.dY = (tab).dY[i_];                                               \
-      out.ldd = (tab).ldd[i_];                                             \
-      out.d = (tab).d[i_];                                                 \
-      out.S = (tab).S[i_];                                                 \
-    }                                                                      \
+// The output owning global d group dgg (wave-uniform) or accumulate_wide_kernel
+// work-group wg (by_wg): each later output that the index reaches overrides
+// the fields (compares, not a variable index: see select_group).
+template <bool by_wg, class Tab>
+__device__ __forceinline__ OutSel select_out_t(const Tab& t, int idx, const uint16_t* p) {
+  OutSel q{t.dY[0], t.ldd[0], t.d[0], t.S[0], out_p(t, 0, p), t.dg_off[0], t.dg_off[1],
+           t.wg_off[0]};
+#pragma unroll
+  for (int i = 1; i < Tab::kN; ++i) {
+    if (i < t.n && idx >= (by_wg ? t.wg_off[i] : t.dg_off[i])) {
+      q.dY = t.dY[i];
+      q.ldd = t.ldd[i];
+      q.d = t.d[i];
+      q.S = t.S[i];
+      q.Pt = out_p(t, i, p);
+      q.dg_first = t.dg_off[i];
+      q.dg_end = t.dg_off[i + 1];
+      q.wg_first = t.wg_off[i];
+    }
   }
+  return q;
+}
+template <class Tab>
+__device__ __forceinline__ OutSel select_out(const Tab& t, int dgg, const uint16_t* p) {
+  return select_out_t<false>(t, dgg, p);
+}
+template <class Tab>
+__device__ __forceinline__ OutSel select_out_wg(const Tab& t, int wg, const uint16_t* p) {
+  return select_out_t<true>(t, wg, p);
+}
 
 // S += dY^T P over a range of 32-token steps for 16 Q columns of d.
 // The P operands of each step reach a per-wave two-slot LDS ring by direct
@@ -649,10 +774,10 @@ struct OutSel {
 // NBW (w / L) .. and steps s_begin + (w % L) + L j (L = 8 / RS waves along
 // the steps); waves of one r part load the same dY rows (cache hits after
 // the first).
-template <int Q, int NB16, bool MASKED>
+template <int Q, int NB16, bool MASKED, class Tab>
 __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
-    OutTable tab, int T, int r, const uint16_t* __restrict__ Pt, int steps_total,
-    int steps_per_split, float* __restrict__ part) {
+    Tab tab, int T, int r, const uint16_t* __restrict__ Pt1, int steps_total, int steps_per_split,
+    float* __restrict__ part) {
   constexpr int DC = 16 * Q;            // d columns per work-group
   constexpr int NREG = Q * NB16 * 4;    // accumulator floats of the tile per lane
   constexpr int NBW = acc_nbw(NB16);    // 16-column r blocks per wave
@@ -677,12 +802,13 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
                             (int)(gridDim.x * gridDim.y));
   const int sp = task / (int)gridDim.x;
   const int dgg = task % (int)gridDim.x;   // d group across outputs
-  LOGRA_SELECT_OUT(tab, dgg, out);
+  const OutSel out = select_out(tab, dgg, Pt1);
   const uint16_t* __restrict__ dY = out.dY;
   const int64_t ldd = out.ldd;
   const int d = out.d;
   float* __restrict__ S = out.S;
-  const int dg = out.dg;                                             // within the output
+  const uint16_t* __restrict__ Pt = out.Pt;
+  const int dg = dgg - out.dg_first;                                 // within the output
   const int dc0 = dg * DC;
   const int col = dc0 + Q * m;
   const int s_begin = sp * steps_per_split;
@@ -873,10 +999,10 @@ __global__ __launch_bounds__(64 * kAccWaves) void accumulate_kernel(
 // matrix-core cycles per SIMD.  Three stages: a step's copies are issued two
 // steps ahead, one barrier per step.  No cross-wave sum: each wave writes its
 // own 128 x 64 block (partial tile or S).
-template <int NB16, bool MASKED>
+template <int NB16, bool MASKED, class Tab>
 __global__ __launch_bounds__(512) void accumulate_wide_kernel(
-    OutTable tab, int T, int r, const uint16_t* __restrict__ Pt, int steps_total,
-    int steps_per_split, int n_dgroups, float* __restrict__ part) {
+    Tab tab, int T, int r, const uint16_t* __restrict__ Pt1, int steps_total, int steps_per_split,
+    int n_dgroups, float* __restrict__ part) {
   constexpr int Q = 8;
   constexpr int NBW = 4;                     // 16-column r blocks per wave
   constexpr int RPW = NB16 / NBW;            // waves along r
@@ -906,27 +1032,13 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
   const int sp = task / (int)gridDim.x;
   const int wg = task % (int)gridDim.x;
   // output of this work-group (wave-uniform compares on the table)
-  int o_sel = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxShared; ++i)
-    if (i < tab.n && wg >= tab.wg_off[i]) o_sel = i;
-  const uint16_t* dY = tab.dY[0];
-  int64_t ldd = tab.ldd[0];
-  int d = tab.d[0];
-  float* S = tab.S[0];
-  int dg_first = tab.dg_off[0], dg_end = tab.dg_off[1], wg_first = tab.wg_off[0];
-#pragma unroll
-  for (int i = 1; i < kMaxShared; ++i) {
-    if (i == o_sel) {
-      dY = tab.dY[i];
-      ldd = tab.ldd[i];
-      d = tab.d[i];
-      S = tab.S[i];
-      dg_first = tab.dg_off[i];
-      dg_end = tab.dg_off[i + 1];
-      wg_first = tab.wg_off[i];
-    }
-  }
+  const OutSel out = select_out_wg(tab, wg, Pt1);
+  const uint16_t* dY = out.dY;
+  const int64_t ldd = out.ldd;
+  const int d = out.d;
+  float* S = out.S;
+  const uint16_t* __restrict__ Pt = out.Pt;
+  const int dg_first = out.dg_first, dg_end = out.dg_end, wg_first = out.wg_first;
   const int col_wg = (wg - wg_first) * DP * 16 * Q;   // first d column of the work-group
   const int dg_local = (wg - wg_first) * DP + dpart;   // this wave's d group in the output
   const bool group_ok = dg_first + dg_local < dg_end;
@@ -1065,10 +1177,10 @@ __global__ __launch_bounds__(512) void accumulate_wide_kernel(
 // S += sum over splits of the partial tiles, in split order.  One thread per
 // four consecutive floats of a tile (four lanes with the same d row and four
 // consecutive r columns).
-template <int Q, int NB16>
+template <int Q, int NB16, class Tab>
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part,
-                                                       int n_split, int n_dgroups,
-                                                       OutTable tab, int r) {
+                                                       int n_split, int n_dgroups, Tab tab,
+                                                       int r) {
   constexpr int NREG = Q * NB16 * 4;
   constexpr int TILE = NREG * 64;
   const int64_t idx4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1076,11 +1188,11 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   if (idx4 * 4 >= per_split) return;
   const int64_t flat = idx4 * 4;
   const int dgg = (int)(flat / TILE);
-  LOGRA_SELECT_OUT(tab, dgg, out);
+  const OutSel out = select_out(tab, dgg, nullptr);
   const int within = (int)(flat % TILE);
   const int i = within >> 6;
   const int ln = within & 63;       // multiple of 4
-  const int drow = acc_drow<Q, NB16>(out.dg * 16 * Q, i, ln);
+  const int drow = acc_drow<Q, NB16>((dgg - out.dg_first) * 16 * Q, i, ln);
   const int rc = acc_rcol<NB16>(i, ln);
   if (drow >= out.d) return;
   float* srow = out.S + (int64_t)drow * r;
@@ -1134,64 +1246,79 @@ bool use_tile_projection(const SketchPlan& p, int nb32, bool gauss) {
   return gauss || p.t_pad / kTileTokens >= 256;
 }
 
-template <int NB, bool GAUSS, bool MASKED>
-void launch_project_t(const SketchPlan& p, const uint16_t* X, int64_t ldx, int T,
-                      int k, uint64_t seed, uint64_t stream, float c,
-                      const uint16_t* Ab, uint16_t* Pt, hipStream_t s) {
+// Groups and their block count in a projection launch.
+inline int proj_groups(const ProjOne&) { return 1; }
+inline int proj_groups(const ProjTable& t) { return t.n; }
+inline bool proj_masked(const ProjOne& t) { return (t.k % 256) != 0; }
+inline bool proj_masked(const ProjTable& t) {
+  bool m = false;
+  for (int g = 0; g < t.n; ++g) m = m || (t.k[g] % 256) != 0;
+  return m;
+}
+inline void set_blocks(ProjOne&, int) {}
+inline void set_blocks(ProjTable& t, int n_blk) { t.n_blk = n_blk; }
+
+template <int NB, bool GAUSS, bool MASKED, class PT>
+void launch_project_t(const SketchPlan& p, const PT& tab, int T, float c, hipStream_t s) {
   constexpr int W = proj_waves(NB);
-  const dim3 grid((unsigned)(p.t_pad / 32));
-  hipLaunchKernelGGL((project_kernel<NB, GAUSS, MASKED, W>), grid, dim3(64 * W), 0,
-                     s, X, ldx, T, k, p.rp, seed, stream, c, Ab, p.k_pad, Pt);
+  const dim3 grid((unsigned)(proj_groups(tab) * (p.t_pad / 32)));
+  hipLaunchKernelGGL((project_kernel<NB, GAUSS, MASKED, W, PT>), grid, dim3(64 * W), 0, s, tab, T,
+                     p.rp, c);
 }
 
-template <int NB>
-hipError_t launch_project(const SketchPlan& p, const uint16_t* X, int64_t ldx,
-                          int T, int k, uint64_t seed, uint64_t stream, bool gauss,
-                          float c, const uint16_t* Ab, uint16_t* Pt, hipStream_t s) {
+// One launch over every group's token blocks.  MASKED (a ragged last chunk of
+// k) when any group's k is not a multiple of 256; the kernels test the edge
+// per chunk, so groups with whole chunks run as without the mask.
+template <int NB, class PT>
+hipError_t launch_project(const SketchPlan& p, PT tab, int T, bool gauss, float c, hipStream_t s) {
+  const bool masked = proj_masked(tab);
   if constexpr (NB >= 2) {
     if (use_tile_projection(p, NB, gauss)) {
-      const bool tmask = (k % 256) != 0;   // ragged T needs no mask (see the kernel)
-      const dim3 grid((unsigned)((p.t_pad + kTileTokens - 1) / kTileTokens));
+      const int n_blk = (int)((p.t_pad + kTileTokens - 1) / kTileTokens);
+      set_blocks(tab, n_blk);
+      const dim3 grid((unsigned)(proj_groups(tab) * n_blk));
       const float cc = gauss ? 1.0f : c;
-#define LOGRA_TILE(G, M)                                                                  \
-  hipLaunchKernelGGL((project_tile_kernel<NB / 2, G, M>), grid, dim3(512), 0, s, X, ldx, T, \
-                     k, p.rp, p.steps, seed, stream, cc, Ab, p.k_pad, Pt)
+#define LOGRA_TILE(G, M)                                                                      \
+  hipLaunchKernelGGL((project_tile_kernel<NB / 2, G, M, PT>), grid, dim3(512), 0, s, tab, T, p.rp, \
+                     p.steps, cc)
       if (gauss) {
-        if (tmask) LOGRA_TILE(true, true);
+        if (masked) LOGRA_TILE(true, true);
         else LOGRA_TILE(true, false);
       } else {
-        if (tmask) LOGRA_TILE(false, true);
+        if (masked) LOGRA_TILE(false, true);
         else LOGRA_TILE(false, false);
       }
 #undef LOGRA_TILE
       return hipGetLastError();
     }
   }
-  const bool masked = (k % 256) != 0;   // ragged T needs no mask (see the kernel)
+  set_blocks(tab, (int)(p.t_pad / 32));
   if (gauss) {
-    if (masked) launch_project_t<NB, true, true>(p, X, ldx, T, k, seed, stream, 1.0f, Ab, Pt, s);
-    else launch_project_t<NB, true, false>(p, X, ldx, T, k, seed, stream, 1.0f, Ab, Pt, s);
+    if (masked) launch_project_t<NB, true, true>(p, tab, T, 1.0f, s);
+    else launch_project_t<NB, true, false>(p, tab, T, 1.0f, s);
   } else {
-    if (masked) launch_project_t<NB, false, true>(p, X, ldx, T, k, seed, stream, c, Ab, Pt, s);
-    else launch_project_t<NB, false, false>(p, X, ldx, T, k, seed, stream, c, Ab, Pt, s);
+    if (masked) launch_project_t<NB, false, true>(p, tab, T, c, s);
+    else launch_project_t<NB, false, false>(p, tab, T, c, s);
   }
   return hipGetLastError();
 }
 
-template <int Q, int NB16>
-hipError_t launch_finalize(const SketchPlan& p, const OutTable& tab, int r, float* part,
+template <int Q, int NB16, class Tab>
+hipError_t launch_finalize(const SketchPlan& p, const Tab& tab, int r, float* part,
                            hipStream_t s) {
   const int64_t quads = (int64_t)p.n_dgroups * Q * NB16 * 4 * 64 / 4;
-  hipLaunchKernelGGL((finalize_kernel<Q, NB16>), dim3((unsigned)((quads + 255) / 256)),
+  hipLaunchKernelGGL((finalize_kernel<Q, NB16, Tab>), dim3((unsigned)((quads + 255) / 256)),
                      dim3(256), 0, s, part, p.n_split, p.n_dgroups, tab, r);
   return hipGetLastError();
 }
 
 // Partial tiles are used with several splits, and for every call of a
 // deferred chain (defer: keep the result there; tab.pending: add to them).
-template <int Q, int NB16>
-hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, int r,
-                             const uint16_t* Pt, float* part, bool defer, hipStream_t s) {
+// Pt1: the P of a one-group call (an OutTable); a LayerOutTable carries each
+// output's own.
+template <int Q, int NB16, class Tab>
+hipError_t launch_accumulate(const SketchPlan& p, const Tab& tab, int T, int r,
+                             const uint16_t* Pt1, float* part, bool defer, hipStream_t s) {
   const dim3 grid((unsigned)p.n_dgroups, (unsigned)p.n_split);
   float* pp = p.n_split > 1 || defer || tab.pending ? part : nullptr;
   // masked for a ragged d group only: rows past T read as zero through the
@@ -1199,20 +1326,20 @@ hipError_t launch_accumulate(const SketchPlan& p, const OutTable& tab, int T, in
   bool masked = false;
   for (int o = 0; o < tab.n; ++o) masked = masked || (tab.d[o] % (16 * Q)) != 0;
   if (masked) {
-    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, true>), grid, dim3(64 * kAccWaves), 0, s,
-                       tab, T, r, Pt, p.steps, p.steps_per_split, pp);
+    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, true, Tab>), grid, dim3(64 * kAccWaves), 0, s,
+                       tab, T, r, Pt1, p.steps, p.steps_per_split, pp);
   } else {
-    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, false>), grid, dim3(64 * kAccWaves), 0, s,
-                       tab, T, r, Pt, p.steps, p.steps_per_split, pp);
+    hipLaunchKernelGGL((accumulate_kernel<Q, NB16, false, Tab>), grid, dim3(64 * kAccWaves), 0, s,
+                       tab, T, r, Pt1, p.steps, p.steps_per_split, pp);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pp == nullptr || defer) return e;
   return launch_finalize<Q, NB16>(p, tab, r, part, s);
 }
 
-template <int NB16>
-hipError_t launch_accumulate_wide(const SketchPlan& p, const OutTable& tab, int T, int r,
-                                  const uint16_t* Pt, float* part, bool defer, hipStream_t s) {
+template <int NB16, class Tab>
+hipError_t launch_accumulate_wide(const SketchPlan& p, const Tab& tab, int T, int r,
+                                  const uint16_t* Pt1, float* part, bool defer, hipStream_t s) {
   constexpr int DP = kAccWaves / (NB16 / 4);
   const dim3 grid((unsigned)p.n_wg, (unsigned)p.n_split);
   float* pp = p.n_split > 1 || defer || tab.pending ? part : nullptr;
@@ -1223,30 +1350,85 @@ hipError_t launch_accumulate_wide(const SketchPlan& p, const OutTable& tab, int 
     masked = masked || (tab.d[o] % (16 * kAccQ)) != 0 ||
              ((tab.dg_off[o + 1] - tab.dg_off[o]) % DP) != 0;
   if (masked) {
-    hipLaunchKernelGGL((accumulate_wide_kernel<NB16, true>), grid, dim3(64 * kAccWaves), 0, s,
-                       tab, T, r, Pt, p.steps, p.steps_per_split, p.n_dgroups, pp);
+    hipLaunchKernelGGL((accumulate_wide_kernel<NB16, true, Tab>), grid, dim3(64 * kAccWaves), 0, s,
+                       tab, T, r, Pt1, p.steps, p.steps_per_split, p.n_dgroups, pp);
   } else {
-    hipLaunchKernelGGL((accumulate_wide_kernel<NB16, false>), grid, dim3(64 * kAccWaves), 0, s,
-                       tab, T, r, Pt, p.steps, p.steps_per_split, p.n_dgroups, pp);
+    hipLaunchKernelGGL((accumulate_wide_kernel<NB16, false, Tab>), grid, dim3(64 * kAccWaves), 0,
+                       s, tab, T, r, Pt1, p.steps, p.steps_per_split, p.n_dgroups, pp);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pp == nullptr || defer) return e;
   return launch_finalize<kAccQ, NB16>(p, tab, r, part, s);
 }
 
+// The projection and accumulate launches of one call with the given tables.
+template <class PT, class Tab>
+hipError_t launch_tables(const SketchPlan& p, const PT& pt, const Tab& tab, const uint16_t* Pt1,
+                         int T, int r, bool gauss, float c, bool defer, float* part,
+                         hipStream_t s) {
+  hipError_t e;
+  switch (p.nb32) {
+    case 1: e = launch_project<1>(p, pt, T, gauss, c, s); break;
+    case 2: e = launch_project<2>(p, pt, T, gauss, c, s); break;
+    case 4: e = launch_project<4>(p, pt, T, gauss, c, s); break;
+    default: e = launch_project<8>(p, pt, T, gauss, c, s); break;
+  }
+  if (e != hipSuccess) return e;
+  if (p.acc_wide) {
+    if (p.rp == 128) return launch_accumulate_wide<8>(p, tab, T, r, Pt1, part, defer, s);
+    return launch_accumulate_wide<16>(p, tab, T, r, Pt1, part, defer, s);
+  }
+  switch (p.rp) {
+    case 16: return launch_accumulate<kAccQ, 1>(p, tab, T, r, Pt1, part, defer, s);
+    case 32: return launch_accumulate<kAccQ, 2>(p, tab, T, r, Pt1, part, defer, s);
+    case 64: return launch_accumulate<kAccQ, 4>(p, tab, T, r, Pt1, part, defer, s);
+    case 128: return launch_accumulate<kAccQ, 8>(p, tab, T, r, Pt1, part, defer, s);
+    default: return launch_accumulate<kAccQ, 16>(p, tab, T, r, Pt1, part, defer, s);
+  }
+}
+
+// The output fields shared by both table types.
+template <class Tab>
+void fill_outputs(Tab& tab, const SketchPlan& p, const SketchOut* outs, bool overwrite,
+                  bool pending) {
+  tab.n = p.n_out;
+  tab.overwrite = overwrite ? 1 : 0;
+  tab.pending = pending ? 1 : 0;
+  for (int o = 0; o <= p.n_out; ++o) {
+    tab.dg_off[o] = p.dg_off[o];
+    tab.wg_off[o] = p.wg_off[o];
+  }
+  for (int o = 0; o < p.n_out; ++o) {
+    tab.dY[o] = outs[o].dY;
+    tab.ldd[o] = outs[o].ldd;
+    tab.d[o] = (int)outs[o].d;
+    tab.S[o] = outs[o].S;
+  }
+}
+
 }  // namespace
 
-bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
-                      SketchPlan* p) {
-  if (T < 0 || k < 1 || r < 1 || r > 256 || n_out < 1 || n_out > kMaxShared) return false;
-  if (T >= (int64_t(1) << 31) || k >= (int64_t(1) << 31)) return false;
+bool make_sketch_plan_groups(int64_t T, int n_groups, const int64_t* k, const int* n_out_g,
+                             const int64_t* d, int r, SketchPlan* p) {
+  if (T < 0 || T >= (int64_t(1) << 31) || r < 1 || r > 256) return false;
+  if (n_groups < 1 || n_groups > kMaxGroups) return false;
   SketchPlan q{};
+  q.n_groups = n_groups;
+  int n_out = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    if (k[g] < 1 || k[g] >= (int64_t(1) << 31)) return false;
+    if (n_out_g[g] < 1 || n_out_g[g] > kMaxShared) return false;
+    q.k_pad[g] = round_up(k[g], 256);
+    q.out_off[g] = n_out;
+    n_out += n_out_g[g];
+  }
+  if (n_out > kMaxOut) return false;
+  q.out_off[n_groups] = n_out;
   q.rp = r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : r <= 128 ? 128 : 256;
   q.p_rows = q.rp < 32 ? 32 : q.rp;
   q.nb32 = q.p_rows / 32;
   q.q_cols = kAccQ;
   q.t_pad = round_up(T > 0 ? T : 1, 32);
-  q.k_pad = round_up(k, 256);
   q.steps = (int)(q.t_pad / 32);
   const int dc = 16 * q.q_cols;
   q.n_out = n_out;
@@ -1302,11 +1484,12 @@ bool make_sketch_plan(int64_t T, int n_out, const int64_t* d, int64_t k, int r,
     off += (size_t)round_up((int64_t)bytes, 256);
     return o;
   };
-  q.off_pt = take((size_t)2 * q.rp * (size_t)q.t_pad * 2);
+  for (int g = 0; g < n_groups; ++g) q.off_pt[g] = take((size_t)2 * q.rp * (size_t)q.t_pad * 2);
   // (one split's worth even when a single split writes S directly: a
   // deferred call keeps its result there)
   q.off_part = take((size_t)q.n_split * q.d_pad * q.rp * 4);
-  q.off_gauss = take((size_t)q.p_rows * (size_t)q.k_pad * 2);
+  for (int g = 0; g < n_groups; ++g)
+    q.off_gauss[g] = take((size_t)q.p_rows * (size_t)q.k_pad[g] * 2);
   q.total = off;
   *p = q;
   return true;
@@ -1320,55 +1503,60 @@ bool set_kernel_choice(int which, int mode) {
   return true;
 }
 
-hipError_t launch_sketch(const SketchPlan& p, const uint16_t* X, int64_t ldx,
-                         const SketchOut* outs, int T, int k, int r, uint64_t seed,
-                         uint64_t stream, int kind, bool overwrite, bool defer, bool pending,
+hipError_t launch_sketch(const SketchPlan& p, const SketchGroup* groups, const SketchOut* outs,
+                         int T, int r, int kind, bool overwrite, bool defer, bool pending,
                          char* ws, hipStream_t s) {
-  uint16_t* Pt = reinterpret_cast<uint16_t*>(ws + p.off_pt);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
-  uint16_t* Ab = reinterpret_cast<uint16_t*>(ws + p.off_gauss);
   const bool gauss = kind == 1;
   const float c = sign_scale(r);
-  hipError_t e = hipSuccess;
-  if (gauss) {
-    const int64_t threads = (int64_t)p.p_rows * (p.k_pad >> 2);
-    hipLaunchKernelGGL(gauss_basis_kernel, dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, s, seed, stream, r, k, p.p_rows, p.k_pad, c, Ab);
-    e = hipGetLastError();
+  for (int g = 0; g < p.n_groups; ++g) {
+    if (!gauss) break;
+    const int64_t threads = (int64_t)p.p_rows * (p.k_pad[g] >> 2);
+    hipLaunchKernelGGL(gauss_basis_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       s, groups[g].seed, groups[g].stream, r, (int)groups[g].k, p.p_rows,
+                       p.k_pad[g], c, reinterpret_cast<uint16_t*>(ws + p.off_gauss[g]));
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  switch (p.nb32) {
-    case 1: e = launch_project<1>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
-    case 2: e = launch_project<2>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
-    case 4: e = launch_project<4>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
-    default: e = launch_project<8>(p, X, ldx, T, k, seed, stream, gauss, c, Ab, Pt, s); break;
+  if (p.n_groups == 1) {
+    const SketchGroup& gr = groups[0];
+    uint16_t* Pt = reinterpret_cast<uint16_t*>(ws + p.off_pt[0]);
+    const ProjOne pt{gr.X, gr.ldx, (int)gr.k, gr.seed, gr.stream,
+                     reinterpret_cast<const uint16_t*>(ws + p.off_gauss[0]), p.k_pad[0], Pt};
+    OutTable tab{};
+    fill_outputs(tab, p, outs, overwrite, pending);
+    return launch_tables(p, pt, tab, Pt, T, r, gauss, c, defer, part, s);
   }
-  if (e != hipSuccess) return e;
-  OutTable tab{};
-  tab.n = p.n_out;
-  tab.overwrite = overwrite ? 1 : 0;
-  tab.pending = pending ? 1 : 0;
-  for (int o = 0; o <= p.n_out; ++o) {
-    tab.dg_off[o] = p.dg_off[o];
-    tab.wg_off[o] = p.wg_off[o];
+  // Projection table: groups with the largest k first, so the longest
+  // work-groups are dispatched first and the short ones fill in behind them.
+  int order[kMaxGroups];
+  for (int g = 0; g < p.n_groups; ++g) order[g] = g;
+  for (int a = 1; a < p.n_groups; ++a)
+    for (int b = a; b > 0 && groups[order[b]].k > groups[order[b - 1]].k; --b) {
+      const int t = order[b];
+      order[b] = order[b - 1];
+      order[b - 1] = t;
+    }
+  ProjTable pt{};
+  pt.n = p.n_groups;
+  for (int j = 0; j < p.n_groups; ++j) {
+    const int g = order[j];
+    const SketchGroup& gr = groups[g];
+    pt.X[j] = gr.X;
+    pt.ldx[j] = gr.ldx;
+    pt.k[j] = (int)gr.k;
+    pt.seed[j] = gr.seed;
+    pt.stream[j] = gr.stream;
+    pt.Ab[j] = reinterpret_cast<const uint16_t*>(ws + p.off_gauss[g]);
+    pt.lda[j] = p.k_pad[g];
+    pt.Pt[j] = reinterpret_cast<uint16_t*>(ws + p.off_pt[g]);
   }
-  for (int o = 0; o < p.n_out; ++o) {
-    tab.dY[o] = outs[o].dY;
-    tab.ldd[o] = outs[o].ldd;
-    tab.d[o] = (int)outs[o].d;
-    tab.S[o] = outs[o].S;
-  }
-  if (p.acc_wide) {
-    if (p.rp == 128) return launch_accumulate_wide<8>(p, tab, T, r, Pt, part, defer, s);
-    return launch_accumulate_wide<16>(p, tab, T, r, Pt, part, defer, s);
-  }
-  switch (p.rp) {
-    case 16: return launch_accumulate<kAccQ, 1>(p, tab, T, r, Pt, part, defer, s);
-    case 32: return launch_accumulate<kAccQ, 2>(p, tab, T, r, Pt, part, defer, s);
-    case 64: return launch_accumulate<kAccQ, 4>(p, tab, T, r, Pt, part, defer, s);
-    case 128: return launch_accumulate<kAccQ, 8>(p, tab, T, r, Pt, part, defer, s);
-    default: return launch_accumulate<kAccQ, 16>(p, tab, T, r, Pt, part, defer, s);
-  }
+  LayerOutTable tab{};
+  fill_outputs(tab, p, outs, overwrite, pending);
+  for (int g = 0; g < p.n_groups; ++g)
+    for (int o = p.out_off[g]; o < p.out_off[g + 1]; ++o)
+      tab.Pt[o] = reinterpret_cast<const uint16_t*>(ws + p.off_pt[g]);
+  return launch_tables(p, pt, tab, nullptr, T, r, gauss, c, defer, part, s);
 }
 
 // S = 0, four floats per thread where the row allows (S of every output is
@@ -1383,6 +1571,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ S, int64_
 }
 
 hipError_t launch_zero_outputs(const SketchOut* outs, int n_out, int r, hipStream_t s) {
+  if (n_out < 0 || n_out > kMaxOut) return hipErrorInvalidValue;
   for (int o = 0; o < n_out; ++o) {
     const int64_t n = outs[o].d * (int64_t)r;
     const int64_t blocks = (n + 1023) / 1024;

@@ -163,7 +163,9 @@ static void check_sketch_rejects(void) {
     const uint16_t* dys[4] = {DY_PTR, (const uint16_t*)fake(0x210000), (const uint16_t*)fake(0x220000), (const uint16_t*)fake(0x230000)};
     const int64_t ldd[4] = {1536, 256, 256, 256};
     const int64_t dd[4] = {1536, 256, 256, 256};
-    float* Ss[4] = {S_PTR, (float*)fake(0x310000), (float*)fake(0x320000), (float*)fake(0x330000)};
+    /* S arrays 1 MiB apart: no two d x r ranges overlap */
+    float* Ss[4] = {(float*)fake(0x3000000), (float*)fake(0x3100000), (float*)fake(0x3200000),
+                    (float*)fake(0x3300000)};
     const size_t wsb = logra_sketch_shared_ws_bytes(16384, 1536, 64, 3, dd);
     EXPECT(wsb > 0);
     EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 0, dys, ldd, dd, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
@@ -172,7 +174,10 @@ static void check_sketch_rejects(void) {
     EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, NULL, dd, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
     EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, NULL, Ss, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
     EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, dd, NULL, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
-    float* dup[3] = {S_PTR, (float*)fake(0x310000), S_PTR};
+    float* dup[3] = {Ss[0], Ss[1], Ss[0]};
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, dd, dup, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
+    float* part[3] = {Ss[0], Ss[1], (float*)fake(0x3000000 + 4096)};   /* partial overlap */
+    EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, dd, part, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
     EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, dd, dup, WS_PTR, wsb, NULL) == LOGRA_EINVAL);
     EXPECT(logra_sketch_accumulate_shared(X_PTR, 1536, 16384, 1536, 64, 1, 0, 0, 0, 3, dys, ldd, dd, Ss, WS_PTR, wsb - 256, NULL) == LOGRA_EWORKSPACE);
     const int64_t bad_ld[3] = {1536, 255, 256};
@@ -248,6 +253,110 @@ static void check_other_rejects(void) {
   EXPECT(logra_calib_copy(S_PTR, X_PTR, 0, NULL) == 0);
 }
 
+/* The layer sketch and the grouped merge: workspace queries over group
+ * structures, and rejected calls. */
+static void check_layer_and_merge_many(void) {
+  logra_sketch_group g[LOGRA_MAX_GROUPS + 1];
+  memset(g, 0, sizeof(g));
+  const int64_t ks[4] = {1536, 1536, 1536, 8960};
+  const int nouts[4] = {3, 1, 2, 1};
+  const int64_t ds[4][4] = {{1536, 256, 256, 0}, {1536, 0, 0, 0}, {8960, 8960, 0, 0}, {1536, 0, 0, 0}};
+  uintptr_t s_next = 0x10000000;
+  for (int i = 0; i < 4; ++i) {
+    g[i].X = X_PTR;
+    g[i].ldx = ks[i];
+    g[i].k = ks[i];
+    g[i].seed = 1234;
+    g[i].n_out = nouts[i];
+    for (int o = 0; o < nouts[i]; ++o) {
+      g[i].dY[o] = DY_PTR;
+      g[i].ldd[o] = ds[i][o];
+      g[i].d[o] = ds[i][o];
+      g[i].S[o] = (float*)fake(s_next);
+      s_next += (uintptr_t)ds[i][o] * 256 * 4 + 4096;
+    }
+  }
+  for (int n = 1; n <= 4; ++n) {
+    for (int ir = 0; ir < N_OF(kRanks); ++ir) {
+      const size_t b = logra_sketch_layer_ws_bytes(16384, kRanks[ir], n, g);
+      EXPECT(b > 0 && b % 256 == 0);
+      if (n == 1)
+        EXPECT(b == logra_sketch_shared_ws_bytes(16384, 1536, kRanks[ir], 3, g[0].d));
+    }
+  }
+  EXPECT(logra_sketch_layer_ws_bytes(16384, 64, 0, g) == 0);
+  EXPECT(logra_sketch_layer_ws_bytes(16384, 64, 5, g) == 0);
+  EXPECT(logra_sketch_layer_ws_bytes(16384, 64, 4, NULL) == 0);
+  EXPECT(logra_sketch_layer_ws_bytes(-1, 64, 4, g) == 0);
+  EXPECT(logra_sketch_layer_ws_bytes(INT64_MAX, INT32_MAX, 4, g) == 0);
+  const size_t ws = logra_sketch_layer_ws_bytes(16384, 64, 4, g);
+  /* bad call-level arguments */
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 0, g, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 5, g, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, NULL, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_layer(16384, 0, 0, 0, 4, g, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 16, 4, g, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 3, 4, g, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, g, WS_PTR, ws - 256, NULL) == LOGRA_EWORKSPACE);
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, g, NULL, ws, NULL) == LOGRA_EWORKSPACE);
+  /* T == 0 without overwrite: nothing to do */
+  EXPECT(logra_sketch_accumulate_layer(0, 64, 0, 0, 4, g, NULL, 0, NULL) == LOGRA_OK);
+  /* one bad group field at a time */
+  logra_sketch_group bad[4];
+  memcpy(bad, g, sizeof(bad));
+  bad[2].X = NULL;
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, bad, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  memcpy(bad, g, sizeof(bad));
+  bad[3].ldx = 8952;
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, bad, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  memcpy(bad, g, sizeof(bad));
+  bad[1].n_out = 0;
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, bad, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  memcpy(bad, g, sizeof(bad));
+  bad[0].n_out = 4;   /* nine outputs in all (and a fourth d of zero) */
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, bad, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  memcpy(bad, g, sizeof(bad));
+  bad[2].S[1] = bad[0].S[2];   /* one accumulator for two outputs */
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, bad, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  memcpy(bad, g, sizeof(bad));
+  bad[2].S[1] = (float*)((char*)bad[2].S[0] + 64);   /* partial overlap */
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, bad, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  memcpy(bad, g, sizeof(bad));
+  bad[1].ldd[0] = (int64_t)1 << 26;
+  EXPECT(logra_sketch_accumulate_layer(16384, 64, 0, 0, 4, bad, WS_PTR, ws, NULL) == LOGRA_EINVAL);
+  /* the grouped merge */
+  logra_merge_item m[LOGRA_MAX_MERGE + 1];
+  memset(m, 0, sizeof(m));
+  for (int i = 0; i <= LOGRA_MAX_MERGE; ++i) {
+    m[i].W = (uint16_t*)fake(0x20000000 + (uintptr_t)i * 0x1000000);
+    m[i].ldw = 1536;
+    m[i].S = (const float*)fake(0x80000000u + (uintptr_t)i * 0x100000);
+    m[i].d = 1536;
+    m[i].k = 1536;
+  }
+  EXPECT(logra_merge_many(0, m, 64, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge_many(LOGRA_MAX_MERGE + 1, m, 64, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge_many(2, NULL, 64, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge_many(2, m, 0, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge_many(2, m, 64, 4, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_merge_many(2, m, 64, 0, NAN, 2e-4f, NULL) == LOGRA_EINVAL);
+  logra_merge_item mb[3];
+  memcpy(mb, m, sizeof(mb));
+  mb[1].W = mb[0].W + 1536 * 100;   /* rows inside the first weight */
+  EXPECT(logra_merge_many(3, mb, 64, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  memcpy(mb, m, sizeof(mb));
+  mb[2].S = (const float*)(mb[1].W + 64);   /* an S inside a W */
+  EXPECT(logra_merge_many(3, mb, 64, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  memcpy(mb, m, sizeof(mb));
+  mb[1].ldw = 1000;
+  EXPECT(logra_merge_many(3, mb, 64, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+  memcpy(mb, m, sizeof(mb));
+  mb[2].d = ((int64_t)1 << 31) - 1;
+  mb[2].k = ((int64_t)1 << 31) - 8;
+  mb[2].ldw = ((int64_t)1 << 31) - 8;
+  EXPECT(logra_merge_many(3, mb, 64, 0, 1.0f, 2e-4f, NULL) == LOGRA_EINVAL);
+}
+
 static void check_kernel_choice(void) {
   EXPECT(logra_set_kernel_choice(2, 0) == LOGRA_EINVAL);
   EXPECT(logra_set_kernel_choice(-1, 0) == LOGRA_EINVAL);
@@ -259,12 +368,52 @@ static void check_kernel_choice(void) {
   EXPECT(logra_set_kernel_choice(LOGRA_CHOICE_ACC_WIDE, LOGRA_CHOICE_AUTO) == LOGRA_OK);
 }
 
+/* The one path that reaches HIP here: T == 0 with the overwrite flag zero
+ * fills exactly the call's outputs.  Only without a visible device (every
+ * launch then fails with a HIP error and nothing runs); the sanitizers check
+ * that the output list is not read past its end. */
+static void check_zero_fill_without_device(void) {
+  int n_dev = 0;
+  if (hipGetDeviceCount(&n_dev) == hipSuccess && n_dev > 0) {
+    printf("a device is visible: zero-fill checks skipped\n");
+    return;
+  }
+  const int st1 = logra_sketch_accumulate(NULL, 0, NULL, 0, 0, 64, 64, 4, 1, 0, 0,
+                                          LOGRA_SKETCH_OVERWRITE, S_PTR, NULL, 0, NULL);
+  EXPECT(st1 == LOGRA_EHIP);
+  const uint16_t* dys[2] = {NULL, NULL};
+  const int64_t ldd[2] = {0, 0}, dd[2] = {64, 32};
+  float* Ss[2] = {S_PTR, (float*)fake(0x3400000)};
+  const int st2 = logra_sketch_accumulate_shared(NULL, 0, 0, 64, 4, 1, 0, 0, LOGRA_SKETCH_OVERWRITE,
+                                                 2, dys, ldd, dd, Ss, NULL, 0, NULL);
+  EXPECT(st2 == LOGRA_EHIP);
+  logra_sketch_group g[2];
+  memset(g, 0, sizeof(g));
+  g[0].k = 64;
+  g[0].n_out = 1;
+  g[0].d[0] = 64;
+  g[0].S[0] = S_PTR;
+  g[1].k = 128;
+  g[1].n_out = 2;
+  g[1].d[0] = 32;
+  g[1].d[1] = 16;
+  g[1].S[0] = (float*)fake(0x3400000);
+  g[1].S[1] = (float*)fake(0x3500000);
+  const int st3 = logra_sketch_accumulate_layer(0, 4, 0, LOGRA_SKETCH_OVERWRITE, 2, g, NULL, 0, NULL);
+  EXPECT(st3 == LOGRA_EHIP);
+  const int st4 = logra_sketch_accumulate_noalloc(NULL, 0, NULL, 0, 0, 64, 64, 4, 1, 0, 0,
+                                                  LOGRA_SKETCH_OVERWRITE, S_PTR, NULL);
+  EXPECT(st4 == LOGRA_EHIP);
+}
+
 int main(void) {
   check_status_strings();
   check_sketch_ws();
   check_sketch_rejects();
   check_other_rejects();
+  check_layer_and_merge_many();
   check_kernel_choice();
+  check_zero_fill_without_device();
   printf("host ABI checks: %d expectations, %d failed\n", g_checks, g_fail);
   return g_fail == 0 ? 0 : 1;
 }

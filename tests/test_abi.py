@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = _lib.header_symbols()
-    assert len(declared) == 15
+    assert len(declared) == 18
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -317,3 +317,130 @@ def test_sketch_noalloc_rejects_before_any_hip_call(L):
     assert call(T=16384, d=5120, k=25600, r=256, ldx=25600, ldd=5120) == EWS
     # T = 0 without the overwrite flag: nothing to do
     assert call(T=0, X=0, dY=0) == OK
+
+
+def _groups(spec):
+    """ctypes logra_sketch_group array; spec: [dict(X, ldx, k, seed, stream,
+    outs=[(dY, ldd, d, S)], n_out=len(outs))]."""
+    arr = (_lib.SketchGroup * max(1, len(spec)))()
+    for g, q in enumerate(spec):
+        outs = q.get("outs", [])
+        arr[g].X, arr[g].ldx, arr[g].k = q.get("X", P), q.get("ldx", 256), q.get("k", 256)
+        arr[g].seed, arr[g].stream = q.get("seed", 1), q.get("stream", 0)
+        arr[g].n_out = q.get("n_out", len(outs))
+        for o, (dY, ldd, d, S) in enumerate(outs):
+            arr[g].dY[o], arr[g].ldd[o], arr[g].d[o], arr[g].S[o] = dY, ldd, d, S
+    return arr
+
+
+def _layer_spec(n_groups=3, per=2, d=256, r=4):
+    """n_groups groups of `per` outputs with disjoint S (d x r floats each)."""
+    nb = d * r * 4
+    return [dict(outs=[(P, 256, d, P + nb * (g * per + o + 1)) for o in range(per)])
+            for g in range(n_groups)]
+
+
+def _layer(L, spec, T=128, r=4, kind=0, flags=0, ws=P, ws_bytes=1 << 30, n_groups=None):
+    arr = _groups(spec)
+    n = len(spec) if n_groups is None else n_groups
+    return L.logra_sketch_accumulate_layer(T, r, kind, flags, n, arr, ws, ws_bytes, None)
+
+
+def _mut(spec, g, **kw):
+    spec = [dict(q) for q in spec]
+    spec[g].update(kw)
+    return spec
+
+
+def _layer_reject_cases():
+    base = _layer_spec()
+    nb = 256 * 4 * 4
+    cases = [
+        (dict(n_groups=0), EINVAL), (dict(n_groups=5), EINVAL), (dict(r=0), EINVAL),
+        (dict(r=257), EINVAL), (dict(kind=2), EINVAL), (dict(flags=8), EINVAL),
+        (dict(flags=3), EINVAL), (dict(flags=2, T=0), EINVAL), (dict(T=-1), EINVAL),
+        (dict(ws=None), EWS), (dict(ws_bytes=256), EWS), (dict(ws=P + 128), EWS),
+        (dict(spec=_mut(base, 1, X=None)), EINVAL), (dict(spec=_mut(base, 1, X=MIS)), EINVAL),
+        (dict(spec=_mut(base, 2, ldx=100)), EINVAL), (dict(spec=_mut(base, 0, k=0)), EINVAL),
+        (dict(spec=_mut(base, 1, n_out=0)), EINVAL), (dict(spec=_mut(base, 1, n_out=5)), EINVAL),
+        (dict(spec=_mut(base, 2, outs=[(None, 256, 256, P + 100 * nb), (P, 256, 256, P + 101 * nb)])),
+         EINVAL),
+        (dict(spec=_mut(base, 2, outs=[(P, 255, 256, P + 100 * nb), (P, 256, 256, P + 101 * nb)])),
+         EINVAL),
+        (dict(spec=_mut(base, 2, outs=[(P, 256, 0, P + 100 * nb), (P, 256, 256, P + 101 * nb)])),
+         EINVAL),
+        # S of group 2 overlapping S of group 0, wholly and in part
+        (dict(spec=_mut(base, 2, outs=[(P, 256, 256, P + nb), (P, 256, 256, P + 101 * nb)])), EINVAL),
+        (dict(spec=_mut(base, 2, outs=[(P, 256, 256, P + nb + 512), (P, 256, 256, P + 101 * nb)])),
+         EINVAL),
+        # nine outputs in all
+        (dict(spec=_layer_spec(n_groups=3, per=3)), EINVAL),
+        (dict(spec=_mut(base, 0, outs=[(P, 256, 256, None), (P, 256, 256, P + 2 * nb)])), EINVAL),
+    ]
+    return cases
+
+
+@pytest.mark.parametrize("kw,status", _layer_reject_cases())
+def test_sketch_layer_rejects(L, kw, status):
+    kw = dict(kw)
+    spec = kw.pop("spec", _layer_spec())
+    assert _layer(L, spec, **kw) == status
+
+
+def test_sketch_layer_T0_and_sizes(L):
+    # T == 0 without the overwrite flag: no pointer is inspected
+    spec = [dict(X=None, outs=[(None, 0, 256, None)]), dict(X=None, outs=[(None, 0, 64, None)] * 2)]
+    assert _layer(L, spec, T=0, ws=None, ws_bytes=0) == OK
+    # one group equals the shared query; the sizes grow with the groups
+    groups = [(1536, [1536, 256, 256]), (1536, [1536]), (1536, [8960, 8960]), (8960, [1536])]
+
+    def q(gs, T=16384, r=64):
+        arr = (_lib.SketchGroup * len(gs))()
+        for g, (k, ds) in enumerate(gs):
+            arr[g].k, arr[g].n_out = k, len(ds)
+            for o, d in enumerate(ds[:_lib.MAX_SHARED]):
+                arr[g].d[o] = d
+        return L.logra_sketch_layer_ws_bytes(T, r, len(gs), arr)
+
+    d3 = (ctypes.c_int64 * 3)(1536, 256, 256)
+    assert q(groups[:1]) == L.logra_sketch_shared_ws_bytes(16384, 1536, 64, 3, d3)
+    full = q(groups)
+    assert full >= 4 * 2 * 64 * 16384 * 2                 # four P buffers at least
+    assert q(groups, T=0) > 0 and q(groups, r=0) == 0 and q(groups, T=-5) == 0
+    assert q([(1536, [])]) == 0 and q([(1536, [64] * 5)]) == 0
+    assert q(groups + [(256, [64])]) == 0                  # five groups
+    assert q([(256, [64] * 4), (256, [64] * 4), (256, [64])]) == 0   # nine outputs
+    assert L.logra_sketch_layer_ws_bytes(16384, 64, 2, None) == 0
+
+
+def _merge_many(L, items, r=4, kind=0, alpha=1.0, eta=1.0, n=None):
+    arr = (_lib.MergeItem * max(1, len(items)))()
+    for i, (W, ldw, S, d, k) in enumerate(items):
+        arr[i].W, arr[i].ldw, arr[i].S, arr[i].d, arr[i].k = W, ldw, S, d, k
+        arr[i].seed, arr[i].stream = 1, 0
+    return L.logra_merge_many(len(items) if n is None else n, arr, r, kind, alpha, eta, None)
+
+
+# three weights of 64 x 256 bf16 (32 KiB each) and their S (64 x 4 floats)
+W_NB, S_NB = 64 * 256 * 2, 64 * 4 * 4
+GOOD = [(P + i * W_NB, 256, P + 8 * W_NB + i * S_NB, 64, 256) for i in range(3)]
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n=0), dict(n=9), dict(r=0), dict(r=257), dict(kind=3), dict(alpha=float("nan")),
+    dict(eta=float("inf")),
+    dict(items=[GOOD[0], (None, 256, P + 9 * W_NB, 64, 256)]),
+    dict(items=[GOOD[0], (P + W_NB, 256, None, 64, 256)]),
+    dict(items=[GOOD[0], (P + W_NB + 8, 256, P + 9 * W_NB, 64, 256)]),     # W misaligned
+    dict(items=[GOOD[0], (P + W_NB, 256, P + 9 * W_NB + 2, 64, 256)]),     # S misaligned
+    dict(items=[GOOD[0], (P + W_NB, 250, P + 9 * W_NB, 64, 256)]),         # ldw < k
+    dict(items=[GOOD[0], (P + W_NB, 256, P + 9 * W_NB, 0, 256)]),
+    dict(items=[GOOD[0], (P + W_NB, 256, P + 9 * W_NB, 64, 0)]),
+    dict(items=[GOOD[0], (P + W_NB // 2, 256, P + 9 * W_NB, 64, 256)]),    # W overlaps W
+    dict(items=[GOOD[0], (P + W_NB, 256, P + 16, 64, 256)]),               # S inside a W
+    dict(items=[GOOD[0], GOOD[0]]),
+])
+def test_merge_many_rejects(L, kw):
+    kw = dict(kw)
+    items = kw.pop("items", GOOD)
+    assert _merge_many(L, items, **kw) == EINVAL
