@@ -99,13 +99,15 @@ int logra_regen_A(uint64_t seed, uint64_t stream, int kind, int32_t r,
  * default each call picks its kernels from the shapes; results of the
  * alternatives agree to fp32 rounding.
  *
- * which: LOGRA_CHOICE_PROJECT_TILE - the 64-token projection tile (only
- *            considered for r > 32);
+ * which: LOGRA_CHOICE_PROJECT_TILE - the projection tile (only considered
+ *            for r > 32); mode 1 forces its 64-token form, mode 2 its
+ *            128-token form where r > 64 (the 64-token form below);
  *        LOGRA_CHOICE_ACC_WIDE - the work-group-wide accumulate kernel (only
  *            considered for r > 64).  It changes the workspace size, so it
  *            must not change between logra_sketch_ws_bytes (or
  *            logra_sketch_shared_ws_bytes) and the call that workspace serves.
- * mode:  LOGRA_CHOICE_AUTO (the default), 0 (never) or 1 (always).
+ * mode:  LOGRA_CHOICE_AUTO (the default), 0 (never) or 1 (always), and 2
+ *        for the projection tile as above.
  * The setting is process-wide: it applies to every later sketch call on any
  * thread until it is set again.  This is the library's only state.
  * Returns LOGRA_OK, or LOGRA_EINVAL for an unknown `which` or `mode`.

@@ -351,45 +351,52 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(PT tab, int T,
   }
 }
 
-// Projection with 64 tokens per work-group, for r >= 64 (chosen by
-// use_tile_projection below).  Waves 0-3 and 4-7 take the two halves of r (NBW 32-row blocks
-// of A each) over the same 256-column chunks of k (chunk lane = wave mod 4),
-// and each chunk lane's X rows reach LDS once for both halves, 32 rows from
-// each of its two waves.  A wave multiplies every sign (or Gaussian) operand
-// it builds with both 32-token blocks, so the Philox words and the +-1
-// expansion cost half as much per product as in project_kernel, whose waves
-// cover one 32-token block (at r = 256 that kernel issues ~24 VALU
-// instructions per MFMA).  The half-chunk steps of all lanes run in lock step
-// with one barrier each: after it, a wave's own copy and its partner's have
+// Projection with 32 TB tokens per work-group, for r >= 64 (chosen by
+// tile_blocks below).  TB = 2: waves 0-3 and 4-7 take the two halves of r
+// (NBW 32-row blocks of A each) over the same 256-column chunks of k (chunk
+// lane = wave mod 4), and each chunk lane's 64 X rows reach LDS once for both
+// halves, 32 rows from each of its two waves.  A wave multiplies every sign
+// (or Gaussian) operand it builds with both 32-token blocks, so the Philox
+// words and the +-1 expansion cost half as much per product as in
+// project_kernel, whose waves cover one 32-token block (at r = 256 that
+// kernel issues ~24 VALU instructions per MFMA).  TB = 4 (from r = 128, where
+// its work-groups still fill the chip): 128 tokens, two chunk lanes x four r
+// parts, so every operand a wave builds meets four token blocks.  Either way
+// 128 KiB of staging.  The half-chunk steps of all lanes run in lock step
+// with one barrier each: after it, a wave's own copy and its partners' have
 // landed and every wave is done reading the other buffer, which is refilled
 // while this step is multiplied.
-constexpr int kTileTokens = 64;
-constexpr int kTileLanes = 4;
+constexpr int tile_lanes(int tb) { return tb == 2 ? 4 : 2; }   // chunk lanes
 
-template <int NBW, bool GAUSS, bool MASKED, class PT>
+template <int NBW, bool GAUSS, bool MASKED, int TB, class PT>
 __global__ __launch_bounds__(512) void project_tile_kernel(PT tab, int T, int rp, int steps_total,
                                                            float c) {
   static_assert(NBW % 2 == 0 || NBW == 1, "sign words pair 32-row blocks");
-  // [chunk lane][half][64 rows x 128 columns bf16], 16-byte pieces swizzled by row
-  __shared__ __attribute__((aligned(16))) unsigned char stage[kTileLanes][2][2 * kHalfBytes];
+  static_assert(TB == 2 || TB == 4, "64- or 128-token tiles");
+  constexpr int kLanes = tile_lanes(TB);   // chunk lanes
+  constexpr int kRParts = 8 / kLanes;      // r parts (= TB: each wave brings 32 rows)
+  constexpr int kTok = 32 * TB;            // tokens per work-group
+  static_assert(kRParts == TB, "a chunk lane's waves bring its TB x 32 X rows");
+  // [chunk lane][half][kTok rows x 128 columns bf16], 16-byte pieces swizzled by row
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kLanes][2][TB * kHalfBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rpart = wave / kTileLanes;   // which half of r
-  const int cl = wave % kTileLanes;      // chunk lane
+  const int rpart = wave / kLanes;       // which part of r
+  const int cl = wave % kLanes;          // chunk lane
   const int m = lane & 31;  // A-operand row (token) and B-operand column (A row)
   const int h = lane >> 5;  // which 64-column quarter of a half this lane feeds
   const ProjSel gs = select_group(tab, (int)blockIdx.x);
   LOGRA_GROUP_FIELDS(gs);
   const int blk = xcd_spread(gs.bl, gs.bl >> 3, gs.n_blk);
-  const int t0 = blk * kTileTokens;
+  const int t0 = blk * kTok;
   const SignMasks smk = sign_masks();
   const int n_chunks = (k + 255) >> 8;
   const int row_base = rpart * NBW * 32;   // first A row of this wave
 
-  f32x16 acc[2][NBW];
+  f32x16 acc[TB][NBW];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(512) void project_tile_kernel(PT tab, int T, int rp
       const int j = (lane & 15) ^ (row & 15);
       int t = t0 + row;
       int col = colbase + 8 * j;
-      if (t0 + kTileTokens > T) t = t < T ? t : T - 1;              // ragged tile only
+      if (t0 + kTok > T) t = t < T ? t : T - 1;                     // ragged tile only
       if (MASKED && (cnk + 1) * 256 > k) col = col < k ? col : 0;  // ragged chunk only
       lds_dma16_nt((const void*)(X + (int64_t)t * ldx + col),
                    lds_addr(dst + (32 * rpart + 4 * i) * (kHalfCols * 2)));
@@ -460,12 +467,14 @@ __global__ __launch_bounds__(512) void project_tile_kernel(PT tab, int T, int rp
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int slot = (8 * h + s) ^ (m & 15);
-      u32x4 a0 = *reinterpret_cast<const u32x4*>(buf + m * (kHalfCols * 2) + slot * 16);
-      u32x4 a1 = *reinterpret_cast<const u32x4*>(buf + (32 + m) * (kHalfCols * 2) + slot * 16);
+      u32x4 a[TB];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        a[tb] = *reinterpret_cast<const u32x4*>(buf + (32 * tb + m) * (kHalfCols * 2) + slot * 16);
       if (edge) {
         const u32x4 keep = keep_mask8(k - (colq + 8 * s));
-        a0 &= keep;
-        a1 &= keep;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) a[tb] &= keep;
       }
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
@@ -478,19 +487,19 @@ __global__ __launch_bounds__(512) void project_tile_kernel(PT tab, int T, int rp
         } else {
           b = signs_to_bf16x8((uint32_t)(sw[nb][hc] >> (8 * s)) & 0xFFu, smk);
         }
-        acc[0][nb] = mfma32(a0, b, acc[0][nb]);
-        acc[1][nb] = mfma32(a1, b, acc[1][nb]);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[tb][nb] = mfma32(a[tb], b, acc[tb][nb]);
       }
     }
   };
 
-  // Lane cl takes chunks cl, cl + 4, ... (physical chunk = logical + block,
-  // mod n_chunks, as in project_kernel); every lane runs 2 ceil(n / 4) steps
-  // so the barriers match, idling past its last chunk.
+  // Lane cl takes chunks cl, cl + kLanes, ... (physical chunk = logical +
+  // block, mod n_chunks, as in project_kernel); every lane runs
+  // 2 ceil(n / kLanes) steps so the barriers match, idling past its last chunk.
   const int rot = blk % n_chunks;
   auto phys = [&](int cc) { cc += rot; return cc < n_chunks ? cc : cc - n_chunks; };
-  const int n_mine = cl < n_chunks ? (n_chunks - cl + kTileLanes - 1) / kTileLanes : 0;
-  const int n_steps = 2 * ((n_chunks + kTileLanes - 1) / kTileLanes);
+  const int n_mine = cl < n_chunks ? (n_chunks - cl + kLanes - 1) / kLanes : 0;
+  const int n_steps = 2 * ((n_chunks + kLanes - 1) / kLanes);
   // One half-step; with the prefetch the loop below runs them in pairs
   // (n_steps is even) so the two operand sets swap roles at compile time.
   GbSet gb_a, gb_b;
@@ -501,11 +510,11 @@ __global__ __launch_bounds__(512) void project_tile_kernel(PT tab, int T, int rp
     __syncthreads();    // ... and its partner's; the other buffer is free
     const int nj = (step + 1) >> 1;
     if (nj < n_mine) {
-      issue(phys(cl + kTileLanes * nj), (step + 1) & 1, stage[cl][(step + 1) & 1]);
-      load_gb(phys(cl + kTileLanes * nj), (step + 1) & 1, nxt);
+      issue(phys(cl + kLanes * nj), (step + 1) & 1, stage[cl][(step + 1) & 1]);
+      load_gb(phys(cl + kLanes * nj), (step + 1) & 1, nxt);
     }
     if (jc < n_mine) {
-      const int pc = phys(cl + kTileLanes * jc);
+      const int pc = phys(cl + kLanes * jc);
       if constexpr (!GAUSS) {
         if (hc == 0) sign_words(pc);
       }
@@ -529,18 +538,21 @@ __global__ __launch_bounds__(512) void project_tile_kernel(PT tab, int T, int rp
   }
   vm_wait<0>();
 
-  // Sum the four chunk lanes of each r half in a fixed order (l0 + l1 + l2 +
-  // l3), one (token block, r block) at a time through LDS, and store the hi/lo
-  // pair in the tiled layout.  Thread t: r half t / 256, r column n_out of the
-  // block, tokens 4 tg .. 4 tg + 3.
+  // Sum the chunk lanes of each r part in a fixed order (l0 + l1 + ...), one
+  // (token block, r block) at a time through LDS, and store the hi/lo pair in
+  // the tiled layout.  Thread t: r part t / (512 / kRParts), r column n_out of
+  // the block, tokens kTpt tg .. kTpt tg + kTpt - 1.
+  constexpr int kThrPart = 512 / kRParts;
+  constexpr int kTpt = 32 / (kThrPart / 32);   // tokens per thread: 4 or 8
+  static_assert(8 * 32 * 33 * 4 <= (int)sizeof(stage), "reduction buffer fits");
   float (*red)[32 * 33] = reinterpret_cast<float (*)[32 * 33]>(&stage[0][0][0]);
-  const int rh = tid >> 8;
+  const int rh = tid / kThrPart;
   const int n_out = tid & 31;
-  const int tg = (tid >> 5) & 7;
+  const int tg = (tid % kThrPart) >> 5;
   const int nb16 = rp >> 4;
   __syncthreads();
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
 #pragma unroll
@@ -549,25 +561,25 @@ __global__ __launch_bounds__(512) void project_tile_kernel(PT tab, int T, int rp
         red[wave][row * 33 + m] = acc[tb][nb][v];
       }
       __syncthreads();
-      const int step = 2 * blk + tb;
+      const int step = TB * blk + tb;
       const int i = (rh * NBW + nb) * 32 + n_out;   // A row / P column
       if (step < steps_total && i < rp) {
-        uint16_t hi[4], lo[4];
+        uint16_t hi[kTpt], lo[kTpt];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int idx = (4 * tg + u) * 33 + n_out;
-          float p = red[rh * kTileLanes][idx];
+        for (int u = 0; u < kTpt; ++u) {
+          const int idx = (kTpt * tg + u) * 33 + n_out;
+          float p = red[rh * kLanes][idx];
 #pragma unroll
-          for (int w = 1; w < kTileLanes; ++w) p += red[rh * kTileLanes + w][idx];
-          if (t0 + 32 * tb + 4 * tg + u >= T) p = 0.0f;   // token past T
+          for (int w = 1; w < kLanes; ++w) p += red[rh * kLanes + w][idx];
+          if (t0 + 32 * tb + kTpt * tg + u >= T) p = 0.0f;   // token past T
           split_bf16(p * c, hi[u], lo[u]);
         }
-        const int u0 = 4 * tg;
+        const int u0 = kTpt * tg;
         const int64_t slot = (int64_t)(((u0 >> 3) * 16 + (i & 15)) * 8 + (u0 & 7));
         uint16_t* ph = Pt + p_block(step, i >> 4, 0, nb16) + slot;
         uint16_t* pl = Pt + p_block(step, i >> 4, 1, nb16) + slot;
 #pragma unroll
-        for (int u = 0; u < 4; u += 2) {
+        for (int u = 0; u < kTpt; u += 2) {
           *reinterpret_cast<uint32_t*>(ph + u) = (uint32_t)hi[u] | ((uint32_t)hi[u + 1] << 16);
           *reinterpret_cast<uint32_t*>(pl + u) = (uint32_t)lo[u] | ((uint32_t)lo[u + 1] << 16);
         }
@@ -1229,21 +1241,28 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
 }
 
 // Kernel-choice overrides set through logra_set_kernel_choice (tests and
-// measurements): -1 automatic, 0 never, 1 always.
+// measurements): -1 automatic, 0 never, 1 always (for the projection tile, 2:
+// always, with 128-token tiles from r = 128).
 std::atomic<int> g_choice_project_tile{-1};
 std::atomic<int> g_choice_acc_wide{-1};
 
-// Whether launch_project takes project_tile_kernel (only from two 32-row
-// blocks of A up).  It builds each basis operand for two token blocks, which
-// pays wherever operand building bounds project_kernel: always for the
-// Gaussian basis, and for the sign basis once its 64-token work-groups still
-// fill all 256 CUs (below that, project_kernel's twice as many work-groups
-// are worth more).
-bool use_tile_projection(const SketchPlan& p, int nb32, bool gauss) {
-  if (nb32 < 2) return false;
+// The token blocks per work-group of project_tile_kernel for this call, or 0
+// for project_kernel (the tile needs two 32-row blocks of A, its 128-token
+// form four).  The tile builds each basis operand for two or four token
+// blocks, which pays wherever operand building bounds project_kernel: always
+// for the Gaussian basis, and for the sign basis once its work-groups still
+// fill all 256 CUs (below that, project_kernel's more work-groups are worth
+// more); the 128-token form wherever its work-groups, all groups together,
+// fill them.
+int tile_blocks(const SketchPlan& p, int nb32, bool gauss) {
+  if (nb32 < 2) return 0;
+  const int tb4 = nb32 >= 4 ? 4 : 2;
   const int mode = g_choice_project_tile.load(std::memory_order_relaxed);
-  if (mode >= 0) return mode == 1;
-  return gauss || p.t_pad / kTileTokens >= 256;
+  if (mode == 0) return 0;
+  if (mode == 1) return 2;
+  if (mode == 2) return tb4;
+  if (nb32 >= 4 && p.n_groups * ((p.t_pad + 127) / 128) >= 256) return 4;
+  return gauss || p.t_pad / 64 >= 256 ? 2 : 0;
 }
 
 // Groups and their block count in a projection launch.
@@ -1273,21 +1292,31 @@ template <int NB, class PT>
 hipError_t launch_project(const SketchPlan& p, PT tab, int T, bool gauss, float c, hipStream_t s) {
   const bool masked = proj_masked(tab);
   if constexpr (NB >= 2) {
-    if (use_tile_projection(p, NB, gauss)) {
-      const int n_blk = (int)((p.t_pad + kTileTokens - 1) / kTileTokens);
+    const int tb = tile_blocks(p, NB, gauss);
+    if (tb > 0) {
+      const int n_blk = (int)((p.t_pad + 32 * tb - 1) / (32 * tb));
       set_blocks(tab, n_blk);
       const dim3 grid((unsigned)(proj_groups(tab) * n_blk));
       const float cc = gauss ? 1.0f : c;
-#define LOGRA_TILE(G, M)                                                                      \
-  hipLaunchKernelGGL((project_tile_kernel<NB / 2, G, M, PT>), grid, dim3(512), 0, s, tab, T, p.rp, \
-                     p.steps, cc)
-      if (gauss) {
-        if (masked) LOGRA_TILE(true, true);
-        else LOGRA_TILE(true, false);
-      } else {
-        if (masked) LOGRA_TILE(false, true);
-        else LOGRA_TILE(false, false);
+#define LOGRA_TILE(G, M, TB)                                                                     \
+  hipLaunchKernelGGL((project_tile_kernel<NB / TB, G, M, TB, PT>), grid, dim3(512), 0, s, tab, T, \
+                     p.rp, p.steps, cc)
+#define LOGRA_TILES(TB)                         \
+  if (gauss) {                                  \
+    if (masked) LOGRA_TILE(true, true, TB);     \
+    else LOGRA_TILE(true, false, TB);           \
+  } else {                                      \
+    if (masked) LOGRA_TILE(false, true, TB);    \
+    else LOGRA_TILE(false, false, TB);          \
+  }
+      if constexpr (NB >= 4) {
+        if (tb == 4) {
+          LOGRA_TILES(4)
+          return hipGetLastError();
+        }
       }
+      LOGRA_TILES(2)
+#undef LOGRA_TILES
 #undef LOGRA_TILE
       return hipGetLastError();
     }
@@ -1496,7 +1525,7 @@ bool make_sketch_plan_groups(int64_t T, int n_groups, const int64_t* k, const in
 }
 
 bool set_kernel_choice(int which, int mode) {
-  if (mode < -1 || mode > 1) return false;
+  if (mode < -1 || mode > (which == 0 ? 2 : 1)) return false;
   if (which == 0) g_choice_project_tile.store(mode, std::memory_order_relaxed);
   else if (which == 1) g_choice_acc_wide.store(mode, std::memory_order_relaxed);
   else return false;

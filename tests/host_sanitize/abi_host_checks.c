@@ -360,7 +360,9 @@ static void check_layer_and_merge_many(void) {
 static void check_kernel_choice(void) {
   EXPECT(logra_set_kernel_choice(2, 0) == LOGRA_EINVAL);
   EXPECT(logra_set_kernel_choice(-1, 0) == LOGRA_EINVAL);
-  EXPECT(logra_set_kernel_choice(LOGRA_CHOICE_PROJECT_TILE, 2) == LOGRA_EINVAL);
+  EXPECT(logra_set_kernel_choice(LOGRA_CHOICE_PROJECT_TILE, 3) == LOGRA_EINVAL);
+  EXPECT(logra_set_kernel_choice(LOGRA_CHOICE_ACC_WIDE, 2) == LOGRA_EINVAL);
+  EXPECT(logra_set_kernel_choice(LOGRA_CHOICE_PROJECT_TILE, 2) == LOGRA_OK);
   for (int which = 0; which < 2; ++which)
     for (int mode = -1; mode <= 1; ++mode)
       EXPECT(logra_set_kernel_choice(which, mode) == LOGRA_OK);

@@ -276,7 +276,9 @@ def test_kernel_choice_setter(L):
     for which in (0, 1):
         for mode in (-1, 0, 1):
             assert L.logra_set_kernel_choice(which, mode) == OK
-        assert L.logra_set_kernel_choice(which, 2) == EINVAL
+        # mode 2 (128-token tiles) exists for the projection tile only
+        assert L.logra_set_kernel_choice(which, 2) == (OK if which == 0 else EINVAL)
+        assert L.logra_set_kernel_choice(which, 3) == EINVAL
         assert L.logra_set_kernel_choice(which, -2) == EINVAL
     assert L.logra_set_kernel_choice(2, 0) == EINVAL
     for which in (0, 1):

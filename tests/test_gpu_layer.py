@@ -138,11 +138,12 @@ def test_sketch_layer_matches_oracle_and_shared_calls(lg, T, spec, r, kind):
             assert rel_fro(a - base, b - base) < 1e-5, (g, o)
 
 
-@pytest.mark.parametrize("project_tile", [0, 1])
+@pytest.mark.parametrize("project_tile", [0, 1, 2])
 @pytest.mark.parametrize("acc_wide", [0, 1])
 def test_sketch_layer_both_kernel_choices(lg, project_tile, acc_wide):
-    """The group table through project_kernel and project_tile_kernel, the
-    per-output P through accumulate_kernel and accumulate_wide_kernel."""
+    """The group table through project_kernel and both forms of
+    project_tile_kernel (64 and 128 tokens), the per-output P through
+    accumulate_kernel and accumulate_wide_kernel."""
     T, r, kind = 2080, 128, 0
     spec = [(520, [300, 136], 3, 0), (256, [64], 4, 1), (1024, [520], 5, 0)]
     say("sketch layer kernel choice", project_tile, acc_wide)

@@ -131,9 +131,10 @@ def test_sketch_matches_oracle(lg, T, d, k, r, kind, n_mb):
     assert err_total < S_TOL, err_total
 
 
-# Both projection kernels on each case (logra_set_kernel_choice with
-# LOGRA_CHOICE_PROJECT_TILE: 0 = the 32-token kernel, 1 = the 64-token tile
-# kernel), ragged and whole tiles alike.
+# Every projection kernel on each case (logra_set_kernel_choice with
+# LOGRA_CHOICE_PROJECT_TILE: 0 = the 32-token kernel, 1 = the 64-token tile,
+# 2 = the 128-token tile where r > 64, else the 64-token one), ragged and
+# whole tiles alike.
 PROJECTION_CASES = [
     # T, d, k, r, kind, n_mb
     (77, 1030, 264, 64, 0, 1),      # 3 steps: the last tile's second block is empty
@@ -144,6 +145,8 @@ PROJECTION_CASES = [
     (640, 256, 2304, 256, 0, 1),    # whole tiles and chunks (unmasked), nine chunks
     (1024, 512, 4096, 64, 0, 1),    # unmasked, one 32-row block per wave
     (2048, 1024, 768, 64, 1, 1),    # Gaussian basis, unmasked tiles
+    (200, 300, 520, 200, 0, 2),     # 128-token tiles: ragged T (second tile partly past T), k, r
+    (256, 128, 1536, 128, 1, 1),    # 128-token tiles, Gaussian, one 32-row block per wave
 ]
 
 
@@ -177,7 +180,7 @@ def test_sketch_fuzz_small_shapes(lg, T, d, k, r, kind, n_mb):
     assert err < S_TOL, err
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("T,d,k,r,kind,n_mb", PROJECTION_CASES)
 def test_sketch_both_projection_kernels(lg, mode, T, d, k, r, kind, n_mb):
     say("sketch projection kernel", mode, T, d, k, r, kind, n_mb)
