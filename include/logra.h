@@ -298,6 +298,82 @@ int logra_sketch_accumulate_layer(int64_t T, int32_t r, int kind, int32_t flags,
                                   size_t ws_bytes, hipStream_t s);
 
 /*
+ * The sketch in two calls: logra_sketch_project computes the projected input
+ * P = X A^T into a buffer of the caller's, and logra_sketch_accumulate_p adds
+ * dY^T P to S.  [LoGRA] Sketch: the inputs are projected before they meet
+ * the backward derivatives; the projection needs only X (available from the
+ * forward pass) and the accumulation only P and dY, so the two halves can
+ * run at different times or on different streams: the projection of the
+ * next microbatch may overlap the accumulation of this one.  Run back to
+ * back on one stream with the same T, k, r, seed, stream, kind and outputs,
+ * the pair launches the kernels of logra_sketch_accumulate (or
+ * logra_sketch_accumulate_shared) on the same tiling, and S receives the same
+ * bits.
+ *
+ * P layout (bf16, logra_sketch_p_bytes(T, r) bytes): with rp = r rounded up
+ * to 16, 32, 64, 128 or 256 and steps = ceil(max(T, 1) / 32), P holds steps
+ * x (rp / 16) x 2 blocks of 512 bf16 values, block (step, b, h) at element
+ * offset ((step (rp / 16) + b) 2 + h) 512.  Element 8 (16 g + n) + e of a
+ * block is token 32 step + 8 g + e (g < 4, e < 8) and column 16 b + n
+ * (n < 16) of p = c X A^T, split as p = hi + lo with hi = RNE_bf16(p) in the
+ * block with h = 0 and lo = RNE_bf16(p - hi) in h = 1; c = 1 / sqrt(r) for
+ * signs and 1 for the Gaussian basis (whose entries already carry it).
+ * Tokens past T hold zeros; columns r .. rp - 1 hold values that the
+ * accumulation ignores.
+ */
+
+/* Bytes of P for T tokens at rank r.  Returns 0 for invalid sizes. */
+size_t logra_sketch_p_bytes(int64_t T, int32_t r);
+
+/* Bytes of scratch logra_sketch_project needs for the Gaussian basis (the
+ * bf16 basis written once per call); the sign basis needs none.  Returns 0
+ * for invalid sizes. */
+size_t logra_sketch_project_ws_bytes(int64_t k, int32_t r);
+
+/*
+ * logra_sketch_project - P = X A^T for one microbatch, in the layout above.
+ * X, ldx, T, k, r, seed, stream, kind: as in logra_sketch_accumulate.
+ * P: device bf16 buffer of p_bytes >= logra_sketch_p_bytes(T, r) bytes,
+ *     16-B aligned, written (its contents on entry do not matter).
+ * ws: for kind == LOGRA_GAUSSIAN, device scratch of
+ *     logra_sketch_project_ws_bytes(k, r) bytes, 256-B aligned, owned by
+ *     the caller; for signs it is not used (may be NULL).
+ * T == 0 is a no-op (returns LOGRA_OK; X, P and ws are not inspected).
+ * X, P and ws must not overlap.
+ * Returns LOGRA_OK, LOGRA_EINVAL (also for a P smaller than required),
+ * LOGRA_EWORKSPACE or LOGRA_EHIP.
+ */
+int logra_sketch_project(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t r,
+                         uint64_t seed, uint64_t stream, int kind, uint16_t* P, size_t p_bytes,
+                         void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Bytes of workspace logra_sketch_accumulate_p needs (the per-split partial
+ * sums; d: host int64[n_out]).  Returns 0 for invalid sizes. */
+size_t logra_sketch_accumulate_p_ws_bytes(int64_t T, int32_t r, int32_t n_out, const int64_t* d);
+
+/*
+ * logra_sketch_accumulate_p - S_o += dY_o^T P for up to LOGRA_MAX_SHARED
+ * outputs o, with P made by logra_sketch_project for the same T and r.
+ * P, p_bytes: as written by logra_sketch_project (p_bytes >=
+ *     logra_sketch_p_bytes(T, r), 16-B aligned); read only.
+ * T, r, flags, n_out, dY, ldd, d, S: as in logra_sketch_accumulate_shared,
+ *     including the deferred chains (every call of a chain uses the same
+ *     ws, T, r and outputs; P may differ from call to call, which is how a
+ *     chain covers the microbatches of a step).
+ * ws: device scratch of logra_sketch_accumulate_p_ws_bytes(T, r, n_out, d)
+ *     bytes, 256-B aligned, owned by the caller (same kernel-choice rule as
+ *     logra_sketch_ws_bytes).
+ * T == 0 is a no-op (P, dY and ws are not inspected); with
+ *     LOGRA_SKETCH_OVERWRITE it sets every S[o] to zero.
+ * P, dY, S and ws must not overlap.
+ * Returns LOGRA_OK, LOGRA_EINVAL, LOGRA_EWORKSPACE or LOGRA_EHIP.
+ */
+int logra_sketch_accumulate_p(const uint16_t* P, size_t p_bytes, int64_t T, int32_t r,
+                              int32_t flags, int32_t n_out, const uint16_t* const* dY,
+                              const int64_t* ldd, const int64_t* d, float* const* S, void* ws,
+                              size_t ws_bytes, hipStream_t s);
+
+/*
  * logra_merge - W <- RNE_bf16(W - alpha * eta * S A), in place.
  * [LoGRA] Sketch: the update is W <- W - alpha eta U A with U = S in the basic
  * SGD variant, merged directly into the weights (no adapter branch).

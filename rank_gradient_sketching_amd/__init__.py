@@ -11,5 +11,7 @@ from .api import (GAUSSIAN, MAX_SHARED, MAX_SWEEP, RADEMACHER, SKETCH_OVERWRITE,
                   kl_budget_schedule, kl_sweep_ws_bytes, kl_ws_bytes, merge, predicted_kl,
                   predicted_kl_sweep, regen_A, sketch_accumulate, sketch_accumulate_shared,
                   sketch_accumulate_layer, sketch_layer_ws_bytes, sketch_layer_workspace,
-                  merge_many, sketch_shared_ws_bytes, sketch_update, sketch_ws_bytes, sketch_workspace)
+                  merge_many, sketch_shared_ws_bytes, sketch_update, sketch_ws_bytes, sketch_workspace,
+                  sketch_p_bytes, sketch_project, sketch_project_ws_bytes, sketch_accumulate_p,
+                  sketch_accumulate_p_ws_bytes)
 from . import sync  # noqa: F401,E402

@@ -92,6 +92,22 @@ SIGNATURES.update({
                                                      ctypes.c_size_t, c_vp]),
     "logra_merge_many": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(MergeItem), ctypes.c_int32,
                                         ctypes.c_int, ctypes.c_float, ctypes.c_float, c_vp]),
+    "logra_sketch_p_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
+    "logra_sketch_project_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
+    "logra_sketch_project": (ctypes.c_int, [c_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64,
+                                            ctypes.c_int, c_vp, ctypes.c_size_t, c_vp,
+                                            ctypes.c_size_t, c_vp]),
+    "logra_sketch_accumulate_p_ws_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32,
+                                                             ctypes.c_int32,
+                                                             ctypes.POINTER(ctypes.c_int64)]),
+    "logra_sketch_accumulate_p": (ctypes.c_int, [c_vp, ctypes.c_size_t, ctypes.c_int64,
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.POINTER(c_vp),
+                                                 ctypes.POINTER(ctypes.c_int64),
+                                                 ctypes.POINTER(ctypes.c_int64),
+                                                 ctypes.POINTER(c_vp), c_vp, ctypes.c_size_t,
+                                                 c_vp]),
 })
 
 OK, EINVAL, EWORKSPACE, EHIP = 0, -1, -2, -3

@@ -185,6 +185,82 @@ def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=Non
     return list(Ss)
 
 
+def sketch_p_bytes(T, r):
+    return int(_lib.lib().logra_sketch_p_bytes(T, r))
+
+
+def sketch_project_ws_bytes(k, r):
+    return int(_lib.lib().logra_sketch_project_ws_bytes(k, r))
+
+
+def sketch_project(X, seed, r, stream=0, kind=RADEMACHER, P=None, ws=None):
+    """P = X A^T for one microbatch (the first half of sketch_accumulate), in
+    the tiled bf16 hi/lo layout of include/logra.h, into a uint8 device tensor
+    of sketch_p_bytes(T, r) bytes (allocated when P is None); returns P.  ws:
+    scratch for the Gaussian basis (allocated when needed and None)."""
+    _require(X, "X", torch.bfloat16, 2)
+    T, k, ldx = _rows(X, "X")
+    need = sketch_p_bytes(T, r)
+    if P is None:
+        P = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+    _require(P, "P", torch.uint8, 1)
+    if kind == GAUSSIAN and ws is None:
+        ws = torch.empty(max(sketch_project_ws_bytes(k, r), 256), dtype=torch.uint8,
+                         device=X.device)
+    ws_ptr, ws_n = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+    st = _lib.lib().logra_sketch_project(X.data_ptr(), ldx, T, k, r, seed, stream, kind,
+                                         P.data_ptr(), P.numel(), ws_ptr, ws_n, _stream(X))
+    _lib.check(st, "logra_sketch_project")
+    return P
+
+
+def sketch_accumulate_p_ws_bytes(T, r, ds):
+    ds = [int(x) for x in ds]
+    arr = (ctypes.c_int64 * max(1, len(ds)))(*ds)
+    return int(_lib.lib().logra_sketch_accumulate_p_ws_bytes(T, r, len(ds), arr))
+
+
+def sketch_accumulate_p(P, dYs, Ss, ws=None, overwrite=False, defer=False, pending=False):
+    """S_o += dY_o^T P in place (the second half of sketch_accumulate, or of
+    sketch_accumulate_shared with several outputs) from a P of sketch_project
+    with the same T and r; returns the list of S.  overwrite, defer and
+    pending as in sketch_accumulate; a deferred chain keeps ws and the
+    outputs and may take a different P in every call."""
+    _require(P, "P", torch.uint8, 1)
+    if isinstance(dYs, torch.Tensor):
+        dYs, Ss = [dYs], [Ss]
+    if not 1 <= len(dYs) <= MAX_SHARED or len(dYs) != len(Ss):
+        raise ValueError(f"between 1 and {MAX_SHARED} (dY, S) pairs")
+    ptr_dy, ldds, ds, ptr_s = [], [], [], []
+    T = r = None
+    for dY, S in zip(dYs, Ss):
+        _require(dY, "dY", torch.bfloat16, 2)
+        _require(S, "S", torch.float32, 2)
+        T2, d, ldd = _rows(dY, "dY")
+        if T is not None and T2 != T:
+            raise ValueError("every dY must have the same number of rows")
+        T = T2
+        if S.shape[0] != d or not S.is_contiguous():
+            raise ValueError("each S must be a contiguous (d, r) float32 tensor")
+        if r is not None and S.shape[1] != r:
+            raise ValueError("every S must have the same rank r")
+        r = S.shape[1]
+        ptr_dy.append(dY.data_ptr())
+        ldds.append(ldd)
+        ds.append(d)
+        ptr_s.append(S.data_ptr())
+    n = len(dYs)
+    if ws is None:
+        ws = torch.empty(max(sketch_accumulate_p_ws_bytes(T, r, ds), 256), dtype=torch.uint8,
+                         device=P.device)
+    st = _lib.lib().logra_sketch_accumulate_p(
+        P.data_ptr(), P.numel(), T, r, _sketch_flags(overwrite, defer, pending), n,
+        (ctypes.c_void_p * n)(*ptr_dy), (ctypes.c_int64 * n)(*ldds), (ctypes.c_int64 * n)(*ds),
+        (ctypes.c_void_p * n)(*ptr_s), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(P))
+    _lib.check(st, "logra_sketch_accumulate_p")
+    return list(Ss)
+
+
 MAX_GROUPS = _lib.MAX_GROUPS
 MAX_LAYER_OUT = _lib.MAX_LAYER_OUT
 

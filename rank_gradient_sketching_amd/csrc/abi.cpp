@@ -110,6 +110,48 @@ namespace {
 // reported as LOGRA_OK with *run = false.
 constexpr int32_t kDeferFlags = LOGRA_SKETCH_DEFER | LOGRA_SKETCH_PENDING;
 
+// The flags of a sketch call: OVERWRITE and the deferral flags; a deferred
+// chain needs tokens in every call, and a deferring call writes no S, so it
+// takes no overwrite flag.
+int flags_check(int32_t flags, int64_t T, bool allow_defer) {
+  if ((flags & ~(LOGRA_SKETCH_OVERWRITE | kDeferFlags)) != 0) return LOGRA_EINVAL;
+  if ((flags & kDeferFlags) != 0) {
+    if (!allow_defer || T < 1) return LOGRA_EINVAL;
+    if ((flags & LOGRA_SKETCH_DEFER) && (flags & LOGRA_SKETCH_OVERWRITE)) return LOGRA_EINVAL;
+  }
+  return LOGRA_OK;
+}
+
+// S of every output: needed by the kernels, and by the zero fill at T == 0
+// (a deferring call never touches S, but its S must still be a valid
+// argument).  One accumulator per output: no two S ranges (d x r floats)
+// overlap.
+int outputs_s_check(const logra::SketchOut* outs, int n_out, int32_t r) {
+  for (int o = 0; o < n_out; ++o) {
+    if (outs[o].S == nullptr || !aligned(outs[o].S, 4)) return LOGRA_EINVAL;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(outs[o].S);
+    const uintptr_t hi = lo + 4 * (uintptr_t)outs[o].d * (uintptr_t)r;
+    for (int o2 = 0; o2 < o; ++o2) {
+      const uintptr_t lo2 = reinterpret_cast<uintptr_t>(outs[o2].S);
+      const uintptr_t hi2 = lo2 + 4 * (uintptr_t)outs[o2].d * (uintptr_t)r;
+      if (lo < hi2 && lo2 < hi) return LOGRA_EINVAL;
+    }
+  }
+  return LOGRA_OK;
+}
+
+// dY of every output (calls with tokens).
+int outputs_dy_check(const logra::SketchOut* outs, int n_out) {
+  for (int o = 0; o < n_out; ++o) {
+    const logra::SketchOut& q = outs[o];
+    if (q.dY == nullptr) return LOGRA_EINVAL;
+    if (!aligned(q.dY, 16) || !ld_ok(q.ldd, q.d)) return LOGRA_EINVAL;
+    // dY is read through 32-bit buffer offsets spanning 32 rows of 2 * ldd bytes
+    if (q.ldd >= kDyStrideLimit) return LOGRA_EINVAL;
+  }
+  return LOGRA_OK;
+}
+
 int sketch_checks(const logra::SketchGroup* groups, int n_groups, int64_t T, int32_t r,
                   int kind, int32_t flags, const logra::SketchOut* outs, void* ws,
                   size_t ws_bytes, logra::SketchPlan* plan, bool* run,
@@ -117,13 +159,8 @@ int sketch_checks(const logra::SketchGroup* groups, int n_groups, int64_t T, int
   *run = false;
   if (n_groups < 1 || n_groups > LOGRA_MAX_GROUPS) return LOGRA_EINVAL;
   if (!rank_ok(r) || !kind_ok(kind)) return LOGRA_EINVAL;
-  if ((flags & ~(LOGRA_SKETCH_OVERWRITE | kDeferFlags)) != 0) return LOGRA_EINVAL;
-  if ((flags & kDeferFlags) != 0) {
-    // a deferred chain: every call has tokens; a deferring call writes no S,
-    // so it takes no overwrite flag
-    if (!allow_defer || T < 1) return LOGRA_EINVAL;
-    if ((flags & LOGRA_SKETCH_DEFER) && (flags & LOGRA_SKETCH_OVERWRITE)) return LOGRA_EINVAL;
-  }
+  int st = flags_check(flags, T, allow_defer);
+  if (st != LOGRA_OK) return st;
   int64_t k[LOGRA_MAX_GROUPS];
   int n_out_g[LOGRA_MAX_GROUPS];
   int64_t d[LOGRA_MAX_LAYER_OUT];
@@ -142,20 +179,8 @@ int sketch_checks(const logra::SketchGroup* groups, int n_groups, int64_t T, int
   }
   if (T < 0 || T >= kDimLimit) return LOGRA_EINVAL;
   if (T == 0 && (flags & LOGRA_SKETCH_OVERWRITE) == 0) return LOGRA_OK;
-  // S of every output: needed by the kernels, and by the zero fill at T == 0
-  // (a deferring call never touches S, but its S must still be a valid
-  // argument).  One accumulator per output: no two S ranges (d x r floats)
-  // overlap.
-  for (int o = 0; o < n_out; ++o) {
-    if (outs[o].S == nullptr || !aligned(outs[o].S, 4)) return LOGRA_EINVAL;
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(outs[o].S);
-    const uintptr_t hi = lo + 4 * (uintptr_t)outs[o].d * (uintptr_t)r;
-    for (int o2 = 0; o2 < o; ++o2) {
-      const uintptr_t lo2 = reinterpret_cast<uintptr_t>(outs[o2].S);
-      const uintptr_t hi2 = lo2 + 4 * (uintptr_t)outs[o2].d * (uintptr_t)r;
-      if (lo < hi2 && lo2 < hi) return LOGRA_EINVAL;
-    }
-  }
+  st = outputs_s_check(outs, n_out, r);
+  if (st != LOGRA_OK) return st;
   if (T == 0) {
     *run = true;
     return LOGRA_OK;
@@ -164,13 +189,8 @@ int sketch_checks(const logra::SketchGroup* groups, int n_groups, int64_t T, int
     const logra::SketchGroup& q = groups[g];
     if (q.X == nullptr || !aligned(q.X, 16) || !ld_ok(q.ldx, q.k)) return LOGRA_EINVAL;
   }
-  for (int o = 0; o < n_out; ++o) {
-    const logra::SketchOut& q = outs[o];
-    if (q.dY == nullptr) return LOGRA_EINVAL;
-    if (!aligned(q.dY, 16) || !ld_ok(q.ldd, q.d)) return LOGRA_EINVAL;
-    // dY is read through 32-bit buffer offsets spanning 32 rows of 2 * ldd bytes
-    if (q.ldd >= kDyStrideLimit) return LOGRA_EINVAL;
-  }
+  st = outputs_dy_check(outs, n_out);
+  if (st != LOGRA_OK) return st;
   if (!logra::make_sketch_plan_groups(T, n_groups, k, n_out_g, d, r, plan)) return LOGRA_EINVAL;
   if (ws == nullptr || ws_bytes < plan->total || !aligned(ws, 256)) return LOGRA_EWORKSPACE;
   *run = true;
@@ -265,6 +285,78 @@ int logra_sketch_accumulate_layer(int64_t T, int32_t r, int kind, int32_t flags,
   const int st = sketch_checks(grp, n_groups, T, r, kind, flags, outs, ws, ws_bytes, &p, &run);
   if (st != LOGRA_OK || !run) return st;
   return run_sketch(p, grp, outs, n_out, T, r, kind, flags, ws, s);
+}
+
+size_t logra_sketch_p_bytes(int64_t T, int32_t r) {
+  const int64_t d = 1;
+  logra::SketchPlan p{};
+  if (!logra::make_sketch_plan(T, 1, &d, 1, r, &p)) return 0;
+  return logra::plan_p_bytes(p);
+}
+
+size_t logra_sketch_project_ws_bytes(int64_t k, int32_t r) {
+  const int64_t d = 1;
+  logra::SketchPlan p{};
+  if (!logra::make_sketch_plan(1, 1, &d, k, r, &p)) return 0;
+  return logra::plan_gauss_bytes(p, 0);
+}
+
+int logra_sketch_project(const uint16_t* X, int64_t ldx, int64_t T, int64_t k, int32_t r,
+                         uint64_t seed, uint64_t stream, int kind, uint16_t* P, size_t p_bytes,
+                         void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!rank_ok(r) || !kind_ok(kind) || !dim_ok(k)) return LOGRA_EINVAL;
+  if (T < 0 || T >= kDimLimit) return LOGRA_EINVAL;
+  if (T == 0) return LOGRA_OK;
+  if (X == nullptr || !aligned(X, 16) || !ld_ok(ldx, k)) return LOGRA_EINVAL;
+  const int64_t d = 1;
+  logra::SketchPlan p{};
+  if (!logra::make_sketch_plan(T, 1, &d, k, r, &p)) return LOGRA_EINVAL;
+  if (P == nullptr || !aligned(P, 16) || p_bytes < logra::plan_p_bytes(p)) return LOGRA_EINVAL;
+  const bool gauss = kind == LOGRA_GAUSSIAN;
+  if (gauss && (ws == nullptr || ws_bytes < logra::plan_gauss_bytes(p, 0) || !aligned(ws, 256)))
+    return LOGRA_EWORKSPACE;
+  const logra::SketchGroup g{X, ldx, k, seed, stream, 1};
+  return hip_status(logra::launch_project_only(p, g, (int)T, r, kind, P,
+                                               gauss ? static_cast<uint16_t*>(ws) : nullptr, s));
+}
+
+size_t logra_sketch_accumulate_p_ws_bytes(int64_t T, int32_t r, int32_t n_out, const int64_t* d) {
+  if (d == nullptr || n_out < 1 || n_out > LOGRA_MAX_SHARED) return 0;
+  logra::SketchPlan p{};
+  if (!logra::make_sketch_plan(T, n_out, d, 1, r, &p)) return 0;
+  return logra::plan_part_bytes(p);
+}
+
+int logra_sketch_accumulate_p(const uint16_t* P, size_t p_bytes, int64_t T, int32_t r,
+                              int32_t flags, int32_t n_out, const uint16_t* const* dY,
+                              const int64_t* ldd, const int64_t* d, float* const* S, void* ws,
+                              size_t ws_bytes, hipStream_t s) {
+  if (n_out < 1 || n_out > LOGRA_MAX_SHARED) return LOGRA_EINVAL;
+  if (dY == nullptr || ldd == nullptr || d == nullptr || S == nullptr) return LOGRA_EINVAL;
+  if (!rank_ok(r)) return LOGRA_EINVAL;
+  int st = flags_check(flags, T, /*allow_defer=*/true);
+  if (st != LOGRA_OK) return st;
+  logra::SketchOut outs[LOGRA_MAX_SHARED];
+  for (int o = 0; o < n_out; ++o) {
+    if (!dim_ok(d[o])) return LOGRA_EINVAL;
+    outs[o] = logra::SketchOut{dY[o], ldd[o], d[o], S[o]};
+  }
+  if (T < 0 || T >= kDimLimit) return LOGRA_EINVAL;
+  if (T == 0 && (flags & LOGRA_SKETCH_OVERWRITE) == 0) return LOGRA_OK;
+  st = outputs_s_check(outs, n_out, r);
+  if (st != LOGRA_OK) return st;
+  if (T == 0) return hip_status(logra::launch_zero_outputs(outs, n_out, r, s));
+  st = outputs_dy_check(outs, n_out);
+  if (st != LOGRA_OK) return st;
+  logra::SketchPlan p{};
+  if (!logra::make_sketch_plan(T, n_out, d, 1, r, &p)) return LOGRA_EINVAL;
+  if (P == nullptr || !aligned(P, 16) || p_bytes < logra::plan_p_bytes(p)) return LOGRA_EINVAL;
+  if (ws == nullptr || ws_bytes < logra::plan_part_bytes(p) || !aligned(ws, 256))
+    return LOGRA_EWORKSPACE;
+  return hip_status(logra::launch_accumulate_only(
+      p, P, outs, (int)T, r, (flags & LOGRA_SKETCH_OVERWRITE) != 0,
+      (flags & LOGRA_SKETCH_DEFER) != 0, (flags & LOGRA_SKETCH_PENDING) != 0,
+      static_cast<float*>(ws), s));
 }
 
 namespace {

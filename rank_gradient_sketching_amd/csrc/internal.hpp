@@ -103,6 +103,29 @@ hipError_t launch_sketch(const SketchPlan& p, const SketchGroup* groups, const S
                          int T, int r, int kind, bool overwrite, bool defer, bool pending,
                          char* ws, hipStream_t s);
 
+// Bytes of one input group's projected input P (bf16 hi and lo parts of
+// t_pad x rp values), of its Gaussian basis (bf16, p_rows x k_pad) and of the
+// partial tiles, as laid out in a call's workspace.
+inline size_t plan_p_bytes(const SketchPlan& p) { return (size_t)2 * p.rp * (size_t)p.t_pad * 2; }
+inline size_t plan_gauss_bytes(const SketchPlan& p, int g) {
+  return (size_t)p.p_rows * (size_t)p.k_pad[g] * 2;
+}
+inline size_t plan_part_bytes(const SketchPlan& p) {
+  return (size_t)p.n_split * p.d_pad * p.rp * 4;
+}
+
+// The two halves of launch_sketch for one input group, with P in a buffer of
+// the caller's: the projection P = X A^T (gauss_ws: plan_gauss_bytes(p, 0)
+// bytes for the Gaussian basis, unused for signs), and the accumulation of
+// p.n_out outputs from such a P (part: plan_part_bytes(p) bytes).  Together
+// they run the kernels of launch_sketch on the same plan, so the results are
+// the same bits.
+hipError_t launch_project_only(const SketchPlan& p, const SketchGroup& g, int T, int r, int kind,
+                               uint16_t* P, uint16_t* gauss_ws, hipStream_t s);
+hipError_t launch_accumulate_only(const SketchPlan& p, const uint16_t* P, const SketchOut* outs,
+                                  int T, int r, bool overwrite, bool defer, bool pending,
+                                  float* part, hipStream_t s);
+
 // S = 0 for n_out outputs of d x r floats (a fill kernel, no memset node).
 hipError_t launch_zero_outputs(const SketchOut* outs, int n_out, int r, hipStream_t s);
 

@@ -1391,18 +1391,22 @@ hipError_t launch_accumulate_wide(const SketchPlan& p, const Tab& tab, int T, in
 }
 
 // The projection and accumulate launches of one call with the given tables.
-template <class PT, class Tab>
-hipError_t launch_tables(const SketchPlan& p, const PT& pt, const Tab& tab, const uint16_t* Pt1,
-                         int T, int r, bool gauss, float c, bool defer, float* part,
-                         hipStream_t s) {
-  hipError_t e;
+// The projection launch of a call (P for every input group of the table).
+template <class PT>
+hipError_t launch_project_phase(const SketchPlan& p, const PT& pt, int T, bool gauss, float c,
+                                hipStream_t s) {
   switch (p.nb32) {
-    case 1: e = launch_project<1>(p, pt, T, gauss, c, s); break;
-    case 2: e = launch_project<2>(p, pt, T, gauss, c, s); break;
-    case 4: e = launch_project<4>(p, pt, T, gauss, c, s); break;
-    default: e = launch_project<8>(p, pt, T, gauss, c, s); break;
+    case 1: return launch_project<1>(p, pt, T, gauss, c, s);
+    case 2: return launch_project<2>(p, pt, T, gauss, c, s);
+    case 4: return launch_project<4>(p, pt, T, gauss, c, s);
+    default: return launch_project<8>(p, pt, T, gauss, c, s);
   }
-  if (e != hipSuccess) return e;
+}
+
+// The accumulate launch (and, unless deferred, the split reduction) of a call.
+template <class Tab>
+hipError_t launch_accumulate_phase(const SketchPlan& p, const Tab& tab, const uint16_t* Pt1, int T,
+                                   int r, bool defer, float* part, hipStream_t s) {
   if (p.acc_wide) {
     if (p.rp == 128) return launch_accumulate_wide<8>(p, tab, T, r, Pt1, part, defer, s);
     return launch_accumulate_wide<16>(p, tab, T, r, Pt1, part, defer, s);
@@ -1414,6 +1418,15 @@ hipError_t launch_tables(const SketchPlan& p, const PT& pt, const Tab& tab, cons
     case 128: return launch_accumulate<kAccQ, 8>(p, tab, T, r, Pt1, part, defer, s);
     default: return launch_accumulate<kAccQ, 16>(p, tab, T, r, Pt1, part, defer, s);
   }
+}
+
+template <class PT, class Tab>
+hipError_t launch_tables(const SketchPlan& p, const PT& pt, const Tab& tab, const uint16_t* Pt1,
+                         int T, int r, bool gauss, float c, bool defer, float* part,
+                         hipStream_t s) {
+  const hipError_t e = launch_project_phase(p, pt, T, gauss, c, s);
+  if (e != hipSuccess) return e;
+  return launch_accumulate_phase(p, tab, Pt1, T, r, defer, part, s);
 }
 
 // The output fields shared by both table types.
@@ -1513,12 +1526,11 @@ bool make_sketch_plan_groups(int64_t T, int n_groups, const int64_t* k, const in
     off += (size_t)round_up((int64_t)bytes, 256);
     return o;
   };
-  for (int g = 0; g < n_groups; ++g) q.off_pt[g] = take((size_t)2 * q.rp * (size_t)q.t_pad * 2);
+  for (int g = 0; g < n_groups; ++g) q.off_pt[g] = take(plan_p_bytes(q));
   // (one split's worth even when a single split writes S directly: a
   // deferred call keeps its result there)
-  q.off_part = take((size_t)q.n_split * q.d_pad * q.rp * 4);
-  for (int g = 0; g < n_groups; ++g)
-    q.off_gauss[g] = take((size_t)q.p_rows * (size_t)q.k_pad[g] * 2);
+  q.off_part = take(plan_part_bytes(q));
+  for (int g = 0; g < n_groups; ++g) q.off_gauss[g] = take(plan_gauss_bytes(q, g));
   q.total = off;
   *p = q;
   return true;
@@ -1586,6 +1598,29 @@ hipError_t launch_sketch(const SketchPlan& p, const SketchGroup* groups, const S
     for (int o = p.out_off[g]; o < p.out_off[g + 1]; ++o)
       tab.Pt[o] = reinterpret_cast<const uint16_t*>(ws + p.off_pt[g]);
   return launch_tables(p, pt, tab, nullptr, T, r, gauss, c, defer, part, s);
+}
+
+hipError_t launch_project_only(const SketchPlan& p, const SketchGroup& g, int T, int r, int kind,
+                               uint16_t* P, uint16_t* gauss_ws, hipStream_t s) {
+  const bool gauss = kind == 1;
+  const float c = sign_scale(r);
+  if (gauss) {
+    const int64_t threads = (int64_t)p.p_rows * (p.k_pad[0] >> 2);
+    hipLaunchKernelGGL(gauss_basis_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       s, g.seed, g.stream, r, (int)g.k, p.p_rows, p.k_pad[0], c, gauss_ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const ProjOne pt{g.X, g.ldx, (int)g.k, g.seed, g.stream, gauss_ws, p.k_pad[0], P};
+  return launch_project_phase(p, pt, T, gauss, c, s);
+}
+
+hipError_t launch_accumulate_only(const SketchPlan& p, const uint16_t* P, const SketchOut* outs,
+                                  int T, int r, bool overwrite, bool defer, bool pending,
+                                  float* part, hipStream_t s) {
+  OutTable tab{};
+  fill_outputs(tab, p, outs, overwrite, pending);
+  return launch_accumulate_phase(p, tab, P, T, r, defer, part, s);
 }
 
 // S = 0, four floats per thread where the row allows (S of every output is

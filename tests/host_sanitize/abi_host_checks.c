@@ -406,6 +406,70 @@ static void check_zero_fill_without_device(void) {
   const int st4 = logra_sketch_accumulate_noalloc(NULL, 0, NULL, 0, 0, 64, 64, 4, 1, 0, 0,
                                                   LOGRA_SKETCH_OVERWRITE, S_PTR, NULL);
   EXPECT(st4 == LOGRA_EHIP);
+  const int st5 = logra_sketch_accumulate_p(NULL, 0, 0, 4, LOGRA_SKETCH_OVERWRITE, 2, dys, ldd, dd,
+                                            Ss, NULL, 0, NULL);
+  EXPECT(st5 == LOGRA_EHIP);
+}
+
+/* The two-call sketch: sizes that add up to the one-call workspace over a
+ * sweep of shapes, and one bad argument at a time for both halves. */
+static void check_split_sketch(void) {
+  const int64_t Ts[] = {1, 31, 33, 1000, 8192, 16384, 65536};
+  for (int it = 0; it < N_OF(Ts); ++it)
+    for (int id = 0; id < N_OF(kDims); id += 3)
+      for (int ir = 0; ir < N_OF(kRanks); ir += 2) {
+        const int64_t T = Ts[it], d = kDims[id], k = 4096;
+        const int32_t r = kRanks[ir];
+        const size_t full = logra_sketch_ws_bytes(T, d, k, r);
+        const size_t pb = logra_sketch_p_bytes(T, r);
+        const size_t gb = logra_sketch_project_ws_bytes(k, r);
+        const size_t ab = logra_sketch_accumulate_p_ws_bytes(T, r, 1, &d);
+        EXPECT((full != 0) == (ab != 0));
+        if (full == 0) continue;
+        EXPECT(pb % 256 == 0 && gb % 256 == 0 && ab % 256 == 0);
+        EXPECT(pb + gb + ab == full);
+      }
+  EXPECT(logra_sketch_p_bytes(64, 0) == 0);
+  EXPECT(logra_sketch_p_bytes(-1, 4) == 0);
+  EXPECT(logra_sketch_p_bytes(INT64_MAX, INT32_MAX) == 0);
+  EXPECT(logra_sketch_project_ws_bytes(0, 4) == 0);
+  EXPECT(logra_sketch_project_ws_bytes(INT64_MIN, 4) == 0);
+  EXPECT(logra_sketch_accumulate_p_ws_bytes(64, 4, 1, NULL) == 0);
+  EXPECT(logra_sketch_accumulate_p_ws_bytes(64, 4, LOGRA_MAX_SHARED + 1, kDims) == 0);
+
+  const int64_t T = 8192, d = 4096, k = 4096;
+  const int32_t r = 64;
+  uint16_t* Pp = (uint16_t*)fake(0x600000);
+  const size_t pb = logra_sketch_p_bytes(T, r), gb = logra_sketch_project_ws_bytes(k, r);
+  EXPECT(logra_sketch_project(NULL, k, T, k, r, 1, 0, 0, Pp, pb, NULL, 0, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_project(X_PTR, k - 8, T, k, r, 1, 0, 0, Pp, pb, NULL, 0, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_project(X_PTR, k, T, k, 0, 1, 0, 0, Pp, pb, NULL, 0, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_project(X_PTR, k, T, k, r, 1, 0, 3, Pp, pb, NULL, 0, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_project(X_PTR, k, T, k, r, 1, 0, 0, NULL, pb, NULL, 0, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_project(X_PTR, k, T, k, r, 1, 0, 0, Pp + 4, pb, NULL, 0, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_project(X_PTR, k, T, k, r, 1, 0, 0, Pp, pb - 1, NULL, 0, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_project(X_PTR, k, T, k, r, 1, 0, 1, Pp, pb, NULL, 0, NULL) == LOGRA_EWORKSPACE);
+  EXPECT(logra_sketch_project(X_PTR, k, T, k, r, 1, 0, 1, Pp, pb, WS_PTR, gb - 1, NULL) == LOGRA_EWORKSPACE);
+  EXPECT(logra_sketch_project(NULL, 0, 0, k, r, 1, 0, 0, NULL, 0, NULL, 0, NULL) == LOGRA_OK);
+
+  const uint16_t* dys[2] = {DY_PTR, DY_PTR};
+  const int64_t ldd[2] = {d, d}, dd[2] = {d, d};
+  float* Ss[2] = {S_PTR, (float*)fake(0x3400000)};
+  const size_t ab = logra_sketch_accumulate_p_ws_bytes(T, r, 2, dd);
+  EXPECT(ab > 0);
+  EXPECT(logra_sketch_accumulate_p(NULL, pb, T, r, 0, 2, dys, ldd, dd, Ss, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb - 1, T, r, 0, 2, dys, ldd, dd, Ss, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, r, 0, 0, dys, ldd, dd, Ss, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, r, 0, LOGRA_MAX_SHARED + 1, dys, ldd, dd, Ss, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, r, 0, 2, NULL, ldd, dd, Ss, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, r, 0, 2, dys, ldd, dd, NULL, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, 0, 0, 2, dys, ldd, dd, Ss, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, r, 3, 2, dys, ldd, dd, Ss, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, r, 0, 2, dys, ldd, dd, Ss, NULL, ab, NULL) == LOGRA_EWORKSPACE);
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, r, 0, 2, dys, ldd, dd, Ss, WS_PTR, ab - 1, NULL) == LOGRA_EWORKSPACE);
+  float* same[2] = {S_PTR, S_PTR};
+  EXPECT(logra_sketch_accumulate_p(Pp, pb, T, r, 0, 2, dys, ldd, dd, same, WS_PTR, ab, NULL) == LOGRA_EINVAL);
+  EXPECT(logra_sketch_accumulate_p(NULL, 0, 0, r, 0, 2, dys, ldd, dd, Ss, NULL, 0, NULL) == LOGRA_OK);
 }
 
 int main(void) {
@@ -416,6 +480,7 @@ int main(void) {
   check_layer_and_merge_many();
   check_kernel_choice();
   check_zero_fill_without_device();
+  check_split_sketch();
   printf("host ABI checks: %d expectations, %d failed\n", g_checks, g_fail);
   return g_fail == 0 ? 0 : 1;
 }

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = _lib.header_symbols()
-    assert len(declared) == 18
+    assert len(declared) == 23
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
