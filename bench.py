@@ -660,6 +660,54 @@ def run_copy_calibration():
     return out
 
 
+def run_read_calibration():
+    """The hand-written read-only stream (liblogra_calib.so: each 16-byte vector
+    loaded once, 32 KB per work-group, nothing written) as the practical ceiling
+    of the sketch's two read passes: 64 MiB (one microbatch of X or dY)
+    rotating over 8 buffers (512 MiB in all, twice the Infinity Cache), with
+    plain and with non-temporal loads, and one 512 MiB pass."""
+    import ctypes
+    from rank_gradient_sketching_amd import build as _b
+    lib = ctypes.CDLL(_b.CALIB_LIB)
+    lib.logra_calib_read.restype = ctypes.c_int
+    lib.logra_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(64, dtype=torch.uint8, device="cuda")
+
+    def read(src, nt):
+        st = lib.logra_calib_read(src.data_ptr(), src.numel() * src.element_size(), nt,
+                                  sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"logra_calib_read failed ({st})")
+
+    out = {}
+    for name, nbytes, n_buf, reps in (("read_64MiB", 64 << 20, 8, 64),
+                                      ("read_512MiB", 512 << 20, 1, 5)):
+        bufs = [torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+                for _ in range(n_buf)]
+        for nt in (0, 1):
+            read(bufs[0], nt)
+            torch.cuda.synchronize()
+            per = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for i in range(reps):
+                    read(bufs[i % n_buf], nt)
+                b.record()
+                torch.cuda.synchronize()
+                per.append(a.elapsed_time(b) / reps)
+            ms = float(np.median(per))
+            out[name + ("_nontemporal" if nt else "")] = dict(
+                bytes_read=nbytes, us=ms * 1e3, GBps=nbytes / (ms * 1e-3) / 1e9,
+                frac_hbm=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+        del bufs
+        torch.cuda.empty_cache()
+    out["kernel"] = "logra_calib_read (hand-written HIP, 32 KB per work-group, no stores)"
+    return out
+
+
 def cpu_baseline(synth, data, budget_s=12.0):
     """The oracle, as it stands, on this host's cores, over whole steps of the
     same workload (four microbatches + merge), until about budget_s seconds."""
@@ -804,6 +852,7 @@ def main():
     update = run_update(lg, synth)
     others = None if args.no_configs else run_other_configs(lg, synth)
     calib = None if args.no_calib else run_copy_calibration()
+    read_cal = None if args.no_calib else run_read_calibration()
     cpu = None if args.no_cpu else cpu_baseline(synth, data, args.cpu_budget)
     if cpu is not None:
         cpu["other_configs"] = cpu_baseline_others(synth)
@@ -839,6 +888,13 @@ def main():
         "sketch": {"tokens_per_s": sk["tokens_per_s"], "GBps": sk["GBps"],
                    "frac_hbm": sk["frac_hbm"], "us_per_call": sk["us_per_call"],
                    "us_per_call_min": sk["us_min"],
+                   # against two passes of the hand-written read stream over one
+                   # microbatch's X and dY (64 MiB each, plain loads)
+                   "read_us_same_bytes": (2 * read_cal["read_64MiB"]["us"]) if read_cal else None,
+                   "frac_of_read": ((2 * read_cal["read_64MiB"]["us"]) / sk["us_per_call"])
+                   if read_cal else None,
+                   "frac_of_read_in_chain": ((2 * read_cal["read_64MiB"]["us"]) /
+                                             layer["chain"]["us_per_call"]) if read_cal else None,
                    **sketch_mfma(cfg["T"], cfg["d"], cfg["k"], cfg["r"], sk["us_per_call"]),
                    # inside the step's deferred chain (one split reduction per step)
                    "in_chain": {k_: layer["chain"][k_] for k_ in
@@ -858,6 +914,7 @@ def main():
         "sketch_update": update,
         "other_configs": others,
         "copy_calibration": calib,
+        "read_calibration": read_cal,
     }
     print(json.dumps(out), flush=True)
     # a parity failure anywhere fails the run (after the line is printed)

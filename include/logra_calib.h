@@ -1,8 +1,8 @@
 /*
  * logra_calib.h - measurement helper shipped next to liblogra (in its own
- * library, liblogra_calib.so): a plain device copy whose achieved bandwidth
- * is the practical HBM ceiling the path's kernels are compared with.  It is
- * not part of the method.
+ * library, liblogra_calib.so): a plain device copy and a plain device read
+ * whose achieved bandwidths are the practical HBM ceilings the path's
+ * kernels are compared with.  They are not part of the method.
  */
 #ifndef LOGRA_CALIB_H
 #define LOGRA_CALIB_H
@@ -19,6 +19,14 @@ extern "C" {
  * device memory, non-overlapping.  Returns 0, -1 (bad argument) or -3 (HIP
  * launch error). */
 int logra_calib_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+/* Reads every byte of src once on stream s (plain loads, or non-temporal
+ * ones with nontemporal != 0) and writes nothing, except possibly 4 bytes at
+ * sink: the practical ceiling of a read-only stream such as the sketch's
+ * two passes over X and dY.  bytes % 16 == 0, src 16-byte and sink 4-byte
+ * aligned device memory.  Returns 0, -1 (bad argument) or -3 (HIP launch
+ * error). */
+int logra_calib_read(const void* src, size_t bytes, int nontemporal, void* sink, hipStream_t s);
 
 #ifdef __cplusplus
 }

@@ -251,6 +251,12 @@ static void check_other_rejects(void) {
   EXPECT(logra_calib_copy(S_PTR, X_PTR, 4095, NULL) != 0);
   EXPECT(logra_calib_copy((void*)fake(0x300004), X_PTR, 4096, NULL) != 0);
   EXPECT(logra_calib_copy(S_PTR, X_PTR, 0, NULL) == 0);
+  EXPECT(logra_calib_read(NULL, 4096, 0, S_PTR, NULL) != 0);
+  EXPECT(logra_calib_read(X_PTR, 4096, 0, NULL, NULL) != 0);
+  EXPECT(logra_calib_read(X_PTR, 4095, 1, S_PTR, NULL) != 0);
+  EXPECT(logra_calib_read((const void*)fake(0x100008), 4096, 0, S_PTR, NULL) != 0);
+  EXPECT(logra_calib_read(X_PTR, 4096, 0, (void*)fake(0x300002), NULL) != 0);
+  EXPECT(logra_calib_read(X_PTR, 0, 0, S_PTR, NULL) == 0);
 }
 
 /* The layer sketch and the grouped merge: workspace queries over group
