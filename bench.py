@@ -147,6 +147,21 @@ def run_layer(lg, synth, steps, warmup):
     total_ms = t0.elapsed_time(t1)
     step_ms = total_ms / steps
 
+    # the same step captured once in a HIP graph and replayed (no entry point
+    # allocates or records a memset, so the whole step captures); reported
+    # beside the eager figure, which is `value`
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_step()
+    graph_step_ms = _time_ms(graph.replay, max(steps // 5, 4))
+    del graph
+
     # ---- average duration of each entry point: the same calls back to back
     # (sketches cycling over the microbatches, merges over copies of W), one
     # event pair around each batch, outside the timed steps
@@ -182,7 +197,7 @@ def run_layer(lg, synth, steps, warmup):
     cb = chain_bytes(T, d, k, r, n_mb) / n_mb
     mb_ = merge_bytes(d, k, r)
     res = dict(
-        cfg=cfg, total_ms=total_ms, step_ms=step_ms, wall_ms=wall_ms,
+        cfg=cfg, total_ms=total_ms, step_ms=step_ms, wall_ms=wall_ms, graph_step_ms=graph_step_ms,
         tokens_per_step=T * n_mb,
         sketch=dict(us_per_call=sk_us, us_min=min(sk_b), bytes_per_call=sb,
                     GBps=sb / (sk_us * 1e-6) / 1e9,
@@ -506,8 +521,23 @@ def run_other_configs(lg, synth):
         for mb, (X, dY) in enumerate(zip(Xs, dYs)):
             lg.sketch_accumulate(X, dY, S, 1234, ws=ws, overwrite=mb == 0)
         lg.merge(W, S, 1234, 0, 0, c["alpha"], c["eta"])
-    report("layer_d256_r4", _time_ms(small, 50), 2 * sketch_bytes(T, d, k, r) + merge_bytes(d, k, r),
-           2 * T)
+    ms_small = _time_ms(small, 50)
+    # The same step captured once in a HIP graph and replayed: the kernel
+    # launches no longer wait on this process's per-call host work.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        small()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        small()
+    ms_graph = _time_ms(graph.replay, 50)
+    report("layer_d256_r4", ms_small, 2 * sketch_bytes(T, d, k, r) + merge_bytes(d, k, r), 2 * T,
+           us_per_step_graph=ms_graph * 1e3,
+           graph_note="the step captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed")
+    del graph
 
     n_layers = 2
     for wl, cfg, r, kind, stream, label, reps in (
@@ -875,6 +905,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": layer["step_ms"],
+        "ms_per_step_graph": layer["graph_step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
