@@ -115,3 +115,69 @@ def test_step_graph_replays_equal_eager(lg, entry, T, d, k, r, kind, n_mb):
         for name, a, b in zip(("S", "W", "q/alpha"), got, ref):
             assert torch.equal(a, b), (rep, name)
     del g
+
+
+@pytest.mark.parametrize("r,kind", [(64, 0), (16, 1)])
+def test_layer_step_graph_replays_equal_eager(lg, r, kind):
+    """A decoder layer's step (q/k/v, o, gate/up, down: four input groups,
+    seven outputs) as one deferred chain of layer calls and one grouped merge."""
+    say("graph layer step", r, kind)
+    T, n_mb, h, kv, mlp = 1040, 2, 384, 64, 1000
+    shapes = {"q": (h, h), "k": (kv, h), "v": (kv, h), "o": (h, h), "gate": (mlp, h),
+              "up": (mlp, h), "down": (h, mlp)}          # (d, k) per projection
+    groups_of = [("qkv", ["q", "k", "v"], h), ("o", ["o"], h), ("gu", ["gate", "up"], h),
+                 ("down", ["down"], mlp)]
+    seed, stream = 77, 2
+    X = {(g, mb): synth.host_normal_bf16((T, k), synth.X_ID, mb=mb, salt=len(g) * 7 + k).cuda()
+         for g, _, k in groups_of for mb in range(n_mb)}
+    dY = {(p, mb): synth.host_normal_bf16((T, shapes[p][0]), synth.DY_ID, mb=mb,
+                                          salt=shapes[p][0] + len(p)).cuda()
+          for p in shapes for mb in range(n_mb)}
+    W0 = {p: synth.host_normal_bf16(shapes[p], synth.W_ID, salt=len(p)).cuda() for p in shapes}
+    spec = [(X[(g, 0)], [dY[(p, 0)] for p in ps], [None] * len(ps), seed + i, stream)
+            for i, (g, ps, _) in enumerate(groups_of)]
+    ws = lg.sketch_layer_workspace(T, r, [(x.shape[1], [t.shape[1] for t in dys])
+                                          for x, dys, _, _, _ in spec])
+
+    def step(S, W):
+        for mb in range(n_mb):
+            last = mb == n_mb - 1
+            groups = [(X[(g, mb)], [dY[(p, mb)] for p in ps], [S[p] for p in ps], seed + i, stream)
+                      for i, (g, ps, _) in enumerate(groups_of)]
+            lg.sketch_accumulate_layer(groups, kind, ws=ws, defer=not last, pending=mb > 0,
+                                       overwrite=last)
+        items = [(W[p], S[p], seed + i, stream) for i, (g, ps, _) in enumerate(groups_of)
+                 for p in ps]
+        lg.merge_many(items, kind, 1.0, 2e-4)
+
+    def fresh():
+        return ({p: torch.full((shapes[p][0], r), float("nan"), device="cuda") for p in shapes},
+                {p: W0[p].clone() for p in shapes})
+
+    S_e, W_e = fresh()
+    step(S_e, W_e)
+    torch.cuda.synchronize()
+    ref = {p: (_bits(S_e[p]), _bits(W_e[p])) for p in shapes}
+
+    S_g, W_g = fresh()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(S_g, W_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(S_g, W_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for p in shapes:
+            W_g[p].copy_(W0[p])
+            S_g[p].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for p in shapes:
+            assert torch.equal(_bits(S_g[p]), ref[p][0]), (rep, p, "S")
+            assert torch.equal(_bits(W_g[p]), ref[p][1]), (rep, p, "W")
+    del g
