@@ -12,11 +12,16 @@ tolerance, while the chosen form stays far inside it:
   u3 = sum w (e^d - 1 - d) (a Taylor polynomial for |d| <= 1/2) and d taken
   relative to a per-row reference difference, not as a difference of two
   fp32 log-sum-exps ([LoGRA] PKL: current vs proposed vocabulary
-  distributions at one temperature).
+  distributions at one temperature);
+- the KL sweep over several multipliers takes e^t - 1 - t from the moments
+  M_2 .. M_8 of the scaled direction where max|alpha| |delta / tau| <= 1,
+  and exactly elsewhere (same PKL section: KL growing as alpha^2 q(D)).
 
 Tolerances: 2e-3 relative Frobenius error on S and on the merged-W delta,
 1e-3 relative error on each token's KL.
 """
+from math import factorial
+
 import numpy as np
 
 from oracle import bf16 as obf16
@@ -146,3 +151,63 @@ def test_predicted_kl_needs_the_row_reference_under_a_logit_offset():
         with_ref = float(np.max(np.abs(_one_pass_kl(z, zp, tau, reference=True) - ref) / ref))
         assert plain > KL_TOL, (off, plain)            # fails the tolerance
         assert with_ref < KL_TOL / 100, (off, with_ref)
+
+
+def _sweep_series_kl(z, delta, alphas, tau, n_moments, thr):
+    """Per-row KL at each multiplier from the sweep kernel's state, in fp64 (the
+    truncation alone): with u = max|alpha| (delta - c) / tau (c the mean of
+    delta over the row's first 64 elements) and w = e^(z/tau - max), the sums
+    s = sum w, u1 = sum w u and M_n = sum w u^n (n = 2 .. n_moments + 1) over
+    the elements with |u| <= thr, and e^t - 1 - t exactly for the others."""
+    amax = max(abs(a) for a in alphas)
+    c = delta[:, :64].mean(axis=1, keepdims=True)
+    u = amax * (delta - c) / tau
+    a = z / tau
+    w = np.exp(a - a.max(axis=1, keepdims=True))
+    on = np.abs(u) <= thr
+    s = w.sum(axis=1)
+    u1 = (w * u).sum(axis=1)
+    uo = np.where(on, u, 0.0)
+    M = {n: (w * uo ** n).sum(axis=1) for n in range(2, n_moments + 2)}
+    out = []
+    for al in alphas:
+        x_ = al / amax
+        t = x_ * np.where(on, 0.0, u)
+        g = (w * (np.expm1(t) - t)).sum(axis=1)
+        g = g + sum(x_ ** n / factorial(n) * M[n] for n in M)
+        x = (x_ * u1 + g) / s
+        out.append(g / s + np.log1p(x) - x)
+    return np.stack(out)
+
+
+def test_kl_sweep_series_truncation():
+    # every element as far out as the series reaches (|u| in [0.8, 1], random
+    # signs): the worst case of the truncation, at the largest multiplier,
+    # where t = u
+    n, V, tau = 8, 8192, 1.0
+    alphas = (0.25, 0.5, 1.0, 2.0)
+    amax = max(alphas)
+    z = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.Z_ID, salt=9, sigma=3.0))
+    rng = np.random.default_rng(9)
+    sign = np.where(rng.random((n, V)) < 0.5, -1.0, 1.0)
+    frac = rng.uniform(0.8, 1.0, (n, V))
+
+    def err(delta, n_moments):
+        ref = okl.kl_sweep_rows(z, delta, alphas, tau)
+        got = _sweep_series_kl(z, delta, alphas, tau, n_moments, 1.0)
+        return float(np.max(np.abs(got - ref) / ref))
+
+    mixed = sign * frac * tau / amax
+    mixed[:, :64] = 0.0               # row reference c = 0: |u| stays in [0.8, 1]
+    # the kernel's seven moments: fifty times inside the bar; three would
+    # exceed it
+    assert err(mixed, 7) < KL_TOL / 50, err(mixed, 7)
+    assert err(mixed, 3) > KL_TOL, err(mixed, 3)
+    # one sign throughout (a common offset of the direction): the row
+    # reference takes the offset out, and what is left is on the series
+    one_signed = -frac * tau / amax
+    assert err(one_signed, 7) < KL_TOL / 50, err(one_signed, 7)
+    # a small-step direction of the sweep workload (N(0, 0.05^2) at alpha up
+    # to 2): the series and the exact sums agree to rounding
+    delta = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.DIR_ID, salt=9, sigma=0.05))
+    assert err(delta, 7) < 1e-7, err(delta, 7)
