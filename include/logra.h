@@ -187,8 +187,9 @@ int logra_sketch_accumulate(const uint16_t* X, int64_t ldx, const uint16_t* dY,
  * Arguments, result and ordering as in logra_sketch_accumulate (same kernels,
  * so the same bits), except that the deferral flags (LOGRA_SKETCH_DEFER,
  * LOGRA_SKETCH_PENDING) are refused with LOGRA_EINVAL: the scratch is shared
- * by every call on the GPU, so nothing may be left pending in it.  The stream's device (the current device for the null
- * stream) selects which GPU's scratch is used.
+ * by every call on the GPU, so nothing may be left pending in it.  The
+ * stream's device (the current device for the null stream) selects which
+ * GPU's scratch is used.
  * Limit: the call needs logra_sketch_ws_bytes(T, d, k, r) bytes of scratch;
  *     beyond LOGRA_NOALLOC_SCRATCH_BYTES it returns LOGRA_EWORKSPACE and
  *     enqueues nothing (d = k = 4096 at r = 64 needs 10.5 MiB for T = 8192;

@@ -278,7 +278,8 @@ int logra_sketch_accumulate_layer(int64_t T, int32_t r, int kind, int32_t flags,
     if (q.n_out < 1 || q.n_out > LOGRA_MAX_SHARED || n_out + q.n_out > LOGRA_MAX_LAYER_OUT)
       return LOGRA_EINVAL;
     grp[g] = logra::SketchGroup{q.X, q.ldx, q.k, q.seed, q.stream, q.n_out};
-    for (int i = 0; i < q.n_out; ++i) outs[n_out++] = logra::SketchOut{q.dY[i], q.ldd[i], q.d[i], q.S[i]};
+    for (int i = 0; i < q.n_out; ++i)
+      outs[n_out++] = logra::SketchOut{q.dY[i], q.ldd[i], q.d[i], q.S[i]};
   }
   logra::SketchPlan p{};
   bool run = false;
@@ -398,7 +399,8 @@ int logra_merge_many(int32_t n, const logra_merge_item* items, int32_t r, int ki
   // (read while every W is written)
   for (int i = 0; i < n; ++i) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(m[i].W);
-    const uintptr_t hi = lo + 2 * ((uintptr_t)(m[i].d - 1) * (uintptr_t)m[i].ldw + (uintptr_t)m[i].k);
+    const uintptr_t hi =
+        lo + 2 * ((uintptr_t)(m[i].d - 1) * (uintptr_t)m[i].ldw + (uintptr_t)m[i].k);
     for (int j = 0; j < n; ++j) {
       const uintptr_t slo = reinterpret_cast<uintptr_t>(m[j].S);
       const uintptr_t shi = slo + 4 * (uintptr_t)m[j].d * (uintptr_t)r;
@@ -441,7 +443,8 @@ int logra_sketch_update(int rule, const float* S, float* m, float* v, float* U,
     for (int j = i + 1; j < 4; ++j) {
       if (!overlap(arr[i], arr[j])) continue;
       const bool same = arr[i] == arr[j];
-      const bool allowed = (j == 3 && i == 0) || (j == 3 && i == 1 && rule == LOGRA_UPDATE_MOMENTUM);
+      const bool allowed =
+          (j == 3 && i == 0) || (j == 3 && i == 1 && rule == LOGRA_UPDATE_MOMENTUM);
       if (!same || !allowed) return LOGRA_EINVAL;
     }
   double bc1 = 1.0, bc2 = 1.0;

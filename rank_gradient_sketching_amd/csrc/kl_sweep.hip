@@ -29,10 +29,11 @@
 // direction out of the moments, where it would dominate them and cancel in
 // the finalisation (and push every element off the series path).
 // So an element costs the same ~20 VALU operations whatever the number of
-// multipliers (dl is never formed: the moments are taken in units of delta
-// and 1/tau enters each row's finalisation).  States merge by rescaling to the larger running max (shuffles
-// inside a wave, LDS across the four waves of a row); rows are finalised in
-// fp64 and a one-work-group kernel forms the weighted means in a fixed order.
+// multipliers (dl itself is never formed: each element's u = amax dl comes
+// from delta with one subtraction and one multiplication).  States merge by
+// rescaling to the larger running max (shuffles inside a wave, LDS across
+// the four waves of a row); rows are finalised in fp64 and a one-work-group
+// kernel forms the weighted means in a fixed order.
 #include <math.h>
 
 #include "common.hpp"
@@ -307,10 +308,14 @@ hipError_t launch_kl_sweep(const uint16_t* z, const uint16_t* dz, int n_tok, int
     for (int i = 0; i < n_alpha; ++i) al.a[i] = (float)((double)alphas[i] / (double)amax);
   }
   hipError_t e;
-  if (n_alpha <= 1) e = launch_rows<1>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
-  else if (n_alpha <= 2) e = launch_rows<2>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
-  else if (n_alpha <= 4) e = launch_rows<4>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
-  else e = launch_rows<8>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
+  if (n_alpha <= 1)
+    e = launch_rows<1>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
+  else if (n_alpha <= 2)
+    e = launch_rows<2>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
+  else if (n_alpha <= 4)
+    e = launch_rows<4>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
+  else
+    e = launch_rows<8>(z, dz, n_tok, vocab, ld, n_alpha, al, inv_tau, su, thr, kl_tok, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kl_sweep_mean_kernel, dim3(1), dim3(1024), 0, s, kl_tok, weight, n_tok,
                      n_alpha, kl_mean);

@@ -431,8 +431,10 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MT tab, int r, float
 #pragma unroll
         for (int i = 0; i < WR / 8; ++i) {
           const int rr = 8 * i + (lane >> 3);
-          const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (wave * WR + rr) * kStRow + 8 * pc);
-          *reinterpret_cast<u32x4*>(W + (int64_t)(row0 + rr) * ldw + col0 + pass * kPassCols + 8 * pc) = v;
+          const u32x4 v =
+              *reinterpret_cast<const u32x4*>(stage + (wave * WR + rr) * kStRow + 8 * pc);
+          *reinterpret_cast<u32x4*>(W + (int64_t)(row0 + rr) * ldw + col0 + pass * kPassCols +
+                                    8 * pc) = v;
         }
       }
     };
@@ -501,7 +503,9 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MT tab, int r, float
 // r = 128 the small-rank shapes measured the same).
 constexpr int merge_rows(int nks, bool gauss) { return nks <= 2 && !gauss ? 128 : 256; }
 constexpr int merge_nt(int nks) { return nks <= 2 ? 1 : 2; }
-constexpr int merge_waves(int nks, bool gauss) { return merge_rows(nks, gauss) / (16 * merge_nt(nks)); }
+constexpr int merge_waves(int nks, bool gauss) {
+  return merge_rows(nks, gauss) / (16 * merge_nt(nks));
+}
 
 template <int NKS, bool MASKED, class MT>
 void launch_merge_m(const MT& tab, int r, bool gauss, float scale, float cr, hipStream_t s,

@@ -84,9 +84,11 @@ void launch_rule(const UpdateArgs& a, bool vec, hipStream_t s) {
   int64_t blocks = (items + 255) / 256;
   if (blocks > 2048) blocks = 2048;   // grid-stride beyond eight work-groups per CU
   if (vec)
-    hipLaunchKernelGGL((sketch_update_kernel<RULE, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((sketch_update_kernel<RULE, true>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((sketch_update_kernel<RULE, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((sketch_update_kernel<RULE, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       s, a);
 }
 
 }  // namespace
@@ -96,7 +98,9 @@ hipError_t launch_sketch_update(int rule, const float* S, float* m, float* v, fl
                                 double bc1, double bc2, hipStream_t s) {
   if (rule == kUpdateSgd && U == S) return hipSuccess;   // U = S in place: nothing to do
   UpdateArgs a{S, m, v, U, n, beta1, beta2, eps, (float)bc1, (float)bc2};
-  auto al16 = [](const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  auto al16 = [](const void* p) {
+    return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+  };
   const bool vec = (n % 4) == 0 && al16(S) && al16(m) && al16(v) && al16(U);
   switch (rule) {
     case kUpdateSgd: launch_rule<kUpdateSgd>(a, vec, s); break;
