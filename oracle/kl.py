@@ -16,7 +16,12 @@ Readings where the pages leave a step open:
     KL(p_cur || p_prop), p = softmax(z / tau), with p_prop the alpha = 1
     proposal; every row has equal weight.
   * controller edges: q = 0 or q < 0 (rounding) gives alpha_max; a NaN q
-    gives a NaN alpha.
+    gives a NaN alpha; an infinite q gives alpha = 0.
+  * masked vocabulary entries: a logit of -inf is a token of probability
+    zero.  Such a token of the current distribution contributes nothing to
+    KL(p || p') (the convention 0 log 0 = 0); a token with p > 0 and p' = 0
+    makes the KL +inf.  A row whose every logit is -inf has no distribution:
+    its KL is NaN.  Other non-finite logits (NaN, +inf) give NaN.
 All arithmetic is fp64.
 """
 import numpy as np
@@ -26,14 +31,23 @@ def log_softmax(a):
     """Row-wise log softmax of a 2-D fp64 array."""
     a = np.asarray(a, np.float64)
     m = a.max(axis=1, keepdims=True)
-    return a - m - np.log(np.exp(a - m).sum(axis=1, keepdims=True))
+    with np.errstate(invalid="ignore"):      # rows with no finite logit give NaN
+        return a - m - np.log(np.exp(a - m).sum(axis=1, keepdims=True))
 
 
 def kl_rows(z_cur, z_prop, tau):
-    """Per-row forward KL(softmax(z_cur/tau) || softmax(z_prop/tau))."""
+    """Per-row forward KL(softmax(z_cur/tau) || softmax(z_prop/tau)), the sum
+    of p (log p - log p') over the tokens with p > 0 (masked tokens, z_cur =
+    -inf, contribute nothing; p > 0 with p' = 0 contributes +inf)."""
     lp = log_softmax(np.asarray(z_cur, np.float64) / tau)
     lq = log_softmax(np.asarray(z_prop, np.float64) / tau)
-    return (np.exp(lp) * (lp - lq)).sum(axis=1)
+    with np.errstate(invalid="ignore"):
+        terms = np.where(lp == -np.inf, 0.0,                    # p = 0
+                         np.where(lq == -np.inf, np.inf,        # p > 0, p' = 0
+                                  np.exp(lp) * (lp - lq)))
+    # (a row with no finite current logit gives NaN from log_softmax, which
+    # propagates, as do NaN and +inf logits)
+    return terms.sum(axis=1)
 
 
 def predicted_kl(z_cur, z_prop, tau):
@@ -63,10 +77,15 @@ def step_size(q, kl_budget, alpha_max):
 # weights.  A zero weight sum gives NaN.
 
 def kl_sweep_rows(z, delta, alphas, tau):
-    """(n_alpha, n_tok) array: row t, multiplier a -> KL(p(z_t) || p(z_t + a delta_t))."""
+    """(n_alpha, n_tok) array: row t, multiplier a -> KL(p(z_t) || p(z_t + a delta_t)).
+    A masked token (z = -inf) stays masked in every proposal, whatever its
+    direction entry."""
     z = np.asarray(z, np.float64)
     delta = np.asarray(delta, np.float64)
-    return np.stack([kl_rows(z, z + float(a) * delta, tau) for a in alphas])
+    masked = z == -np.inf
+    with np.errstate(invalid="ignore"):
+        props = [np.where(masked, -np.inf, z + float(a) * delta) for a in alphas]
+    return np.stack([kl_rows(z, zp, tau) for zp in props])
 
 
 def predicted_kl_sweep(z, delta, alphas, tau, weights=None):

@@ -293,6 +293,62 @@ def test_kl_special_cases():
     np.testing.assert_allclose(kl.kl_rows(z, zp, 1.0), ident, rtol=1e-9)
 
 
+def test_kl_masked_entries():
+    # Masked tokens (logit -inf): probability zero.  Against the plain
+    # definitions: the KL over the sub-vocabulary of unmasked tokens, and
+    # scipy's rel_entr, whose conventions are 0 log(0/q) = 0 and
+    # p log(p/0) = +inf.
+    rng = np.random.default_rng(31)
+    z = rng.standard_normal((6, 700)) * 3
+    zp = z + rng.standard_normal(z.shape) * 0.3
+    mask = rng.random(z.shape) < 0.2
+    mask[:, :5] = True                       # masked entries at the row start too
+    zm = np.where(mask, -np.inf, z)
+    zpm = np.where(mask, -np.inf, zp)
+    got = kl.kl_rows(zm, zpm, 1.0)
+    for t in range(z.shape[0]):
+        keep = ~mask[t]
+        sub = kl.kl_rows(z[t:t + 1, keep], zp[t:t + 1, keep], 1.0)[0]
+        np.testing.assert_allclose(got[t], sub, rtol=1e-12)
+        pq = scipy.special.softmax(zm[t]), scipy.special.softmax(zpm[t])
+        np.testing.assert_allclose(got[t], scipy.special.rel_entr(*pq).sum(), rtol=1e-10)
+    # p = 0 where p' > 0 adds nothing: mask only the current row
+    got2 = kl.kl_rows(zm, zp, 1.0)
+    ref2 = [scipy.special.rel_entr(scipy.special.softmax(zm[t]),
+                                   scipy.special.softmax(zp[t])).sum() for t in range(6)]
+    np.testing.assert_allclose(got2, ref2, rtol=1e-10)
+    # p > 0 where p' = 0: +inf, and the controller then takes no step
+    zp3 = zp.copy()
+    zp3[:, 7] = -np.inf
+    assert np.all(kl.kl_rows(z, zp3, 1.0) == np.inf)
+    assert kl.step_size(kl.predicted_kl(z, zp3, 1.0), 2e-4, 4.0) == 0.0
+    # no finite current logit, a NaN or a +inf logit: NaN
+    bad = z[:3].copy()
+    bad[0, :] = -np.inf
+    bad[1, 9] = np.nan
+    bad[2, 9] = np.inf
+    assert np.all(np.isnan(kl.kl_rows(bad, zp[:3], 1.0)))
+    assert np.isnan(kl.kl_rows(z[:1], np.where(np.arange(700) == 3, np.nan, zp[:1]), 1.0)[0])
+
+
+def test_kl_sweep_masked_entries():
+    # A masked token stays masked in every proposal, whatever its direction
+    # entry (NaN and inf included): the sweep equals the sweep over the
+    # unmasked sub-vocabulary.
+    rng = np.random.default_rng(32)
+    z = rng.standard_normal((4, 500)) * 3
+    delta = rng.standard_normal(z.shape) * 0.2
+    mask = rng.random(z.shape) < 0.3
+    zm = np.where(mask, -np.inf, z)
+    dm = np.where(mask, rng.choice([np.nan, np.inf, -np.inf, 1e30], z.shape), delta)
+    alphas = [0.25, 1.0, -2.0]
+    got = kl.kl_sweep_rows(zm, dm, alphas, 1.0)
+    for t in range(z.shape[0]):
+        keep = ~mask[t]
+        sub = kl.kl_sweep_rows(z[t:t + 1, keep], delta[t:t + 1, keep], alphas, 1.0)[:, 0]
+        np.testing.assert_allclose(got[:, t], sub, rtol=1e-12)
+
+
 def test_predicted_kl_scales_as_alpha_squared(golden):
     # Mean predicted KL ~ alpha^2 q(D): halving alpha quarters it.  Logits and
     # direction as in the controller workload (z ~ N(0, 3^2), delta ~ N(0, 0.05^2)),
