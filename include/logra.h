@@ -477,7 +477,13 @@ size_t logra_kl_ws_bytes(int64_t n_tok, int64_t vocab);
  * (forward KL, z_prop = logits after the alpha = 1 proposal), in one pass
  * over both rows; q = mean_t KL_t (equal weight per row);
  * alpha = min(alpha_max, sqrt(kl_budget / q)); q <= 0 gives alpha_max; a NaN
- * q gives a NaN alpha.
+ * q gives a NaN alpha; q = +inf gives alpha = 0.
+ * Masked tokens: a logit of -inf is a token of probability zero.  One with
+ * z_cur = -inf adds nothing to KL_t (its proposed mass, if any, still enters
+ * the proposal's normaliser); one with finite z_cur and z_prop = -inf
+ * (p > 0, p' = 0) makes KL_t = +inf.  A row with no finite z_cur, and NaN or
+ * +inf logits, give a NaN KL_t.  Rows with a -inf logit take a second pass
+ * over their data.
  *
  * z_cur, z_prop: device bf16[n_tok x ld], ld >= vocab, ld % 8 == 0, 16-B
  *     aligned.
@@ -514,6 +520,11 @@ size_t logra_kl_sweep_ws_bytes(int64_t n_tok, int32_t n_alpha);
  * (forward KL), and kl_mean[i] = sum_t w_t KL_t(alpha_i) / sum_t w_t in fp64
  * (w_t = weight[t], or 1 when weight is NULL; a token mask or per-response
  * averaging is a choice of weights; a zero weight sum gives NaN).
+ * Masked tokens: a current logit of -inf is a token of probability zero and
+ * stays masked in every proposal, whatever its delta entry (NaN and inf
+ * included); a row with no finite z gives NaN, and so do NaN or +inf logits.
+ * A non-finite delta at an unmasked token is not specified (NaN or +-inf).
+ * Rows with a -inf logit take a second pass over their data.
  * Per element the cost does not depend on n_alpha: the multipliers enter
  * through weighted moments of delta (see kl_sweep.hip); the relative
  * truncation of that expansion is below 1.1e-5.

@@ -26,6 +26,17 @@
 // proposed logits (a shift of the whole row, e.g. a bias-like update) out of
 // g, whose fp32 sums would otherwise carry e^c - 1 - c and cancel against
 // log1p(x) - x (an offset of -3 had cost ~40 % of a row's KL).
+// Masked tokens: a logit of -inf is a token of probability zero.  Such a
+// token of the current row adds nothing to the KL, and one with a finite
+// current logit but a -inf proposed logit (p > 0, p' = 0) makes the row's
+// KL +inf.  The first pass over a row does not look for them (z' - z is NaN
+// or infinite there and leaves some sum of the state non-finite); a row
+// whose merged state is not finite is read a second time in masked mode,
+// which leaves the tokens with p = 0 out of the expectations (their
+// proposed mass, when p' > 0, still enters the proposal's normaliser), notes
+// those with p > 0 and p' = 0, and takes the row reference from the tokens
+// where neither logit is -inf.  Rows of finite logits pay one check; NaN and
+// +inf logits still give NaN.
 #include <math.h>
 
 #include "common.hpp"
@@ -70,16 +81,30 @@ __device__ __forceinline__ float excess_exp(float d) {
 }
 
 // Adds n (<= 8) elements to the state; z and zq are bf16 pairs, dref the
-// row's reference difference.
-__device__ __forceinline__ void kl_group(KlState& st, const float* z,
+// row's reference difference.  MASK (the second pass): `hit` notes a token
+// with p > 0 and p' = 0; a token with p = 0 adds nothing to s, u1 or the
+// excess, but when p' > 0 it still belongs to the proposal's normaliser:
+// with R = sum over such tokens of e^((z' - c)/tau) / sum_p>0 e^(z/tau),
+// KL = log(E_p[e^d] + R) - E_p[d], so R joins u3 (as 2^(b - m) with
+// b = (z' - c) log2e / tau, which also joins the running max).
+template <bool MASK>
+__device__ __forceinline__ void kl_group(KlState& st, bool& hit, const float* z,
                                          const float* zq, int n, float l2t,
                                          float inv_tau, float dref) {
-  float a2[8], dd[8];
+  float a2[8], dd[8], b2[8];
   float cmax = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     a2[e] = e < n ? z[e] * l2t : -INFINITY;
-    dd[e] = e < n ? ((zq[e] - z[e]) - dref) * inv_tau : 0.0f;
+    if constexpr (MASK) {
+      const bool pz = z[e] == -INFINITY, pq = zq[e] == -INFINITY;
+      if (e < n && pq && !pz) hit = true;
+      dd[e] = e < n && !pz && !pq ? ((zq[e] - z[e]) - dref) * inv_tau : 0.0f;
+      b2[e] = e < n && pz && !pq ? (zq[e] - dref) * l2t : -INFINITY;
+      cmax = fmaxf(cmax, b2[e]);
+    } else {
+      dd[e] = e < n ? ((zq[e] - z[e]) - dref) * inv_tau : 0.0f;
+    }
     cmax = fmaxf(cmax, a2[e]);
   }
   if (cmax > st.m) {
@@ -91,11 +116,16 @@ __device__ __forceinline__ void kl_group(KlState& st, const float* z,
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    if (e < n) {
+    // (a masked token, p = 0, is skipped outright: while a thread has seen
+    // nothing else its running max is -inf, and 2^(-inf - -inf) is NaN)
+    if (e < n && (!MASK || a2[e] != -INFINITY)) {
       const float w = exp2_normal(a2[e] - st.m);
       st.s += w;
       st.u1 = fmaf(w, dd[e], st.u1);
       st.u3 = fmaf(w, excess_exp(dd[e]), st.u3);
+    }
+    if constexpr (MASK) {
+      if (b2[e] != -INFINITY) st.u3 += exp2_normal(b2[e] - st.m);
     }
   }
 }
@@ -103,25 +133,42 @@ __device__ __forceinline__ void kl_group(KlState& st, const float* z,
 // Mean of zq - z over the first min(V, 64) elements of a row: lane l takes
 // element l, then a butterfly sum.  Every lane (and every wave of the row)
 // ends with the same bits: each level adds the same two partial sums, and
-// fp32 addition is commutative.
+// fp32 addition is commutative.  MASK: over the tokens among them where
+// neither logit is -inf (0 when there is none).
+template <bool MASK>
 __device__ __forceinline__ float row_reference(const uint16_t* a, const uint16_t* b, int V) {
   const int lane = threadIdx.x & 63;
   const int nref = V < 64 ? V : 64;
-  float x = lane < nref ? bf16_to_f32(b[lane]) - bf16_to_f32(a[lane]) : 0.0f;
+  if constexpr (MASK) {
+    const float za = lane < nref ? bf16_to_f32(a[lane]) : 0.0f;
+    const float zb = lane < nref ? bf16_to_f32(b[lane]) : 0.0f;
+    const bool ok = lane < nref && za != -INFINITY && zb != -INFINITY;
+    float x = ok ? zb - za : 0.0f;
+    float cnt = ok ? 1.0f : 0.0f;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x / (float)nref;
+    for (int off = 32; off > 0; off >>= 1) {
+      x += __shfl_xor(x, off);
+      cnt += __shfl_xor(cnt, off);
+    }
+    return cnt > 0.0f ? x / cnt : 0.0f;
+  } else {
+    float x = lane < nref ? bf16_to_f32(b[lane]) - bf16_to_f32(a[lane]) : 0.0f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x / (float)nref;
+  }
 }
 
-__global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
-    const uint16_t* __restrict__ zc, const uint16_t* __restrict__ zp, int V,
-    int64_t ld, float inv_tau, float* __restrict__ kl_out) {
-  __shared__ KlState wst[kKlThreads / 64];
-  const int64_t row = blockIdx.x;
-  const uint16_t* a = zc + row * ld;
-  const uint16_t* b = zp + row * ld;
-  const float l2t = kLog2e * inv_tau;
-  const float dref = row_reference(a, b, V);
+__device__ __forceinline__ bool state_finite(const KlState& t) {
+  return isfinite(t.s) && isfinite(t.u1) && isfinite(t.u3);
+}
+
+// One pass over a row: this thread's elements, then the wave's butterfly
+// (every lane ends with the wave's state).
+template <bool MASK>
+__device__ __forceinline__ KlState kl_row_pass(const uint16_t* a, const uint16_t* b, int V,
+                                               float l2t, float inv_tau, bool& hit) {
+  const float dref = row_reference<MASK>(a, b, V);
   KlState st{-INFINITY, 0.0f, 0.0f, 0.0f};
   // logits are read once: non-temporal loads (5 % faster over 65536 x 152064)
   const int nfull = V >> 3;
@@ -136,7 +183,7 @@ __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
       zq[2 * p] = bf16_lo(vb[p]);
       zq[2 * p + 1] = bf16_hi(vb[p]);
     }
-    kl_group(st, z, zq, 8, l2t, inv_tau, dref);
+    kl_group<MASK>(st, hit, z, zq, 8, l2t, inv_tau, dref);
   }
   const int tail = V - 8 * nfull;
   if (tail > 0 && (int)threadIdx.x == nfull % kKlThreads) {
@@ -146,9 +193,9 @@ __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
       z[e] = e < tail ? bf16_to_f32(a[8 * nfull + e]) : 0.0f;
       zq[e] = e < tail ? bf16_to_f32(b[8 * nfull + e]) : 0.0f;
     }
-    kl_group(st, z, zq, tail, l2t, inv_tau, dref);
+    kl_group<MASK>(st, hit, z, zq, tail, l2t, inv_tau, dref);
   }
-  // wave reduction (fixed butterfly), then the four waves in order
+  // wave reduction (fixed butterfly)
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     KlState o;
@@ -158,16 +205,51 @@ __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
     o.u3 = __shfl_xor(st.u3, off);
     st = kl_merge(st, o);
   }
+  return st;
+}
+
+__global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
+    const uint16_t* __restrict__ zc, const uint16_t* __restrict__ zp, int V,
+    int64_t ld, float inv_tau, float* __restrict__ kl_out) {
+  __shared__ KlState wst[kKlThreads / 64];
+  __shared__ int whit[kKlThreads / 64];
+  const int64_t row = blockIdx.x;
+  const uint16_t* a = zc + row * ld;
+  const uint16_t* b = zp + row * ld;
+  const float l2t = kLog2e * inv_tau;
   const int wave = threadIdx.x >> 6;
+  bool hit = false;
+  KlState st = kl_row_pass<false>(a, b, V, l2t, inv_tau, hit);
   if ((threadIdx.x & 63) == 0) wst[wave] = st;
   __syncthreads();
+  // every thread reads the four wave states, so the choice below is the
+  // same in the whole work-group
+  bool finite = true;
+#pragma unroll
+  for (int w = 0; w < kKlThreads / 64; ++w) finite = finite && state_finite(wst[w]);
+  if (!finite) {
+    __syncthreads();   // every thread has read wst
+    st = kl_row_pass<true>(a, b, V, l2t, inv_tau, hit);
+    const bool wave_hit = __ballot(hit) != 0ull;
+    if ((threadIdx.x & 63) == 0) {
+      wst[wave] = st;
+      whit[wave] = wave_hit ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  // then the four waves in order
   if (threadIdx.x == 0) {
     KlState t = wst[0];
 #pragma unroll
     for (int w = 1; w < kKlThreads / 64; ++w) t = kl_merge(t, wst[w]);
+    bool any_hit = false;
+    if (!finite) {
+#pragma unroll
+      for (int w = 0; w < kKlThreads / 64; ++w) any_hit = any_hit || whit[w] != 0;
+    }
     const double s = t.s;
     const double x = ((double)t.u1 + (double)t.u3) / s;
-    const double kl = (double)t.u3 / s + (log1p(x) - x);
+    const double kl = any_hit ? (double)INFINITY : (double)t.u3 / s + (log1p(x) - x);
     kl_out[row] = (float)kl;
   }
 }
@@ -191,7 +273,7 @@ __global__ __launch_bounds__(1024) void kl_mean_kernel(const float* __restrict__
     double alpha;
     if (isnan(q)) {
       alpha = NAN;
-    } else if (q <= 0.0) {
+    } else if (q <= 0.0) {   // (q = +inf gives alpha = sqrt(0) = 0 below)
       alpha = alpha_max;
     } else {
       alpha = fmin((double)alpha_max, sqrt((double)kl_budget / q));

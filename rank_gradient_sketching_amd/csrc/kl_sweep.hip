@@ -28,6 +28,13 @@
 // KL(alpha) unchanged, and taking it out keeps a common offset of the
 // direction out of the moments, where it would dominate them and cancel in
 // the finalisation (and push every element off the series path).
+// Masked tokens: a current logit of -inf is a token of probability zero, and
+// it stays masked in every proposal whatever its direction entry (NaN and
+// inf included).  The first pass over a row does not look for them (they
+// leave some sum of the state non-finite); a row whose merged state is not
+// finite is read a second time in masked mode, which skips those tokens and
+// takes the direction reference from the others.  Rows of finite inputs pay
+// one check.
 // So an element costs the same ~20 VALU operations whatever the number of
 // multipliers (dl itself is never formed: each element's u = amax dl comes
 // from delta with one subtraction and one multiplication).  States merge by
@@ -106,7 +113,7 @@ struct Multipliers {
 // as = alpha / max|alpha| (alpha dz / tau = as u).  The weight exponent is
 // z l2t - m in one fma (the running max is taken over z: l2t > 0 and
 // rounding is monotonic, so max(z) l2t rounds to the max of the z l2t).
-template <int NA>
+template <bool MASK, int NA>
 __device__ __forceinline__ void sw_group(SwState<NA>& st, const float* z, const float* dz,
                                          int n, float l2t, float su, float thr,
                                          const Multipliers& as, float dref) {
@@ -121,7 +128,9 @@ __device__ __forceinline__ void sw_group(SwState<NA>& st, const float* z, const 
   const float nm = -st.m;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    if (e < n) {
+    // MASK: a masked token (z = -inf) is skipped outright, its direction
+    // entry unread
+    if (e < n && (!MASK || z[e] != -INFINITY)) {
       const float w = exp2_normal(fmaf(z[e], l2t, nm));
       const float d = (dz[e] - dref) * su;
       st.s += w;
@@ -156,28 +165,48 @@ __device__ __forceinline__ SwState<NA> sw_shfl_xor(const SwState<NA>& st, int of
 
 // Mean of delta over the first min(V, 64) elements of a row by a butterfly
 // sum; every lane and wave of the row ends with the same bits (each level
-// adds the same two partial sums, and fp32 addition is commutative).
-__device__ __forceinline__ float direction_reference(const uint16_t* dr, int V) {
+// adds the same two partial sums, and fp32 addition is commutative).  MASK:
+// over the unmasked tokens among them (0 when there is none).
+template <bool MASK>
+__device__ __forceinline__ float direction_reference(const uint16_t* zr, const uint16_t* dr,
+                                                     int V) {
   const int lane = threadIdx.x & 63;
   const int nref = V < 64 ? V : 64;
-  float x = lane < nref ? bf16_to_f32(dr[lane]) : 0.0f;
+  if constexpr (MASK) {
+    const bool ok = lane < nref && bf16_to_f32(zr[lane]) != -INFINITY;
+    float x = ok ? bf16_to_f32(dr[lane]) : 0.0f;
+    float cnt = ok ? 1.0f : 0.0f;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x / (float)nref;
+    for (int off = 32; off > 0; off >>= 1) {
+      x += __shfl_xor(x, off);
+      cnt += __shfl_xor(cnt, off);
+    }
+    return cnt > 0.0f ? x / cnt : 0.0f;
+  } else {
+    float x = lane < nref ? bf16_to_f32(dr[lane]) : 0.0f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x / (float)nref;
+  }
 }
 
-// One work-group per row: kl_out[i * n_tok + row] = KL_row(alpha_i).
 template <int NA>
-__global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
-    const uint16_t* __restrict__ z, const uint16_t* __restrict__ dz, int V, int64_t ld,
-    int n_tok, int na, Multipliers al, float inv_tau, float su, float thr,
-    float* __restrict__ kl_out) {
-  __shared__ SwState<NA> wst[kSwThreads / 64];
-  const int64_t row = blockIdx.x;
-  const uint16_t* zr = z + row * ld;
-  const uint16_t* dr = dz + row * ld;
-  const float l2t = kSwLog2e * inv_tau;
-  const float dref = direction_reference(dr, V);
+__device__ __forceinline__ bool sw_finite(const SwState<NA>& t) {
+  bool f = isfinite(t.s) && isfinite(t.u1);
+#pragma unroll
+  for (int n = 0; n < kMoments; ++n) f = f && isfinite(t.M[n]);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) f = f && isfinite(t.r[i]);
+  return f;
+}
+
+// One pass over a row: this thread's elements, then the wave's butterfly
+// (every lane ends with the wave's state).
+template <bool MASK, int NA>
+__device__ __forceinline__ SwState<NA> sw_row_pass(const uint16_t* zr, const uint16_t* dr, int V,
+                                                   float l2t, float su, float thr,
+                                                   const Multipliers& al) {
+  const float dref = direction_reference<MASK>(zr, dr, V);
   SwState<NA> st;
   st.m = -INFINITY;
   st.s = 0.0f;
@@ -200,7 +229,7 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
       dd[2 * p] = bf16_lo(vb[p]);
       dd[2 * p + 1] = bf16_hi(vb[p]);
     }
-    sw_group(st, zz, dd, 8, l2t, su, thr, al, dref);
+    sw_group<MASK>(st, zz, dd, 8, l2t, su, thr, al, dref);
   }
   const int tail = V - 8 * nfull;
   if (tail > 0 && (int)threadIdx.x == nfull % kSwThreads) {
@@ -210,14 +239,41 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
       zz[e] = e < tail ? bf16_to_f32(zr[8 * nfull + e]) : 0.0f;
       dd[e] = e < tail ? bf16_to_f32(dr[8 * nfull + e]) : 0.0f;
     }
-    sw_group(st, zz, dd, tail, l2t, su, thr, al, dref);
+    sw_group<MASK>(st, zz, dd, tail, l2t, su, thr, al, dref);
   }
-  // wave reduction (fixed butterfly), then the four waves in order
+  // wave reduction (fixed butterfly)
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) st = sw_merge(st, sw_shfl_xor(st, off));
+  return st;
+}
+
+// One work-group per row: kl_out[i * n_tok + row] = KL_row(alpha_i).
+template <int NA>
+__global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
+    const uint16_t* __restrict__ z, const uint16_t* __restrict__ dz, int V, int64_t ld,
+    int n_tok, int na, Multipliers al, float inv_tau, float su, float thr,
+    float* __restrict__ kl_out) {
+  __shared__ SwState<NA> wst[kSwThreads / 64];
+  const int64_t row = blockIdx.x;
+  const uint16_t* zr = z + row * ld;
+  const uint16_t* dr = dz + row * ld;
+  const float l2t = kSwLog2e * inv_tau;
   const int wave = threadIdx.x >> 6;
+  SwState<NA> st = sw_row_pass<false, NA>(zr, dr, V, l2t, su, thr, al);
   if ((threadIdx.x & 63) == 0) wst[wave] = st;
   __syncthreads();
+  // every thread reads the four wave states, so the choice is the same in
+  // the whole work-group
+  bool finite = true;
+#pragma unroll
+  for (int w = 0; w < kSwThreads / 64; ++w) finite = finite && sw_finite(wst[w]);
+  if (!finite) {
+    __syncthreads();   // every thread has read wst
+    st = sw_row_pass<true, NA>(zr, dr, V, l2t, su, thr, al);
+    if ((threadIdx.x & 63) == 0) wst[wave] = st;
+    __syncthreads();
+  }
+  // then the four waves in order
   if (threadIdx.x == 0) {
     SwState<NA> t = wst[0];
 #pragma unroll

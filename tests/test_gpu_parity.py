@@ -727,6 +727,52 @@ def test_kl_controller_edges(lg):
     assert np.isnan(q) and np.isnan(a)
 
 
+@pytest.mark.parametrize("n,V", [(12, 4099), (6, 152064)])
+def test_predicted_kl_masked_vocabulary(lg, n, V):
+    # logits of -inf: tokens of probability zero.  Rows 0 .. n-5 masked at the
+    # same tokens in z and z' (row 0 at its whole first 64, where the row
+    # reference is taken; row 1 at its first three), row n-4 in z only
+    # (p = 0, p' > 0), row n-3 unmasked, row n-2 with one token of p > 0 and
+    # p' = 0 (KL +inf), row n-1 masked everywhere (NaN)
+    say("kl masked", n, V)
+    rng = np.random.default_rng(V + n)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V + 3)
+    dirn = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V + 3, sigma=0.05)
+    zp = synth.proposal_logits(z, dirn, 1.0)
+    mask = torch.from_numpy(rng.random((n, V)) < 0.1)
+    mask[0, :64] = True
+    mask[1, :3] = True
+    mask[n - 3:] = False
+    ninf = float("-inf")
+    zm, zpm = z.clone(), zp.clone()
+    zm[: n - 3][mask[: n - 3]] = ninf
+    zpm[: n - 4][mask[: n - 4]] = ninf
+    zpm[n - 2, 5] = ninf
+    zm[n - 1] = ninf
+    zpm[n - 1] = ninf
+    ld = -(-V // 8) * 8
+    z_g, zp_g = padded_bf16(zm, ld), padded_bf16(zpm, ld)
+    kl_tok = torch.empty(n, device="cuda")
+    out = lg.predicted_kl(z_g, zp_g, 1.0, 2e-4, 4.0, kl_tok=kl_tok)
+    torch.cuda.synchronize()
+    ref = okl.kl_rows(synth.bf16_to_f64(zm), synth.bf16_to_f64(zpm), 1.0)
+    got = kl_tok.cpu().numpy().astype(np.float64)
+    assert np.isinf(ref[n - 2]) and np.isnan(ref[n - 1])
+    assert got[n - 2] == np.inf, got[n - 2]
+    assert np.isnan(got[n - 1]), got[n - 1]
+    np.testing.assert_allclose(got[: n - 2], ref[: n - 2], rtol=1e-3, atol=1e-9)
+    assert np.isnan(out.cpu().numpy()).all()          # the NaN row reaches q and alpha
+    # the finite rows alone: q and alpha against the oracle
+    out_f = lg.predicted_kl(z_g[: n - 2], zp_g[: n - 2], 1.0, 2e-4, 4.0)
+    q, alpha = out_f.cpu().numpy().astype(np.float64)
+    q_ref = float(ref[: n - 2].mean())
+    assert abs(q / q_ref - 1) < Q_TOL, (q, q_ref)
+    assert abs(alpha / okl.step_size(q_ref, 2e-4, 4.0) - 1) < 1e-3
+    # with the +inf row: q = +inf and the controller takes no step
+    q, alpha = lg.predicted_kl(z_g[: n - 1], zp_g[: n - 1], 1.0, 2e-4, 4.0).cpu().tolist()
+    assert q == float("inf") and alpha == 0.0
+
+
 # ------------------------------------------------------- predicted-KL sweep
 
 SWEEP_CASES = [
@@ -794,6 +840,40 @@ def test_kl_sweep_alpha_squared_law_and_edges(lg):
     shift = torch.full((n, V), 0.75, dtype=torch.bfloat16, device="cuda")
     flat = lg.predicted_kl_sweep(z_g, shift, [1.0, 4.0], 1.0).cpu().numpy()
     assert np.all(np.abs(flat) < 1e-6)
+
+
+@pytest.mark.parametrize("n,V", [(8, 4099), (4, 152064)])
+def test_predicted_kl_sweep_masked_vocabulary(lg, n, V):
+    # masked tokens (z = -inf) stay masked in every proposal whatever their
+    # direction entry (NaN, +-inf or finite here); row 0 masked at its whole
+    # first 64 (the direction reference), row n-1 unmasked, row n-2 masked
+    # everywhere (NaN at every multiplier)
+    say("kl sweep masked", n, V)
+    rng = np.random.default_rng(V * 3 + n)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V + 5)
+    dirn = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V + 5, sigma=0.05)
+    mask = torch.from_numpy(rng.random((n, V)) < 0.1)
+    mask[0, :64] = True
+    mask[n - 1] = False
+    mask[n - 2] = True
+    junk = torch.from_numpy(rng.choice([np.nan, np.inf, -np.inf, 3.0], (n, V))).to(torch.bfloat16)
+    zm = torch.where(mask, torch.tensor(float("-inf"), dtype=torch.bfloat16), z)
+    dm = torch.where(mask, junk, dirn)
+    alphas = [0.25, 1.0, -2.0]
+    ld = -(-V // 8) * 8
+    z_g, d_g = padded_bf16(zm, ld), padded_bf16(dm, ld)
+    kl_tok = torch.empty(len(alphas), n, device="cuda")
+    lg.predicted_kl_sweep(z_g, d_g, alphas, 1.0, kl_tok=kl_tok)
+    torch.cuda.synchronize()
+    ref = okl.kl_sweep_rows(synth.bf16_to_f64(zm), synth.bf16_to_f64(dm), alphas, 1.0)
+    got = kl_tok.cpu().numpy().astype(np.float64)
+    assert np.isnan(ref[:, n - 2]).all() and np.isnan(got[:, n - 2]).all()
+    keep = [t for t in range(n) if t != n - 2]
+    np.testing.assert_allclose(got[:, keep], ref[:, keep], rtol=1e-3, atol=1e-9)
+    # the means over the rows with a distribution
+    means = lg.predicted_kl_sweep(padded_bf16(zm[keep], ld), padded_bf16(dm[keep], ld), alphas,
+                                  1.0).cpu().numpy()
+    np.testing.assert_allclose(means, ref[:, keep].mean(axis=1), rtol=Q_TOL)
 
 
 def test_rollout_payload_apply_is_bitwise_the_trainer_merge(lg):
