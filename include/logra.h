@@ -483,7 +483,10 @@ size_t logra_kl_ws_bytes(int64_t n_tok, int64_t vocab);
  * the proposal's normaliser); one with finite z_cur and z_prop = -inf
  * (p > 0, p' = 0) makes KL_t = +inf.  A row with no finite z_cur, and NaN or
  * +inf logits, give a NaN KL_t.  Rows with a -inf logit take a second pass
- * over their data.
+ * over their data, and so do rows whose one-pass result would be a small
+ * difference of large terms (a proposal offset that the row's first 64
+ * tokens do not carry): that pass is centred on the p-weighted mean of
+ * z_prop - z_cur.
  *
  * z_cur, z_prop: device bf16[n_tok x ld], ld >= vocab, ld % 8 == 0, 16-B
  *     aligned.
@@ -524,7 +527,10 @@ size_t logra_kl_sweep_ws_bytes(int64_t n_tok, int32_t n_alpha);
  * stays masked in every proposal, whatever its delta entry (NaN and inf
  * included); a row with no finite z gives NaN, and so do NaN or +inf logits.
  * A non-finite delta at an unmasked token is not specified (NaN or +-inf).
- * Rows with a -inf logit take a second pass over their data.
+ * Rows with a -inf logit take a second pass over their data, and so do rows
+ * whose one-pass result would be a small difference of large terms (a
+ * direction offset that the row's first 64 tokens do not carry): that pass
+ * is centred on the p-weighted mean of delta.
  * Per element the cost does not depend on n_alpha: the multipliers enter
  * through weighted moments of delta (see kl_sweep.hip); the relative
  * truncation of that expansion is below 1.1e-5.

@@ -37,6 +37,10 @@
 // those with p > 0 and p' = 0, and takes the row reference from the tokens
 // where neither logit is -inf.  Rows of finite logits pay one check; NaN and
 // +inf logits still give NaN.
+// The reference itself is checked the same way: a row whose KL came out as
+// a small difference of large terms (the first 64 tokens missed an offset
+// the rest of the row carries) is read again about the p-weighted mean of
+// z' - z, which its state already holds (see amplified).
 #include <math.h>
 
 #include "common.hpp"
@@ -86,13 +90,20 @@ __device__ __forceinline__ float excess_exp(float d) {
 // excess, but when p' > 0 it still belongs to the proposal's normaliser:
 // with R = sum over such tokens of e^((z' - c)/tau) / sum_p>0 e^(z/tau),
 // KL = log(E_p[e^d] + R) - E_p[d], so R joins u3 (as 2^(b - m) with
-// b = (z' - c) log2e / tau, which also joins the running max).
+// b = (z' - c) log2e / tau, which also joins the running max).  The
+// `b_of` lambda below forms b.
 template <bool MASK>
 __device__ __forceinline__ void kl_group(KlState& st, bool& hit, const float* z,
                                          const float* zq, int n, float l2t,
                                          float inv_tau, float dref) {
-  float a2[8], dd[8], b2[8];
+  float a2[8], dd[8];
   float cmax = -INFINITY;
+  // b: the scaled proposed logit of a token with p = 0 and p' > 0 (-inf
+  // otherwise); formed again where it is added, rather than held in eight
+  // more registers
+  auto b_of = [&](int e) {
+    return e < n && z[e] == -INFINITY && zq[e] != -INFINITY ? (zq[e] - dref) * l2t : -INFINITY;
+  };
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     a2[e] = e < n ? z[e] * l2t : -INFINITY;
@@ -100,8 +111,7 @@ __device__ __forceinline__ void kl_group(KlState& st, bool& hit, const float* z,
       const bool pz = z[e] == -INFINITY, pq = zq[e] == -INFINITY;
       if (e < n && pq && !pz) hit = true;
       dd[e] = e < n && !pz && !pq ? ((zq[e] - z[e]) - dref) * inv_tau : 0.0f;
-      b2[e] = e < n && pz && !pq ? (zq[e] - dref) * l2t : -INFINITY;
-      cmax = fmaxf(cmax, b2[e]);
+      cmax = fmaxf(cmax, b_of(e));
     } else {
       dd[e] = e < n ? ((zq[e] - z[e]) - dref) * inv_tau : 0.0f;
     }
@@ -125,7 +135,8 @@ __device__ __forceinline__ void kl_group(KlState& st, bool& hit, const float* z,
       st.u3 = fmaf(w, excess_exp(dd[e]), st.u3);
     }
     if constexpr (MASK) {
-      if (b2[e] != -INFINITY) st.u3 += exp2_normal(b2[e] - st.m);
+      const float b = b_of(e);
+      if (b != -INFINITY) st.u3 += exp2_normal(b - st.m);
     }
   }
 }
@@ -163,12 +174,11 @@ __device__ __forceinline__ bool state_finite(const KlState& t) {
   return isfinite(t.s) && isfinite(t.u1) && isfinite(t.u3);
 }
 
-// One pass over a row: this thread's elements, then the wave's butterfly
-// (every lane ends with the wave's state).
+// One pass over a row with reference difference dref: this thread's
+// elements, then the wave's butterfly (every lane ends with the wave's state).
 template <bool MASK>
 __device__ __forceinline__ KlState kl_row_pass(const uint16_t* a, const uint16_t* b, int V,
-                                               float l2t, float inv_tau, bool& hit) {
-  const float dref = row_reference<MASK>(a, b, V);
+                                               float l2t, float inv_tau, float dref, bool& hit) {
   KlState st{-INFINITY, 0.0f, 0.0f, 0.0f};
   // logits are read once: non-temporal loads (5 % faster over 65536 x 152064)
   const int nfull = V >> 3;
@@ -208,7 +218,35 @@ __device__ __forceinline__ KlState kl_row_pass(const uint16_t* a, const uint16_t
   return st;
 }
 
-__global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
+// A row is read once more, re-centred, when its KL came out as a small
+// difference of large terms.  With the reference c near the p-weighted mean
+// of z' - z, E_p[g] is about the KL (both ~ Var_p(d) / 2 on small steps); an
+// offset of the proposal that the row's first 64 tokens do not share leaves
+// E_p[d] far from 0, E_p[g] ~ E_p[d^2] / 2 = (Var_p(d) + E_p[d]^2) / 2, and
+// the fp32 sums' rounding enlarged by E_p[g] / KL.  The pass is repeated
+// when that ratio exceeds 8, the KL estimated from the same state in fp32
+// (rough exactly when the ratio is large, which is all the test needs).  The
+// state already holds the fix: E_p[d] = u1 / s, so the next pass takes
+// c + tau u1 / s.
+__device__ __forceinline__ bool amplified(const KlState& t) {
+  const float e1 = t.u1 / t.s, g = t.u3 / t.s;
+  const float x = e1 + g;
+  return g > 8.0f * (g + (log1pf(x) - x));
+}
+
+// The four wave states merged in order; every thread that calls this gets
+// the same bits, so choices made on the result are work-group uniform.
+__device__ __forceinline__ KlState merged_state(const KlState* wst) {
+  KlState t = wst[0];
+#pragma unroll
+  for (int w = 1; w < kKlThreads / 64; ++w) t = kl_merge(t, wst[w]);
+  return t;
+}
+
+// (eight work-groups per CU, i.e. eight waves per SIMD: the one-pass loop
+// needs ~50 VGPRs, and the second pass, which would take ~70, spills a few
+// registers instead; measured ~3 % faster than seven waves per SIMD)
+__global__ __launch_bounds__(kKlThreads, 8) void kl_rows_kernel(
     const uint16_t* __restrict__ zc, const uint16_t* __restrict__ zp, int V,
     int64_t ld, float inv_tau, float* __restrict__ kl_out) {
   __shared__ KlState wst[kKlThreads / 64];
@@ -218,35 +256,44 @@ __global__ __launch_bounds__(kKlThreads) void kl_rows_kernel(
   const uint16_t* b = zp + row * ld;
   const float l2t = kLog2e * inv_tau;
   const int wave = threadIdx.x >> 6;
+  const bool lead = (threadIdx.x & 63) == 0;
   bool hit = false;
-  KlState st = kl_row_pass<false>(a, b, V, l2t, inv_tau, hit);
-  if ((threadIdx.x & 63) == 0) wst[wave] = st;
+  float dref = row_reference<false>(a, b, V);
+  KlState st = kl_row_pass<false>(a, b, V, l2t, inv_tau, dref, hit);
+  if (lead) wst[wave] = st;
   __syncthreads();
-  // every thread reads the four wave states, so the choice below is the
-  // same in the whole work-group
-  bool finite = true;
-#pragma unroll
-  for (int w = 0; w < kKlThreads / 64; ++w) finite = finite && state_finite(wst[w]);
-  if (!finite) {
-    __syncthreads();   // every thread has read wst
-    st = kl_row_pass<true>(a, b, V, l2t, inv_tau, hit);
+  KlState t = merged_state(wst);
+  // A second pass, always in masked mode (on finite data it does the plain
+  // pass's arithmetic): when the state is not finite (masked tokens or other
+  // non-finite data), and again, re-centred, when the result is a small
+  // difference of large terms.  One copy of the masked pass, in a loop that
+  // is not unrolled.
+  bool again = !state_finite(t);
+  if (again) {
+    dref = row_reference<true>(a, b, V);
+  } else if (t.s > 0.0f && amplified(t)) {
+    again = true;
+    dref = (float)((double)dref + (double)(t.u1 / t.s) / (double)inv_tau);
+  }
+  bool any_hit = false;
+#pragma nounroll
+  for (int k = 0; k < 2 && again; ++k) {
+    __syncthreads();   // every thread has read wst and whit
+    hit = false;
+    st = kl_row_pass<true>(a, b, V, l2t, inv_tau, dref, hit);
     const bool wave_hit = __ballot(hit) != 0ull;
-    if ((threadIdx.x & 63) == 0) {
+    if (lead) {
       wst[wave] = st;
       whit[wave] = wave_hit ? 1 : 0;
     }
     __syncthreads();
+    t = merged_state(wst);
+#pragma unroll
+    for (int w = 0; w < kKlThreads / 64; ++w) any_hit = any_hit || whit[w] != 0;
+    again = !any_hit && state_finite(t) && t.s > 0.0f && amplified(t);
+    if (again) dref = (float)((double)dref + (double)(t.u1 / t.s) / (double)inv_tau);
   }
-  // then the four waves in order
   if (threadIdx.x == 0) {
-    KlState t = wst[0];
-#pragma unroll
-    for (int w = 1; w < kKlThreads / 64; ++w) t = kl_merge(t, wst[w]);
-    bool any_hit = false;
-    if (!finite) {
-#pragma unroll
-      for (int w = 0; w < kKlThreads / 64; ++w) any_hit = any_hit || whit[w] != 0;
-    }
     const double s = t.s;
     const double x = ((double)t.u1 + (double)t.u3) / s;
     const double kl = any_hit ? (double)INFINITY : (double)t.u3 / s + (log1p(x) - x);

@@ -34,7 +34,10 @@
 // leave some sum of the state non-finite); a row whose merged state is not
 // finite is read a second time in masked mode, which skips those tokens and
 // takes the direction reference from the others.  Rows of finite inputs pay
-// one check.
+// one check.  The reference itself is checked the same way: a row whose KLs
+// may be a small difference of large terms (the first 64 tokens missed an
+// offset the rest of the row carries) is read again about the p-weighted
+// mean of the direction, which its state already holds (sw_amplified).
 // So an element costs the same ~20 VALU operations whatever the number of
 // multipliers (dl itself is never formed: each element's u = amax dl comes
 // from delta with one subtraction and one multiplication).  States merge by
@@ -200,13 +203,12 @@ __device__ __forceinline__ bool sw_finite(const SwState<NA>& t) {
   return f;
 }
 
-// One pass over a row: this thread's elements, then the wave's butterfly
-// (every lane ends with the wave's state).
+// One pass over a row with direction reference dref: this thread's
+// elements, then the wave's butterfly (every lane ends with the wave's state).
 template <bool MASK, int NA>
 __device__ __forceinline__ SwState<NA> sw_row_pass(const uint16_t* zr, const uint16_t* dr, int V,
                                                    float l2t, float su, float thr,
-                                                   const Multipliers& al) {
-  const float dref = direction_reference<MASK>(zr, dr, V);
+                                                   const Multipliers& al, float dref) {
   SwState<NA> st;
   st.m = -INFINITY;
   st.s = 0.0f;
@@ -247,9 +249,35 @@ __device__ __forceinline__ SwState<NA> sw_row_pass(const uint16_t* zr, const uin
   return st;
 }
 
+// A row is read once more, re-centred, when its KLs may have come out as a
+// small difference of large terms.  With the reference near the p-weighted
+// mean of the direction, g / s is about KL (both ~ alpha^2 Var_p(u) / 2 on
+// small steps); an offset that the row's first 64 tokens do not share leaves
+// E_p[u] far from 0 and the truncation and rounding of the sums enlarged by
+// E_p[u^2] / Var_p(u).  The pass is repeated when that ratio may exceed 8:
+// E_p[u]^2 > (7/8) E_p[u^2], taken as (u1/s)^2 > (7/8) M_2/s (M_2 holds
+// the series elements, nearly all of them on small steps; when many are off
+// the series this errs towards one more pass).  E_p[u] = u1 / s, so the next
+// pass takes dref + u1 / (s su).
+template <int NA>
+__device__ __forceinline__ bool sw_amplified(const SwState<NA>& t) {
+  const float e1 = t.u1 / t.s;
+  return e1 * e1 > 0.875f * (t.M[0] / t.s);
+}
+
+// The four wave states merged in order; every thread that calls this gets
+// the same bits, so choices made on the result are work-group uniform.
+template <int NA>
+__device__ __forceinline__ SwState<NA> sw_merged(const SwState<NA>* wst) {
+  SwState<NA> t = wst[0];
+#pragma unroll
+  for (int w = 1; w < kSwThreads / 64; ++w) t = sw_merge(t, wst[w]);
+  return t;
+}
+
 // One work-group per row: kl_out[i * n_tok + row] = KL_row(alpha_i).
 template <int NA>
-__global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
+__global__ __launch_bounds__(kSwThreads, 8) void kl_sweep_rows_kernel(
     const uint16_t* __restrict__ z, const uint16_t* __restrict__ dz, int V, int64_t ld,
     int n_tok, int na, Multipliers al, float inv_tau, float su, float thr,
     float* __restrict__ kl_out) {
@@ -259,25 +287,36 @@ __global__ __launch_bounds__(kSwThreads) void kl_sweep_rows_kernel(
   const uint16_t* dr = dz + row * ld;
   const float l2t = kSwLog2e * inv_tau;
   const int wave = threadIdx.x >> 6;
-  SwState<NA> st = sw_row_pass<false, NA>(zr, dr, V, l2t, su, thr, al);
-  if ((threadIdx.x & 63) == 0) wst[wave] = st;
+  const bool lead = (threadIdx.x & 63) == 0;
+  float dref = direction_reference<false>(zr, dr, V);
+  SwState<NA> st = sw_row_pass<false, NA>(zr, dr, V, l2t, su, thr, al, dref);
+  if (lead) wst[wave] = st;
   __syncthreads();
-  // every thread reads the four wave states, so the choice is the same in
-  // the whole work-group
-  bool finite = true;
-#pragma unroll
-  for (int w = 0; w < kSwThreads / 64; ++w) finite = finite && sw_finite(wst[w]);
-  if (!finite) {
-    __syncthreads();   // every thread has read wst
-    st = sw_row_pass<true, NA>(zr, dr, V, l2t, su, thr, al);
-    if ((threadIdx.x & 63) == 0) wst[wave] = st;
-    __syncthreads();
+  SwState<NA> t = sw_merged(wst);
+  // A second pass, always in masked mode (on finite data it does the plain
+  // pass's arithmetic): when the state is not finite (masked tokens or other
+  // non-finite data), and again, re-centred, when the KLs may be a small
+  // difference of large terms.  One copy of the masked pass, in a loop that
+  // is not unrolled.
+  bool again = !sw_finite(t);
+  if (again) {
+    dref = direction_reference<true>(zr, dr, V);
+  } else if (t.s > 0.0f && sw_amplified(t)) {
+    again = true;
+    dref = (float)((double)dref + (double)(t.u1 / t.s) / (double)su);
   }
-  // then the four waves in order
+#pragma nounroll
+  for (int k = 0; k < 2 && again; ++k) {
+    __syncthreads();   // every thread has read wst
+    st = sw_row_pass<true, NA>(zr, dr, V, l2t, su, thr, al, dref);
+    if (lead) wst[wave] = st;
+    __syncthreads();
+    t = sw_merged(wst);
+    again = k == 0 && sw_finite(t) && t.s > 0.0f && sw_amplified(t);
+    if (again) dref = (float)((double)dref + (double)(t.u1 / t.s) / (double)su);
+  }
+  // then the multipliers' KLs (fp64)
   if (threadIdx.x == 0) {
-    SwState<NA> t = wst[0];
-#pragma unroll
-    for (int w = 1; w < kSwThreads / 64; ++w) t = sw_merge(t, wst[w]);
     const double s = t.s;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {

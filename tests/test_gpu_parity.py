@@ -727,6 +727,28 @@ def test_kl_controller_edges(lg):
     assert np.isnan(q) and np.isnan(a)
 
 
+@pytest.mark.parametrize("n,V,offset", [(6, 152064, 0.75), (6, 152064, -3.0), (16, 4099, 2.0)])
+def test_predicted_kl_offset_missed_by_the_row_reference(lg, n, V, offset):
+    # the proposal carries a per-row offset everywhere except on the row's
+    # first 64 tokens, where the reference is taken: the one-pass result is a
+    # small difference of large terms, and the row is read again about the
+    # p-weighted mean of z' - z.  Bar 1e-4 (ten times below the parity bar)
+    say("kl offset past the reference", n, V, offset)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V + 11)
+    noise = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V + 11, sigma=0.01)
+    shift = torch.linspace(-0.25, 0.25, n).view(n, 1) + offset
+    shift = shift.expand(n, V).clone()
+    shift[:, :64] = 0.0
+    zp = (z.float() + shift + noise.float()).to(torch.bfloat16)
+    ld = -(-V // 8) * 8
+    kl_tok = torch.empty(n, device="cuda")
+    out = lg.predicted_kl(padded_bf16(z, ld), padded_bf16(zp, ld), 1.0, 2e-4, 4.0, kl_tok=kl_tok)
+    torch.cuda.synchronize()
+    ref_rows = okl.kl_rows(synth.bf16_to_f64(z), synth.bf16_to_f64(zp), 1.0)
+    np.testing.assert_allclose(kl_tok.cpu().numpy(), ref_rows, rtol=1e-4, atol=1e-9)
+    assert abs(out[0].item() / ref_rows.mean() - 1) < Q_TOL
+
+
 @pytest.mark.parametrize("n,V", [(12, 4099), (6, 152064)])
 def test_predicted_kl_masked_vocabulary(lg, n, V):
     # logits of -inf: tokens of probability zero.  Rows 0 .. n-5 masked at the
@@ -840,6 +862,31 @@ def test_kl_sweep_alpha_squared_law_and_edges(lg):
     shift = torch.full((n, V), 0.75, dtype=torch.bfloat16, device="cuda")
     flat = lg.predicted_kl_sweep(z_g, shift, [1.0, 4.0], 1.0).cpu().numpy()
     assert np.all(np.abs(flat) < 1e-6)
+
+
+@pytest.mark.parametrize("n,V,offset,spread", [(6, 152064, 0.45, 0.025), (8, 4099, -0.35, 0.01),
+                                               (4, 32000, 3.0, 0.05)])
+def test_predicted_kl_sweep_offset_missed_by_the_direction_reference(lg, n, V, offset, spread):
+    # the direction carries an offset everywhere except on the row's first 64
+    # tokens, where the reference is taken (at alpha = 2 the first two cases
+    # put max|alpha| |delta| near the series bound with a narrow spread, the
+    # third puts it far past it): the row is read again about the p-weighted
+    # mean of the direction.  Bar 1e-4 (ten times below the parity bar)
+    say("kl sweep offset past the reference", n, V, offset, spread)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V + 13)
+    base = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V + 13, sigma=spread)
+    off = torch.full((n, V), offset) + torch.linspace(0, 0.05, n).view(n, 1)
+    off[:, :64] = 0.0
+    dirn = (base.float() + off).to(torch.bfloat16)
+    alphas = [0.25, 0.5, 1.0, 2.0]
+    ld = -(-V // 8) * 8
+    kl_tok = torch.empty(len(alphas), n, device="cuda")
+    out = lg.predicted_kl_sweep(padded_bf16(z, ld), padded_bf16(dirn, ld), alphas, 1.0,
+                                kl_tok=kl_tok)
+    torch.cuda.synchronize()
+    ref_rows = okl.kl_sweep_rows(synth.bf16_to_f64(z), synth.bf16_to_f64(dirn), alphas, 1.0)
+    np.testing.assert_allclose(kl_tok.cpu().numpy(), ref_rows, rtol=1e-4, atol=1e-9)
+    np.testing.assert_allclose(out.cpu().numpy(), ref_rows.mean(axis=1), rtol=Q_TOL)
 
 
 @pytest.mark.parametrize("n,V", [(8, 4099), (4, 152064)])
