@@ -92,21 +92,31 @@ def _excess_f32(d):
     return g
 
 
-def _one_pass_kl(z, zp, tau, reference):
-    """Per-row KL from the kernels' fp32 state (s, u1, u3), finalised in fp64:
-    KL = u3/s + log1p(x) - x with x = (u1 + u3)/s.  With `reference`, d is
-    taken relative to the mean of z' - z over the row's first 64 elements."""
+def _one_pass_state(z, zp, tau, dref):
+    """The kernels' fp32 state (s, u1, u3) with d = (z' - z - dref) / tau."""
     a = (z / tau).astype(np.float32)
     raw = (zp - z).astype(np.float32)
-    if reference:
-        n = min(64, z.shape[1])
-        dref = (raw[:, :n].sum(axis=1, dtype=np.float32) / np.float32(n)).astype(np.float32)
+    if dref is not None:
         raw = (raw - dref[:, None]).astype(np.float32)
     d = (raw * np.float32(1.0 / tau)).astype(np.float32)
     w = np.exp(a - a.max(axis=1, keepdims=True)).astype(np.float32)
     s = _lane_sums(w).astype(np.float64)
     u1 = _lane_sums(w * d).astype(np.float64)
     u3 = _lane_sums(w * _excess_f32(d)).astype(np.float64)
+    return s, u1, u3
+
+
+def _first64_reference(z, zp):
+    raw = (zp - z).astype(np.float32)
+    n = min(64, z.shape[1])
+    return (raw[:, :n].sum(axis=1, dtype=np.float32) / np.float32(n)).astype(np.float32)
+
+
+def _one_pass_kl(z, zp, tau, reference):
+    """Per-row KL from the kernels' fp32 state (s, u1, u3), finalised in fp64:
+    KL = u3/s + log1p(x) - x with x = (u1 + u3)/s.  With `reference`, d is
+    taken relative to the mean of z' - z over the row's first 64 elements."""
+    s, u1, u3 = _one_pass_state(z, zp, tau, _first64_reference(z, zp) if reference else None)
     x = (u1 + u3) / s
     return u3 / s + np.log1p(x) - x
 
@@ -211,3 +221,34 @@ def test_kl_sweep_series_truncation():
     # to 2): the series and the exact sums agree to rounding
     delta = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.DIR_ID, salt=9, sigma=0.05))
     assert err(delta, 7) < 1e-7, err(delta, 7)
+
+
+def test_predicted_kl_recentres_an_offset_the_first_64_tokens_miss():
+    # the proposal's offset is carried by every token but the first 64: the
+    # first-64 reference leaves E_p[d] ~ the offset, and the one-pass state's
+    # KL is a small difference of large terms; the kernels see it in the
+    # state (E_p[g] over eight times the KL) and read the row again about
+    # E_p[d] = u1 / s, which brings the result back inside the bar
+    n, V, tau = 8, 152064, 1.0
+    z = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.Z_ID, salt=7, sigma=3.0))
+    noise = synth.bf16_to_f64(synth.host_normal_bf16((n, V), synth.DIR_ID, salt=7, sigma=0.01))
+    off = np.full((n, V), 0.75)
+    off[:, :64] = 0.0
+    zp = obf16.round_f64(z + off + noise)
+    ref = okl.kl_rows(z, zp, tau)
+
+    def finish(state):
+        s, u1, u3 = state
+        x = (u1 + u3) / s
+        return u3 / s + np.log1p(x) - x, u1 / s, u3 / s
+
+    c0 = _first64_reference(z, zp)
+    kl0, e1, g = finish(_one_pass_state(z, zp, tau, c0))
+    first = float(np.max(np.abs(kl0 - ref) / ref))
+    assert first > KL_TOL, first                      # fails the tolerance
+    assert np.all(g > 8 * kl0)                        # the kernels' trigger
+    c1 = (c0.astype(np.float64) + e1 * tau).astype(np.float32)
+    kl1, _, g1 = finish(_one_pass_state(z, zp, tau, c1))
+    second = float(np.max(np.abs(kl1 - ref) / ref))
+    assert second < KL_TOL / 50, second
+    assert np.all(g1 < 8 * kl1)                       # no third pass
