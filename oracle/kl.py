@@ -74,7 +74,8 @@ def step_size(q, kl_budget, alpha_max):
 # rounding to bf16), so the alpha^2 law holds on the inputs as given.
 # Readings: the weighted mean uses non-negative per-row weights (None means
 # equal weights); a token mask or per-response averaging is a choice of
-# weights.  A zero weight sum gives NaN.
+# weights, and a row of weight zero is left out whatever its KL.  A zero
+# weight sum gives NaN.
 
 def kl_sweep_rows(z, delta, alphas, tau):
     """(n_alpha, n_tok) array: row t, multiplier a -> KL(p(z_t) || p(z_t + a delta_t)).
@@ -89,7 +90,9 @@ def kl_sweep_rows(z, delta, alphas, tau):
 
 
 def predicted_kl_sweep(z, delta, alphas, tau, weights=None):
-    """Weighted mean over rows of kl_sweep_rows, one value per multiplier."""
+    """Weighted mean over rows of kl_sweep_rows, one value per multiplier.  A
+    row of weight zero is left out whatever its KL (a masked position, e.g.
+    padding past a response's end, may have no distribution at all)."""
     rows = kl_sweep_rows(z, delta, alphas, tau)
     if weights is None:
         return rows.mean(axis=1)
@@ -97,4 +100,6 @@ def predicted_kl_sweep(z, delta, alphas, tau, weights=None):
     tot = w.sum()
     if tot == 0.0:
         return np.full(rows.shape[0], np.nan)
-    return (rows * w[None, :]).sum(axis=1) / tot
+    with np.errstate(invalid="ignore"):
+        terms = np.where(w[None, :] != 0.0, rows * w[None, :], 0.0)
+    return terms.sum(axis=1) / tot

@@ -349,6 +349,24 @@ def test_kl_sweep_masked_entries():
         np.testing.assert_allclose(got[:, t], sub, rtol=1e-12)
 
 
+def test_kl_sweep_zero_weight_rows_are_left_out():
+    # a token mask: rows of weight zero do not enter the mean, even when
+    # they have no distribution (every logit -inf: NaN KL)
+    rng = np.random.default_rng(33)
+    z = rng.standard_normal((5, 300)) * 3
+    delta = rng.standard_normal(z.shape) * 0.1
+    z[2] = -np.inf
+    w = np.array([1.0, 0.5, 0.0, 2.0, 0.0])
+    alphas = [0.5, 1.0]
+    got = kl.predicted_kl_sweep(z, delta, alphas, 1.0, w)
+    keep = w != 0
+    ref = kl.predicted_kl_sweep(z[keep], delta[keep], alphas, 1.0, w[keep])
+    np.testing.assert_allclose(got, ref, rtol=1e-14)
+    rows = kl.kl_sweep_rows(z, delta, alphas, 1.0)
+    assert np.isnan(rows[:, 2]).all()
+    np.testing.assert_allclose(got, (rows[:, keep] * w[keep]).sum(axis=1) / w.sum(), rtol=1e-14)
+
+
 def test_predicted_kl_scales_as_alpha_squared(golden):
     # Mean predicted KL ~ alpha^2 q(D): halving alpha quarters it.  Logits and
     # direction as in the controller workload (z ~ N(0, 3^2), delta ~ N(0, 0.05^2)),
