@@ -522,7 +522,9 @@ size_t logra_kl_sweep_ws_bytes(int64_t n_tok, int32_t n_alpha);
  *   KL_t(alpha_i) = KL(softmax(z[t] / tau) || softmax((z[t] + alpha_i delta[t]) / tau))
  * (forward KL), and kl_mean[i] = sum_t w_t KL_t(alpha_i) / sum_t w_t in fp64
  * (w_t = weight[t], or 1 when weight is NULL; a token mask or per-response
- * averaging is a choice of weights; a zero weight sum gives NaN).
+ * averaging is a choice of weights; a row of weight zero is left out whatever
+ * its KL_t, e.g. a padded position with every logit -inf; a zero weight sum
+ * gives NaN).
  * Masked tokens: a current logit of -inf is a token of probability zero and
  * stays masked in every proposal, whatever its delta entry (NaN and inf
  * included); a row with no finite z gives NaN, and so do NaN or +inf logits.

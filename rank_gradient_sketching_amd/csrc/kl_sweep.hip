@@ -338,7 +338,9 @@ __global__ __launch_bounds__(kSwThreads, 8) void kl_sweep_rows_kernel(
 }
 
 // kl_mean[i] = sum_t w_t KL_t(alpha_i) / sum_t w_t in fp64, in a fixed order
-// (equal weights when `weight` is null; a zero weight sum gives NaN).
+// (equal weights when `weight` is null; a zero weight sum gives NaN).  A row
+// of weight zero is left out whatever its KL: a masked position (padding
+// with every logit -inf, say) may have none.
 __global__ __launch_bounds__(1024) void kl_sweep_mean_kernel(const float* __restrict__ kl,
                                                              const float* __restrict__ weight,
                                                              int n, int na,
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(1024) void kl_sweep_mean_kernel(const float* __rest
     double acc = 0.0, wacc = 0.0;
     for (int t = threadIdx.x; t < n; t += 1024) {
       const double w = weight ? (double)weight[t] : 1.0;
-      acc += w * (double)row[t];
+      if (w != 0.0) acc += w * (double)row[t];
       wacc += w;
     }
 #pragma unroll

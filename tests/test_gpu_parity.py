@@ -889,6 +889,35 @@ def test_predicted_kl_sweep_offset_missed_by_the_direction_reference(lg, n, V, o
     np.testing.assert_allclose(out.cpu().numpy(), ref_rows.mean(axis=1), rtol=Q_TOL)
 
 
+@pytest.mark.parametrize("V", [1, 3, 65])
+def test_kl_masked_tiny_vocabularies(lg, V):
+    # vocabularies shorter than the reference window, with masked tokens
+    # (each row keeps at least one): both entry points against the oracle
+    n = 16
+    say("kl masked tiny", V)
+    rng = np.random.default_rng(V + 101)
+    z = synth.host_normal_bf16((n, V), synth.Z_ID, salt=V + 17)
+    dirn = synth.host_normal_bf16((n, V), synth.DIR_ID, salt=V + 17, sigma=0.3)
+    zp = synth.proposal_logits(z, dirn, 1.0)
+    mask = torch.from_numpy(rng.random((n, V)) < 0.3)
+    for t in range(n):
+        mask[t, t % V] = False          # every row keeps a token
+    ninf = torch.tensor(float("-inf"), dtype=torch.bfloat16)
+    zm = torch.where(mask, ninf, z)
+    zpm = torch.where(mask, ninf, zp)
+    dm = torch.where(mask, torch.tensor(float("nan"), dtype=torch.bfloat16), dirn)
+    ld = -(-V // 8) * 8
+    kl_tok = torch.empty(n, device="cuda")
+    lg.predicted_kl(padded_bf16(zm, ld), padded_bf16(zpm, ld), 1.0, 2e-4, 4.0, kl_tok=kl_tok)
+    sw_tok = torch.empty(2, n, device="cuda")
+    lg.predicted_kl_sweep(padded_bf16(zm, ld), padded_bf16(dm, ld), [0.5, 2.0], 1.0, kl_tok=sw_tok)
+    torch.cuda.synchronize()
+    ref = okl.kl_rows(synth.bf16_to_f64(zm), synth.bf16_to_f64(zpm), 1.0)
+    ref_sw = okl.kl_sweep_rows(synth.bf16_to_f64(zm), synth.bf16_to_f64(dm), [0.5, 2.0], 1.0)
+    np.testing.assert_allclose(kl_tok.cpu().numpy(), ref, rtol=1e-3, atol=1e-9)
+    np.testing.assert_allclose(sw_tok.cpu().numpy(), ref_sw, rtol=1e-3, atol=1e-9)
+
+
 @pytest.mark.parametrize("n,V", [(8, 4099), (4, 152064)])
 def test_predicted_kl_sweep_masked_vocabulary(lg, n, V):
     # masked tokens (z = -inf) stay masked in every proposal whatever their
@@ -921,6 +950,16 @@ def test_predicted_kl_sweep_masked_vocabulary(lg, n, V):
     means = lg.predicted_kl_sweep(padded_bf16(zm[keep], ld), padded_bf16(dm[keep], ld), alphas,
                                   1.0).cpu().numpy()
     np.testing.assert_allclose(means, ref[:, keep].mean(axis=1), rtol=Q_TOL)
+    # the same through a token mask: the fully masked row has weight zero and
+    # is left out (its NaN does not reach the mean)
+    w = np.ones(n)
+    w[n - 2] = 0.0
+    w[1] = 0.5
+    means_w = lg.predicted_kl_sweep(z_g, d_g, alphas, 1.0,
+                                    weight=torch.tensor(w, dtype=torch.float32, device="cuda"))
+    ref_w = okl.predicted_kl_sweep(synth.bf16_to_f64(zm), synth.bf16_to_f64(dm), alphas, 1.0, w)
+    assert np.isfinite(ref_w).all()
+    np.testing.assert_allclose(means_w.cpu().numpy(), ref_w, rtol=Q_TOL)
 
 
 def test_rollout_payload_apply_is_bitwise_the_trainer_merge(lg):
