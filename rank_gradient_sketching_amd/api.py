@@ -50,6 +50,18 @@ def _require(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
 
 
+def _ws(ws, name="ws"):
+    """(device address, bytes) of a caller's workspace: a contiguous GPU tensor
+    (a host tensor's address would reach the kernels)."""
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if ws.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {ws.device})")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
 def _rows(t, name):
     """(rows, cols, row stride) of a 2-D tensor whose rows are contiguous."""
     if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
@@ -131,8 +143,7 @@ def sketch_accumulate(X, dY, S, seed, stream=0, kind=RADEMACHER, ws=None, overwr
         ws = sketch_workspace(T, d, k, r, X.device)
     st = _lib.lib().logra_sketch_accumulate(
         X.data_ptr(), ldx, dY.data_ptr(), ldd, T, d, k, r, seed, stream, kind,
-        _sketch_flags(overwrite, defer, pending), S.data_ptr(), ws.data_ptr(),
-        ws.numel() * ws.element_size(), _stream(X))
+        _sketch_flags(overwrite, defer, pending), S.data_ptr(), *_ws(ws), _stream(X))
     _lib.check(st, "logra_sketch_accumulate")
     return S
 
@@ -180,7 +191,7 @@ def sketch_accumulate_shared(X, dYs, Ss, seed, stream=0, kind=RADEMACHER, ws=Non
         X.data_ptr(), ldx, T, k, r, seed, stream, kind, _sketch_flags(overwrite, defer, pending), n,
         (ctypes.c_void_p * n)(*ptr_dy),
         (ctypes.c_int64 * n)(*ldds), (ctypes.c_int64 * n)(*ds), (ctypes.c_void_p * n)(*ptr_s),
-        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(X))
+        *_ws(ws), _stream(X))
     _lib.check(st, "logra_sketch_accumulate_shared")
     return list(Ss)
 
@@ -204,10 +215,12 @@ def sketch_project(X, seed, r, stream=0, kind=RADEMACHER, P=None, ws=None):
     if P is None:
         P = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
     _require(P, "P", torch.uint8, 1)
+    if not P.is_contiguous():
+        raise ValueError("P must be a contiguous uint8 buffer")
     if kind == GAUSSIAN and ws is None:
         ws = torch.empty(max(sketch_project_ws_bytes(k, r), 256), dtype=torch.uint8,
                          device=X.device)
-    ws_ptr, ws_n = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+    ws_ptr, ws_n = _ws(ws) if ws is not None else (None, 0)
     st = _lib.lib().logra_sketch_project(X.data_ptr(), ldx, T, k, r, seed, stream, kind,
                                          P.data_ptr(), P.numel(), ws_ptr, ws_n, _stream(X))
     _lib.check(st, "logra_sketch_project")
@@ -227,6 +240,8 @@ def sketch_accumulate_p(P, dYs, Ss, ws=None, overwrite=False, defer=False, pendi
     pending as in sketch_accumulate; a deferred chain keeps ws and the
     outputs and may take a different P in every call."""
     _require(P, "P", torch.uint8, 1)
+    if not P.is_contiguous():
+        raise ValueError("P must be a contiguous uint8 buffer")
     if isinstance(dYs, torch.Tensor):
         dYs, Ss = [dYs], [Ss]
     if not 1 <= len(dYs) <= MAX_SHARED or len(dYs) != len(Ss):
@@ -256,7 +271,7 @@ def sketch_accumulate_p(P, dYs, Ss, ws=None, overwrite=False, defer=False, pendi
     st = _lib.lib().logra_sketch_accumulate_p(
         P.data_ptr(), P.numel(), T, r, _sketch_flags(overwrite, defer, pending), n,
         (ctypes.c_void_p * n)(*ptr_dy), (ctypes.c_int64 * n)(*ldds), (ctypes.c_int64 * n)(*ds),
-        (ctypes.c_void_p * n)(*ptr_s), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(P))
+        (ctypes.c_void_p * n)(*ptr_s), *_ws(ws), _stream(P))
     _lib.check(st, "logra_sketch_accumulate_p")
     return list(Ss)
 
@@ -330,8 +345,8 @@ def sketch_accumulate_layer(groups, kind=RADEMACHER, ws=None, overwrite=False, d
         ws = sketch_layer_workspace(T, r, [(g[0].shape[1], [dy.shape[1] for dy in g[1]])
                                            for g in groups], X0.device)
     st = _lib.lib().logra_sketch_accumulate_layer(
-        T, r, kind, _sketch_flags(overwrite, defer, pending), len(groups), arr, ws.data_ptr(),
-        ws.numel() * ws.element_size(), _stream(X0))
+        T, r, kind, _sketch_flags(overwrite, defer, pending), len(groups), arr, *_ws(ws),
+        _stream(X0))
     _lib.check(st, "logra_sketch_accumulate_layer")
 
 
@@ -434,7 +449,7 @@ def predicted_kl(z_cur, z_prop, tau, kl_budget, alpha_max, out=None, kl_tok=None
     if kl_tok is None:
         if ws is None:
             ws = torch.empty(max(kl_ws_bytes(n, V), 256), dtype=torch.uint8, device=z_cur.device)
-        ws_ptr, ws_n = ws.data_ptr(), ws.numel() * ws.element_size()
+        ws_ptr, ws_n = _ws(ws)
     st = _lib.lib().logra_predicted_kl(z_cur.data_ptr(), z_prop.data_ptr(), n, V, ld,
                                        float(tau), float(kl_budget), float(alpha_max),
                                        out.data_ptr(), kl_ptr, ws_ptr, ws_n, _stream(z_cur))
@@ -481,7 +496,7 @@ def predicted_kl_sweep(z, delta, alphas, tau, weight=None, out=None, kl_tok=None
         if ws is None:
             ws = torch.empty(max(kl_sweep_ws_bytes(n, len(al)), 256), dtype=torch.uint8,
                              device=z.device)
-        ws_ptr, ws_n = ws.data_ptr(), ws.numel() * ws.element_size()
+        ws_ptr, ws_n = _ws(ws)
     st = _lib.lib().logra_predicted_kl_sweep(z.data_ptr(), delta.data_ptr(), n, V, ld, c_al,
                                              len(al), float(tau), w_ptr, out.data_ptr(), kl_ptr,
                                              ws_ptr, ws_n, _stream(z))

@@ -469,6 +469,32 @@ def test_sketch_deterministic(lg):
     np.testing.assert_array_equal(outs[0], outs[2])
 
 
+def test_binding_refuses_host_and_strided_buffers(lg):
+    # a workspace or P that is not one contiguous block of device memory is
+    # refused before anything reaches the library (a host address would
+    # reach the kernels)
+    say("binding buffer checks")
+    T, d, k, r = 64, 128, 256, 16
+    X = synth.host_normal_bf16((T, k), synth.X_ID, salt=3).cuda()
+    dY = synth.host_normal_bf16((T, d), synth.DY_ID, salt=3).cuda()
+    S = torch.zeros(d, r, device="cuda")
+    n = lg.sketch_ws_bytes(T, d, k, r)
+    for ws in (torch.empty(n, dtype=torch.uint8),                        # host memory
+               torch.empty(2 * n, dtype=torch.uint8, device="cuda")[::2]):  # strided
+        with pytest.raises(ValueError):
+            lg.sketch_accumulate(X, dY, S, 1, ws=ws)
+    with pytest.raises(ValueError):
+        lg.sketch_project(X, 1, r, P=torch.empty(2 * lg.sketch_p_bytes(T, r), dtype=torch.uint8,
+                                                 device="cuda")[::2])
+    z = synth.host_normal_bf16((4, 512), synth.Z_ID, salt=3).cuda()
+    with pytest.raises(ValueError):
+        lg.predicted_kl(z, z, 1.0, 2e-4, 4.0, ws=torch.empty(4096, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        lg.predicted_kl_sweep(z, z, [1.0], 1.0, ws=torch.empty(4096, dtype=torch.uint8))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S).item() == 0          # nothing ran
+
+
 def test_sketch_zero_tokens_is_noop(lg):
     S = torch.ones(16, 4, device="cuda")
     X = torch.empty(0, 32, dtype=torch.bfloat16, device="cuda")
