@@ -124,14 +124,16 @@ def traffic(fetch_dir, write_dir, copy_bytes):
 
 
 MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU")
+STALL_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU")
 
 
-def mfma_table(run_dir):
+def mfma_table(run_dir, counters=MFMA_COUNTERS):
     """[(kernel, grid, dispatches, {counter: median per dispatch})] of the library's kernels."""
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
     for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
-            if "logra" not in r["Kernel_Name"] or r["Counter_Name"] not in MFMA_COUNTERS:
+            if "logra" not in r["Kernel_Name"] or r["Counter_Name"] not in counters:
                 continue
             key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
             vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
@@ -161,7 +163,38 @@ def main():
     m.add_argument("--out", required=True)
     m.add_argument("--cmd", required=True)
     m.add_argument("--title", default="Matrix-core and VALU counters")
+    w = sub.add_parser("stalls")
+    w.add_argument("pmc_dir")
+    w.add_argument("--out", required=True)
+    w.add_argument("--cmd", required=True)
+    w.add_argument("--title", default="Where the waves spend their cycles")
     a = ap.parse_args()
+    if a.cmd_name == "stalls":
+        lines = [f"# {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
+                 f"Kernel sources: `{kernel_source_hash()}`", "",
+                 "Per dispatch (median over dispatches of the same kernel and grid size). "
+                 "Shares per wave are fractions of SQ_WAVE_CYCLES (the cycles the waves were "
+                 "alive): waiting for any instruction's operands or resources "
+                 "(SQ_WAIT_INST_ANY), issuing VALU, scalar, vector-memory and LDS instructions "
+                 "(SQ_ACTIVE_INST_*). VALU busy per SIMD = SQ_ACTIVE_INST_VALU / (4 SIMDs x "
+                 "SQ_BUSY_CU_CYCLES), the share of a SIMD's cycles in which some wave on it "
+                 "issued VALU work.", "",
+                 "| kernel | grid (threads) | dispatches | VALU instr | wait | VALU | scalar | "
+                 "vector memory | LDS | VALU busy per SIMD |",
+                 "|---|---|---|---|---|---|---|---|---|---|"]
+        for kn, grid, n, c in mfma_table(a.pmc_dir, STALL_COUNTERS):
+            wc = c.get("SQ_WAVE_CYCLES", 0.0)
+            busy = c.get("SQ_BUSY_CU_CYCLES", 0.0)
+
+            def share(name):
+                return f"{c.get(name, 0.0) / wc:.3f}" if wc else "-"
+            simd = f"{c.get('SQ_ACTIVE_INST_VALU', 0.0) / (4.0 * busy):.3f}" if busy else "-"
+            lines.append(f"| `{kn}` | {grid} | {n} | {c.get('SQ_INSTS_VALU', 0.0):.0f} | "
+                         f"{share('SQ_WAIT_INST_ANY')} | {share('SQ_ACTIVE_INST_VALU')} | "
+                         f"{share('SQ_ACTIVE_INST_SCA')} | {share('SQ_ACTIVE_INST_VMEM')} | "
+                         f"{share('SQ_ACTIVE_INST_LDS')} | {simd} |")
+        open(a.out, "w").write("\n".join(lines) + "\n")
+        return
     if a.cmd_name == "mfma":
         lines = [f"# {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
                  f"Kernel sources: `{kernel_source_hash()}`", "",
