@@ -7,8 +7,10 @@ one deferred chain: the first three calls keep their contributions in the
 workspace and the fourth writes S, so the split reduction runs once per step)
 and the rank-64 update is merged into the bf16 weights (logra_merge,
 alpha * eta = 2e-4).  Inputs are synthetic, seeded, generated on the GPU and
-resident in HBM before the timed region; the four microbatches (512 MiB) are
-streamed in turn, so nothing is re-read from the 256 MB Infinity Cache.
+resident in HBM before the timed region; consecutive steps take two
+different sets of four microbatches (1 GiB in all), so that no input is
+re-read from the 256 MB Infinity Cache (with one set, a step's dY was partly
+still there a step later: X is read non-temporally and does not displace it).
 
 Printed: one JSON line.  `value` is tokens sketched and merged per second for
 the whole step.  Extra objects report the sketch and merge bandwidth against
@@ -97,9 +99,16 @@ def run_layer(lg, synth, steps, warmup):
     cfg = synth.WORKLOADS[WORKLOAD]
     d, k, r, T, n_mb = cfg["d"], cfg["k"], cfg["r"], cfg["T"], cfg["n_mb"]
     seed, stream, kind, alpha, eta = cfg["seed"], cfg["stream"], cfg["kind"], cfg["alpha"], cfg["eta"]
-    log(f"[bench] generating {WORKLOAD}: {n_mb} x T={T}, d=k={d}, r={r}")
-    Xs = [synth.device_normal_bf16((T, k), synth.X_ID, WORKLOAD, mb) for mb in range(n_mb)]
-    dYs = [synth.device_normal_bf16((T, d), synth.DY_ID, WORKLOAD, mb) for mb in range(n_mb)]
+    # Two sets of the step's microbatches, used by alternate steps: X is read
+    # non-temporally and does not stay in the 256 MB Infinity Cache, so with
+    # one set the 4 x 64 MiB of dY came back a step later partly from that
+    # cache (measured: 155 us per step with one set, 166 us with two or
+    # three); with two sets 448 MiB of other dY pass between two uses of a
+    # buffer.  Every step still sketches n_mb microbatches of T tokens.
+    n_sets = 2 * n_mb
+    log(f"[bench] generating {WORKLOAD}: {n_mb} x T={T}, d=k={d}, r={r} ({n_sets} buffer sets)")
+    Xs = [synth.device_normal_bf16((T, k), synth.X_ID, WORKLOAD, mb) for mb in range(n_sets)]
+    dYs = [synth.device_normal_bf16((T, d), synth.DY_ID, WORKLOAD, mb) for mb in range(n_sets)]
     W0 = synth.device_normal_bf16((d, k), synth.W_ID, WORKLOAD)
     W = W0.clone()
     S = torch.zeros(d, r, device="cuda")
@@ -111,59 +120,67 @@ def run_layer(lg, synth, steps, warmup):
     log("[bench] parity step")
     S.fill_(float("nan"))
 
-    def sketch_chain():
-        # one deferred chain over the step's microbatches: S written by the last call
-        for mb, (X, dY) in enumerate(zip(Xs, dYs)):
+    def sketch_chain(half=0):
+        # one deferred chain over a step's microbatches (buffer set `half`):
+        # S written by the last call
+        for mb in range(n_mb):
             last = mb == n_mb - 1
+            X, dY = Xs[half * n_mb + mb], dYs[half * n_mb + mb]
             lg.sketch_accumulate(X, dY, S, seed, stream, kind, ws=ws, defer=not last,
                                  pending=mb > 0, overwrite=last)
 
-    sketch_chain()
+    sketch_chain(0)
     lg.merge(W, S, seed, stream, kind, alpha, eta)
     torch.cuda.synchronize()
-    parity = check_layer_parity(synth, Xs, dYs, W0, W, S, cfg)
+    parity = check_layer_parity(synth, Xs[:n_mb], dYs[:n_mb], W0, W, S, cfg)
     log(f"[bench] parity {parity}")
 
     # ---- timed steps: back to back, one event pair around all of them (an
-    # event recorded between calls would sit inside the step)
-    def one_step():
+    # event recorded between calls would sit inside the step); step i takes
+    # buffer set i % 2
+    def one_step(half):
         # the chain's last call stores S (overwrite): no separate zero fill
-        sketch_chain()
+        sketch_chain(half)
         lg.merge(W, S, seed, stream, kind, alpha, eta)
 
-    for _ in range(warmup):
-        one_step()
+    for i in range(warmup):
+        one_step(i % 2)
     torch.cuda.synchronize()
     log(f"[bench] timing {steps} steps")
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
-    for _ in range(steps):
-        one_step()
+    for i in range(steps):
+        one_step(i % 2)
     t1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - wall0) * 1e3
     total_ms = t0.elapsed_time(t1)
     step_ms = total_ms / steps
 
-    # the same step captured once in a HIP graph and replayed (no entry point
-    # allocates or records a memset, so the whole step captures); reported
-    # beside the eager figure, which is `value`
+    # the same steps captured once in a HIP graph and replayed (no entry point
+    # allocates or records a memset, so the whole step captures): two steps
+    # per graph, one on each buffer set; reported beside the eager figure,
+    # which is `value`
+    def two_steps():
+        one_step(0)
+        one_step(1)
+
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        one_step()
+        two_steps()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        one_step()
-    graph_step_ms = _time_ms(graph.replay, max(steps // 5, 4))
+        two_steps()
+    graph_step_ms = _time_ms(graph.replay, max(steps // 10, 4)) / 2
     del graph
 
     # ---- average duration of each entry point: the same calls back to back
-    # (sketches cycling over the microbatches, merges over copies of W), one
+    # (sketches cycling over both buffer sets, merges over copies of W), one
     # event pair around each batch, outside the timed steps
     reps = max(steps, 20)
 
@@ -179,10 +196,12 @@ def run_layer(lg, synth, steps, warmup):
 
     # five batches each; the median batch mean is the figure, the minimum is
     # reported beside it
-    sk_b = [batch_us(lambda i: lg.sketch_accumulate(Xs[i % n_mb], dYs[i % n_mb], S, seed, stream,
-                                                    kind, ws=ws), reps * n_mb) for _ in range(5)]
-    # whole deferred chains back to back (per call: the chain's time / n_mb)
-    ch_b = [batch_us(lambda i: sketch_chain(), reps) / n_mb for _ in range(5)]
+    sk_b = [batch_us(lambda i: lg.sketch_accumulate(Xs[i % n_sets], dYs[i % n_sets], S, seed,
+                                                    stream, kind, ws=ws), reps * n_mb)
+            for _ in range(5)]
+    # whole deferred chains back to back, alternating buffer sets (per call:
+    # the chain's time / n_mb)
+    ch_b = [batch_us(lambda i: sketch_chain(i % 2), reps) / n_mb for _ in range(5)]
     # merges cycle over at least 16 copies of W, 512 MiB in all: twice the
     # 256 MB Infinity Cache, as inside a step (where W was last touched a
     # step earlier); one W repeated would be served from that cache
@@ -210,7 +229,7 @@ def run_layer(lg, synth, steps, warmup):
     res["sketch"]["frac_hbm"] = res["sketch"]["GBps"] / HBM_PEAK_GBPS
     res["chain"]["frac_hbm"] = res["chain"]["GBps"] / HBM_PEAK_GBPS
     res["merge"]["frac_hbm"] = res["merge"]["GBps"] / HBM_PEAK_GBPS
-    return res, (Xs, dYs, W0, cfg)
+    return res, (Xs[:n_mb], dYs[:n_mb], W0, cfg)
 
 
 def check_layer_parity(synth, Xs, dYs, W0, W, S, cfg):
@@ -915,7 +934,7 @@ def main():
                    "tokens_per_microbatch": cfg["T"], "microbatches": cfg["n_mb"],
                    "global_batch": cfg["T"] * cfg["n_mb"], "seq_len": None,
                    "alpha_eta": cfg["alpha"] * cfg["eta"], "projection": "rademacher",
-                   "parallelism": "single-gpu"},
+                   "buffer_sets": 2 * cfg["n_mb"], "parallelism": "single-gpu"},
         "sketch": {"tokens_per_s": sk["tokens_per_s"], "GBps": sk["GBps"],
                    "frac_hbm": sk["frac_hbm"], "us_per_call": sk["us_per_call"],
                    "us_per_call_min": sk["us_min"],
