@@ -302,10 +302,9 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
 }
 
 // The same copy with the non-temporal hint, for data read once (the layer
-// input X of the projection).  Measured on the headline sketch: X copies
-// non-temporal took the call from 41.3 to 38.2 us, most of it in the
-// accumulate launch that follows (whose dY loads stay temporal: marking both
-// streams non-temporal measured slower than marking neither).
+// input X of the projection).  Measured on the headline step with no input
+// re-read from the Infinity Cache: temporal X copies made the step ~2 %
+// slower (166.8 -> 170 us) and a lone call ~2 % slower.
 __device__ __forceinline__ void lds_dma16_nt(const void* src, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(

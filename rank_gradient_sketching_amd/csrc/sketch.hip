@@ -629,6 +629,12 @@ struct DyStage {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data (gfx9)
+// Cache policy of the dY loads: non-temporal (the nt bit).  dY is read once
+// per call; measured with no input re-read from the Infinity Cache (a step
+// takes other buffers than the step before): the d = k = 4096 step 166.8 ->
+// 162.8 us, the 1.5B-shaped layer calls 5-6 % (r = 16) and 1.5-3 % (r = 64)
+// faster, a lone call without a chain ~2 % slower.
+constexpr int kNonTemporal = 2;
 
 // The lane's fixed part of the offset: row 8 g4 of the step, column col
 // (the row's first group when col is past d).
@@ -654,15 +660,15 @@ __device__ __forceinline__ void load_dy_stage(const uint16_t* __restrict__ dY,
     const int so = (int)((uint32_t)e * (uint32_t)ldd * 2u);
     uint32_t v[Q / 2];
     if constexpr (Q == 8) {
-      const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, 0);
+      const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNonTemporal);
 #pragma unroll
       for (int u = 0; u < 4; ++u) v[u] = (uint32_t)x[u];
     } else if constexpr (Q == 4) {
-      const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, 0);
+      const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, kNonTemporal);
       v[0] = (uint32_t)x[0];
       v[1] = (uint32_t)x[1];
     } else {
-      v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0);
+      v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, kNonTemporal);
     }
 #pragma unroll
     for (int u = 0; u < Q / 2; ++u) st.R[e][u] = v[u];
